@@ -1,0 +1,194 @@
+/*
+ * kvq.h -- C ABI of libkvq: a quantized KV cache with fused single-query decode attention,
+ * implemented as hand-written HIP kernels for AMD Instinct MI355X (gfx950, CDNA4).
+ *
+ * The operations follow three pages:
+ *   [P1] chipfoundryservices.com, "KV Cache Quantization"
+ *   [P2] llmdaily.org, "KV-cache quantization -- making long-context inference fit in memory"
+ *   [P3] oh-bug.com, "KV Cache Quantization in Practice: Managing Memory and Throughput for
+ *        Long-Context Inference"
+ * P1 "How KV Cache Quantization Works" gives the shape of the API: quantize keys and values
+ * after they are computed, store the quantized tensors, dequantize when attention needs them.
+ * P2 "How this connects to paging and prefix caching" requires that a cached block be read with
+ * its own quantization format and scales, so the format travels with every cache descriptor.
+ *
+ * Conventions for every call:
+ *   - All buffer pointers are DEVICE pointers owned by the caller (for example torch tensors);
+ *     the library allocates no device memory and keeps no per-cache state.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are asynchronous and
+ *     stream-ordered; only kvq_read_error() synchronises.
+ *   - Misuse that the host can see (null pointers, unsupported formats, misaligned buffers,
+ *     inconsistent sizes) returns a status before anything is launched.  Faults only the device
+ *     can see (a full cache, a block-table entry outside the pool) set bits in the caller's
+ *     device error word `err` (atomic OR), skip the offending sequence without advancing its
+ *     counters, and leave the other sequences' results intact.
+ *   - Reentrant for distinct caches; two calls that write the same cache must be ordered on one
+ *     stream.  No C++ exception crosses this boundary.
+ *
+ * Storage layout (a format of this library; all multi-byte values little-endian):
+ *   tile        16 consecutive compressed token slots of one (sequence, kv head).
+ *   tile index  contiguous: (b * H_kv + h) * (capacity / 16) + slot / 16
+ *               paged:      block_table[b][slot / 16] * H_kv + h     (a block holds 16 tokens)
+ *   K codes     row-major: byte (tile * 16 + slot % 16) * RB, RB = head_dim * bits / 8; channel c
+ *               of a row at bit c * bits (little-endian inside each byte).
+ *   V codes     token-interleaved inside each tile: the tile is (head_dim / 8) * 4 chunks of
+ *               4 * bits bytes; chunk (t / 4) * (head_dim / 8) + c / 8 holds channels
+ *               8 * (c / 8) .. + 7 of the tile rows 4 * (t / 4) .. + 3.  Inside a chunk, with
+ *               E = 32 / bits fields per 32-bit word and r = 2 * (c % 8) + (t % 4) / 2, element
+ *               (t, c) is field (r % (E/2)) + (E/2) * (t % 2) of word r / (E/2).
+ *   codes       offset binary: symmetric q in [-Q, Q] is stored as q + 2^(bits-1); asymmetric
+ *               codes are stored as they are (0 .. 2^bits - 1).
+ *   scales/zeros fp16.  Per-token groups: [tile][head_dim / group][16].  Per-channel key groups
+ *               (contiguous caches only): [b][h][capacity / group][head_dim].
+ *   window      bf16 [b][h][residual][head_dim].
+ *   counters    n_quant[b] compressed tokens, n_res[b] window tokens (int32, device).
+ */
+#ifndef KVQ_H_
+#define KVQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_EINVAL = 1,   /* null pointer, non-positive size, inconsistent descriptor */
+  KVQ_ENOTSUP = 2,  /* a combination this library does not implement (see each call) */
+  KVQ_EALIGN = 3,   /* a buffer pointer that is not 16-byte aligned */
+  KVQ_ENOSPACE = 4, /* workspace smaller than kvq_decode_workspace_bytes() */
+  KVQ_ELAUNCH = 5,  /* the HIP runtime refused a launch */
+  KVQ_EDEVICE = 6   /* kvq_read_error() found device error bits */
+} kvq_status;
+
+/* Quantization scheme of one side [P2, "From BF16 to INT8, INT4, or even fewer bits"]:
+ *   KVQ_SYM   s = max|x| / (2^(b-1) - 1), q = clip(round(x / s), -Q, Q), x^ = s q
+ *   KVQ_ASYM  min-max with a zero-point: s = (max - min) / (2^b - 1), z = min,
+ *             u = clip(round((x - z) / s), 0, 2^b - 1), x^ = s u + z
+ * round() is half away from zero; x / s is an IEEE fp32 division by the stored fp16 scale;
+ * the fp32 scale is rounded once to fp16 (nearest even).  A group whose scale is 0 stores
+ * code 0 (symmetric) or u = 0 (asymmetric). */
+enum { KVQ_SYM = 0, KVQ_ASYM = 1 };
+
+/* Grouping direction [P2, "Why scales and groups matter"; P3, "Why Can't You Quantize the KV
+ * Cache Like Ordinary Activations?"]: one scale (and zero-point) per group of `group` channels
+ * of one token, or, for keys only, per channel over `group` consecutive tokens. */
+enum { KVQ_PER_TOKEN = 0, KVQ_PER_CHANNEL = 1 };
+
+/* Device error bits. */
+enum {
+  KVQ_ERR_CAPACITY = 1, /* append: a contiguous sequence has no free compressed slot */
+  KVQ_ERR_BLOCK = 2,    /* a block-table entry outside [0, num_blocks) or beyond max_blocks */
+  KVQ_ERR_TOKENS = 4    /* decode: n_quant + n_res exceeded max_tokens (sequence skipped) */
+};
+
+/* Buffers of a cache, for kvq_buffer_bytes(). */
+enum {
+  KVQ_BUF_K_CODES = 0, KVQ_BUF_V_CODES = 1, KVQ_BUF_K_SCALE = 2, KVQ_BUF_V_SCALE = 3,
+  KVQ_BUF_K_ZERO = 4, KVQ_BUF_V_ZERO = 5, KVQ_BUF_K_RES = 6, KVQ_BUF_V_RES = 7
+};
+
+typedef struct {
+  int32_t bits;   /* 2, 4 or 8 */
+  int32_t scheme; /* KVQ_SYM or KVQ_ASYM */
+  int32_t axis;   /* KVQ_PER_TOKEN or KVQ_PER_CHANNEL (keys only) */
+  int32_t group;  /* PER_TOKEN: channels per group, 32, 64 or 128.
+                     PER_CHANNEL: tokens per group, 16, 32 or 64, dividing `residual`. */
+} kvq_side;
+
+typedef struct {
+  kvq_side k, v;
+  int32_t residual; /* BF16 window length R in tokens: 0 (none) or a multiple of 16, <= 256
+                       [P2, "Why some systems keep a full-precision window"] */
+  int32_t head_dim; /* 128 */
+} kvq_format;
+
+/* A batch cache.  Contiguous when block_table == NULL (capacity slots per sequence); paged
+ * otherwise [P2, "How this connects to paging and prefix caching"]: each sequence's
+ * compressed slots live in 16-token blocks of a shared pool, found through its row of the
+ * block table.  Blocks that a call writes must belong to that sequence alone. */
+typedef struct {
+  kvq_format fmt;
+  int32_t batch;      /* sequences B, 1 .. 4096 */
+  int32_t n_kv_heads; /* H_kv */
+  int32_t capacity;   /* contiguous: compressed slots per sequence, a multiple of 16 and of a
+                         per-channel key group; paged: 0 */
+  int32_t num_blocks; /* paged: blocks in the pool; contiguous: 0 */
+  int32_t max_blocks; /* paged: row length of block_table; contiguous: 0 */
+  const int32_t *block_table; /* paged: [batch][max_blocks] int32; contiguous: NULL */
+  uint8_t *k_codes, *v_codes;   /* sized by kvq_buffer_bytes(), 16-byte aligned */
+  uint16_t *k_scale, *v_scale;  /* fp16 bit patterns */
+  uint16_t *k_zero, *v_zero;    /* fp16 bit patterns; NULL for a KVQ_SYM side */
+  uint16_t *k_res, *v_res;      /* bf16 window; NULL when residual == 0 */
+  int32_t *n_quant, *n_res;     /* [batch] counters; zero for an empty cache */
+  int32_t *err;                 /* one int32 error word; the caller zero-initialises it */
+} kvq_cache;
+
+/* Bytes of buffer `which` (KVQ_BUF_*) for a contiguous cache (num_blocks == 0, `capacity`
+ * slots per sequence) or a paged pool of `num_blocks` blocks.  Returns 0 for a buffer the
+ * format does not use, or for an invalid format.  Pure host arithmetic. */
+size_t kvq_buffer_bytes(const kvq_format *fmt, int32_t batch, int32_t n_kv_heads,
+                        int32_t capacity, int32_t num_blocks, int32_t which);
+
+/* Check a format without a cache: KVQ_OK, KVQ_EINVAL or KVQ_ENOTSUP.  Supported: head_dim 128;
+ * bits 2/4/8, the same for K and V; per-token groups 32/64/128; per-channel grouping for keys
+ * only, with residual > 0 divisible by the group.  Pure host code. */
+kvq_status kvq_check_format(const kvq_format *fmt);
+
+/* Append n_new >= 1 new tokens to every sequence of the batch.
+ *   k_new, v_new: bf16 [batch][n_new][n_kv_heads][head_dim], device, 16-byte aligned.
+ * The result equals n_new single-token appends, each of which (P1 "How KV Cache Quantization
+ * Works": quantize after computation; P2 "Why some systems keep a full-precision window"):
+ *   - without a window, quantizes the token into compressed slot n_quant (n_quant += 1);
+ *   - with a window of R tokens, first flushes it if it already holds R tokens (quantizes the
+ *     R window rows into slots n_quant .. n_quant+R-1, n_quant += R, n_res = 0), then copies
+ *     the token into window row n_res (n_res += 1).
+ * After T appends to an empty sequence with R > 0: n_res = (T-1) mod R + 1.
+ * Paged caches: the block table must already map every slot the call may write.
+ * Device faults: KVQ_ERR_CAPACITY (contiguous slots exhausted), KVQ_ERR_BLOCK (a needed table
+ * entry is outside [0, num_blocks) or beyond max_blocks); the sequence is left unchanged.
+ * Launches two kernels on `stream`. */
+kvq_status kvq_quantize_append(const kvq_cache *cache, const void *k_new, const void *v_new,
+                               int32_t n_new, void *stream);
+
+/* Flush every sequence whose window holds exactly R tokens; other sequences are untouched.
+ * Optional: kvq_quantize_append() flushes by itself when a token finds the window full, and
+ * calling this first never changes any result.  No-op launch-free return when R == 0. */
+kvq_status kvq_flush_residual(const kvq_cache *cache, void *stream);
+
+/* Workspace bytes kvq_decode_attention() needs for n_q_heads and a host bound max_tokens on
+ * n_quant[b] + n_res[b] over the batch.  Pure host arithmetic. */
+size_t kvq_decode_workspace_bytes(const kvq_cache *cache, int32_t n_q_heads, int32_t max_tokens);
+
+/* Single-query decode attention [P2, "Why the KV cache grows so quickly", attention equation]:
+ * for each sequence b and query head hq, with kv head h = floor(hq * H_kv / H_q),
+ *   out[b][hq] = softmax(sm_scale * q[b][hq] . K^T) V
+ * over the dequantized compressed tokens 0 .. n_quant[b]-1 followed by the BF16 window rows
+ * 0 .. n_res[b]-1.  K and V are dequantized in registers as they stream from HBM (P3,
+ * "Misconception 1": the dequantization must be fused into the attention kernel).
+ *   q:   bf16 [batch][n_q_heads][head_dim], device; n_q_heads = G * n_kv_heads, G in 1,2,4,8
+ *   out: fp32 [batch][n_q_heads][head_dim], device; an empty sequence gets zeros
+ *   sm_scale: typically 1 / sqrt(head_dim)
+ *   max_tokens: host upper bound on n_quant[b] + n_res[b] (sizes the split over the sequence)
+ *   workspace: >= kvq_decode_workspace_bytes(cache, n_q_heads, max_tokens) bytes, device
+ * KVQ_ENOTSUP for a per-token key format with (head_dim / group) * G > 16.
+ * Device faults: KVQ_ERR_BLOCK (a table entry outside the pool: that tile is skipped).
+ * Launches two kernels on `stream`. */
+kvq_status kvq_decode_attention(const kvq_cache *cache, const void *q, int32_t n_q_heads,
+                                float sm_scale, int32_t max_tokens, float *out, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/* Synchronise `stream`, copy the device error word into *host_err and return KVQ_EDEVICE if
+ * any bit is set, KVQ_OK otherwise.  The word is not cleared. */
+kvq_status kvq_read_error(const kvq_cache *cache, int32_t *host_err, void *stream);
+
+/* A static string naming a status. */
+const char *kvq_status_str(kvq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H_ */

@@ -1,0 +1,335 @@
+// kvq_append.hip -- quantize-and-append and window flush kernels (gfx950).
+//
+// Quantizers [P2 = llmdaily.org "KV-cache quantization -- making long-context inference fit in
+// memory", section "From BF16 to INT8, INT4, or even fewer bits"]:
+//   symmetric   s = max|x| / (2^(b-1) - 1),  q = clip(round(x / s), -Q, Q)
+//   asymmetric  s = (max - min) / (2^b - 1), z = min, u = clip(round((x - z) / s), 0, 2^b - 1)
+// with the fp32 scale rounded once to fp16 (nearest even) and x / s an IEEE fp32 division by the
+// stored scale; round() is half away from zero.  Groups [P2, "Why scales and groups matter"]:
+// per token over `group` channels, or, for keys, per channel over `group` tokens [P3 =
+// oh-bug.com "KV Cache Quantization in Practice", "Why Can't You Quantize the KV Cache Like
+// Ordinary Activations?"].  The window [P2, "Why some systems keep a full-precision window"]:
+// new tokens enter a BF16 window of R rows; when a token finds it full, the R rows are
+// quantized into the compressed cache first.
+//
+// One call = two kernels on one stream:
+//   quantize_kernel  grid (segments, B * H_kv): every slot the call moves into the compressed
+//                    cache -- window rows and/or new rows -- is quantized into LDS, then packed
+//                    into the storage layout (K rows, token-interleaved V tiles, fp16 metadata).
+//                    A segment is 16 slots (one tile), or one per-channel key group.
+//   tail_kernel      grid (B): checks the whole slot range, copies the new window rows and only
+//                    then advances the counters, so a faulty sequence is left unchanged.
+#include "kvq_dev.h"
+
+#pragma clang fp contract(off)
+
+namespace kvq {
+
+// --- group quantizers; `get(i)` returns element i as fp32 (exact bf16 widening) --------------
+
+template <class Get>
+__device__ __forceinline__ void quant_sym(Get get, int n, int bits, uint16_t& s16out,
+                                          uint8_t* codes, int stride) {
+  const int Q = (1 << (bits - 1)) - 1;
+  float m = 0.0f;
+  for (int i = 0; i < n; i++) m = fmaxf(m, fabsf(get(i)));
+  const float s32 = m / static_cast<float>(Q);
+  const __half sh = __float2half_rn(s32);
+  const float sf = __half2float(sh);
+  for (int i = 0; i < n; i++) {
+    int q = 0;
+    if (sf != 0.0f) {
+      float r = roundf(get(i) / sf);
+      r = fminf(fmaxf(r, static_cast<float>(-Q)), static_cast<float>(Q));
+      q = static_cast<int>(r);
+    }
+    codes[i * stride] = static_cast<uint8_t>(q + (1 << (bits - 1)));
+  }
+  s16out = __half_as_ushort(sh);
+}
+
+template <class Get>
+__device__ __forceinline__ void quant_asym(Get get, int n, int bits, uint16_t& s16out,
+                                           uint16_t& z16out, uint8_t* codes, int stride) {
+  const int M = (1 << bits) - 1;
+  float lo = get(0), hi = lo;
+  for (int i = 1; i < n; i++) {
+    const float x = get(i);
+    lo = fminf(lo, x);
+    hi = fmaxf(hi, x);
+  }
+  const float range = hi - lo;
+  const float s32 = range / static_cast<float>(M);
+  const __half sh = __float2half_rn(s32);
+  const __half zh = __float2half_rn(lo);
+  const float sf = __half2float(sh), zf = __half2float(zh);
+  for (int i = 0; i < n; i++) {
+    int u = 0;
+    if (sf != 0.0f) {
+      const float diff = get(i) - zf;
+      float r = roundf(diff / sf);
+      r = fminf(fmaxf(r, 0.0f), static_cast<float>(M));
+      u = static_cast<int>(r);
+    }
+    codes[i * stride] = static_cast<uint8_t>(u);
+  }
+  s16out = __half_as_ushort(sh);
+  z16out = __half_as_ushort(zh);
+}
+
+// Row j of the slots this call moves into the compressed cache: the window rows first, then
+// the new rows.
+__device__ __forceinline__ const uint16_t* pending_row(const CacheDev& c, const uint16_t* fresh,
+                                                       int n_new, int b, int h, int j, int nr,
+                                                       bool key) {
+  if (j < nr) return (key ? c.kres : c.vres) + ((static_cast<size_t>(b) * c.H + h) * c.R + j) * D;
+  return fresh + ((static_cast<size_t>(b) * n_new + (j - nr)) * c.H + h) * D;
+}
+
+// Position (slot-in-tile t, channel ch) of field f of word q of a V tile (inverse of the layout).
+__device__ __forceinline__ void v_field_owner(int bits, int q, int f, int& t, int& ch) {
+  const int E = 32 / bits, Hh = E / 2;
+  const int chunk = q / bits, word = q % bits;
+  const int g = chunk / (D / 8), n = chunk % (D / 8);
+  const int k = f % Hh, half = f / Hh;
+  const int r = word * Hh + k;
+  const int jj = r / 2, p = r % 2;
+  t = 4 * g + 2 * p + half;
+  ch = 8 * n + jj;
+}
+
+template <int S>
+__global__ __launch_bounds__(256) void quantize_kernel(CacheDev c, const uint16_t* knew,
+                                                       const uint16_t* vnew, int n_new, int mode) {
+  __shared__ uint8_t lk[S][D];
+  __shared__ uint8_t lv[S][D];
+  __shared__ uint16_t mk_s[S * 4], mk_z[S * 4], mv_s[S * 4], mv_z[S * 4];
+  __shared__ uint16_t pc_s[D], pc_z[D];
+  __shared__ int s_ok;
+
+  const int tid = threadIdx.x;
+  const int b = blockIdx.y / c.H, h = blockIdx.y % c.H;
+  const int nq = c.n_quant[b];
+  int nr = c.R > 0 ? c.n_res[b] : 0;
+  if (nq < 0 || nr < 0 || nr > c.R) return;  // corrupt counters: reported by tail_kernel
+  int F, total, nra;
+  step_counts(mode, c.R, nr, n_new, F, total, nra);
+  if (F <= 0) return;
+  const int seg0 = (nq / S) * S + static_cast<int>(blockIdx.x) * S;
+  const int lo = max(seg0, nq), hi = min(seg0 + S, nq + F);
+  if (lo >= hi) return;
+  if (!c.table && nq + F > c.cap) return;  // reported by tail_kernel; nothing written
+  if (c.k.axis == KVQ_PER_CHANNEL && (lo != seg0 || hi != seg0 + S)) return;  // whole groups only
+  if (tid == 0) {
+    int ok = 1;
+    if (c.table)
+      for (int t = seg0 / TILE; t < (seg0 + S) / TILE; t++) {
+        bool tok = true;
+        (void)tile_index(c, b, h, t, tok);
+        if (!tok) ok = 0;
+      }
+    s_ok = ok;
+  }
+  __syncthreads();
+  if (!s_ok) return;
+
+  const SideDev K = c.k, V = c.v;
+  const int ngk = (K.axis == KVQ_PER_TOKEN) ? D / K.group : 0;
+  const int ngv = D / V.group;
+  const int nk_items = (K.axis == KVQ_PER_TOKEN) ? S * ngk : D;
+  const int nv_items = S * ngv;
+
+  // Phase 1: codes and metadata of this segment into LDS.
+  for (int it = tid; it < nk_items + nv_items; it += blockDim.x) {
+    if (it < nk_items) {
+      if (K.axis == KVQ_PER_TOKEN) {
+        const int j = it / ngk, g = it % ngk;
+        const int slot = seg0 + j;
+        if (slot < lo || slot >= hi) continue;
+        const uint16_t* row = pending_row(c, knew, n_new, b, h, slot - nq, nr, true) + g * K.group;
+        auto get = [&](int i) { return bf16_to_f32(row[i]); };
+        uint16_t s16 = 0, z16 = 0;
+        if (K.scheme == KVQ_SYM)
+          quant_sym(get, K.group, K.bits, s16, &lk[j][g * K.group], 1);
+        else
+          quant_asym(get, K.group, K.bits, s16, z16, &lk[j][g * K.group], 1);
+        mk_s[j * 4 + g] = s16;
+        mk_z[j * 4 + g] = z16;
+      } else {
+        // per-channel keys: the segment is exactly one group of S tokens (lo == seg0, hi ==
+        // seg0 + S: flushes move whole windows, R is a multiple of the group)
+        const int ch = it;
+        auto get = [&](int j) {
+          return bf16_to_f32(pending_row(c, knew, n_new, b, h, seg0 + j - nq, nr, true)[ch]);
+        };
+        uint16_t s16 = 0, z16 = 0;
+        if (K.scheme == KVQ_SYM)
+          quant_sym(get, S, K.bits, s16, &lk[0][ch], D);
+        else
+          quant_asym(get, S, K.bits, s16, z16, &lk[0][ch], D);
+        pc_s[ch] = s16;
+        pc_z[ch] = z16;
+      }
+    } else {
+      const int iv = it - nk_items;
+      const int j = iv / ngv, g = iv % ngv;
+      const int slot = seg0 + j;
+      if (slot < lo || slot >= hi) continue;
+      const uint16_t* row = pending_row(c, vnew, n_new, b, h, slot - nq, nr, false) + g * V.group;
+      auto get = [&](int i) { return bf16_to_f32(row[i]); };
+      uint16_t s16 = 0, z16 = 0;
+      if (V.scheme == KVQ_SYM)
+        quant_sym(get, V.group, V.bits, s16, &lv[j][g * V.group], 1);
+      else
+        quant_asym(get, V.group, V.bits, s16, z16, &lv[j][g * V.group], 1);
+      mv_s[j * 4 + g] = s16;
+      mv_z[j * 4 + g] = z16;
+    }
+  }
+  __syncthreads();
+
+  // Phase 2a: K rows, one 32-bit word per item.
+  {
+    const int E = 32 / K.bits, DW = D / E, RB = D * K.bits / 8;
+    const int n_items = (hi - lo) * DW;
+    for (int it = tid; it < n_items; it += blockDim.x) {
+      const int slot = lo + it / DW, w = it % DW;
+      bool ok = true;
+      const long tile = tile_index(c, b, h, slot / TILE, ok);
+      uint32_t word = 0;
+      for (int f = 0; f < E; f++)
+        word |= static_cast<uint32_t>(lk[slot - seg0][w * E + f]) << (f * K.bits);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(c.kc + (tile * TILE + slot % TILE) * RB) + w;
+      *dst = word;
+    }
+  }
+  // Phase 2b: V tiles, one 32-bit word per item; words shared with slots outside [lo, hi)
+  // keep those slots' bits (read-modify-write by the single owner of the tile).
+  {
+    const int E = 32 / V.bits;
+    const int words = (D / 8) * 4 * V.bits;  // per tile
+    const int t_first = seg0 / TILE, n_tiles = S / TILE;
+    const long tile_bytes = static_cast<long>(TILE) * D * V.bits / 8;
+    for (int it = tid; it < n_tiles * words; it += blockDim.x) {
+      const int tl = t_first + it / words, q = it % words;
+      const int base_slot = tl * TILE;
+      if (base_slot + TILE <= lo || base_slot >= hi) continue;
+      bool ok = true;
+      const long tile = tile_index(c, b, h, tl, ok);
+      uint32_t val = 0, mask = 0;
+      for (int f = 0; f < E; f++) {
+        int t, ch;
+        v_field_owner(V.bits, q, f, t, ch);
+        const int slot = base_slot + t;
+        if (slot >= lo && slot < hi) {
+          val |= static_cast<uint32_t>(lv[slot - seg0][ch]) << (f * V.bits);
+          mask |= ((1u << V.bits) - 1u) << (f * V.bits);
+        }
+      }
+      uint32_t* dst = reinterpret_cast<uint32_t*>(c.vc + tile * tile_bytes) + q;
+      if (mask != 0xFFFFFFFFu) val = (*dst & ~mask) | val;
+      *dst = val;
+    }
+  }
+  // Phase 2c: metadata.
+  if (K.axis == KVQ_PER_TOKEN) {
+    for (int it = tid; it < (hi - lo) * ngk; it += blockDim.x) {
+      const int slot = lo + it / ngk, g = it % ngk;
+      bool ok = true;
+      const long tile = tile_index(c, b, h, slot / TILE, ok);
+      const size_t idx = (static_cast<size_t>(tile) * ngk + g) * TILE + slot % TILE;
+      c.ks[idx] = mk_s[(slot - seg0) * 4 + g];
+      if (K.scheme == KVQ_ASYM) c.kz[idx] = mk_z[(slot - seg0) * 4 + g];
+    }
+  } else {
+    const int tau = seg0 / S;
+    for (int ch = tid; ch < D; ch += blockDim.x) {
+      const size_t idx = ((static_cast<size_t>(b) * c.H + h) * (c.cap / S) + tau) * D + ch;
+      c.ks[idx] = pc_s[ch];
+      if (K.scheme == KVQ_ASYM) c.kz[idx] = pc_z[ch];
+    }
+  }
+  for (int it = tid; it < (hi - lo) * ngv; it += blockDim.x) {
+    const int slot = lo + it / ngv, g = it % ngv;
+    bool ok = true;
+    const long tile = tile_index(c, b, h, slot / TILE, ok);
+    const size_t idx = (static_cast<size_t>(tile) * ngv + g) * TILE + slot % TILE;
+    c.vs[idx] = mv_s[(slot - seg0) * 4 + g];
+    if (V.scheme == KVQ_ASYM) c.vz[idx] = mv_z[(slot - seg0) * 4 + g];
+  }
+}
+
+__global__ __launch_bounds__(256) void tail_kernel(CacheDev c, const uint16_t* knew,
+                                                   const uint16_t* vnew, int n_new, int mode) {
+  __shared__ int s_bad;
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const int nq = c.n_quant[b];
+  const int nr = c.R > 0 ? c.n_res[b] : 0;
+  int F, total, nra;
+  step_counts(mode, c.R, nr, n_new, F, total, nra);
+  if (tid == 0) s_bad = (nq < 0 || nr < 0 || nr > c.R) ? KVQ_ERR_CAPACITY : 0;
+  __syncthreads();
+  if (F > 0 && !s_bad) {
+    if (!c.table) {
+      if (nq + F > c.cap && tid == 0) s_bad = KVQ_ERR_CAPACITY;
+    } else {
+      for (int t = nq / TILE + tid; t <= (nq + F - 1) / TILE; t += blockDim.x) {
+        bool ok = true;
+        (void)tile_index(c, b, 0, t, ok);
+        if (!ok) atomicOr(&s_bad, KVQ_ERR_BLOCK);
+      }
+    }
+  }
+  __syncthreads();
+  if (s_bad) {
+    if (tid == 0) atomicOr(c.err, s_bad);
+    return;
+  }
+  if (mode == MODE_APPEND && c.R > 0) {
+    // window rows j' in [max(0, nr - F), nra) receive new row F + j' - nr
+    const int j0 = max(0, nr - F);
+    const int rows = nra - j0;
+    const int per_row = D * 2 / 16;  // 16-byte pieces per bf16 row
+    const int n_items = 2 * c.H * rows * per_row;
+    for (int it = tid; it < n_items; it += blockDim.x) {
+      const int piece = it % per_row;
+      int rest = it / per_row;
+      const int jr = j0 + rest % rows;
+      rest /= rows;
+      const int h = rest % c.H;
+      const bool key = rest / c.H == 0;
+      const uint16_t* src = (key ? knew : vnew) +
+                            ((static_cast<size_t>(b) * n_new + (F + jr - nr)) * c.H + h) * D;
+      uint16_t* dst = (key ? c.kres : c.vres) + ((static_cast<size_t>(b) * c.H + h) * c.R + jr) * D;
+      reinterpret_cast<uint4*>(dst)[piece] = reinterpret_cast<const uint4*>(src)[piece];
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    c.n_quant[b] = nq + F;
+    c.n_res[b] = nra;
+  }
+}
+
+// Host-side launch of one append/flush call.
+hipError_t launch_append(const CacheDev& c, const uint16_t* knew, const uint16_t* vnew, int n_new,
+                         int mode, hipStream_t stream) {
+  const int S = (c.k.axis == KVQ_PER_CHANNEL) ? c.k.group : TILE;
+  // slots one call can move: at most n_new + R rounded down to a window multiple
+  const int f_max = (mode == MODE_FLUSH) ? c.R : (c.R == 0 ? n_new : n_new + c.R);
+  const int segs = (f_max + S - 1) / S + 1;
+  dim3 grid(segs, c.B * c.H);
+  switch (S) {
+    case 16: quantize_kernel<16><<<grid, 256, 0, stream>>>(c, knew, vnew, n_new, mode); break;
+    case 32: quantize_kernel<32><<<grid, 256, 0, stream>>>(c, knew, vnew, n_new, mode); break;
+    case 64: quantize_kernel<64><<<grid, 256, 0, stream>>>(c, knew, vnew, n_new, mode); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  tail_kernel<<<c.B, 256, 0, stream>>>(c, knew, vnew, n_new, mode);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

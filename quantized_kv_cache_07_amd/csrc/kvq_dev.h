@@ -1,0 +1,94 @@
+// kvq_dev.h -- device-side definitions shared by the HIP sources of libkvq (gfx950).
+//
+// The storage layout and the quantizer rules are the ones documented in include/kvq.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+constexpr int D = 128;    // head dimension
+constexpr int TILE = 16;  // compressed slots per tile (and tokens per paged block)
+
+struct SideDev {
+  int bits, scheme, axis, group;
+};
+
+// A cache descriptor as the kernels see it (passed by value).
+struct CacheDev {
+  SideDev k, v;
+  int R, B, H, cap, num_blocks, max_blocks;
+  const int32_t* table;  // nullptr: contiguous
+  uint8_t* kc;
+  uint8_t* vc;
+  uint16_t* ks;
+  uint16_t* vs;
+  uint16_t* kz;
+  uint16_t* vz;
+  uint16_t* kres;
+  uint16_t* vres;
+  int32_t* n_quant;
+  int32_t* n_res;
+  int32_t* err;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Tile index of compressed slot `slot` of (b, h); ok=false when a paged entry is unusable.
+__device__ __forceinline__ long tile_index(const CacheDev& c, int b, int h, int tile, bool& ok) {
+  if (c.table) {
+    if (tile >= c.max_blocks) {
+      ok = false;
+      return 0;
+    }
+    int blk = c.table[static_cast<size_t>(b) * c.max_blocks + tile];
+    if (blk < 0 || blk >= c.num_blocks) {
+      ok = false;
+      return 0;
+    }
+    return static_cast<long>(blk) * c.H + h;
+  }
+  return (static_cast<long>(b) * c.H + h) * (c.cap / TILE) + tile;
+}
+
+// Decode-attention launch parameters.
+struct DecodeParams {
+  CacheDev c;
+  const uint16_t* q;   // [B][Hq][D] bf16
+  float* out;          // [B][Hq][D] fp32
+  int32_t* ws_prefix;  // [B + 1] first work item of each sequence
+  float* ws_ml;        // [items_cap][H][G][2] running max (log2 domain), sum
+  float* ws_acc;       // [items_cap][H][G][D] unnormalised output
+  int Hq, chunk, items_cap, max_tokens;
+  float sm_log2;       // sm_scale * log2(e)
+};
+
+// Slots one append/flush call moves into the compressed cache (F), window tokens before the
+// call plus new tokens (total), and window length afterwards.  Equal, by construction, to
+// n_new single-token appends each flushing a full window before copying the token in.
+enum { MODE_APPEND = 0, MODE_FLUSH = 1 };
+
+__device__ __forceinline__ void step_counts(int mode, int R, int nr, int n_new, int& F,
+                                            int& total, int& nr_after) {
+  if (R == 0) nr = 0;
+  if (mode == MODE_FLUSH) {
+    F = (R > 0 && nr == R) ? R : 0;
+    total = nr;
+    nr_after = nr - F;
+    return;
+  }
+  total = nr + n_new;
+  if (R == 0)
+    F = n_new;
+  else
+    F = total > R ? R * ((total - 1) / R) : 0;
+  nr_after = total - F;
+}
+
+}  // namespace kvq

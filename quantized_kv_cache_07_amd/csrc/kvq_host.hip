@@ -1,0 +1,338 @@
+// kvq_host.hip -- the C ABI of libkvq: validation, sizing, launch configuration.
+//
+// Everything a host can check is checked here before any launch; see include/kvq.h for the
+// contract of each call.
+#include <cstdlib>
+#include <cstring>
+
+#include "kvq_dev.h"
+#include "kvq_measure.h"
+
+namespace kvq {
+
+hipError_t launch_append(const CacheDev& c, const uint16_t* knew, const uint16_t* vnew, int n_new,
+                         int mode, hipStream_t stream);
+size_t decode_lds_bytes(int B);
+
+hipError_t launch_decode(const DecodeParams& p, int bits, int GQ, int NP, bool kpc, int grid,
+                         hipStream_t s);
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+kvq_status check_side(const kvq_side& s, bool is_key, int residual) {
+  if (s.bits != 2 && s.bits != 4 && s.bits != 8) return KVQ_ENOTSUP;
+  if (s.scheme != KVQ_SYM && s.scheme != KVQ_ASYM) return KVQ_EINVAL;
+  if (s.axis == KVQ_PER_TOKEN) {
+    if (s.group != 32 && s.group != 64 && s.group != 128) return KVQ_ENOTSUP;
+  } else if (s.axis == KVQ_PER_CHANNEL) {
+    if (!is_key) return KVQ_ENOTSUP;
+    if (s.group != 16 && s.group != 32 && s.group != 64) return KVQ_ENOTSUP;
+    if (residual <= 0 || residual % s.group != 0) return KVQ_EINVAL;
+  } else {
+    return KVQ_EINVAL;
+  }
+  return KVQ_OK;
+}
+
+kvq_status check_format(const kvq_format* f) {
+  if (!f) return KVQ_EINVAL;
+  if (f->head_dim != D) return KVQ_ENOTSUP;
+  if (f->residual < 0 || f->residual > 256 || f->residual % TILE != 0) return KVQ_EINVAL;
+  kvq_status s = check_side(f->k, true, f->residual);
+  if (s != KVQ_OK) return s;
+  s = check_side(f->v, false, f->residual);
+  if (s != KVQ_OK) return s;
+  if (f->k.bits != f->v.bits) return KVQ_ENOTSUP;
+  return KVQ_OK;
+}
+
+kvq_status check_cache(const kvq_cache* c) {
+  if (!c) return KVQ_EINVAL;
+  kvq_status s = check_format(&c->fmt);
+  if (s != KVQ_OK) return s;
+  if (c->batch < 1 || c->batch > 4096 || c->n_kv_heads < 1) return KVQ_EINVAL;
+  if (static_cast<long>(c->batch) * c->n_kv_heads > 65535) return KVQ_ENOTSUP;
+  if (c->block_table) {
+    if (c->num_blocks < 1 || c->max_blocks < 1) return KVQ_EINVAL;
+    if (c->fmt.k.axis == KVQ_PER_CHANNEL) return KVQ_ENOTSUP;
+  } else {
+    if (c->capacity < TILE || c->capacity % TILE != 0) return KVQ_EINVAL;
+    if (c->fmt.k.axis == KVQ_PER_CHANNEL && c->capacity % c->fmt.k.group != 0) return KVQ_EINVAL;
+  }
+  if (!c->k_codes || !c->v_codes || !c->k_scale || !c->v_scale || !c->n_quant || !c->n_res ||
+      !c->err)
+    return KVQ_EINVAL;
+  if (c->fmt.k.scheme == KVQ_ASYM && !c->k_zero) return KVQ_EINVAL;
+  if (c->fmt.v.scheme == KVQ_ASYM && !c->v_zero) return KVQ_EINVAL;
+  if (c->fmt.residual > 0 && (!c->k_res || !c->v_res)) return KVQ_EINVAL;
+  const void* al[] = {c->k_codes, c->v_codes, c->k_scale, c->v_scale};
+  for (const void* p : al)
+    if (!aligned16(p)) return KVQ_EALIGN;
+  if ((c->k_zero && !aligned16(c->k_zero)) || (c->v_zero && !aligned16(c->v_zero)) ||
+      (c->k_res && !aligned16(c->k_res)) || (c->v_res && !aligned16(c->v_res)))
+    return KVQ_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(c->n_quant) & 3u) || (reinterpret_cast<uintptr_t>(c->n_res) & 3u) ||
+      (reinterpret_cast<uintptr_t>(c->err) & 3u))
+    return KVQ_EALIGN;
+  return KVQ_OK;
+}
+
+CacheDev to_dev(const kvq_cache* c) {
+  CacheDev d;
+  d.k = {c->fmt.k.bits, c->fmt.k.scheme, c->fmt.k.axis, c->fmt.k.group};
+  d.v = {c->fmt.v.bits, c->fmt.v.scheme, c->fmt.v.axis, c->fmt.v.group};
+  d.R = c->fmt.residual;
+  d.B = c->batch;
+  d.H = c->n_kv_heads;
+  d.cap = c->block_table ? 0 : c->capacity;
+  d.num_blocks = c->block_table ? c->num_blocks : 0;
+  d.max_blocks = c->block_table ? c->max_blocks : 0;
+  d.table = c->block_table;
+  d.kc = c->k_codes;
+  d.vc = c->v_codes;
+  d.ks = c->k_scale;
+  d.vs = c->v_scale;
+  d.kz = c->k_zero;
+  d.vz = c->v_zero;
+  d.kres = c->k_res;
+  d.vres = c->v_res;
+  d.n_quant = c->n_quant;
+  d.n_res = c->n_res;
+  d.err = c->err;
+  return d;
+}
+
+// Slots per work unit of the decode split: the largest of 1024..128 (multiple of 16) that still
+// gives about 2048 units (8 waves per CU), chunks of one sequence balanced in length.
+int pick_chunk(int B, int H, int max_tokens) {
+  if (const char* e = std::getenv("KVQ_CHUNK")) {
+    int v = std::atoi(e);
+    if (v >= TILE && v <= 1024 && v % TILE == 0) return v;
+  }
+  int ch = 1024;
+  while (ch > 128 && static_cast<long>(B) * H * ((max_tokens + ch - 1) / ch) < 2048) ch >>= 1;
+  const int n = (max_tokens + ch - 1) / ch;          // chunks of the longest sequence
+  int even = (max_tokens + n - 1) / n;                // balanced length
+  even = (even + TILE - 1) / TILE * TILE;
+  return even < TILE ? TILE : (even > 1024 ? 1024 : even);
+}
+
+struct WsLayout {
+  int chunk, items_cap, G;
+  size_t prefix_off, ml_off, acc_off, total;
+};
+
+WsLayout ws_layout(const kvq_cache* c, int n_q_heads, int max_tokens) {
+  WsLayout w;
+  w.G = n_q_heads / c->n_kv_heads;
+  w.chunk = pick_chunk(c->batch, c->n_kv_heads, max_tokens);
+  const long per_seq = (max_tokens + w.chunk - 1) / w.chunk;
+  w.items_cap = static_cast<int>(static_cast<long>(c->batch) * (per_seq < 1 ? 1 : per_seq));
+  w.prefix_off = 0;
+  w.ml_off = ((static_cast<size_t>(c->batch) + 1) * 4 + 255) & ~static_cast<size_t>(255);
+  w.acc_off = w.ml_off + ((static_cast<size_t>(w.items_cap) * c->n_kv_heads * w.G * 2 * 4 + 255) &
+                          ~static_cast<size_t>(255));
+  w.total = w.acc_off + static_cast<size_t>(w.items_cap) * c->n_kv_heads * w.G * D * 4;
+  return w;
+}
+
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+}  // namespace
+
+// ---- measurement kernels ------------------------------------------------------------------
+
+constexpr int MEASURE_BLOCKS = 4096;
+
+__global__ __launch_bounds__(256) void measure_read_kernel(const uint4* __restrict__ src, size_t n16,
+                                                           float* __restrict__ sink) {
+  uint32_t x = 0;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x) {
+    const uint4 v = src[i];
+    x ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  __shared__ uint32_t red[256];
+  red[threadIdx.x] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = 0;
+    for (int i = 0; i < 256; i++) r ^= red[i];
+    sink[blockIdx.x] = static_cast<float>(r & 0xFFFF);
+  }
+}
+
+__global__ __launch_bounds__(256) void measure_copy_kernel(uint4* __restrict__ dst,
+                                                           const uint4* __restrict__ src, size_t n16) {
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    dst[i] = src[i];
+}
+
+}  // namespace kvq
+
+using namespace kvq;
+
+extern "C" {
+
+size_t kvq_buffer_bytes(const kvq_format* fmt, int32_t batch, int32_t n_kv_heads, int32_t capacity,
+                        int32_t num_blocks, int32_t which) {
+  if (check_format(fmt) != KVQ_OK || batch < 1 || n_kv_heads < 1) return 0;
+  const bool paged = num_blocks > 0;
+  if (!paged && (capacity < TILE || capacity % TILE)) return 0;
+  const size_t tiles = paged ? static_cast<size_t>(num_blocks) * n_kv_heads
+                             : static_cast<size_t>(batch) * n_kv_heads * (capacity / TILE);
+  const kvq_side& s = (which == KVQ_BUF_K_CODES || which == KVQ_BUF_K_SCALE ||
+                       which == KVQ_BUF_K_ZERO || which == KVQ_BUF_K_RES)
+                          ? fmt->k
+                          : fmt->v;
+  switch (which) {
+    case KVQ_BUF_K_CODES:
+    case KVQ_BUF_V_CODES:
+      return tiles * TILE * D * s.bits / 8;
+    case KVQ_BUF_K_SCALE:
+    case KVQ_BUF_V_SCALE:
+    case KVQ_BUF_K_ZERO:
+    case KVQ_BUF_V_ZERO: {
+      if ((which == KVQ_BUF_K_ZERO || which == KVQ_BUF_V_ZERO) && s.scheme != KVQ_ASYM) return 0;
+      if (s.axis == KVQ_PER_TOKEN) return tiles * (D / s.group) * TILE * 2;
+      if (paged || capacity % s.group) return 0;
+      return static_cast<size_t>(batch) * n_kv_heads * (capacity / s.group) * D * 2;
+    }
+    case KVQ_BUF_K_RES:
+    case KVQ_BUF_V_RES:
+      return static_cast<size_t>(batch) * n_kv_heads * fmt->residual * D * 2;
+    default:
+      return 0;
+  }
+}
+
+kvq_status kvq_check_format(const kvq_format* fmt) { return check_format(fmt); }
+
+kvq_status kvq_quantize_append(const kvq_cache* cache, const void* k_new, const void* v_new,
+                               int32_t n_new, void* stream) {
+  kvq_status s = check_cache(cache);
+  if (s != KVQ_OK) return s;
+  if (n_new < 1 || !k_new || !v_new) return KVQ_EINVAL;
+  if (!aligned16(k_new) || !aligned16(v_new)) return KVQ_EALIGN;
+  const CacheDev d = to_dev(cache);
+  hipError_t e = launch_append(d, static_cast<const uint16_t*>(k_new),
+                               static_cast<const uint16_t*>(v_new), n_new, MODE_APPEND,
+                               static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ELAUNCH;
+}
+
+kvq_status kvq_flush_residual(const kvq_cache* cache, void* stream) {
+  kvq_status s = check_cache(cache);
+  if (s != KVQ_OK) return s;
+  if (cache->fmt.residual == 0) return KVQ_OK;
+  const CacheDev d = to_dev(cache);
+  hipError_t e = launch_append(d, nullptr, nullptr, 0, MODE_FLUSH, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ELAUNCH;
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t n_q_heads, int32_t max_tokens) {
+  if (check_cache(cache) != KVQ_OK || n_q_heads < 1 || max_tokens < 1 ||
+      n_q_heads % cache->n_kv_heads)
+    return 0;
+  return ws_layout(cache, n_q_heads, max_tokens).total;
+}
+
+kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int32_t n_q_heads,
+                                float sm_scale, int32_t max_tokens, float* out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  kvq_status s = check_cache(cache);
+  if (s != KVQ_OK) return s;
+  if (!q || !out || !workspace || n_q_heads < 1 || max_tokens < 1) return KVQ_EINVAL;
+  if (n_q_heads % cache->n_kv_heads) return KVQ_EINVAL;
+  const int G = n_q_heads / cache->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return KVQ_ENOTSUP;
+  const bool kpc = cache->fmt.k.axis == KVQ_PER_CHANNEL;
+  if (!kpc && (D / cache->fmt.k.group) * G > 16) return KVQ_ENOTSUP;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVQ_EALIGN;
+  const WsLayout w = ws_layout(cache, n_q_heads, max_tokens);
+  if (workspace_bytes < w.total) return KVQ_ENOSPACE;
+  const int ngv = D / cache->fmt.v.group;
+  const int NP = (2 * G * ngv + 15) / 16;
+
+  DecodeParams p;
+  p.c = to_dev(cache);
+  p.q = static_cast<const uint16_t*>(q);
+  p.out = out;
+  char* ws = static_cast<char*>(workspace);
+  p.ws_prefix = reinterpret_cast<int32_t*>(ws + w.prefix_off);
+  p.ws_ml = reinterpret_cast<float*>(ws + w.ml_off);
+  p.ws_acc = reinterpret_cast<float*>(ws + w.acc_off);
+  p.Hq = n_q_heads;
+  p.chunk = w.chunk;
+  p.items_cap = w.items_cap;
+  p.max_tokens = max_tokens;
+  p.sm_log2 = sm_scale * 1.4426950408889634f;
+
+  const long units = static_cast<long>(w.items_cap) * cache->n_kv_heads;
+  long grid = (units + 3) / 4;
+  const long cap = static_cast<long>(device_cus()) * 4;
+  if (grid > cap) grid = cap;
+  if (grid < 1) grid = 1;
+  if (std::getenv("KVQ_DEBUG"))
+    fprintf(stderr, "[kvq] decode B=%d H=%d G=%d bits=%d chunk=%d items_cap=%d grid=%ld lds=%zu\n",
+            cache->batch, cache->n_kv_heads, G, cache->fmt.k.bits, w.chunk, w.items_cap, grid,
+            decode_lds_bytes(cache->batch));
+  hipError_t e = launch_decode(p, cache->fmt.k.bits, G, NP,
+                               kpc, static_cast<int>(grid), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ELAUNCH;
+}
+
+kvq_status kvq_read_error(const kvq_cache* cache, int32_t* host_err, void* stream) {
+  if (!cache || !cache->err || !host_err) return KVQ_EINVAL;
+  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return KVQ_ELAUNCH;
+  if (hipMemcpy(host_err, cache->err, sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess)
+    return KVQ_ELAUNCH;
+  return *host_err ? KVQ_EDEVICE : KVQ_OK;
+}
+
+const char* kvq_status_str(kvq_status status) {
+  switch (status) {
+    case KVQ_OK: return "KVQ_OK";
+    case KVQ_EINVAL: return "KVQ_EINVAL: invalid argument or descriptor";
+    case KVQ_ENOTSUP: return "KVQ_ENOTSUP: combination not implemented";
+    case KVQ_EALIGN: return "KVQ_EALIGN: buffer not 16-byte aligned";
+    case KVQ_ENOSPACE: return "KVQ_ENOSPACE: workspace too small";
+    case KVQ_ELAUNCH: return "KVQ_ELAUNCH: HIP launch failed";
+    case KVQ_EDEVICE: return "KVQ_EDEVICE: device error bits set";
+    default: return "unknown kvq_status";
+  }
+}
+
+int32_t kvq_measure_read_sink_floats(void) { return MEASURE_BLOCKS; }
+
+kvq_status kvq_measure_read(const void* buf, size_t bytes, float* sink, void* stream) {
+  if (!buf || !sink || bytes == 0 || bytes % 16) return KVQ_EINVAL;
+  if (!aligned16(buf)) return KVQ_EALIGN;
+  measure_read_kernel<<<MEASURE_BLOCKS, 256, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const uint4*>(buf), bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_ELAUNCH;
+}
+
+kvq_status kvq_measure_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  if (!dst || !src || bytes == 0 || bytes % 16) return KVQ_EINVAL;
+  if (!aligned16(dst) || !aligned16(src)) return KVQ_EALIGN;
+  measure_copy_kernel<<<MEASURE_BLOCKS, 256, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<uint4*>(dst), static_cast<const uint4*>(src), bytes / 16);
+  return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_ELAUNCH;
+}
+
+}  // extern "C"

@@ -18,3 +18,11 @@ def orc():
     from oracle import oracle
     oracle.lib()
     return oracle
+
+
+def pytest_sessionstart(session):
+    """Build libkvq.so (hipcc) and the C oracle (gcc) only when they are missing."""
+    lib = os.path.join(ROOT, "quantized_kv_cache_07_amd", "libkvq.so")
+    if not os.path.exists(lib):
+        from quantized_kv_cache_07_amd import build
+        build.build()

@@ -1,0 +1,155 @@
+"""Shared helpers of the parity tests: build the same cache on the GPU (through the C ABI) and in
+the CPU oracle from the same seeded inputs, step both, and compare.
+
+Comparison rules: every byte of the code, scale and zero-point buffers equal (both sides start
+from zero-filled buffers and write only valid slots); window rows below n_res equal; counters
+equal; attention outputs within |o - o_ref| <= 2e-3 + 1e-2 |o_ref| elementwise.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+import torch
+
+import kvq_inputs as ki
+from oracle import oracle
+
+ATOL, RTOL = 2e-3, 1e-2
+SM_SCALE = float(np.float32(1.0 / math.sqrt(128)))
+
+
+def kvq():
+    from quantized_kv_cache_07_amd import kvq as mod
+    return mod
+
+
+@dataclasses.dataclass
+class Pair:
+    w: ki.Workload
+    cache: object
+    seqs: list
+    lens: list
+    table: np.ndarray | None
+    num_blocks: int
+    capacity: int
+    steps: int = 0
+
+
+def build_pair(k_side, v_side, B, Hq, H, R, lens, paged=False, seed=1, device="cuda",
+               extra_tokens=64, capacity=None, bulk=False, laplace=0.0, k_outliers=0,
+               k_outlier_scale=1.0) -> Pair:
+    K = kvq()
+    w = ki.Workload("case", seed, B, Hq, H, max(max(lens), 1), ki.Side(*k_side), ki.Side(*v_side),
+                    residual=R, paged=paged, laplace_outliers=laplace,
+                    k_outlier_channels=k_outliers, k_outlier_scale=k_outlier_scale)
+    table, nblk = None, 0
+    if paged:
+        table, nblk = ki.block_tables(w, lens, extra_tokens=extra_tokens)
+        cap_oracle = table.shape[1] * 16
+        cache = K.Cache(k_side, v_side, B, H, residual=R, block_table=torch.from_numpy(table),
+                        num_blocks=nblk, device=device)
+    else:
+        gt = k_side[3] if k_side[2] == ki.PER_CHANNEL else 16
+        need = max(lens) + R + extra_tokens
+        cap = capacity or int(math.ceil(need / max(gt, 16)) * max(gt, 16))
+        cap_oracle = cap
+        cache = K.Cache(k_side, v_side, B, H, residual=R, capacity=cap, device=device)
+    seqs = [oracle.Sequence(k_side, v_side, H, R, cap_oracle) for _ in range(B)]
+    if bulk:
+        assert len(set(lens)) == 1
+        ks, vs = zip(*[ki.prefill_kv(w, b, lens[0]) for b in range(B)])
+        kn, vn = torch.stack(ks), torch.stack(vs)
+        K.quantize_append(cache, kn.to(device).contiguous(), vn.to(device).contiguous())
+        for b in range(B):
+            seqs[b].append(ki.bf16_bits(ks[b]), ki.bf16_bits(vs[b]))
+    else:
+        for b in range(B):
+            if lens[b] == 0:
+                continue
+            k, v = ki.prefill_kv(w, b, lens[b])
+            K.quantize_append(cache, k[None].to(device).contiguous(), v[None].to(device).contiguous(),
+                              desc=cache.sequence(b))
+            seqs[b].append(ki.bf16_bits(k), ki.bf16_bits(v))
+    return Pair(w, cache, seqs, list(lens), table, nblk, cap_oracle if not paged else 0)
+
+
+def step(pr: Pair, flush_first: bool = False, n_new: int = 1) -> None:
+    """Append n_new tokens to every sequence (one batch call), optionally flushing first."""
+    K = kvq()
+    ks, vs = [], []
+    for j in range(n_new):
+        k, v = ki.step_kv(pr.w, pr.steps + j)
+        ks.append(k)
+        vs.append(v)
+    k = torch.cat(ks, dim=1)
+    v = torch.cat(vs, dim=1)
+    dev = pr.cache.n_quant.device
+    if flush_first:
+        K.flush_residual(pr.cache)
+        for s in pr.seqs:
+            s.flush()
+    K.quantize_append(pr.cache, k.to(dev).contiguous(), v.to(dev).contiguous())
+    for b, s in enumerate(pr.seqs):
+        s.append(ki.bf16_bits(k[b]), ki.bf16_bits(v[b]))
+    pr.steps += n_new
+
+
+def oracle_images(pr: Pair) -> dict:
+    c = pr.cache
+    im = oracle.empty_images(c.k_side, c.v_side, c.batch, c.n_kv_heads, c.residual,
+                             capacity=pr.capacity, num_blocks=pr.num_blocks)
+    for b, s in enumerate(pr.seqs):
+        s.pack(b, im, None if pr.table is None else pr.table[b])
+    return im
+
+
+def _u16(t):
+    return t.detach().cpu().numpy().view(np.uint16)
+
+
+def compare_state(pr: Pair) -> None:
+    torch.cuda.synchronize()
+    c = pr.cache
+    assert kvq().read_error(c) == 0
+    nq = c.n_quant.cpu().numpy()
+    nr = c.n_res.cpu().numpy()
+    assert list(nq) == [s.n_quant for s in pr.seqs], (list(nq), [s.n_quant for s in pr.seqs])
+    assert list(nr) == [s.n_res for s in pr.seqs], (list(nr), [s.n_res for s in pr.seqs])
+    im = oracle_images(pr)
+    for name in ("k_codes", "v_codes"):
+        got = getattr(c, name).cpu().numpy()
+        bad = np.nonzero(got != im[name])[0]
+        assert bad.size == 0, f"{name}: {bad.size} bytes differ, first at {bad[:8]}"
+    for name in ("k_scale", "v_scale", "k_zero", "v_zero"):
+        t = getattr(c, name)
+        if t is None:
+            continue
+        got = _u16(t)
+        bad = np.nonzero(got != im[name])[0]
+        assert bad.size == 0, f"{name}: {bad.size} values differ, first at {bad[:8]}"
+    if c.residual:
+        for name in ("k_res", "v_res"):
+            got = _u16(getattr(c, name)).reshape(c.batch, c.n_kv_heads, c.residual, 128)
+            ref = im[name].reshape(c.batch, c.n_kv_heads, c.residual, 128)
+            for b in range(c.batch):
+                assert np.array_equal(got[b, :, :nr[b]], ref[b, :, :nr[b]]), f"{name} seq {b}"
+
+
+def compare_attention(pr: Pair, q_seed_step: int = 0, max_tokens: int | None = None):
+    K = kvq()
+    dev = pr.cache.n_quant.device
+    q = ki.queries(pr.w, q_seed_step, dev)
+    mt = max_tokens or max(s.n_quant + s.n_res for s in pr.seqs) or 1
+    out = K.decode_attention(pr.cache, q, max_tokens=mt, sm_scale=SM_SCALE)
+    torch.cuda.synchronize()
+    assert K.read_error(pr.cache) == 0
+    got = out.cpu().numpy()
+    qb = ki.bf16_bits(q)
+    ref = np.stack([s.attend(qb[b], SM_SCALE) for b, s in enumerate(pr.seqs)])
+    err = np.abs(got - ref)
+    ok = err <= ATOL + RTOL * np.abs(ref)
+    assert ok.all(), (f"attention: {int((~ok).sum())} of {ok.size} outside tolerance; "
+                      f"max abs err {err.max():.3e} at {np.unravel_index(err.argmax(), err.shape)}")
+    return float(err.max()), got

@@ -1,0 +1,135 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same seeded inputs.
+
+Codes, scales, zero-points, window rows and counters must be bit-exact; attention outputs must
+lie within 2e-3 + 1e-2 |ref| of the oracle's fp64 attention on the same dequantized values.
+Sizes span several 16-slot tiles, several decode chunks and ragged tails.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import kvq_cases as kc
+
+pytestmark = pytest.mark.gpu
+
+SYM8 = (8, 0, 0, 128)
+SYM4 = (4, 0, 0, 64)
+SYM2_32 = (2, 0, 0, 32)
+ASYM4_32 = (4, 1, 0, 32)
+ASYM2_32 = (2, 1, 0, 32)
+KPC2 = (2, 1, 1, 32)
+KPC4S = (4, 0, 1, 16)
+
+
+def announce(**kw):
+    print("case:", kw, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+
+
+CASES = [
+    # k, v, B, Hq, H, R, lens, paged
+    ("int8-mha-tiny", SYM8, SYM8, 1, 1, 1, 0, [256], False),
+    ("int8-mha-ragged", SYM8, SYM8, 3, 4, 4, 0, [5, 300, 1031], False),
+    ("int4-gqa4", SYM4, SYM4, 2, 8, 2, 0, [777, 1500], False),
+    ("int4-gqa4-window", SYM4, SYM4, 2, 8, 2, 32, [777, 190], False),
+    ("int4-paged-window", SYM4, SYM4, 3, 8, 2, 128, [1000, 129, 40], True),
+    ("int2-sym-g32", SYM2_32, SYM2_32, 2, 4, 2, 0, [333, 64], False),
+    ("asym4-g32", ASYM4_32, ASYM4_32, 2, 4, 2, 16, [250, 999], False),
+    ("kivi-int2", KPC2, ASYM2_32, 2, 8, 2, 128, [700, 1300], False),
+    ("kpc4-sym-g16", KPC4S, SYM4, 2, 4, 1, 32, [100, 50], False),
+    ("gqa8-int8", SYM8, SYM8, 1, 16, 2, 0, [600], False),
+    ("gqa2-int4-paged", SYM4, SYM4, 2, 4, 2, 0, [300, 17], True),
+]
+
+
+@pytest.mark.parametrize("name,k,v,B,Hq,H,R,lens,paged", CASES, ids=[c[0] for c in CASES])
+def test_prefill_step_and_attention(name, k, v, B, Hq, H, R, lens, paged):
+    announce(test="prefill_step_and_attention", name=name)
+    pr = kc.build_pair(k, v, B, Hq, H, R, lens, paged=paged, seed=hash(name) % 1000)
+    kc.compare_state(pr)
+    kc.compare_attention(pr)
+    kc.step(pr, flush_first=False)
+    kc.step(pr, flush_first=True)
+    kc.compare_state(pr)
+    kc.compare_attention(pr, q_seed_step=1)
+
+
+def test_bulk_append_equals_single_appends():
+    """One n_new = 37 call equals 37 one-token calls (both compared to the oracle, which
+    appends one token at a time by definition)."""
+    announce(test="bulk_append")
+    pr = kc.build_pair(SYM4, SYM4, 2, 8, 2, 32, [100, 100], bulk=True, seed=5)
+    kc.compare_state(pr)
+    kc.step(pr, n_new=37)
+    kc.compare_state(pr)
+    kc.compare_attention(pr)
+    pr2 = kc.build_pair(KPC2, ASYM2_32, 1, 4, 1, 64, [70], seed=6)
+    kc.step(pr2, n_new=150)
+    kc.compare_state(pr2)
+    kc.compare_attention(pr2)
+
+
+def test_window_edge_states():
+    """Windows exactly full, empty compressed part, single token."""
+    announce(test="window_edges")
+    pr = kc.build_pair(SYM4, SYM4, 4, 8, 2, 32, [32, 1, 33, 64])
+    kc.compare_state(pr)
+    kc.compare_attention(pr)
+    for _ in range(3):
+        kc.step(pr)
+    kc.compare_state(pr)
+    kc.compare_attention(pr)
+
+
+def test_empty_sequence_gives_zeros():
+    announce(test="empty_sequence")
+    pr = kc.build_pair(SYM8, SYM8, 3, 2, 2, 0, [0, 40, 0])
+    err, got = kc.compare_attention(pr, max_tokens=64)
+    assert np.all(got[0] == 0) and np.all(got[2] == 0)
+
+
+def test_deterministic_and_paged_equals_contiguous():
+    announce(test="determinism_paging")
+    a = kc.build_pair(SYM4, SYM4, 2, 8, 2, 128, [900, 333], paged=False, seed=9)
+    b = kc.build_pair(SYM4, SYM4, 2, 8, 2, 128, [900, 333], paged=True, seed=9)
+    _, o1 = kc.compare_attention(a)
+    _, o2 = kc.compare_attention(a)
+    assert np.array_equal(o1, o2)
+    _, o3 = kc.compare_attention(b)
+    assert np.array_equal(o1, o3)
+
+
+def test_device_faults_leave_other_sequences_intact():
+    """A block-table entry outside the pool and a full contiguous cache set error bits; the
+    faulty sequence's counters do not move and the other sequences proceed."""
+    announce(test="device_faults")
+    K = kc.kvq()
+    pr = kc.build_pair(SYM4, SYM4, 2, 4, 2, 0, [30, 30], paged=True, seed=12, extra_tokens=16)
+    bad = pr.cache.block_table.clone()
+    bad[1, 1] = pr.num_blocks + 5  # slot 30's block for sequence 1 is now outside the pool
+    pr.cache.block_table.copy_(bad)
+    pr.cache.desc = pr.cache._describe()
+    nq0 = pr.cache.n_quant.cpu().tolist()
+    k, v = kc.ki.step_kv(pr.w, 0)
+    K.quantize_append(pr.cache, k.cuda().contiguous(), v.cuda().contiguous())
+    torch.cuda.synchronize()
+    assert K.read_error(pr.cache) & K.ERR_BLOCK
+    nq1 = pr.cache.n_quant.cpu().tolist()
+    assert nq1[1] == nq0[1] and nq1[0] == nq0[0] + 1
+    # contiguous cache that is full
+    pr2 = kc.build_pair(SYM8, SYM8, 2, 2, 2, 0, [16, 5], capacity=16, seed=13)
+    k, v = kc.ki.step_kv(pr2.w, 0)
+    K.quantize_append(pr2.cache, k.cuda().contiguous(), v.cuda().contiguous())
+    torch.cuda.synchronize()
+    assert K.read_error(pr2.cache) & K.ERR_CAPACITY
+    assert pr2.cache.n_quant.cpu().tolist() == [16, 6]
