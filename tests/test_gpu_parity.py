@@ -7,6 +7,7 @@ Sizes span several 16-slot tiles, several decode chunks and ragged tails.
 from __future__ import annotations
 
 import sys
+import zlib
 
 import numpy as np
 import pytest
@@ -55,7 +56,7 @@ CASES = [
 @pytest.mark.parametrize("name,k,v,B,Hq,H,R,lens,paged", CASES, ids=[c[0] for c in CASES])
 def test_prefill_step_and_attention(name, k, v, B, Hq, H, R, lens, paged):
     announce(test="prefill_step_and_attention", name=name)
-    pr = kc.build_pair(k, v, B, Hq, H, R, lens, paged=paged, seed=hash(name) % 1000)
+    pr = kc.build_pair(k, v, B, Hq, H, R, lens, paged=paged, seed=zlib.crc32(name.encode()) % 1000)
     kc.compare_state(pr)
     kc.compare_attention(pr)
     kc.step(pr, flush_first=False)
