@@ -1,0 +1,416 @@
+"""Benchmark: one decode step of the quantized KV cache on one MI355X.
+
+A step is one pass of the whole hot path over one batch: flush every full BF16 window, append one
+new token per sequence (quantized, or copied into the window), then single-query decode attention
+over every cached token with the K/V codes dequantized in registers.  Inputs are seeded synthetic
+tensors generated on the GPU (kvq_inputs); the cache is resident in HBM before timing starts.
+
+Default workload: the paged mixed batch (64 sequences, lengths log-uniform in [1024, 131072],
+16-token blocks in shuffled physical order, H_q=32, H_kv=8, head_dim 128, INT4 symmetric group 64
+with fp16 scales, 128-token BF16 window).  It is the largest single-GPU configuration and the only
+one that exercises every step (flush, append, window, paged addressing, attention, combine).
+
+Output: one JSON line (rank 0, N=1).  `value` is whole-step algorithmic bytes / step time in GB/s;
+`roofline` prices the decode-attention call (its split-K kernel plus the combine kernel) against
+MI355X's 8 TB/s; `cpu_baseline` times the CPU oracle's fp64 attention on a bounded sample of the
+same sequences.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5|c4|c3|c2x32|c2|c1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+HEAD_DIM = 128
+
+
+# ------------------------------------------------------------------------------------------
+# Algorithmic bytes
+# ------------------------------------------------------------------------------------------
+
+def side_token_bytes(side) -> float:
+    """Bytes of one (token, kv head) row of one side: codes plus per-token metadata, or the
+    per-token share of per-channel metadata."""
+    bits, scheme, axis, group = side
+    meta = 2 * (2 if scheme == 1 else 1)
+    codes = HEAD_DIM * bits / 8
+    if axis == 0:
+        return codes + (HEAD_DIM // group) * meta
+    return codes + HEAD_DIM * meta / group
+
+
+def attention_bytes(w, nq, nr) -> float:
+    """Codes + metadata of every attended compressed token, the BF16 window rows, q (bf16), the
+    output (fp32) and the block-table entries (paged).  Split-K partials are not counted."""
+    H, Hq = w.n_kv_heads, w.n_q_heads
+    per_tok = side_token_bytes(w.k.astuple()) + side_token_bytes(w.v.astuple())
+    total = 0.0
+    for a, r in zip(nq, nr):
+        total += a * H * per_tok + r * H * HEAD_DIM * 2 * 2
+        total += Hq * HEAD_DIM * (2 + 4)
+        if w.paged:
+            total += -(-a // 16) * 4
+    return total
+
+
+def append_bytes(w, nq_before, nr_before) -> tuple[float, int]:
+    """Bytes of one flush-where-due + append-one step, and the number of flushing sequences."""
+    H, R = w.n_kv_heads, w.residual
+    row_bf16 = H * HEAD_DIM * 2
+    per_tok = side_token_bytes(w.k.astuple()) + side_token_bytes(w.v.astuple())
+    total, flushes = 0.0, 0
+    for a, r in zip(nq_before, nr_before):
+        total += 2 * row_bf16  # read the new K and V rows
+        if R == 0:
+            total += H * per_tok
+        else:
+            if r == R:
+                flushes += 1
+                total += R * 2 * row_bf16 + R * H * per_tok
+            total += 2 * row_bf16  # window write
+    return total, flushes
+
+
+def advance(w, nq, nr):
+    """Host copy of the per-sequence state machine: flush a full window, then append one."""
+    R = w.residual
+    nq, nr = list(nq), list(nr)
+    for b in range(len(nq)):
+        if R == 0:
+            nq[b] += 1
+        else:
+            if nr[b] == R:
+                nq[b] += R
+                nr[b] = 0
+            nr[b] += 1
+    return nq, nr
+
+
+# ------------------------------------------------------------------------------------------
+# Workload state on the GPU
+# ------------------------------------------------------------------------------------------
+
+class State:
+    pass
+
+
+def setup(name: str, extra_steps: int, device="cuda"):
+    import torch
+
+    import kvq_inputs as ki
+    from quantized_kv_cache_07_amd import kvq
+
+    layers = 1
+    base = name
+    if name == "c2x32":
+        base, layers = "c2", 32
+    w = ki.CONFIGS[base]
+    lens = ki.lengths(w)
+    R = w.residual
+    st = State()
+    st.name, st.w, st.layers, st.lens = name, w, layers, lens
+    k_side, v_side = w.k.astuple(), w.v.astuple()
+    st.caches = []
+    for layer in range(layers):
+        lw = w if layers == 1 else ki.Workload(**{**w.__dict__, "seed": 1000 * w.seed + layer})
+        if w.paged:
+            table, nblk = ki.block_tables(lw, lens, extra_tokens=R + extra_steps + 32)
+            cache = kvq.Cache(k_side, v_side, w.batch, w.n_kv_heads, residual=R,
+                              block_table=torch.from_numpy(table), num_blocks=nblk, device=device)
+        else:
+            gt = w.k.group if w.k.axis == ki.PER_CHANNEL else 16
+            cap = -(-(max(lens) + R + extra_steps + 16) // gt) * gt
+            cache = kvq.Cache(k_side, v_side, w.batch, w.n_kv_heads, residual=R, capacity=cap,
+                              device=device)
+        for b in range(w.batch):
+            # prefill in pieces of at most 16384 tokens; the window state is carried by the cache
+            t0 = 0
+            while t0 < lens[b]:
+                n = min(16384, lens[b] - t0)
+                k, v = ki.prefill_kv(lw, b, n, device=device, t0=t0)
+                kvq.quantize_append(cache, k[None].contiguous(), v[None].contiguous(),
+                                    desc=cache.sequence(b))
+                t0 += n
+        st.caches.append((lw, cache))
+    torch.cuda.synchronize()
+    for _, cache in st.caches:
+        if kvq.read_error(cache):
+            raise RuntimeError("device error during prefill")
+    if R:
+        st.nq = [R * ((t - 1) // R) for t in lens]
+        st.nr = [t - a for t, a in zip(lens, st.nq)]
+    else:
+        st.nq, st.nr = list(lens), [0] * w.batch
+    got_nq = st.caches[0][1].n_quant.cpu().tolist()
+    got_nr = st.caches[0][1].n_res.cpu().tolist()
+    assert got_nq == st.nq and got_nr == st.nr, "prefill counters disagree with the state machine"
+    st.max_tokens = max(lens) + extra_steps + 1
+    st.ws = torch.empty(kvq.workspace_bytes(st.caches[0][1], w.n_q_heads, st.max_tokens),
+                        dtype=torch.uint8, device=device)
+    st.out = torch.empty((w.batch, w.n_q_heads, HEAD_DIM), dtype=torch.float32, device=device)
+    return st
+
+
+def make_step_inputs(st, n_steps: int, device="cuda"):
+    import kvq_inputs as ki
+    st.step_in = []
+    for s in range(n_steps):
+        per_layer = []
+        for lw, _ in st.caches:
+            k, v = ki.step_kv(lw, s, device)
+            q = ki.queries(lw, s + 1, device)
+            per_layer.append((k.contiguous(), v.contiguous(), q.contiguous()))
+        st.step_in.append(per_layer)
+
+
+def run_step(st, s: int) -> None:
+    from quantized_kv_cache_07_amd import kvq
+    w = st.w
+    for (lw, cache), (k, v, q) in zip(st.caches, st.step_in[s]):
+        if w.step_append or st.layers > 1:
+            if w.residual:
+                kvq.flush_residual(cache)
+            kvq.quantize_append(cache, k, v)
+        kvq.decode_attention(cache, q, st.max_tokens, out=st.out, workspace=st.ws)
+
+
+def attention_only(st, q) -> None:
+    from quantized_kv_cache_07_amd import kvq
+    for _, cache in st.caches:
+        kvq.decode_attention(cache, q, st.max_tokens, out=st.out, workspace=st.ws)
+
+
+# ------------------------------------------------------------------------------------------
+# CPU baseline: the oracle, as it stands, on a bounded sample of the same sequences
+# ------------------------------------------------------------------------------------------
+
+def cpu_baseline(st, gpu_out0, q0, budget_s: float = 15.0):
+    import numpy as np
+
+    import kvq_inputs as ki
+    from oracle import oracle
+
+    w = st.w
+    lw = st.caches[0][0]
+    sm = float(np.float32(1.0 / math.sqrt(HEAD_DIM)))
+    order = sorted(range(w.batch), key=lambda b: st.lens[b])  # shortest first: bounded sample
+    qb = ki.bf16_bits(q0)
+    used, t_attn, nbytes, max_err = [], 0.0, 0.0, 0.0
+    ok = True
+    for b in order:
+        T = st.lens[b]
+        seq = oracle.Sequence(w.k.astuple(), w.v.astuple(), w.n_kv_heads, w.residual,
+                              -(-(T + w.residual + 64) // 64) * 64)
+        k, v = ki.prefill_kv(lw, b, T, device="cpu")
+        seq.append(ki.bf16_bits(k), ki.bf16_bits(v))
+        t0 = time.perf_counter()
+        ref = seq.attend(qb[b], sm)
+        dt = time.perf_counter() - t0
+        t_attn += dt
+        nbytes += attention_bytes(w, [seq.n_quant], [seq.n_res])
+        used.append((b, T))
+        err = np.abs(gpu_out0[b] - ref)
+        max_err = max(max_err, float(err.max()))
+        ok = ok and bool(np.all(err <= 2e-3 + 1e-2 * np.abs(ref)))
+        if t_attn >= budget_s:
+            break
+    return {
+        "value": nbytes / t_attn / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"fp64 oracle attention (all {w.n_q_heads} query heads) over sequences "
+                   f"{[b for b, _ in used]} with {sum(t for _, t in used)} cached tokens, "
+                   f"{t_attn:.1f} s on one host core; same algorithmic-byte count as the GPU"),
+    }, {"sequences": [b for b, _ in used], "max_abs_err": max_err, "within_tolerance": ok}
+
+
+# ------------------------------------------------------------------------------------------
+# Counter-derived traffic committed under profiles/
+# ------------------------------------------------------------------------------------------
+
+def decode_source_hash() -> str:
+    p = os.path.join(ROOT, "quantized_kv_cache_07_amd", "csrc", "kvq_decode.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def counter_traffic(workload: str):
+    """Per-launch HBM bytes of the decode kernel from the committed rocprofv3 counter summary,
+    or None when there is none for this workload or the kernel source changed since."""
+    p = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("kvq_decode_hip_sha256_16") != decode_source_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+# ------------------------------------------------------------------------------------------
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c5", choices=["c1", "c2", "c2x32", "c3", "c4", "c5"])
+    ap.add_argument("--attn-reps", type=int, default=50)
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
+              f"(the path is sharded by sequence or kv head across GPUs, not built here)",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import kvq_inputs as ki
+    from quantized_kv_cache_07_amd import kvq
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = "cuda"
+    n_total = a.warmup + a.steps
+    print(f"[bench] setup {a.workload}", file=sys.stderr, flush=True)
+    t_setup = time.perf_counter()
+    st = setup(a.workload, n_total + 1, dev)
+    w = st.w
+
+    # Output of the prefilled state, kept for the parity check of the CPU sample.
+    q0 = ki.queries(st.caches[0][0], 0, dev)
+    kvq.decode_attention(st.caches[0][1], q0, st.max_tokens, out=st.out, workspace=st.ws)
+    torch.cuda.synchronize()
+    gpu_out0 = st.out.cpu().numpy().copy()
+    make_step_inputs(st, n_total, dev)
+    torch.cuda.synchronize()
+    print(f"[bench] setup done in {time.perf_counter() - t_setup:.1f} s", file=sys.stderr,
+          flush=True)
+
+    # Host copy of the state machine, for the algorithmic bytes of each step.
+    appends = w.step_append or st.layers > 1
+    nq, nr = st.nq, st.nr
+    step_bytes, attn_tokens, flushes = [], 0, 0
+    for s in range(n_total):
+        ab, fl = (0.0, 0)
+        if appends:
+            ab, fl = append_bytes(w, nq, nr)
+            nq, nr = advance(w, nq, nr)
+        if s >= a.warmup:
+            step_bytes.append(st.layers * (ab + attention_bytes(w, nq, nr)))
+            attn_tokens += st.layers * (sum(nq) + sum(nr))
+            flushes += st.layers * fl
+
+    for s in range(a.warmup):
+        run_step(st, s)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record()
+    for s in range(a.warmup, n_total):
+        run_step(st, s)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    t_ms = e0.elapsed_time(e1)
+    for _, cache in st.caches:
+        if kvq.read_error(cache):
+            raise RuntimeError("device error during the timed steps")
+    assert st.caches[0][1].n_quant.cpu().tolist() == nq, "counter drift"
+    assert st.caches[0][1].n_res.cpu().tolist() == nr, "counter drift"
+    ms_per_step = t_ms / a.steps
+    gbs = sum(step_bytes) / (t_ms * 1e-3) / 1e9
+    tok_s = attn_tokens / (t_ms * 1e-3)
+
+    # Decode-attention call alone, on the final state, back to back on the current stream.
+    q = st.step_in[-1][0][2]
+    for _ in range(3):
+        attention_only(st, q)
+    torch.cuda.synchronize()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record()
+    for _ in range(a.attn_reps):
+        attention_only(st, q)
+    a1.record()
+    torch.cuda.synchronize()
+    attn_us = a0.elapsed_time(a1) * 1e3 / (a.attn_reps * st.layers)
+    attn_b = attention_bytes(w, nq, nr)
+    achieved = attn_b / (attn_us * 1e-6) / 1e9
+    traffic = counter_traffic(a.workload)
+
+    # Measured read-stream ceiling (128-bit loads over 4 GiB, same stream).
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.empty(kvq.lib.kvq_measure_read_sink_floats(), dtype=torch.float32, device=dev)
+    kvq.measure_read(buf, sink)
+    torch.cuda.synchronize()
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record()
+    for _ in range(10):
+        kvq.measure_read(buf, sink)
+    r1.record()
+    torch.cuda.synchronize()
+    stream_gbs = 10 * buf.numel() / (r0.elapsed_time(r1) * 1e-3) / 1e9
+    del buf
+
+    cpu, parity = None, None
+    if not a.no_cpu:
+        print("[bench] cpu baseline", file=sys.stderr, flush=True)
+        cpu, parity = cpu_baseline(st, gpu_out0, q0, a.cpu_budget)
+        cpu["cores_available"] = os.cpu_count()
+
+    desc = w.description if st.layers == 1 else (
+        "worked example: 32 layers x " + w.description.split(": ", 1)[1])
+    line = {
+        "metric": "quantized-KV decode attention: effective HBM GB/s (% of peak), KV tokens/s",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 codes, fp16 scales, fp32 accumulate" if w.k.bits == 4 else
+                 f"int{w.k.bits} codes, fp16 scales, fp32 accumulate",
+        "data": "synthetic (seeded counter-hash generator, generated on the GPU)",
+        "config": {"workload": f"{a.workload}: {desc}", "batch": w.batch,
+                   "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": HEAD_DIM,
+                   "layers": st.layers, "tokens_min": min(st.lens), "tokens_max": max(st.lens),
+                   "cached_tokens": int(sum(st.lens)), "residual": w.residual,
+                   "paged": w.paged, "step": ("flush where due + append 1 + attention"
+                                              if appends else "attention")},
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+        "kv_tokens_per_s": round(tok_s, 1),
+        "flushes_in_timed_steps": flushes,
+        "wall_s_timed": round(wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "decode attention call: decode_kernel + combine_kernel",
+                     "algorithmic_bytes_per_launch": int(attn_b),
+                     "avg_launch_us": round(attn_us, 3)},
+        "stream_read_ceiling_gbs": round(stream_gbs, 1),
+        "cpu_baseline": cpu,
+        "parity_sample": parity,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

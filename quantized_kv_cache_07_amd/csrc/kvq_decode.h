@@ -1,0 +1,936 @@
+// kvq_decode.h -- single-query decode attention over the quantized cache (gfx950 kernels).
+//
+//   out[b][hq] = softmax(sm_scale * q K^T) V          [P2 = llmdaily.org "KV-cache quantization --
+//   making long-context inference fit in memory", "Why the KV cache grows so quickly", attention
+//   equation], over the compressed tokens, dequantized in registers as they stream in (P3 =
+//   oh-bug.com "KV Cache Quantization in Practice", "Misconception 1": a kernel gains from
+//   quantization only when the dequantization is fused into it), followed by the BF16 window.
+//
+// Work decomposition.  A work unit is 32 compressed slots (a pair of 16-slot tiles) or 32 window
+// rows of one (sequence, kv head).  Units are numbered sequence by sequence, kv head by kv head,
+// from a prefix sum every workgroup rebuilds from the device counters (no host sync).  Workgroup
+// k of NB owns the contiguous unit range [k U / NB, (k+1) U / NB): the load is balanced to one
+// unit whatever the length mix.  Inside a workgroup the four waves interleave the units of each
+// (sequence, kv head) segment; at a segment end the waves merge in LDS and the workgroup writes
+// either the normalised output (the segment was the whole sequence) or a partial (max, sum,
+// o[128]) that combine_kernel merges with a log-sum-exp rescale.
+//
+// One unit on one wave (lane = 16 g + n):
+//   QK^T  4 MFMA 16x16x32 f16 per tile: D[token][col] = sum_k A[token][k] B[k][col], A = key
+//         codes of token n turned into exact f16 integers (0x6400 exponent trick), B = the query
+//         rows of the GQA group, one column per (key group, query head) with the other groups'
+//         channels zeroed, so per-token group scales apply to the products; per-channel key
+//         scales are folded into the query (hi + lo f16 parts) once per key group.
+//   softmax  online, in log2 units; the running max is only raised when a score exceeds it by
+//         more than 8 (weights stay <= 2^8), so the accumulator is rarely rescaled.
+//   PV    8 MFMA 16x16x32 f16 per pair and row block: D[row][ch] = sum_t P[row][t] V[t][ch] with
+//         rows (hi/lo part, value group, query head) of w * s_v, 32 tokens (both tiles) deep.
+//   Codes of the next unit are loaded as soon as the current ones are consumed.
+#pragma once
+
+#include <cfloat>
+
+#include "kvq_dev.h"
+
+namespace kvq {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int WAVES = 4;
+constexpr int RED_STRIDE = D + 4;  // floats per LDS row of the merge buffer
+constexpr float LAZY_LOG2 = 8.0f;  // raise the running max only past this margin
+
+// ---- small helpers ------------------------------------------------------------------------
+
+__device__ __forceinline__ f16x2 as_h2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
+__device__ __forceinline__ uint32_t h2_bits(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+// Two f32 to two f16, rounding toward zero (v_cvt_pkrtz_f16_f32).
+__device__ __forceinline__ f16x2 pkrtz(float a, float b) {
+  return __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+__device__ __forceinline__ f16x2 h2s(float x) { return f16x2{(_Float16)x, (_Float16)x}; }
+__device__ __forceinline__ float f16_lo(uint32_t u) {
+  return (float)__builtin_bit_cast(_Float16, static_cast<unsigned short>(u & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t u) {
+  return (float)__builtin_bit_cast(_Float16, static_cast<unsigned short>(u >> 16));
+}
+
+// DPP row rotate (within 16-lane rows) by S lanes.
+template <int S>
+__device__ __forceinline__ float row_ror(float x) {
+  static_assert(S >= 1 && S <= 15, "row_ror");
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x120 + S, 0xF, 0xF, false));
+}
+
+// Values every lane of a wave agrees on, made scalar (the compiler cannot see it for LDS loads).
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ long uni(long v) {
+  const unsigned long long u = static_cast<unsigned long long>(v);
+  const unsigned lo = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(u));
+  const unsigned hi = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(u >> 32));
+  return static_cast<long>((static_cast<unsigned long long>(hi) << 32) | lo);
+}
+
+// A load through the scalar data cache: `ptr` must be the same on every lane and the memory
+// must not change while the kernel runs (block tables and counters).
+__device__ __forceinline__ int ld_uniform(const int32_t* ptr) {
+  return *(const __attribute__((address_space(4))) int32_t*)(ptr);
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---- code unpacking -----------------------------------------------------------------------
+// A word holds E = 32 / KB fields; pair k (0 <= k < E/2) is (field k, field k + E/2), returned
+// as the exact f16 values (u - off).  Pair index r = word * (E/2) + k.
+
+// Constants of the unpacking, held in registers: gfx950 VOP3 instructions (v_and_or_b32) take
+// no literal operands, so with literals every and-or would split into two instructions.
+struct UnpackRegs {
+  uint32_t magic;  // VGPR: 0x64006400, f16 1024.0 in both halves
+  uint32_t m_lo, m_hi;  // SGPRs: masks of the two fields a pair needs (per bit width)
+};
+
+template <int KB>
+__device__ __forceinline__ UnpackRegs unpack_regs() {
+  UnpackRegs r;
+  r.magic = 0x64006400u;
+  asm volatile("" : "+v"(r.magic));
+  if constexpr (KB == 8) {
+    asm volatile("s_mov_b32 %0, 0x00ff00ff" : "=s"(r.m_lo));
+    r.m_hi = r.m_lo;
+  } else if constexpr (KB == 4) {
+    asm volatile("s_mov_b32 %0, 0x000f000f" : "=s"(r.m_lo));
+    asm volatile("s_mov_b32 %0, 0x00f000f0" : "=s"(r.m_hi));
+  } else {
+    asm volatile("s_mov_b32 %0, 0x00030003" : "=s"(r.m_lo));
+    r.m_hi = r.m_lo;
+  }
+  return r;
+}
+
+// A word holds E = 32 / KB fields; pair k (0 <= k < E/2) is (field k, field k + E/2), returned
+// as the exact f16 values (u - off).  Pair index r = word * (E/2) + k.
+template <int KB>
+__device__ __forceinline__ f16x2 upair(const uint32_t* w, int r, float off, const UnpackRegs& u) {
+  constexpr int HH = 16 / KB;
+  const uint32_t x = w[r / HH];
+  const int k = r % HH;
+  if constexpr (KB == 8) {
+    const uint32_t s = k ? (x >> 8) : x;
+    return as_h2((s & u.m_lo) | u.magic) - h2s(1024.0f + off);
+  } else if constexpr (KB == 4) {
+    const uint32_t s = (k >= 2) ? (x >> 8) : x;
+    if ((k & 1) == 0) return as_h2((s & u.m_lo) | u.magic) - h2s(1024.0f + off);
+    return __builtin_elementwise_fma(as_h2((s & u.m_hi) | u.magic), h2s(0.0625f),
+                                     h2s(-(64.0f + off)));
+  } else {
+    static_assert(KB == 2, "bits");
+    // field k sits at bit 2k (k < 5) or, after a shift by 10, at bit 2(k - 5)
+    const int sh = (k >= 5) ? 2 * (k - 5) : 2 * k;
+    const uint32_t s = ((k >= 5) ? (x >> 10) : x) >> sh;
+    const float scl = 1.0f;
+    (void)scl;
+    return as_h2((s & u.m_lo) | u.magic) - h2s(1024.0f + off);
+  }
+}
+
+// QK A operand of MFMA j: pairs 4 j .. 4 j + 3 of the lane's key slice.
+template <int KB>
+__device__ __forceinline__ f16x8 kop(const uint32_t* w, int j, float off, const UnpackRegs& u) {
+  const uint4 v = uint4{h2_bits(upair<KB>(w, 4 * j, off, u)), h2_bits(upair<KB>(w, 4 * j + 1, off, u)),
+                        h2_bits(upair<KB>(w, 4 * j + 2, off, u)), h2_bits(upair<KB>(w, 4 * j + 3, off, u))};
+  return __builtin_bit_cast(f16x8, v);
+}
+
+// PV B operand of MFMA j (channel 8 n + j): tokens 4 g .. 4 g + 3 of tile A, then of tile B
+// (value pairs 2 j and 2 j + 1 hold tokens (0, 1) and (2, 3) of channel j).
+template <int KB>
+__device__ __forceinline__ f16x8 vop(const uint32_t* wa, const uint32_t* wb, int j, float off,
+                                     const UnpackRegs& u) {
+  const uint4 v = uint4{h2_bits(upair<KB>(wa, 2 * j, off, u)), h2_bits(upair<KB>(wa, 2 * j + 1, off, u)),
+                        h2_bits(upair<KB>(wb, 2 * j, off, u)), h2_bits(upair<KB>(wb, 2 * j + 1, off, u))};
+  return __builtin_bit_cast(f16x8, v);
+}
+
+// Channel (0..31 inside a lane's 32-channel key slice) of element i of QK MFMA j: element i is
+// half i % 2 of pair 4 j + i / 2.
+template <int KB>
+__device__ __forceinline__ constexpr int kchan(int j, int i) {
+  constexpr int HH = 16 / KB;
+  const int r = 4 * j + i / 2;
+  return (r / HH) * 2 * HH + (r % HH) + HH * (i % 2);
+}
+
+// Eight f16/bf16 values at channels base + kchan(j, 0..7) from a natural-order LDS row.
+template <int KB>
+__device__ __forceinline__ u16x8 gather_kchan(const uint16_t* row, int j) {
+  if constexpr (KB == 2) {
+    const int c0 = 16 * (j / 2) + 4 * (j % 2);
+    const u16x4 a = *reinterpret_cast<const u16x4*>(row + c0);
+    const u16x4 b = *reinterpret_cast<const u16x4*>(row + c0 + 8);
+    return __builtin_shufflevector(a, b, 0, 4, 1, 5, 2, 6, 3, 7);
+  } else {
+    const u16x8 a = *reinterpret_cast<const u16x8*>(row + 8 * j);
+    if constexpr (KB == 4) return __builtin_shufflevector(a, a, 0, 4, 1, 5, 2, 6, 3, 7);
+    else return __builtin_shufflevector(a, a, 0, 2, 1, 3, 4, 6, 5, 7);
+  }
+}
+
+template <int KB>
+__device__ __forceinline__ void load_words(const uint8_t* ptr, uint32_t (&w)[KB]) {
+  if constexpr (KB == 8) {
+    const uint4 a = reinterpret_cast<const uint4*>(ptr)[0];
+    const uint4 b = reinterpret_cast<const uint4*>(ptr)[1];
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+  } else if constexpr (KB == 4) {
+    const uint4 a = *reinterpret_cast<const uint4*>(ptr);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+  } else {
+    const uint2 a = *reinterpret_cast<const uint2*>(ptr);
+    w[0] = a.x; w[1] = a.y;
+  }
+}
+
+// ---- per-unit register data ----------------------------------------------------------------
+
+template <int KB, int NP, bool KPC, bool ASYM>
+struct UnitData {
+  uint32_t kw[2][KB];  // key slices of tiles A and B (token n, channels 32 g .. 32 g + 31)
+  uint32_t vw[2][KB];  // value chunks of tiles A and B (tokens 4 g .. 4 g + 3, channels 8 n ..)
+  uint2 ks[2];         // per-token keys: scale of tokens 4 g .. 4 g + 3 (column's group)
+  uint2 kz[2];         // per-token asymmetric keys: zero-points
+  uint2 vs[NP][2];     // value scales of tokens 4 g .. 4 g + 3 (row's group), tiles A, B
+  uint2 vz[NP][2];     // asymmetric values: zero-points
+  uint4 fs, fz;        // per-channel keys: scale / zero of the folding lane's 8 channels
+};
+
+// ---- the kernel ----------------------------------------------------------------------------
+
+struct DecodeLds {
+  // byte offsets inside the dynamic LDS block
+  static constexpr int red = 0;                                   // [WAVES][16][RED_STRIDE] f32
+  static constexpr int mw = red + WAVES * 16 * RED_STRIDE * 4;    // [WAVES][8] f32
+  static constexpr int lw = mw + WAVES * 8 * 4;                   // [WAVES][8] f32
+  static constexpr int zw = lw + WAVES * 8 * 4;                   // [WAVES][32] f32
+  static constexpr int ztw = zw + WAVES * 32 * 4;                 // [WAVES][8] f32
+  static constexpr int qs = ztw + WAVES * 8 * 4;                  // [8][D] bf16
+  static constexpr int pre = qs + 8 * D * 2;                      // [B + 1] int
+  // per-channel key folding buffer [WAVES][2][8][D] f16 overlays `red` (never live together)
+  static constexpr int kf = red;
+  static_assert(WAVES * 2 * 8 * D * 2 <= WAVES * 16 * RED_STRIDE * 4, "kf overlay");
+  static size_t bytes(int B) { return static_cast<size_t>(pre) + 4 * static_cast<size_t>(B + 1); }
+};
+
+// Work units of one sequence (per kv head), or -1 when its counters are out of range.
+__device__ __forceinline__ int seq_units(const CacheDev& c, int max_tokens, int b) {
+  const int nq = c.n_quant[b], nr = c.R > 0 ? c.n_res[b] : 0;
+  if (nq < 0 || nr < 0 || nr > c.R || (!c.table && nq > c.cap) ||
+      (c.table && (nq + TILE - 1) / TILE > c.max_blocks) || nq > max_tokens - nr)
+    return -1;
+  return (nq + 31) / 32 + (nr + 31) / 32;
+}
+
+template <int KB, int G, bool KPC, int NP, bool ASYM>
+__global__ __launch_bounds__(256, 3) void decode_kernel(DecodeParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const CacheDev& c = p.c;
+  const int B = c.B, H = c.H;
+  const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63;
+  const int g = lane >> 4, n = lane & 15;
+
+  float* red = reinterpret_cast<float*>(smem + DecodeLds::red);
+  float* mw = reinterpret_cast<float*>(smem + DecodeLds::mw);
+  float* lw = reinterpret_cast<float*>(smem + DecodeLds::lw);
+  float* zw = reinterpret_cast<float*>(smem + DecodeLds::zw);
+  float* ztw = reinterpret_cast<float*>(smem + DecodeLds::ztw);
+  uint16_t* qs = reinterpret_cast<uint16_t*>(smem + DecodeLds::qs);
+  int* pre = reinterpret_cast<int*>(smem + DecodeLds::pre);
+  uint16_t* kf = reinterpret_cast<uint16_t*>(smem + DecodeLds::kf) + wave * 2 * 8 * D;
+
+  // ---- units per sequence, prefix sum (every workgroup; workgroup 0 publishes it) ----
+  {
+    const int per = (B + 255) / 256;
+    int* scan = reinterpret_cast<int*>(red);
+    int s = 0;
+    for (int i = tid * per; i < min(B, (tid + 1) * per); i++) {
+      const int un = seq_units(c, p.max_tokens, i);
+      if (un < 0) {
+        if (blockIdx.x == 0) atomicOr(c.err, KVQ_ERR_TOKENS);
+      } else {
+        s += un * H;
+      }
+    }
+    scan[tid] = s;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int v = (tid >= off) ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    int run = scan[tid] - s;
+    for (int i = tid * per; i < min(B, (tid + 1) * per); i++) {
+      pre[i] = run;
+      run += max(seq_units(c, p.max_tokens, i), 0) * H;
+    }
+    if (tid == 255) pre[B] = scan[255];
+    __syncthreads();
+    if (blockIdx.x == 0)
+      for (int i = tid; i <= B; i += 256) p.ws_pre[i] = pre[i];
+  }
+
+  const int U = uni(pre[B]);
+  const long long NBl = gridDim.x;
+  const int u0 = static_cast<int>((static_cast<long long>(blockIdx.x) * U) / NBl);
+  const int u1 = static_cast<int>((static_cast<long long>(blockIdx.x + 1) * U) / NBl);
+
+  const int kgroup = c.k.group, vgroup = c.v.group;
+  const int ngk = KPC ? 2 : D / kgroup;  // QK columns per head: key groups, or hi/lo parts
+  const int ngv = D / vgroup;
+  constexpr float koff = ASYM ? 0.0f : static_cast<float>(1 << (KB - 1));
+  constexpr float voff = koff;
+  const int hh = n % G;          // query head of QK column n and of PV row 16 pp + n
+  const int cg = (n / G) % ngk;  // key group (or hi/lo part) of QK column n
+  constexpr int RBK = D * KB / 8;
+  constexpr long TILE_BYTES = static_cast<long>(TILE) * D * KB / 8;
+  constexpr int VCH = 4 * KB;  // bytes of a lane's value chunk
+
+  int u = u0;
+  bool first_seg = true;
+  while (u < u1) {
+    // ---- locate the segment: sequence b, kv head h, first unit kk ----
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= u) lo = mid; else hi = mid - 1;
+    }
+    const int b = uni(lo);
+    const int pb0 = uni(pre[b]);
+    const int ub = uni((pre[b + 1] - pb0) / H);
+    const int h = (u - pb0) / ub, kk = (u - pb0) % ub;
+    const int seg_abs_end = pb0 + (h + 1) * ub;
+    const int uend = min(u1, seg_abs_end);
+    const bool complete = (kk == 0) && (uend == seg_abs_end);
+    const int slot = first_seg ? 0 : 1;
+    const int nq = ld_uniform(c.n_quant + b);
+    const int nr = c.R > 0 ? ld_uniform(c.n_res + b) : 0;
+    const int uq = (nq + 31) / 32;
+    const int xend = kk + (uend - u);
+
+    // ---- stage the GQA group's query rows (bf16) ----
+    __syncthreads();
+    if (tid < G * (D / 8)) {
+      const uint4* src = reinterpret_cast<const uint4*>(
+          p.q + (static_cast<size_t>(b) * p.Hq + static_cast<size_t>(h) * G) * D);
+      reinterpret_cast<uint4*>(qs)[tid] = src[tid];
+    }
+    __syncthreads();
+
+    // ---- QK operand: f16 query, masked to the column's key group ----
+    f16x8 qb[4];
+    float qsum = 0.0f;  // asymmetric per-token keys: sum of q over the column's group
+    float zt = 0.0f;    // asymmetric per-channel keys: sum of q * zero over the key group
+    if constexpr (!KPC) {
+      const bool in_grp = ((32 * g) / kgroup) == cg;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const u16x8 raw = gather_kchan<KB>(qs + hh * D + 32 * g, j);
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+          const float x = in_grp ? bf16_to_f32(raw[i]) : 0.0f;
+          qb[j][i] = static_cast<_Float16>(x);
+          if constexpr (ASYM) qsum += x;
+        }
+      }
+      if constexpr (ASYM) {
+        qsum += __shfl_xor(qsum, 16);
+        qsum += __shfl_xor(qsum, 32);
+      }
+    }
+
+    float m_run = -FLT_MAX, l_run = 0.0f;
+    f32x4 acc[NP][8];
+#pragma unroll
+    for (int pp = 0; pp < NP; pp++)
+#pragma unroll
+      for (int j = 0; j < 8; j++) acc[pp][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float zacc[NP];
+#pragma unroll
+    for (int pp = 0; pp < NP; pp++) zacc[pp] = 0.0f;
+
+    // PV row roles: row 16 pp + n is (part, value group, head hh)
+    int rpart[NP], rgv[NP];
+#pragma unroll
+    for (int pp = 0; pp < NP; pp++) {
+      const int row = 16 * pp + n;
+      rpart[pp] = row / (G * ngv);
+      rgv[pp] = (row / G) % ngv;
+    }
+
+    // ---- online softmax over the 8 raw scores of a pair; returns the weights in s2 ----
+    // m_run is in log2 units; weights are exp2(score * sm_log2 - m_run).  The running max starts
+    // at a finite sentinel, so empty waves never form inf - inf.
+    auto softmax = [&](float (&s2)[8], int nvA, int nvB) {
+      const bool full = nvA == 16 && nvB == 16;
+      if (!full) {
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+          if (4 * g + (i & 3) >= (i < 4 ? nvA : nvB)) s2[i] = -INFINITY;
+      }
+      float tmax = fmaxf(fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3])),
+                         fmaxf(fmaxf(s2[4], s2[5]), fmaxf(s2[6], s2[7])));
+      tmax *= p.sm_log2;
+      if (__ballot(tmax > m_run + LAZY_LOG2) != 0) {
+        float hm = fmaxf(tmax, __shfl_xor(tmax, 16));
+        hm = fmaxf(hm, __shfl_xor(hm, 32));
+        const float mn = fmaxf(m_run, hm);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+        l_run *= alpha;
+#pragma unroll
+        for (int pp = 0; pp < NP; pp++) zacc[pp] *= alpha;
+        float al[G];
+#pragma unroll
+        for (int q = 0; q < G; q++)
+          al[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), q));
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          float a;
+          if constexpr (G <= 4) a = al[r % G];
+          else a = (g & 1) ? al[4 + r] : al[r];
+#pragma unroll
+          for (int pp = 0; pp < NP; pp++)
+#pragma unroll
+            for (int j = 0; j < 8; j++) acc[pp][j][r] *= a;
+        }
+        m_run = mn;
+      }
+      float ls = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        s2[i] = __builtin_amdgcn_exp2f(fmaf(s2[i], p.sm_log2, -m_run));  // -inf -> 0
+        ls += s2[i];
+      }
+      l_run += ls;
+    };
+
+    // sum the per-group (or hi/lo) columns of one head, for 8 scores at once
+    auto fold_cols8 = [&](float (&v)[8]) {
+      if (ngk >= 2) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) v[i] += row_ror<G>(v[i]);
+        if constexpr (2 * G < 16) {
+          if (ngk >= 4) {
+#pragma unroll
+            for (int i = 0; i < 8; i++) v[i] += row_ror<2 * G>(v[i]);
+          }
+        }
+      }
+    };
+
+    int x = kk + wave;
+    const int xq_end = min(xend, uq);
+
+    // ---------------------------- compressed units ----------------------------
+    if (x < xq_end) {
+      const long seq_tile0 = (static_cast<long>(b) * H + h) * (c.cap / TILE);
+      const int* trow = c.table ? c.table + static_cast<size_t>(b) * c.max_blocks : nullptr;
+      // physical tile of sequence tile t, or -1 for an unusable block-table entry
+      auto phys_of = [&](int t) -> long {
+        if (!trow) return seq_tile0 + t;
+        const int blk = ld_uniform(trow + t);
+        if (blk < 0 || blk >= c.num_blocks) return -1;
+        return static_cast<long>(blk) * H + h;
+      };
+      const int fold_c0 = 8 * (lane & 15);  // per-channel keys: channels this lane folds
+      auto kpc_meta = [&](int tau) -> size_t {
+        return ((static_cast<size_t>(b) * H + h) * (c.cap / kgroup) + tau) * D + fold_c0;
+      };
+
+      UnitData<KB, NP, KPC, ASYM> d{};
+      const UnpackRegs ur = unpack_regs<KB>();
+      bool bad_block = false;
+      // Every unit issues the same loads (an unusable or absent tile reads tile 0 of the buffer
+      // and is ignored), so the compiler can count outstanding loads exactly.
+      auto load_k = [&](int xx, long pA, long pB) {
+        pA = max(pA, 0L);
+        pB = max(pB, 0L);
+        load_words<KB>(c.kc + pA * TILE_BYTES + n * RBK + g * (RBK / 4), d.kw[0]);
+        load_words<KB>(c.kc + pB * TILE_BYTES + n * RBK + g * (RBK / 4), d.kw[1]);
+        if constexpr (KPC) {
+          const size_t mi = kpc_meta((32 * xx) / kgroup);
+          d.fs = *reinterpret_cast<const uint4*>(c.ks + mi);
+          if constexpr (ASYM) d.fz = *reinterpret_cast<const uint4*>(c.kz + mi);
+        } else {
+#pragma unroll
+          for (int t = 0; t < 2; t++) {
+            const long pt = t ? pB : pA;
+            const size_t mi = (static_cast<size_t>(pt) * ngk + cg) * TILE + 4 * g;
+            d.ks[t] = *reinterpret_cast<const uint2*>(c.ks + mi);
+            if constexpr (ASYM) d.kz[t] = *reinterpret_cast<const uint2*>(c.kz + mi);
+          }
+        }
+      };
+      auto load_v = [&](long pA, long pB) {
+        pA = max(pA, 0L);
+        pB = max(pB, 0L);
+        load_words<KB>(c.vc + pA * TILE_BYTES + (g * (D / 8) + n) * VCH, d.vw[0]);
+        load_words<KB>(c.vc + pB * TILE_BYTES + (g * (D / 8) + n) * VCH, d.vw[1]);
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+          const long pt = t ? pB : pA;
+#pragma unroll
+          for (int pp = 0; pp < NP; pp++) {
+            const size_t mi = (static_cast<size_t>(pt) * ngv + rgv[pp]) * TILE + 4 * g;
+            d.vs[pp][t] = *reinterpret_cast<const uint2*>(c.vs + mi);
+            if constexpr (ASYM) d.vz[pp][t] = *reinterpret_cast<const uint2*>(c.vz + mi);
+          }
+        }
+      };
+      // per-channel keys: fold one key group's scales (and zero-points) into the query
+      auto kpc_fold = [&](uint4 fs, uint4 fz) {
+        const uint32_t sw[4] = {fs.x, fs.y, fs.z, fs.w};
+        const uint32_t zwd[4] = {fz.x, fz.y, fz.z, fz.w};
+#pragma unroll
+        for (int r0 = 0; r0 < G; r0 += 4) {
+          const int hw = r0 + (lane >> 4);
+          float zp = 0.0f;
+          if (hw < G) {
+            const u16x8 q8 = *reinterpret_cast<const u16x8*>(qs + hw * D + fold_c0);
+            u16x8 hi8, lo8;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+              const float qv = bf16_to_f32(q8[i]);
+              const float sv = (i & 1) ? f16_hi(sw[i / 2]) : f16_lo(sw[i / 2]);
+              const float pv = qv * sv;  // exact: 8-bit x 11-bit significands
+              const _Float16 ph = static_cast<_Float16>(pv);
+              const _Float16 pl = static_cast<_Float16>(pv - static_cast<float>(ph));
+              hi8[i] = __builtin_bit_cast(unsigned short, ph);
+              lo8[i] = __builtin_bit_cast(unsigned short, pl);
+              if constexpr (ASYM) zp += qv * ((i & 1) ? f16_hi(zwd[i / 2]) : f16_lo(zwd[i / 2]));
+            }
+            *reinterpret_cast<u16x8*>(kf + hw * D + fold_c0) = hi8;
+            *reinterpret_cast<u16x8*>(kf + (8 + hw) * D + fold_c0) = lo8;
+          }
+          if constexpr (ASYM) {
+            zp += row_ror<8>(zp);
+            zp += row_ror<4>(zp);
+            zp += row_ror<2>(zp);
+            zp += row_ror<1>(zp);
+            if ((lane & 15) == 0 && hw < G) ztw[wave * 8 + hw] = zp;
+          }
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+          qb[j] = __builtin_bit_cast(f16x8, gather_kchan<KB>(kf + (cg * 8 + hh) * D + 32 * g, j));
+        if constexpr (ASYM) zt = ztw[wave * 8 + hh];
+        wave_lds_sync();
+      };
+
+      long pA = phys_of(2 * x);
+      long pB = (32 * x + 16 < nq) ? phys_of(2 * x + 1) : -1;
+      load_k(x, pA, pB);
+      load_v(pA, pB);
+      for (; x < xq_end; x += WAVES) {
+        const int xn = x + WAVES;
+        const bool more = xn < xq_end;
+        // after the last unit, reload the current tiles (cache hits) so the load count per
+        // iteration stays fixed
+        const long nA = more ? phys_of(2 * xn) : pA;
+        const long nB = more ? ((32 * xn + 16 < nq) ? phys_of(2 * xn + 1) : -1) : pB;
+        // valid tokens of tiles A and B (a tile whose block is unusable counts as empty)
+        const int nvA = pA >= 0 ? min(16, nq - 32 * x) : 0;
+        const int nvB = pB >= 0 ? min(16, nq - 32 * x - 16) : 0;
+        bad_block |= pA < 0 || (32 * x + 16 < nq && pB < 0);
+
+        // ---- QK^T of both tiles (two independent MFMA chains, interleaved) ----
+        // Tiles past the sequence end hold finite codes of a stand-in tile; their scores are
+        // masked below, so the MFMAs run unconditionally.
+        if constexpr (KPC) kpc_fold(d.fs, d.fz);
+        f32x4 dq[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        if constexpr (KPC) {
+          if (kgroup == 16 && nvB > 0) {
+            // tile B opens its own key group: finish tile A with the current fold first
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+              dq[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop<KB>(d.kw[0], j, koff, ur), qb[j], dq[0], 0, 0, 0);
+            const size_t mi = kpc_meta(2 * x + 1);
+            const uint4 fs2 = *reinterpret_cast<const uint4*>(c.ks + mi);
+            uint4 fz2 = uint4{0, 0, 0, 0};
+            if constexpr (ASYM) fz2 = *reinterpret_cast<const uint4*>(c.kz + mi);
+            kpc_fold(fs2, fz2);
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+              dq[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop<KB>(d.kw[1], j, koff, ur), qb[j], dq[1], 0, 0, 0);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+              dq[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop<KB>(d.kw[0], j, koff, ur), qb[j], dq[0], 0, 0, 0);
+              dq[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop<KB>(d.kw[1], j, koff, ur), qb[j], dq[1], 0, 0, 0);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            dq[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop<KB>(d.kw[0], j, koff, ur), qb[j], dq[0], 0, 0, 0);
+            dq[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop<KB>(d.kw[1], j, koff, ur), qb[j], dq[1], 0, 0, 0);
+          }
+        }
+        float s2[8];
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+          if constexpr (KPC) {
+#pragma unroll
+            for (int r = 0; r < 4; r++) s2[4 * t + r] = dq[t][r] + row_ror<G>(dq[t][r]) + zt;
+          } else {
+            const uint2 k2 = d.ks[t];
+            s2[4 * t + 0] = dq[t][0] * f16_lo(k2.x);
+            s2[4 * t + 1] = dq[t][1] * f16_hi(k2.x);
+            s2[4 * t + 2] = dq[t][2] * f16_lo(k2.y);
+            s2[4 * t + 3] = dq[t][3] * f16_hi(k2.y);
+            if constexpr (ASYM) {
+              const uint2 z2 = d.kz[t];
+              s2[4 * t + 0] += f16_lo(z2.x) * qsum;
+              s2[4 * t + 1] += f16_hi(z2.x) * qsum;
+              s2[4 * t + 2] += f16_lo(z2.y) * qsum;
+              s2[4 * t + 3] += f16_hi(z2.y) * qsum;
+            }
+          }
+        }
+        if constexpr (!KPC) fold_cols8(s2);
+        load_k(more ? xn : x, nA, nB);  // key registers are free again
+
+        softmax(s2, nvA, nvB);  // s2 now holds the weights
+
+        // ---- P rows (hi / lo f16 parts of w * s_v) and PV ----
+        // Rows 16 pp + n with part >= 2 are never read back, so they are left as computed.
+        // A stand-in tile's scales may be anything: its tokens' products are selected away.
+        const bool full = nvA == 16 && nvB == 16;
+        f16x8 pa[NP];
+#pragma unroll
+        for (int pp = 0; pp < NP; pp++) {
+          const float sel = (rpart[pp] == 1) ? 1.0f : 0.0f;
+          float ws[8];
+#pragma unroll
+          for (int t = 0; t < 2; t++) {
+            const uint2 s2v = d.vs[pp][t];
+            ws[4 * t + 0] = s2[4 * t + 0] * f16_lo(s2v.x);
+            ws[4 * t + 1] = s2[4 * t + 1] * f16_hi(s2v.x);
+            ws[4 * t + 2] = s2[4 * t + 2] * f16_lo(s2v.y);
+            ws[4 * t + 3] = s2[4 * t + 3] * f16_hi(s2v.y);
+            if constexpr (ASYM) {
+              const uint2 z2v = d.vz[pp][t];
+              const float zv[4] = {f16_lo(z2v.x), f16_hi(z2v.x), f16_lo(z2v.y), f16_hi(z2v.y)};
+              float zp = 0.0f;
+#pragma unroll
+              for (int r = 0; r < 4; r++) zp += (full || s2[4 * t + r] != 0.0f) ? s2[4 * t + r] * zv[r] : 0.0f;
+              zacc[pp] += zp;
+            }
+          }
+          if (!full) {
+#pragma unroll
+            for (int i = 0; i < 8; i++) ws[i] = (s2[i] != 0.0f) ? ws[i] : 0.0f;
+          }
+          uint32_t pk[4];
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const f16x2 hi2 = pkrtz(ws[2 * i], ws[2 * i + 1]);
+            const float r0 = fmaf(-sel, static_cast<float>(hi2[0]), ws[2 * i]);
+            const float r1 = fmaf(-sel, static_cast<float>(hi2[1]), ws[2 * i + 1]);
+            pk[i] = h2_bits(pkrtz(r0, r1));
+          }
+          pa[pp] = __builtin_bit_cast(f16x8, uint4{pk[0], pk[1], pk[2], pk[3]});
+        }
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+          const f16x8 vb = vop<KB>(d.vw[0], d.vw[1], j, voff, ur);
+#pragma unroll
+          for (int pp = 0; pp < NP; pp++)
+            acc[pp][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[pp], vb, acc[pp][j], 0, 0, 0);
+        }
+        load_v(nA, nB);  // value registers are free again
+        pA = nA;
+        pB = nB;
+      }
+      if (bad_block && lane == 0) atomicOr(c.err, KVQ_ERR_BLOCK);
+    }
+
+    // ---------------------------- BF16 window units ----------------------------
+    if (x < xend) {
+      // bf16 query operand in natural channel order, masked like the f16 one
+      bf16x8 qw[4];
+      const bool keep = KPC ? (cg == 0) : (((32 * g) / kgroup) == cg);
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        u16x8 raw = *reinterpret_cast<const u16x8*>(qs + hh * D + 32 * g + 8 * j);
+        if (!keep) raw = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        qw[j] = __builtin_bit_cast(bf16x8, raw);
+      }
+      const uint16_t* kr = c.kres + (static_cast<size_t>(b) * H + h) * c.R * D;
+      const uint16_t* vr = c.vres + (static_cast<size_t>(b) * H + h) * c.R * D;
+      for (; x < xend; x += WAVES) {
+        const int r0 = 32 * (x - uq);
+        const int nvA = min(16, nr - r0), nvB = max(0, min(16, nr - r0 - 16));
+        float s2[8];
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+          f32x4 dq = f32x4{0.f, 0.f, 0.f, 0.f};
+          if ((t ? nvB : nvA) > 0) {
+            const uint4* rowp = reinterpret_cast<const uint4*>(kr + (r0 + 16 * t + n) * D + 32 * g);
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+              dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rowp[j]), qw[j],
+                                                           dq, 0, 0, 0);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; r++) s2[4 * t + r] = dq[r];
+        }
+        fold_cols8(s2);
+        softmax(s2, nvA, nvB);
+        // P rows: bf16 hi / lo parts of w (truncation; hi + lo carries 16 significant bits)
+        bf16x8 pb[NP];
+#pragma unroll
+        for (int pp = 0; pp < NP; pp++) {
+          uint32_t pk[4];
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            uint32_t e2[2];
+#pragma unroll
+            for (int k2 = 0; k2 < 2; k2++) {
+              const float wv = s2[2 * i + k2];
+              const float lo_v = wv - __uint_as_float(__float_as_uint(wv) & 0xFFFF0000u);
+              e2[k2] = __float_as_uint(rpart[pp] == 1 ? lo_v : wv) >> 16;
+            }
+            pk[i] = e2[0] | (e2[1] << 16);
+          }
+          pb[pp] = __builtin_bit_cast(bf16x8, uint4{pk[0], pk[1], pk[2], pk[3]});
+        }
+        // V rows of tokens (tile A 4g..4g+3, tile B 4g..4g+3), channels 8n .. 8n+7, in two halves
+#pragma unroll
+        for (int hf = 0; hf < 2; hf++) {
+          uint2 vrow[8];
+#pragma unroll
+          for (int i = 0; i < 8; i++) {
+            const int t = i / 4, row = r0 + 16 * t + 4 * g + (i % 4);
+            const bool ok = 4 * g + (i % 4) < (t ? nvB : nvA);
+            vrow[i] = ok ? *reinterpret_cast<const uint2*>(vr + row * D + 8 * n + 4 * hf) : uint2{0, 0};
+          }
+#pragma unroll
+          for (int jj = 0; jj < 4; jj++) {
+            u16x8 col;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+              const uint32_t wv = (jj < 2) ? vrow[i].x : vrow[i].y;
+              col[i] = static_cast<unsigned short>((jj & 1) ? (wv >> 16) : (wv & 0xFFFFu));
+            }
+            const int j = 4 * hf + jj;
+#pragma unroll
+            for (int pp = 0; pp < NP; pp++)
+              acc[pp][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb[pp], __builtin_bit_cast(bf16x8, col),
+                                                                   acc[pp][j], 0, 0, 0);
+          }
+        }
+      }
+    }
+
+    // ---------------------------- merge the four waves ----------------------------
+    float lsum = l_run + __shfl_xor(l_run, 16);
+    lsum += __shfl_xor(lsum, 32);
+    float zs[NP];
+#pragma unroll
+    for (int pp = 0; pp < NP; pp++) {
+      zs[pp] = zacc[pp] + __shfl_xor(zacc[pp], 16);
+      zs[pp] += __shfl_xor(zs[pp], 32);
+    }
+    __syncthreads();  // every wave is done with kf (overlays red)
+    if (lane < G) {
+      mw[wave * 8 + lane] = m_run;
+      lw[wave * 8 + lane] = lsum;
+    }
+    if (lane < 16) {
+#pragma unroll
+      for (int pp = 0; pp < NP; pp++) zw[wave * 32 + 16 * pp + lane] = zs[pp];
+    }
+    constexpr int NO = (G * D + 255) / 256;
+    float O[NO], Mx[NO], e[NO][WAVES];
+#pragma unroll
+    for (int pp = 0; pp < NP; pp++) {
+      if (pp > 0) __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 8; j++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) red[(wave * 16 + 4 * g + r) * RED_STRIDE + 8 * n + j] = acc[pp][j][r];
+      __syncthreads();
+#pragma unroll
+      for (int oi = 0; oi < NO; oi++) {
+        const int o = tid + 256 * oi;
+        if (o >= G * D) continue;
+        const int oh = o / D, ch = o % D;
+        const int gv = ch / vgroup;
+        if (pp == 0) {
+          float M = -FLT_MAX;
+#pragma unroll
+          for (int wv = 0; wv < WAVES; wv++) M = fmaxf(M, mw[wv * 8 + oh]);
+          Mx[oi] = M;
+          O[oi] = 0.0f;
+#pragma unroll
+          for (int wv = 0; wv < WAVES; wv++) {
+            const float mv = mw[wv * 8 + oh];
+            e[oi][wv] = __builtin_amdgcn_exp2f(mv - M);  // waves without tokens hold -FLT_MAX
+          }
+          if constexpr (ASYM) {
+            const int row0 = gv * G + oh;
+#pragma unroll
+            for (int wv = 0; wv < WAVES; wv++) O[oi] += e[oi][wv] * zw[wv * 32 + row0];
+          }
+        }
+#pragma unroll
+        for (int part = 0; part < 2; part++) {
+          const int row = (part * ngv + gv) * G + oh;
+          if (row / 16 != pp) continue;
+#pragma unroll
+          for (int wv = 0; wv < WAVES; wv++)
+            O[oi] += e[oi][wv] * red[(wv * 16 + row % 16) * RED_STRIDE + ch];
+        }
+      }
+    }
+#pragma unroll
+    for (int oi = 0; oi < NO; oi++) {
+      const int o = tid + 256 * oi;
+      if (o >= G * D) continue;
+      const int oh = o / D, ch = o % D;
+      float L = 0.0f;
+#pragma unroll
+      for (int wv = 0; wv < WAVES; wv++) L += e[oi][wv] * lw[wv * 8 + oh];
+      if (complete) {
+        p.out[(static_cast<size_t>(b) * p.Hq + static_cast<size_t>(h) * G + oh) * D + ch] =
+            (L > 0.0f) ? O[oi] / L : 0.0f;
+      } else {
+        float* part =
+            p.ws_part + ((static_cast<size_t>(blockIdx.x) * 2 + slot) * G + oh) * PART_STRIDE;
+        if (ch == 0) {
+          part[0] = Mx[oi];
+          part[1] = L;
+        }
+        part[4 + ch] = O[oi];
+      }
+    }
+    u = uend;
+    first_seg = false;
+  }
+}
+
+// First workgroup whose unit range [k U / NB, (k+1) U / NB) contains unit u.
+__device__ __forceinline__ int block_of(long long u, long long U, long long NB) {
+  return static_cast<int>(((u + 1) * NB - 1) / U);
+}
+
+// Merge the partials of each (sequence, kv head) that more than one workgroup worked on; write
+// zeros for empty sequences.  One workgroup per (sequence, kv head).
+template <int G>
+__global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
+  const int H = p.c.H, B = p.c.B;
+  const int b = blockIdx.x / H, h = blockIdx.x % H;
+  const int* pre = p.ws_pre;
+  const long long U = pre[B], NB = p.nblocks;
+  const int ub = (pre[b + 1] - pre[b]) / H;
+  float* dst = p.out + (static_cast<size_t>(b) * p.Hq + static_cast<size_t>(h) * G) * D;
+  if (ub == 0) {
+    for (int o = threadIdx.x; o < G * D; o += 256) dst[o] = 0.0f;
+    return;
+  }
+  const long long us = pre[b] + static_cast<long long>(h) * ub, ue = us + ub;
+  const int kf = block_of(us, U, NB), kl = block_of(ue - 1, U, NB);
+  if (kf == kl) return;  // one workgroup saw the whole sequence and wrote the output
+  const int s0 = ((static_cast<long long>(kf) * U) / NB == us) ? 0 : 1;
+  constexpr int NO = (G * D + 255) / 256;
+#pragma unroll
+  for (int oi = 0; oi < NO; oi++) {
+    const int o = threadIdx.x + 256 * oi;
+    if (o >= G * D) continue;
+    const int oh = o / D, ch = o % D;
+    auto part_of = [&](int k) -> const float* {
+      const int s = (k == kf) ? s0 : 0;
+      return p.ws_part + ((static_cast<size_t>(k) * 2 + s) * G + oh) * PART_STRIDE;
+    };
+    // a workgroup whose unit range is empty wrote nothing
+    auto empty = [&](int k) {
+      return (static_cast<long long>(k) * U) / NB == (static_cast<long long>(k + 1) * U) / NB;
+    };
+    float M = -INFINITY;
+    for (int k = kf; k <= kl; k++)
+      if (!empty(k)) M = fmaxf(M, part_of(k)[0]);
+    float L = 0.0f, O = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll 8
+      for (int k = kf; k <= kl; k++) {
+        if (empty(k)) continue;
+        const float* pt = part_of(k);
+        const float m = pt[0];
+        const float e = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+        L += e * pt[1];
+        O += e * pt[4 + ch];
+      }
+    }
+    dst[o] = (L > 0.0f) ? O / L : 0.0f;
+  }
+}
+
+// Workgroups of decode_kernel that are resident at once on the current device.  Each workgroup
+// owns 1/NB of the units, so the grid must never exceed what runs concurrently.
+template <int KB, int G, bool KPC, int NP, bool ASYM>
+int decode_resident_blocks(size_t lds) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<KB, G, KPC, NP, ASYM>,
+                                                   256, lds) != hipSuccess)
+    return 0;
+  return cus * per_cu;
+}
+
+template <int KB, int G, bool KPC, int NP, bool ASYM>
+hipError_t launch_decode_t(const DecodeParams& p0, hipStream_t s) {
+  DecodeParams p = p0;
+  const size_t lds = DecodeLds::bytes(p.c.B);
+  const int resident = decode_resident_blocks<KB, G, KPC, NP, ASYM>(lds);
+  if (resident <= 0) return hipErrorInvalidConfiguration;
+  if (p.nblocks > resident) p.nblocks = resident;
+  decode_kernel<KB, G, KPC, NP, ASYM><<<p.nblocks, 256, lds, s>>>(p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  combine_kernel<G><<<p.c.B * p.c.H, 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+template <int KB, bool ASYM>
+hipError_t launch_decode_bits(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s) {
+#define KVQ_CASE(GG, NN)                                                        \
+  if (G == GG && NP == NN)                                                      \
+    return kpc ? launch_decode_t<KB, GG, true, NN, ASYM>(p, s)                 \
+               : launch_decode_t<KB, GG, false, NN, ASYM>(p, s);
+  KVQ_CASE(1, 1)
+  KVQ_CASE(2, 1)
+  KVQ_CASE(4, 1)
+  KVQ_CASE(4, 2)
+  KVQ_CASE(8, 1)
+  KVQ_CASE(8, 2)
+#undef KVQ_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvq

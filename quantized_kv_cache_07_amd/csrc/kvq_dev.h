@@ -60,14 +60,15 @@ __device__ __forceinline__ long tile_index(const CacheDev& c, int b, int h, int 
 // Decode-attention launch parameters.
 struct DecodeParams {
   CacheDev c;
-  const uint16_t* q;   // [B][Hq][D] bf16
-  float* out;          // [B][Hq][D] fp32
-  int32_t* ws_prefix;  // [B + 1] first work item of each sequence
-  float* ws_ml;        // [items_cap][H][G][2] running max (log2 domain), sum
-  float* ws_acc;       // [items_cap][H][G][D] unnormalised output
-  int Hq, chunk, items_cap, max_tokens;
-  float sm_log2;       // sm_scale * log2(e)
+  const uint16_t* q;  // [B][Hq][D] bf16
+  float* out;         // [B][Hq][D] fp32
+  int32_t* ws_pre;    // [B + 1] prefix over sequences of work units (all kv heads)
+  float* ws_part;     // [nblocks][2][G][PART_STRIDE] partial (max, sum, pad, pad, o[D])
+  int Hq, max_tokens, nblocks;
+  float sm_log2;      // sm_scale * log2(e)
 };
+
+constexpr int PART_STRIDE = D + 4;
 
 // Slots one append/flush call moves into the compressed cache (F), window tokens before the
 // call plus new tokens (total), and window length afterwards.  Equal, by construction, to

@@ -12,10 +12,12 @@ namespace kvq {
 
 hipError_t launch_append(const CacheDev& c, const uint16_t* knew, const uint16_t* vnew, int n_new,
                          int mode, hipStream_t stream);
-size_t decode_lds_bytes(int B);
-
-hipError_t launch_decode(const DecodeParams& p, int bits, int GQ, int NP, bool kpc, int grid,
-                         hipStream_t s);
+hipError_t launch_decode_b2s(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s);
+hipError_t launch_decode_b4s(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s);
+hipError_t launch_decode_b8s(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s);
+hipError_t launch_decode_b2a(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s);
+hipError_t launch_decode_b4a(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s);
+hipError_t launch_decode_b8a(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s);
 
 namespace {
 
@@ -45,6 +47,7 @@ kvq_status check_format(const kvq_format* f) {
   s = check_side(f->v, false, f->residual);
   if (s != KVQ_OK) return s;
   if (f->k.bits != f->v.bits) return KVQ_ENOTSUP;
+  if (f->k.scheme != f->v.scheme) return KVQ_ENOTSUP;
   return KVQ_OK;
 }
 
@@ -104,37 +107,37 @@ CacheDev to_dev(const kvq_cache* c) {
   return d;
 }
 
-// Slots per work unit of the decode split: the largest of 1024..128 (multiple of 16) that still
-// gives about 2048 units (8 waves per CU), chunks of one sequence balanced in length.
-int pick_chunk(int B, int H, int max_tokens) {
-  if (const char* e = std::getenv("KVQ_CHUNK")) {
-    int v = std::atoi(e);
-    if (v >= TILE && v <= 1024 && v % TILE == 0) return v;
-  }
-  int ch = 1024;
-  while (ch > 128 && static_cast<long>(B) * H * ((max_tokens + ch - 1) / ch) < 2048) ch >>= 1;
-  const int n = (max_tokens + ch - 1) / ch;          // chunks of the longest sequence
-  int even = (max_tokens + n - 1) / n;                // balanced length
-  even = (even + TILE - 1) / TILE * TILE;
-  return even < TILE ? TILE : (even > 1024 ? 1024 : even);
+// Decode work units are 32 compressed slots or 32 window rows of one (sequence, kv head); the
+// grid is persistent (about four workgroups per compute unit), each workgroup owning a
+// contiguous range of units.  The workspace holds the unit prefix sum and two partial slots
+// per workgroup.
+struct WsLayout {
+  int G, nblocks;
+  size_t pre_off, part_off, total;
+};
+
+long units_bound(const kvq_cache* c, int max_tokens) {
+  const long per_seq = (static_cast<long>(max_tokens) + 31) / 32 + 1;
+  return static_cast<long>(c->batch) * c->n_kv_heads * per_seq;
 }
 
-struct WsLayout {
-  int chunk, items_cap, G;
-  size_t prefix_off, ml_off, acc_off, total;
-};
+int device_cus();
 
 WsLayout ws_layout(const kvq_cache* c, int n_q_heads, int max_tokens) {
   WsLayout w;
   w.G = n_q_heads / c->n_kv_heads;
-  w.chunk = pick_chunk(c->batch, c->n_kv_heads, max_tokens);
-  const long per_seq = (max_tokens + w.chunk - 1) / w.chunk;
-  w.items_cap = static_cast<int>(static_cast<long>(c->batch) * (per_seq < 1 ? 1 : per_seq));
-  w.prefix_off = 0;
-  w.ml_off = ((static_cast<size_t>(c->batch) + 1) * 4 + 255) & ~static_cast<size_t>(255);
-  w.acc_off = w.ml_off + ((static_cast<size_t>(w.items_cap) * c->n_kv_heads * w.G * 2 * 4 + 255) &
-                          ~static_cast<size_t>(255));
-  w.total = w.acc_off + static_cast<size_t>(w.items_cap) * c->n_kv_heads * w.G * D * 4;
+  long nb = static_cast<long>(device_cus()) * 4;
+  if (const char* e = std::getenv("KVQ_DECODE_BLOCKS")) {
+    const long v = std::atol(e);
+    if (v >= 1 && v <= 65536) nb = v;
+  }
+  const long ub = units_bound(c, max_tokens);
+  if (nb > ub) nb = ub;
+  if (nb < 1) nb = 1;
+  w.nblocks = static_cast<int>(nb);
+  w.pre_off = 0;
+  w.part_off = ((static_cast<size_t>(c->batch) + 1) * 4 + 255) & ~static_cast<size_t>(255);
+  w.total = w.part_off + static_cast<size_t>(w.nblocks) * 2 * w.G * PART_STRIDE * 4;
   return w;
 }
 
@@ -266,33 +269,35 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int32_t n
   const WsLayout w = ws_layout(cache, n_q_heads, max_tokens);
   if (workspace_bytes < w.total) return KVQ_ENOSPACE;
   const int ngv = D / cache->fmt.v.group;
-  const int NP = (2 * G * ngv + 15) / 16;
+  const int rows = 2 * G * ngv;  // PV rows: (hi/lo part, value group, query head)
+  if (rows > 32) return KVQ_ENOTSUP;
+  const int NP = rows > 16 ? 2 : 1;
+  if (units_bound(cache, max_tokens) * 64 >= (1L << 31)) return KVQ_ENOTSUP;
 
   DecodeParams p;
   p.c = to_dev(cache);
   p.q = static_cast<const uint16_t*>(q);
   p.out = out;
   char* ws = static_cast<char*>(workspace);
-  p.ws_prefix = reinterpret_cast<int32_t*>(ws + w.prefix_off);
-  p.ws_ml = reinterpret_cast<float*>(ws + w.ml_off);
-  p.ws_acc = reinterpret_cast<float*>(ws + w.acc_off);
+  p.ws_pre = reinterpret_cast<int32_t*>(ws + w.pre_off);
+  p.ws_part = reinterpret_cast<float*>(ws + w.part_off);
   p.Hq = n_q_heads;
-  p.chunk = w.chunk;
-  p.items_cap = w.items_cap;
   p.max_tokens = max_tokens;
+  p.nblocks = w.nblocks;
   p.sm_log2 = sm_scale * 1.4426950408889634f;
 
-  const long units = static_cast<long>(w.items_cap) * cache->n_kv_heads;
-  long grid = (units + 3) / 4;
-  const long cap = static_cast<long>(device_cus()) * 4;
-  if (grid > cap) grid = cap;
-  if (grid < 1) grid = 1;
   if (std::getenv("KVQ_DEBUG"))
-    fprintf(stderr, "[kvq] decode B=%d H=%d G=%d bits=%d chunk=%d items_cap=%d grid=%ld lds=%zu\n",
-            cache->batch, cache->n_kv_heads, G, cache->fmt.k.bits, w.chunk, w.items_cap, grid,
-            decode_lds_bytes(cache->batch));
-  hipError_t e = launch_decode(p, cache->fmt.k.bits, G, NP,
-                               kpc, static_cast<int>(grid), static_cast<hipStream_t>(stream));
+    fprintf(stderr, "[kvq] decode B=%d H=%d G=%d bits=%d NP=%d kpc=%d blocks=%d ws=%zu\n",
+            cache->batch, cache->n_kv_heads, G, cache->fmt.k.bits, NP, kpc ? 1 : 0, w.nblocks,
+            w.total);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  const bool asym = cache->fmt.k.scheme == KVQ_ASYM;
+  switch (cache->fmt.k.bits) {
+    case 2: e = asym ? launch_decode_b2a(p, G, NP, kpc, st) : launch_decode_b2s(p, G, NP, kpc, st); break;
+    case 4: e = asym ? launch_decode_b4a(p, G, NP, kpc, st) : launch_decode_b4s(p, G, NP, kpc, st); break;
+    default: e = asym ? launch_decode_b8a(p, G, NP, kpc, st) : launch_decode_b8s(p, G, NP, kpc, st); break;
+  }
   return e == hipSuccess ? KVQ_OK : KVQ_ELAUNCH;
 }
 
