@@ -103,6 +103,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(CacheDev c, const uint16_
                                                        const uint16_t* vnew, int n_new, int mode) {
   __shared__ uint8_t lk[S][D];
   __shared__ uint8_t lv[S][D];
+  __shared__ __align__(16) uint16_t xs[S][2][D];  // pending bf16 rows (keys, values)
   __shared__ uint16_t mk_s[S * 4], mk_z[S * 4], mv_s[S * 4], mv_z[S * 4];
   __shared__ uint16_t pc_s[D], pc_z[D];
   __shared__ int s_ok;
@@ -136,54 +137,105 @@ __global__ __launch_bounds__(256) void quantize_kernel(CacheDev c, const uint16_
   const SideDev K = c.k, V = c.v;
   const int ngk = (K.axis == KVQ_PER_TOKEN) ? D / K.group : 0;
   const int ngv = D / V.group;
-  const int nk_items = (K.axis == KVQ_PER_TOKEN) ? S * ngk : D;
-  const int nv_items = S * ngv;
 
-  // Phase 1: codes and metadata of this segment into LDS.
-  for (int it = tid; it < nk_items + nv_items; it += blockDim.x) {
-    if (it < nk_items) {
-      if (K.axis == KVQ_PER_TOKEN) {
-        const int j = it / ngk, g = it % ngk;
-        const int slot = seg0 + j;
-        if (slot < lo || slot >= hi) continue;
-        const uint16_t* row = pending_row(c, knew, n_new, b, h, slot - nq, nr, true) + g * K.group;
-        auto get = [&](int i) { return bf16_to_f32(row[i]); };
-        uint16_t s16 = 0, z16 = 0;
-        if (K.scheme == KVQ_SYM)
-          quant_sym(get, K.group, K.bits, s16, &lk[j][g * K.group], 1);
-        else
-          quant_asym(get, K.group, K.bits, s16, z16, &lk[j][g * K.group], 1);
-        mk_s[j * 4 + g] = s16;
-        mk_z[j * 4 + g] = z16;
+  // Phase 0: the pending bf16 rows of this segment into LDS (16-byte pieces).
+  {
+    const int pieces = D * 2 / 16;
+    const int n_items = (hi - lo) * 2 * pieces;
+    for (int it = tid; it < n_items; it += blockDim.x) {
+      const int piece = it % pieces;
+      const int side = (it / pieces) % 2;
+      const int slot = lo + it / (2 * pieces);
+      const uint16_t* row =
+          pending_row(c, side ? vnew : knew, n_new, b, h, slot - nq, nr, side == 0);
+      reinterpret_cast<uint4*>(&xs[slot - seg0][side][0])[piece] =
+          reinterpret_cast<const uint4*>(row)[piece];
+    }
+  }
+  __syncthreads();
+
+  // Phase 1a: per-token groups.  One wave per (slot, side) row; lane l holds channels 2l and
+  // 2l + 1, and the group's maximum (or minimum and maximum) is reduced across its lanes.
+  {
+    const int wave = tid >> 6, lane = tid & 63;
+    const bool k_pt = K.axis == KVQ_PER_TOKEN;
+    const int nside = k_pt ? 2 : 1;  // per-channel keys are quantized in phase 1b
+    const int rows = (hi - lo) * nside;
+    for (int it = wave; it < rows; it += blockDim.x >> 6) {
+      const int side = k_pt ? (it % 2) : 1;
+      const int j = lo - seg0 + it / nside;
+      const SideDev& sd = side ? V : K;
+      const int gl = sd.group / 2;  // lanes per group
+      const float x0 = bf16_to_f32(xs[j][side][2 * lane]);
+      const float x1 = bf16_to_f32(xs[j][side][2 * lane + 1]);
+      uint8_t* codes = side ? &lv[j][0] : &lk[j][0];
+      uint16_t s16, z16 = 0;
+      int u0, u1;
+      if (sd.scheme == KVQ_SYM) {
+        const int Q = (1 << (sd.bits - 1)) - 1;
+        float m = fmaxf(fabsf(x0), fabsf(x1));
+        for (int o = 1; o < gl; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+        const float s32 = m / static_cast<float>(Q);
+        const __half sh = __float2half_rn(s32);
+        const float sf = __half2float(sh);
+        int q0 = 0, q1 = 0;
+        if (sf != 0.0f) {
+          q0 = static_cast<int>(fminf(fmaxf(roundf(x0 / sf), static_cast<float>(-Q)), static_cast<float>(Q)));
+          q1 = static_cast<int>(fminf(fmaxf(roundf(x1 / sf), static_cast<float>(-Q)), static_cast<float>(Q)));
+        }
+        u0 = q0 + (1 << (sd.bits - 1));
+        u1 = q1 + (1 << (sd.bits - 1));
+        s16 = __half_as_ushort(sh);
       } else {
-        // per-channel keys: the segment is exactly one group of S tokens (lo == seg0, hi ==
-        // seg0 + S: flushes move whole windows, R is a multiple of the group)
-        const int ch = it;
-        auto get = [&](int j) {
-          return bf16_to_f32(pending_row(c, knew, n_new, b, h, seg0 + j - nq, nr, true)[ch]);
-        };
-        uint16_t s16 = 0, z16 = 0;
-        if (K.scheme == KVQ_SYM)
-          quant_sym(get, S, K.bits, s16, &lk[0][ch], D);
-        else
-          quant_asym(get, S, K.bits, s16, z16, &lk[0][ch], D);
-        pc_s[ch] = s16;
-        pc_z[ch] = z16;
+        const int M = (1 << sd.bits) - 1;
+        float lo_v = fminf(x0, x1), hi_v = fmaxf(x0, x1);
+        for (int o = 1; o < gl; o <<= 1) {
+          lo_v = fminf(lo_v, __shfl_xor(lo_v, o));
+          hi_v = fmaxf(hi_v, __shfl_xor(hi_v, o));
+        }
+        const float range = hi_v - lo_v;
+        const float s32 = range / static_cast<float>(M);
+        const __half sh = __float2half_rn(s32);
+        const __half zh = __float2half_rn(lo_v);
+        const float sf = __half2float(sh), zf = __half2float(zh);
+        int a0 = 0, a1 = 0;
+        if (sf != 0.0f) {
+          const float d0 = x0 - zf, d1 = x1 - zf;
+          a0 = static_cast<int>(fminf(fmaxf(roundf(d0 / sf), 0.0f), static_cast<float>(M)));
+          a1 = static_cast<int>(fminf(fmaxf(roundf(d1 / sf), 0.0f), static_cast<float>(M)));
+        }
+        u0 = a0;
+        u1 = a1;
+        s16 = __half_as_ushort(sh);
+        z16 = __half_as_ushort(zh);
       }
-    } else {
-      const int iv = it - nk_items;
-      const int j = iv / ngv, g = iv % ngv;
-      const int slot = seg0 + j;
-      if (slot < lo || slot >= hi) continue;
-      const uint16_t* row = pending_row(c, vnew, n_new, b, h, slot - nq, nr, false) + g * V.group;
-      auto get = [&](int i) { return bf16_to_f32(row[i]); };
+      codes[2 * lane] = static_cast<uint8_t>(u0);
+      codes[2 * lane + 1] = static_cast<uint8_t>(u1);
+      if ((lane % gl) == 0) {
+        const int g = lane / gl;
+        if (side) {
+          mv_s[j * 4 + g] = s16;
+          mv_z[j * 4 + g] = z16;
+        } else {
+          mk_s[j * 4 + g] = s16;
+          mk_z[j * 4 + g] = z16;
+        }
+      }
+    }
+  }
+
+  // Phase 1b: per-channel keys: the segment is exactly one group of S tokens (lo == seg0, hi ==
+  // seg0 + S: flushes move whole windows, R is a multiple of the group); a thread per channel.
+  if (K.axis == KVQ_PER_CHANNEL) {
+    for (int ch = tid; ch < D; ch += blockDim.x) {
+      auto get = [&](int j) { return bf16_to_f32(xs[j][0][ch]); };
       uint16_t s16 = 0, z16 = 0;
-      if (V.scheme == KVQ_SYM)
-        quant_sym(get, V.group, V.bits, s16, &lv[j][g * V.group], 1);
+      if (K.scheme == KVQ_SYM)
+        quant_sym(get, S, K.bits, s16, &lk[0][ch], D);
       else
-        quant_asym(get, V.group, V.bits, s16, z16, &lv[j][g * V.group], 1);
-      mv_s[j * 4 + g] = s16;
-      mv_z[j * 4 + g] = z16;
+        quant_asym(get, S, K.bits, s16, z16, &lk[0][ch], D);
+      pc_s[ch] = s16;
+      pc_z[ch] = z16;
     }
   }
   __syncthreads();

@@ -92,14 +92,12 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // ---- code unpacking -----------------------------------------------------------------------
-// A word holds E = 32 / KB fields; pair k (0 <= k < E/2) is (field k, field k + E/2), returned
-// as the exact f16 values (u - off).  Pair index r = word * (E/2) + k.
-
 // Constants of the unpacking, held in registers: gfx950 VOP3 instructions (v_and_or_b32) take
 // no literal operands, so with literals every and-or would split into two instructions.
 struct UnpackRegs {
-  uint32_t magic;  // VGPR: 0x64006400, f16 1024.0 in both halves
-  uint32_t m_lo, m_hi;  // SGPRs: masks of the two fields a pair needs (per bit width)
+  uint32_t magic;       // VGPR: 0x64006400, f16 1024.0 in both halves
+  uint32_t m_lo, m_hi;  // SGPRs: masks of the fields a pair needs (per bit width)
+  uint32_t m2[5];       // 2-bit codes: 0x00030003 << 2k, k = 0..4
 };
 
 template <int KB>
@@ -114,8 +112,12 @@ __device__ __forceinline__ UnpackRegs unpack_regs() {
     asm volatile("s_mov_b32 %0, 0x000f000f" : "=s"(r.m_lo));
     asm volatile("s_mov_b32 %0, 0x00f000f0" : "=s"(r.m_hi));
   } else {
-    asm volatile("s_mov_b32 %0, 0x00030003" : "=s"(r.m_lo));
-    r.m_hi = r.m_lo;
+    asm volatile("s_mov_b32 %0, 0x00030003" : "=s"(r.m2[0]));
+    asm volatile("s_mov_b32 %0, 0x000c000c" : "=s"(r.m2[1]));
+    asm volatile("s_mov_b32 %0, 0x00300030" : "=s"(r.m2[2]));
+    asm volatile("s_mov_b32 %0, 0x00c000c0" : "=s"(r.m2[3]));
+    asm volatile("s_mov_b32 %0, 0x03000300" : "=s"(r.m2[4]));
+    r.m_lo = r.m_hi = 0;
   }
   return r;
 }
@@ -137,12 +139,14 @@ __device__ __forceinline__ f16x2 upair(const uint32_t* w, int r, float off, cons
                                      h2s(-(64.0f + off)));
   } else {
     static_assert(KB == 2, "bits");
-    // field k sits at bit 2k (k < 5) or, after a shift by 10, at bit 2(k - 5)
+    // field k sits at bit 2k (k < 5) or, after a shift by 10, at bit 2 (k - 5); the masked
+    // code reads as 1024 + 2^sh u, and one fma takes it to u - off
+    const uint32_t s = (k >= 5) ? (x >> 10) : x;
     const int sh = (k >= 5) ? 2 * (k - 5) : 2 * k;
-    const uint32_t s = ((k >= 5) ? (x >> 10) : x) >> sh;
-    const float scl = 1.0f;
-    (void)scl;
-    return as_h2((s & u.m_lo) | u.magic) - h2s(1024.0f + off);
+    const float scl = 1.0f / static_cast<float>(1 << sh);
+    const f16x2 v = as_h2((s & u.m2[sh / 2]) | u.magic);
+    if (sh == 0) return v - h2s(1024.0f + off);
+    return __builtin_elementwise_fma(v, h2s(scl), h2s(-(1024.0f * scl + off)));
   }
 }
 
@@ -244,7 +248,7 @@ __device__ __forceinline__ int seq_units(const CacheDev& c, int max_tokens, int 
 }
 
 template <int KB, int G, bool KPC, int NP, bool ASYM>
-__global__ __launch_bounds__(256, 3) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256, NP == 1 ? 3 : 2) void decode_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const CacheDev& c = p.c;
   const int B = c.B, H = c.H;
@@ -296,6 +300,12 @@ __global__ __launch_bounds__(256, 3) void decode_kernel(DecodeParams p) {
   const long long NBl = gridDim.x;
   const int u0 = static_cast<int>((static_cast<long long>(blockIdx.x) * U) / NBl);
   const int u1 = static_cast<int>((static_cast<long long>(blockIdx.x + 1) * U) / NBl);
+  if (u0 == u1) {
+    // An empty range still owns slot 0, which the combine may read: make it neutral.
+    float* part = p.ws_part + static_cast<size_t>(blockIdx.x) * 2 * G * PART_STRIDE;
+    for (int i = tid; i < G * PART_STRIDE; i += 256) part[i] = (i % PART_STRIDE == 0) ? -FLT_MAX : 0.0f;
+    return;
+  }
 
   const int kgroup = c.k.group, vgroup = c.v.group;
   const int ngk = KPC ? 2 : D / kgroup;  // QK columns per head: key groups, or hi/lo parts
@@ -454,10 +464,35 @@ __global__ __launch_bounds__(256, 3) void decode_kernel(DecodeParams p) {
         if (blk < 0 || blk >= c.num_blocks) return -1;
         return static_cast<long>(blk) * H + h;
       };
-      const int fold_c0 = 8 * (lane & 15);  // per-channel keys: channels this lane folds
+      // Per-channel keys: lane l folds the eight channels of QK MFMA block (g', j') = (blk / 4,
+      // blk % 4), blk = l % 16, for head l / 16 (and + 4): channels 32 g' + kchan(j', 0..7), which
+      // are the run 8 blk .. 8 blk + 7 (8- and 4-bit) or two runs of four (2-bit).
+      const int fold_blk = lane & 15;
+      const int fold_c0 = (KB == 2) ? 32 * (fold_blk / 4) + 16 * ((fold_blk % 4) / 2) + 4 * (fold_blk % 2)
+                                    : 8 * fold_blk;
       auto kpc_meta = [&](int tau) -> size_t {
         return ((static_cast<size_t>(b) * H + h) * (c.cap / kgroup) + tau) * D + fold_c0;
       };
+      auto load_meta8 = [&](const uint16_t* base, size_t mi) -> uint4 {
+        if constexpr (KB == 2) {
+          const uint2 a = *reinterpret_cast<const uint2*>(base + mi);
+          const uint2 bb = *reinterpret_cast<const uint2*>(base + mi + 8);
+          return uint4{a.x, a.y, bb.x, bb.y};
+        } else {
+          return *reinterpret_cast<const uint4*>(base + mi);
+        }
+      };
+      // the query of the folding lane's channels, in MFMA element order, as f32 (per segment)
+      float qfold[(G + 3) / 4][8];
+      if constexpr (KPC) {
+#pragma unroll
+        for (int r0 = 0; r0 < G; r0 += 4) {
+          const int hw = min(r0 + (lane >> 4), G - 1);
+          const u16x8 q8 = gather_kchan<KB>(qs + hw * D + 32 * (fold_blk / 4), fold_blk % 4);
+#pragma unroll
+          for (int i = 0; i < 8; i++) qfold[r0 / 4][i] = bf16_to_f32(q8[i]);
+        }
+      }
 
       UnitData<KB, NP, KPC, ASYM> d{};
       const UnpackRegs ur = unpack_regs<KB>();
@@ -471,8 +506,8 @@ __global__ __launch_bounds__(256, 3) void decode_kernel(DecodeParams p) {
         load_words<KB>(c.kc + pB * TILE_BYTES + n * RBK + g * (RBK / 4), d.kw[1]);
         if constexpr (KPC) {
           const size_t mi = kpc_meta((32 * xx) / kgroup);
-          d.fs = *reinterpret_cast<const uint4*>(c.ks + mi);
-          if constexpr (ASYM) d.fz = *reinterpret_cast<const uint4*>(c.kz + mi);
+          d.fs = load_meta8(c.ks, mi);
+          if constexpr (ASYM) d.fz = load_meta8(c.kz, mi);
         } else {
 #pragma unroll
           for (int t = 0; t < 2; t++) {
@@ -501,28 +536,34 @@ __global__ __launch_bounds__(256, 3) void decode_kernel(DecodeParams p) {
       };
       // per-channel keys: fold one key group's scales (and zero-points) into the query
       auto kpc_fold = [&](uint4 fs, uint4 fz) {
+        // metadata words hold the lane's 8 channels in natural order; element i of the MFMA
+        // block is natural index nat(i)
         const uint32_t sw[4] = {fs.x, fs.y, fs.z, fs.w};
         const uint32_t zwd[4] = {fz.x, fz.y, fz.z, fz.w};
+        auto nat = [](int i) { return (KB == 8) ? ((i & 4) | ((i & 1) << 1) | ((i >> 1) & 1)) : ((i >> 1) | ((i & 1) << 2)); };
 #pragma unroll
         for (int r0 = 0; r0 < G; r0 += 4) {
           const int hw = r0 + (lane >> 4);
           float zp = 0.0f;
           if (hw < G) {
-            const u16x8 q8 = *reinterpret_cast<const u16x8*>(qs + hw * D + fold_c0);
-            u16x8 hi8, lo8;
+            float pv[8];
 #pragma unroll
             for (int i = 0; i < 8; i++) {
-              const float qv = bf16_to_f32(q8[i]);
-              const float sv = (i & 1) ? f16_hi(sw[i / 2]) : f16_lo(sw[i / 2]);
-              const float pv = qv * sv;  // exact: 8-bit x 11-bit significands
-              const _Float16 ph = static_cast<_Float16>(pv);
-              const _Float16 pl = static_cast<_Float16>(pv - static_cast<float>(ph));
-              hi8[i] = __builtin_bit_cast(unsigned short, ph);
-              lo8[i] = __builtin_bit_cast(unsigned short, pl);
-              if constexpr (ASYM) zp += qv * ((i & 1) ? f16_hi(zwd[i / 2]) : f16_lo(zwd[i / 2]));
+              const int k = nat(i);
+              const float sv = (k & 1) ? f16_hi(sw[k / 2]) : f16_lo(sw[k / 2]);
+              pv[i] = qfold[r0 / 4][i] * sv;  // exact: 8-bit x 11-bit significands
+              if constexpr (ASYM) zp += qfold[r0 / 4][i] * ((k & 1) ? f16_hi(zwd[k / 2]) : f16_lo(zwd[k / 2]));
             }
-            *reinterpret_cast<u16x8*>(kf + hw * D + fold_c0) = hi8;
-            *reinterpret_cast<u16x8*>(kf + (8 + hw) * D + fold_c0) = lo8;
+            uint32_t hw4[4], lw4[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              const f16x2 hi2 = pkrtz(pv[2 * i], pv[2 * i + 1]);
+              hw4[i] = h2_bits(hi2);
+              lw4[i] = h2_bits(pkrtz(pv[2 * i] - static_cast<float>(hi2[0]),
+                                     pv[2 * i + 1] - static_cast<float>(hi2[1])));
+            }
+            *reinterpret_cast<uint4*>(kf + hw * D + 8 * fold_blk) = uint4{hw4[0], hw4[1], hw4[2], hw4[3]};
+            *reinterpret_cast<uint4*>(kf + (8 + hw) * D + 8 * fold_blk) = uint4{lw4[0], lw4[1], lw4[2], lw4[3]};
           }
           if constexpr (ASYM) {
             zp += row_ror<8>(zp);
@@ -535,7 +576,7 @@ __global__ __launch_bounds__(256, 3) void decode_kernel(DecodeParams p) {
         wave_lds_sync();
 #pragma unroll
         for (int j = 0; j < 4; j++)
-          qb[j] = __builtin_bit_cast(f16x8, gather_kchan<KB>(kf + (cg * 8 + hh) * D + 32 * g, j));
+          qb[j] = *reinterpret_cast<const f16x8*>(kf + (cg * 8 + hh) * D + 8 * (4 * g + j));
         if constexpr (ASYM) zt = ztw[wave * 8 + hh];
         wave_lds_sync();
       };
@@ -568,9 +609,9 @@ __global__ __launch_bounds__(256, 3) void decode_kernel(DecodeParams p) {
             for (int j = 0; j < 4; j++)
               dq[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop<KB>(d.kw[0], j, koff, ur), qb[j], dq[0], 0, 0, 0);
             const size_t mi = kpc_meta(2 * x + 1);
-            const uint4 fs2 = *reinterpret_cast<const uint4*>(c.ks + mi);
+            const uint4 fs2 = load_meta8(c.ks, mi);
             uint4 fz2 = uint4{0, 0, 0, 0};
-            if constexpr (ASYM) fz2 = *reinterpret_cast<const uint4*>(c.kz + mi);
+            if constexpr (ASYM) fz2 = load_meta8(c.kz, mi);
             kpc_fold(fs2, fz2);
 #pragma unroll
             for (int j = 0; j < 4; j++)
@@ -839,9 +880,17 @@ __device__ __forceinline__ int block_of(long long u, long long U, long long NB) 
 }
 
 // Merge the partials of each (sequence, kv head) that more than one workgroup worked on; write
-// zeros for empty sequences.  One workgroup per (sequence, kv head).
+// zeros for empty sequences.  One workgroup of 1024 threads per (sequence, kv head): each
+// output is merged by CG threads over interleaved partials, then across them in LDS.
+constexpr int COMBINE_THREADS = 1024;
+
 template <int G>
-__global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
+__global__ __launch_bounds__(COMBINE_THREADS) void combine_kernel(DecodeParams p) {
+  constexpr int OUTS = G * D;
+  constexpr int PASS = OUTS < 256 ? OUTS : 256;  // outputs per pass
+  constexpr int CG = COMBINE_THREADS / PASS;     // threads per output
+  constexpr int NPASS = OUTS / PASS;
+  __shared__ float sm[CG][PASS], sl[CG][PASS], so[CG][PASS];
   const int H = p.c.H, B = p.c.B;
   const int b = blockIdx.x / H, h = blockIdx.x % H;
   const int* pre = p.ws_pre;
@@ -849,43 +898,47 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
   const int ub = (pre[b + 1] - pre[b]) / H;
   float* dst = p.out + (static_cast<size_t>(b) * p.Hq + static_cast<size_t>(h) * G) * D;
   if (ub == 0) {
-    for (int o = threadIdx.x; o < G * D; o += 256) dst[o] = 0.0f;
+    for (int o = threadIdx.x; o < OUTS; o += COMBINE_THREADS) dst[o] = 0.0f;
     return;
   }
   const long long us = pre[b] + static_cast<long long>(h) * ub, ue = us + ub;
   const int kf = block_of(us, U, NB), kl = block_of(ue - 1, U, NB);
   if (kf == kl) return;  // one workgroup saw the whole sequence and wrote the output
   const int s0 = ((static_cast<long long>(kf) * U) / NB == us) ? 0 : 1;
-  constexpr int NO = (G * D + 255) / 256;
-#pragma unroll
-  for (int oi = 0; oi < NO; oi++) {
-    const int o = threadIdx.x + 256 * oi;
-    if (o >= G * D) continue;
+  const int oi = threadIdx.x % PASS, cgi = threadIdx.x / PASS;
+  for (int pass = 0; pass < NPASS; pass++) {
+    const int o = pass * PASS + oi;
     const int oh = o / D, ch = o % D;
-    auto part_of = [&](int k) -> const float* {
-      const int s = (k == kf) ? s0 : 0;
-      return p.ws_part + ((static_cast<size_t>(k) * 2 + s) * G + oh) * PART_STRIDE;
-    };
-    // a workgroup whose unit range is empty wrote nothing
-    auto empty = [&](int k) {
-      return (static_cast<long long>(k) * U) / NB == (static_cast<long long>(k + 1) * U) / NB;
-    };
-    float M = -INFINITY;
-    for (int k = kf; k <= kl; k++)
-      if (!empty(k)) M = fmaxf(M, part_of(k)[0]);
-    float L = 0.0f, O = 0.0f;
-    if (M != -INFINITY) {
-#pragma unroll 8
-      for (int k = kf; k <= kl; k++) {
-        if (empty(k)) continue;
-        const float* pt = part_of(k);
-        const float m = pt[0];
-        const float e = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
-        L += e * pt[1];
-        O += e * pt[4 + ch];
-      }
+    float M = -FLT_MAX, L = 0.0f, O = 0.0f;
+#pragma unroll 4
+    for (int k = kf + cgi; k <= kl; k += CG) {
+      const float* pt =
+          p.ws_part + ((static_cast<size_t>(k) * 2 + (k == kf ? s0 : 0)) * G + oh) * PART_STRIDE;
+      const float m = pt[0], l = pt[1], v = pt[4 + ch];
+      const float mn = fmaxf(M, m);
+      const float a = __builtin_amdgcn_exp2f(M - mn), e = __builtin_amdgcn_exp2f(m - mn);
+      L = L * a + l * e;
+      O = O * a + v * e;
+      M = mn;
     }
-    dst[o] = (L > 0.0f) ? O / L : 0.0f;
+    sm[cgi][oi] = M;
+    sl[cgi][oi] = L;
+    so[cgi][oi] = O;
+    __syncthreads();
+    if (cgi == 0) {
+      float Mt = -FLT_MAX;
+#pragma unroll
+      for (int q = 0; q < CG; q++) Mt = fmaxf(Mt, sm[q][oi]);
+      float Lt = 0.0f, Ot = 0.0f;
+#pragma unroll
+      for (int q = 0; q < CG; q++) {
+        const float e = __builtin_amdgcn_exp2f(sm[q][oi] - Mt);
+        Lt += e * sl[q][oi];
+        Ot += e * so[q][oi];
+      }
+      dst[o] = (Lt > 0.0f) ? Ot / Lt : 0.0f;
+    }
+    __syncthreads();
   }
 }
 
@@ -913,7 +966,7 @@ hipError_t launch_decode_t(const DecodeParams& p0, hipStream_t s) {
   decode_kernel<KB, G, KPC, NP, ASYM><<<p.nblocks, 256, lds, s>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  combine_kernel<G><<<p.c.B * p.c.H, 256, 0, s>>>(p);
+  combine_kernel<G><<<p.c.B * p.c.H, COMBINE_THREADS, 0, s>>>(p);
   return hipGetLastError();
 }
 
