@@ -241,8 +241,71 @@ def cpu_baseline(st, gpu_out0, q0, budget_s: float = 15.0):
 # ------------------------------------------------------------------------------------------
 
 def decode_source_hash() -> str:
-    p = os.path.join(ROOT, "quantized_kv_cache_07_amd", "csrc", "kvq_decode.hip")
+    """Hash of the decode-attention kernel source (the counters go stale when it changes)."""
+    p = os.path.join(ROOT, "quantized_kv_cache_07_amd", "csrc", "kvq_decode.h")
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+CALIBRATION_BYTES = 1 << 30  # plain copy of known size, for scaling the byte counters
+
+
+def _counter_rows(directory: str):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        rows.extend(csv.DictReader(open(f)))
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {directory}")
+    return rows
+
+
+def _per_dispatch(rows, counter: str, kernel_substr: str) -> float:
+    """Mean over dispatches of a kernel of one counter (summed over its dimensions)."""
+    per = {}
+    for r in rows:
+        if r["Counter_Name"] != counter or kernel_substr not in r["Kernel_Name"]:
+            continue
+        per[r.get("Dispatch_Id") or r.get("Correlation_Id")] = (
+            per.get(r.get("Dispatch_Id") or r.get("Correlation_Id"), 0.0) + float(r["Counter_Value"]))
+    if not per:
+        raise SystemExit(f"no {counter} samples for {kernel_substr}")
+    return sum(per.values()) / len(per)
+
+
+def summarize_counters(fetch_dir: str, write_dir: str, workload: str, command: str) -> dict:
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of one decode-attention call (decode_kernel +
+    combine_kernel), each scaled by what the counter reads for a plain copy of known size."""
+    fr, wr = _counter_rows(fetch_dir), _counter_rows(write_dir)
+    copy_f = _per_dispatch(fr, "FETCH_SIZE", "measure_copy_kernel") * 1024
+    copy_w = _per_dispatch(wr, "WRITE_SIZE", "measure_copy_kernel") * 1024
+    kf, kw = CALIBRATION_BYTES / copy_f, CALIBRATION_BYTES / copy_w
+    out = {"workload": workload, "command": command,
+           "kvq_decode_h_sha256_16": decode_source_hash(),
+           "calibration": {"copy_bytes": CALIBRATION_BYTES, "fetch_counter_bytes": copy_f,
+                           "write_counter_bytes": copy_w, "fetch_scale": kf, "write_scale": kw}}
+    total = 0.0
+    for name in ("decode_kernel", "combine_kernel"):
+        f = _per_dispatch(fr, "FETCH_SIZE", name) * 1024 * kf
+        w = _per_dispatch(wr, "WRITE_SIZE", name) * 1024 * kw
+        out[name] = {"fetch_bytes": round(f), "write_bytes": round(w)}
+        total += f + w
+    out["bytes_per_launch"] = round(total)
+    return out
+
+
+def summarize_stats(stats_csv: str, command: str, title: str) -> str:
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = [f"# {title}", "", "Command (from the repository root on the GPU box):", "",
+             f"    {command}", "",
+             f"{'kernel':58s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
+    for r in rows:
+        if "kvq" not in r["Name"]:
+            continue
+        lines.append(f"{r['Name'][:58]:58s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
+                     f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f}")
+    return "\n".join(lines) + "\n"
 
 
 def counter_traffic(workload: str):
@@ -268,7 +331,21 @@ def main() -> int:
     ap.add_argument("--attn-reps", type=int, default=50)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/decode_<workload>_traffic.json from two rocprofv3 --pmc runs")
+    ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV",
+                    help="print a text summary of a rocprofv3 --stats kernel table")
+    ap.add_argument("--command", default="", help="the profiling command, recorded in summaries")
     a = ap.parse_args()
+    if a.summarize_counters:
+        d = summarize_counters(*a.summarize_counters, a.workload, a.command)
+        out = os.path.join(ROOT, "profiles", f"decode_{a.workload}_traffic.json")
+        json.dump(d, open(out, "w"), indent=1)
+        print(json.dumps(d, indent=1))
+        return 0
+    if a.summarize_stats:
+        print(summarize_stats(a.summarize_stats, a.command, f"kvq kernels, workload {a.workload}"), end="")
+        return 0
     if a.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
               f"(the path is sharded by sequence or kv head across GPUs, not built here)",
@@ -364,6 +441,11 @@ def main() -> int:
     r1.record()
     torch.cuda.synchronize()
     stream_gbs = 10 * buf.numel() / (r0.elapsed_time(r1) * 1e-3) / 1e9
+    # plain copies of known size: the reference for scaling the hardware byte counters
+    half = CALIBRATION_BYTES
+    for _ in range(3):
+        kvq.measure_copy(buf[half:2 * half], buf[:half])
+    torch.cuda.synchronize()
     del buf
 
     cpu, parity = None, None

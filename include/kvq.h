@@ -133,8 +133,8 @@ size_t kvq_buffer_bytes(const kvq_format *fmt, int32_t batch, int32_t n_kv_heads
                         int32_t capacity, int32_t num_blocks, int32_t which);
 
 /* Check a format without a cache: KVQ_OK, KVQ_EINVAL or KVQ_ENOTSUP.  Supported: head_dim 128;
- * bits 2/4/8, the same for K and V; per-token groups 32/64/128; per-channel grouping for keys
- * only, with residual > 0 divisible by the group.  Pure host code. */
+ * bits 2/4/8 and one scheme, the same for K and V; per-token groups 32/64/128; per-channel
+ * grouping for keys only, with residual > 0 divisible by the group.  Pure host code. */
 kvq_status kvq_check_format(const kvq_format *fmt);
 
 /* Append n_new >= 1 new tokens to every sequence of the batch.
@@ -173,7 +173,10 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *cache, int32_t n_q_heads, int
  *   sm_scale: typically 1 / sqrt(head_dim)
  *   max_tokens: host upper bound on n_quant[b] + n_res[b] (sizes the split over the sequence)
  *   workspace: >= kvq_decode_workspace_bytes(cache, n_q_heads, max_tokens) bytes, device
- * KVQ_ENOTSUP for a per-token key format with (head_dim / group) * G > 16.
+ * KVQ_ENOTSUP for a per-token key format with (head_dim / key group) * G > 16, or for
+ * 2 * G * (head_dim / value group) > 32.
+ * The workspace needs no initialisation and holds nothing between calls; two calls that run at
+ * the same time need two workspaces.
  * Device faults: KVQ_ERR_BLOCK (a table entry outside the pool: that tile is skipped).
  * Launches two kernels on `stream`. */
 kvq_status kvq_decode_attention(const kvq_cache *cache, const void *q, int32_t n_q_heads,
