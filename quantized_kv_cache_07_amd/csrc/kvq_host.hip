@@ -158,15 +158,16 @@ int device_cus() {
 
 // ---- measurement kernels ------------------------------------------------------------------
 
-constexpr int MEASURE_BLOCKS = 4096;
+constexpr int MEASURE_BLOCKS = 2048;  // eight 256-thread workgroups per compute unit
 
 __global__ __launch_bounds__(256) void measure_read_kernel(const uint4* __restrict__ src, size_t n16,
                                                            float* __restrict__ sink) {
   uint32_t x = 0;
   for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16;
        i += static_cast<size_t>(gridDim.x) * blockDim.x) {
-    const uint4 v = src[i];
-    x ^= v.x ^ v.y ^ v.z ^ v.w;
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + i);
+    x ^= v[0] ^ v[1] ^ v[2] ^ v[3];
   }
   __shared__ uint32_t red[256];
   red[threadIdx.x] = x;
