@@ -1,7 +1,8 @@
 """Benchmark: one decode step of the quantized KV cache on one MI355X.
 
-A step is one pass of the whole hot path over one batch: flush every full BF16 window, append one
-new token per sequence (quantized, or copied into the window), then single-query decode attention
+A step is one pass of the whole hot path over one batch: append one new token per sequence (which
+flushes every full BF16 window first, then quantizes the token or copies it into the window), then
+single-query decode attention
 over every cached token with the K/V codes dequantized in registers.  Inputs are seeded synthetic
 tensors generated on the GPU (kvq_inputs); the cache is resident in HBM before timing starts.
 
@@ -179,8 +180,8 @@ def run_step(st, s: int) -> None:
     w = st.w
     for (lw, cache), (k, v, q) in zip(st.caches, st.step_in[s]):
         if w.step_append or st.layers > 1:
-            if w.residual:
-                kvq.flush_residual(cache)
+            # the append flushes every full window before adding the token (kvq.h contract);
+            # a separate kvq_flush_residual call would only add two launches
             kvq.quantize_append(cache, k, v)
         kvq.decode_attention(cache, q, st.max_tokens, out=st.out, workspace=st.ws)
 

@@ -368,8 +368,10 @@ __global__ __launch_bounds__(256) void tail_kernel(CacheDev c, const uint16_t* k
 hipError_t launch_append(const CacheDev& c, const uint16_t* knew, const uint16_t* vnew, int n_new,
                          int mode, hipStream_t stream) {
   const int S = (c.k.axis == KVQ_PER_CHANNEL) ? c.k.group : TILE;
-  // slots one call can move: at most n_new + R rounded down to a window multiple
-  const int f_max = (mode == MODE_FLUSH) ? c.R : (c.R == 0 ? n_new : n_new + c.R);
+  // slots one call can move: n_new without a window, else whole windows: R floor((n_res + n_new
+  // - 1) / R) <= R floor((R + n_new - 1) / R)
+  const int f_max = (mode == MODE_FLUSH) ? c.R
+                    : (c.R == 0 ? n_new : c.R * ((c.R + n_new - 1) / c.R));
   const int segs = (f_max + S - 1) / S + 1;
   dim3 grid(segs, c.B * c.H);
   switch (S) {
