@@ -29,6 +29,7 @@
 #pragma once
 
 #include <cfloat>
+#include <type_traits>
 
 #include "kvq_dev.h"
 
@@ -148,6 +149,56 @@ __device__ __forceinline__ f16x2 upair(const uint32_t* w, int r, float off, cons
     if (sh == 0) return v - h2s(1024.0f + off);
     return __builtin_elementwise_fma(v, h2s(scl), h2s(-(1024.0f * scl + off)));
   }
+}
+
+// Scale of pair k's fields in the bias-free form: the masked field reads as 1024 + alpha u.
+template <int KB>
+__device__ __forceinline__ constexpr int pair_alpha(int k) {
+  if constexpr (KB == 8) return 1;
+  else if constexpr (KB == 4) return (k & 1) ? 16 : 1;
+  else return 1 << (2 * (k >= 5 ? k - 5 : k));
+}
+
+// Pair r as the raw f16 values 1024 + alpha u (one and-or, no bias removal).  The bias is
+// removed inside the matrix products: the other operand is divided by alpha and a constant
+// operand holding -(1024 + alpha off) cancels the rest.
+template <int KB>
+__device__ __forceinline__ uint32_t rawpair(const uint32_t* w, int r, const UnpackRegs& u) {
+  constexpr int HH = 16 / KB;
+  const uint32_t x = w[r / HH];
+  const int k = r % HH;
+  if constexpr (KB == 8) {
+    return ((k ? (x >> 8) : x) & u.m_lo) | u.magic;
+  } else if constexpr (KB == 4) {
+    const uint32_t s = (k >= 2) ? (x >> 8) : x;
+    return (s & ((k & 1) ? u.m_hi : u.m_lo)) | u.magic;
+  } else {
+    const uint32_t s = (k >= 5) ? (x >> 10) : x;
+    const int sh = (k >= 5) ? 2 * (k - 5) : 2 * k;
+    return (s & u.m2[sh / 2]) | u.magic;
+  }
+}
+
+// alpha of element i of QK MFMA j (pair 4 j + i / 2) and of element i of a PV B operand
+// (pairs 2 j, 2 j + 1 of tile A, then of tile B)
+template <int KB>
+__device__ __forceinline__ constexpr int kelem_alpha(int j, int i) {
+  return pair_alpha<KB>((4 * j + i / 2) % (16 / KB));
+}
+template <int KB>
+__device__ __forceinline__ constexpr int velem_alpha(int j, int i) {
+  return pair_alpha<KB>((2 * j + (i / 2) % 2) % (16 / KB));
+}
+
+template <int KB>
+__device__ __forceinline__ f16x8 kop_raw(const uint32_t* w, int j, const UnpackRegs& u) {
+  return __builtin_bit_cast(f16x8, uint4{rawpair<KB>(w, 4 * j, u), rawpair<KB>(w, 4 * j + 1, u),
+                                         rawpair<KB>(w, 4 * j + 2, u), rawpair<KB>(w, 4 * j + 3, u)});
+}
+template <int KB>
+__device__ __forceinline__ f16x8 vop_raw(const uint32_t* wa, const uint32_t* wb, int j, const UnpackRegs& u) {
+  return __builtin_bit_cast(f16x8, uint4{rawpair<KB>(wa, 2 * j, u), rawpair<KB>(wa, 2 * j + 1, u),
+                                         rawpair<KB>(wb, 2 * j, u), rawpair<KB>(wb, 2 * j + 1, u)});
 }
 
 // QK A operand of MFMA j: pairs 4 j .. 4 j + 3 of the lane's key slice.
@@ -327,6 +378,14 @@ __global__ __launch_bounds__(256, NP == 1 ? 3 : 2) void decode_kernel(DecodePara
   const int ngv = D / vgroup;
   constexpr float koff = ASYM ? 0.0f : static_cast<float>(1 << (KB - 1));
   constexpr float voff = koff;
+  // Value codes enter PV raw (1024 + alpha u) when alpha depends only on the token position
+  // (8- and 4-bit); the weights then carry 1 / alpha and one more product with vbias removes the
+  // bias.  2-bit fields change alpha with the channel, so they are unpacked exactly instead.
+  constexpr bool VBF = KB != 2;
+  f16x8 vbias;
+#pragma unroll
+  for (int i = 0; i < 8; i++)
+    vbias[i] = static_cast<_Float16>(-(1024.0f + static_cast<float>(velem_alpha<KB>(0, i)) * voff));
   const int hh = n % G;          // query head of QK column n and of PV row 16 pp + n
   const int cg = (n / G) % ngk;  // key group (or hi/lo part) of QK column n
   constexpr int RBK = D * KB / 8;
@@ -366,6 +425,7 @@ __global__ __launch_bounds__(256, NP == 1 ? 3 : 2) void decode_kernel(DecodePara
 
     // ---- QK operand: f16 query, masked to the column's key group ----
     f16x8 qb[4];
+    f32x4 dq0 = f32x4{0.f, 0.f, 0.f, 0.f};  // QK accumulator start of every tile
     float qsum = 0.0f;  // asymmetric per-token keys: sum of q over the column's group
     float zt = 0.0f;    // asymmetric per-channel keys: sum of q * zero over the key group
     if constexpr (!KPC) {
@@ -376,13 +436,22 @@ __global__ __launch_bounds__(256, NP == 1 ? 3 : 2) void decode_kernel(DecodePara
 #pragma unroll
         for (int i = 0; i < 8; i++) {
           const float x = in_grp ? bf16_to_f32(raw[i]) : 0.0f;
-          qb[j][i] = static_cast<_Float16>(x);
+          qb[j][i] = static_cast<_Float16>(x * (1.0f / static_cast<float>(kelem_alpha<KB>(j, i))));
           if constexpr (ASYM) qsum += x;
         }
       }
       if constexpr (ASYM) {
         qsum += __shfl_xor(qsum, 16);
         qsum += __shfl_xor(qsum, 32);
+      }
+      // every token row starts at -sum_i qb_i (1024 + alpha_i off): the bias of the raw codes
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        f16x8 bias;
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+          bias[i] = static_cast<_Float16>(-(1024.0f + static_cast<float>(kelem_alpha<KB>(j, i)) * koff));
+        dq0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(bias, qb[j], dq0, 0, 0, 0);
       }
     }
 
@@ -408,7 +477,9 @@ __global__ __launch_bounds__(256, NP == 1 ? 3 : 2) void decode_kernel(DecodePara
     // ---- online softmax over the 8 raw scores of a pair; returns the weights in s2 ----
     // m_run is in log2 units; weights are exp2(score * sm_log2 - m_run).  The running max starts
     // at a finite sentinel, so empty waves never form inf - inf.
-    auto softmax = [&](float (&s2)[8], int nvA, int nvB) {
+    // With vfold, element i's weight comes out divided by alpha_i of the value codes it meets
+    // (the raw-code PV operand), which only shifts its exponent.
+    auto softmax = [&](float (&s2)[8], int nvA, int nvB, auto vfold) {
       const bool full = nvA == 16 && nvB == 16;
       if (!full) {
 #pragma unroll
@@ -445,8 +516,15 @@ __global__ __launch_bounds__(256, NP == 1 ? 3 : 2) void decode_kernel(DecodePara
       float ls = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; i++) {
-        s2[i] = __builtin_amdgcn_exp2f(fmaf(s2[i], p.sm_log2, -m_run));  // -inf -> 0
-        ls += s2[i];
+        if constexpr (decltype(vfold)::value) {
+          constexpr float sh[8] = {0.f, 0.f, 4.f, 4.f, 0.f, 0.f, 4.f, 4.f};
+          const float a = (KB == 4) ? sh[i] : 0.0f;  // log2 alpha_i
+          s2[i] = __builtin_amdgcn_exp2f(fmaf(s2[i], p.sm_log2, -m_run - a));  // -inf -> 0
+          ls = fmaf(s2[i], (KB == 4 && sh[i] != 0.f) ? 16.0f : 1.0f, ls);
+        } else {
+          s2[i] = __builtin_amdgcn_exp2f(fmaf(s2[i], p.sm_log2, -m_run));  // -inf -> 0
+          ls += s2[i];
+        }
       }
       l_run += ls;
     };
@@ -639,10 +717,12 @@ __global__ __launch_bounds__(256, NP == 1 ? 3 : 2) void decode_kernel(DecodePara
             }
           }
         } else {
+          dq[0] = dq0;
+          dq[1] = dq0;
 #pragma unroll
           for (int j = 0; j < 4; j++) {
-            dq[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop<KB>(d.kw[0], j, koff, ur), qb[j], dq[0], 0, 0, 0);
-            dq[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop<KB>(d.kw[1], j, koff, ur), qb[j], dq[1], 0, 0, 0);
+            dq[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop_raw<KB>(d.kw[0], j, ur), qb[j], dq[0], 0, 0, 0);
+            dq[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop_raw<KB>(d.kw[1], j, ur), qb[j], dq[1], 0, 0, 0);
           }
         }
         float s2[8];
@@ -669,7 +749,7 @@ __global__ __launch_bounds__(256, NP == 1 ? 3 : 2) void decode_kernel(DecodePara
         if constexpr (!KPC) fold_cols8(s2);
         load_k(more ? xn : x, nA, nB);  // key registers are free again
 
-        softmax(s2, nvA, nvB);  // s2 now holds the weights
+        softmax(s2, nvA, nvB, std::integral_constant<bool, VBF>{});  // s2: weights / alpha
 
         // ---- P rows (hi / lo f16 parts of w * s_v) and PV ----
         // Rows 16 pp + n with part >= 2 are never read back, so they are left as computed.
@@ -692,7 +772,10 @@ __global__ __launch_bounds__(256, NP == 1 ? 3 : 2) void decode_kernel(DecodePara
               const float zv[4] = {f16_lo(z2v.x), f16_hi(z2v.x), f16_lo(z2v.y), f16_hi(z2v.y)};
               float zp = 0.0f;
 #pragma unroll
-              for (int r = 0; r < 4; r++) zp += (full || s2[4 * t + r] != 0.0f) ? s2[4 * t + r] * zv[r] : 0.0f;
+              for (int r = 0; r < 4; r++) {
+                const float wa = VBF ? s2[4 * t + r] * static_cast<float>(velem_alpha<KB>(0, r)) : s2[4 * t + r];
+                zp += (full || s2[4 * t + r] != 0.0f) ? wa * zv[r] : 0.0f;
+              }
               zacc[pp] += zp;
             }
           }
@@ -712,10 +795,21 @@ __global__ __launch_bounds__(256, NP == 1 ? 3 : 2) void decode_kernel(DecodePara
         }
 #pragma unroll
         for (int j = 0; j < 8; j++) {
-          const f16x8 vb = vop<KB>(d.vw[0], d.vw[1], j, voff, ur);
+          if constexpr (VBF) {
+            // raw codes 1024 + alpha u against weights / alpha, then the bias: -(1024 + alpha off)
+            const f16x8 vb = vop_raw<KB>(d.vw[0], d.vw[1], j, ur);
 #pragma unroll
-          for (int pp = 0; pp < NP; pp++)
-            acc[pp][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[pp], vb, acc[pp][j], 0, 0, 0);
+            for (int pp = 0; pp < NP; pp++)
+              acc[pp][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[pp], vb, acc[pp][j], 0, 0, 0);
+#pragma unroll
+            for (int pp = 0; pp < NP; pp++)
+              acc[pp][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[pp], vbias, acc[pp][j], 0, 0, 0);
+          } else {
+            const f16x8 vb = vop<KB>(d.vw[0], d.vw[1], j, voff, ur);
+#pragma unroll
+            for (int pp = 0; pp < NP; pp++)
+              acc[pp][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[pp], vb, acc[pp][j], 0, 0, 0);
+          }
         }
         load_v(nA, nB);  // value registers are free again
         pA = nA;
@@ -755,7 +849,7 @@ __global__ __launch_bounds__(256, NP == 1 ? 3 : 2) void decode_kernel(DecodePara
           for (int r = 0; r < 4; r++) s2[4 * t + r] = dq[r];
         }
         fold_cols8(s2);
-        softmax(s2, nvA, nvB);
+        softmax(s2, nvA, nvB, std::false_type{});
         // P rows: bf16 hi / lo parts of w (truncation; hi + lo carries 16 significant bits)
         bf16x8 pb[NP];
 #pragma unroll
