@@ -108,7 +108,9 @@ typedef struct {
 /* A batch cache.  Contiguous when block_table == NULL (capacity slots per sequence); paged
  * otherwise [P2, "How this connects to paging and prefix caching"]: each sequence's
  * compressed slots live in 16-token blocks of a shared pool, found through its row of the
- * block table.  Blocks that a call writes must belong to that sequence alone. */
+ * block table.  Blocks that a call writes must belong to that sequence alone.
+ * Calls return KVQ_ENOTSUP when batch * n_kv_heads > 65535 or when a buffer would hold 2^31 or
+ * more 16-slot tiles (batch * n_kv_heads * capacity / 16, or num_blocks * n_kv_heads). */
 typedef struct {
   kvq_format fmt;
   int32_t batch;      /* sequences B, 1 .. 4096 */

@@ -86,6 +86,13 @@ __device__ __forceinline__ int ld_uniform(const int32_t* ptr) {
   return *(const __attribute__((address_space(4))) int32_t*)(ptr);
 }
 
+// max(a, b, c) in one instruction; the operands are never NaN here.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -486,8 +493,9 @@ __global__ __launch_bounds__(256, NP == 1 ? 3 : 2) void decode_kernel(DecodePara
         for (int i = 0; i < 8; i++)
           if (4 * g + (i & 3) >= (i < 4 ? nvA : nvB)) s2[i] = -INFINITY;
       }
-      float tmax = fmaxf(fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3])),
-                         fmaxf(fmaxf(s2[4], s2[5]), fmaxf(s2[6], s2[7])));
+      const float m01 = max3f(s2[0], s2[1], s2[2]);
+      const float m02 = max3f(s2[3], s2[4], s2[5]);
+      float tmax = max3f(max3f(s2[6], s2[7], m01), m02, m02);
       tmax *= p.sm_log2;
       if (__ballot(tmax > m_run + LAZY_LOG2) != 0) {
         float hm = fmaxf(tmax, __shfl_xor(tmax, 16));
@@ -513,20 +521,15 @@ __global__ __launch_bounds__(256, NP == 1 ? 3 : 2) void decode_kernel(DecodePara
         }
         m_run = mn;
       }
-      float ls = 0.0f;
+      constexpr bool A16 = decltype(vfold)::value && KB == 4;  // alpha 16 at i % 4 >= 2
 #pragma unroll
       for (int i = 0; i < 8; i++) {
-        if constexpr (decltype(vfold)::value) {
-          constexpr float sh[8] = {0.f, 0.f, 4.f, 4.f, 0.f, 0.f, 4.f, 4.f};
-          const float a = (KB == 4) ? sh[i] : 0.0f;  // log2 alpha_i
-          s2[i] = __builtin_amdgcn_exp2f(fmaf(s2[i], p.sm_log2, -m_run - a));  // -inf -> 0
-          ls = fmaf(s2[i], (KB == 4 && sh[i] != 0.f) ? 16.0f : 1.0f, ls);
-        } else {
-          s2[i] = __builtin_amdgcn_exp2f(fmaf(s2[i], p.sm_log2, -m_run));  // -inf -> 0
-          ls += s2[i];
-        }
+        const float a = (A16 && (i & 2)) ? 4.0f : 0.0f;  // log2 alpha_i
+        s2[i] = __builtin_amdgcn_exp2f(fmaf(s2[i], p.sm_log2, -m_run - a));  // -inf -> 0
       }
-      l_run += ls;
+      const float l1 = (s2[0] + s2[1]) + (s2[4] + s2[5]);
+      const float l16 = (s2[2] + s2[3]) + (s2[6] + s2[7]);
+      l_run += A16 ? fmaf(l16, 16.0f, l1) : l1 + l16;
     };
 
     // sum the per-group (or hi/lo) columns of one head, for 8 scores at once
@@ -548,14 +551,14 @@ __global__ __launch_bounds__(256, NP == 1 ? 3 : 2) void decode_kernel(DecodePara
 
     // ---------------------------- compressed units ----------------------------
     if (x < xq_end) {
-      const long seq_tile0 = (static_cast<long>(b) * H + h) * (c.cap / TILE);
+      const int seq_tile0 = (b * H + h) * (c.cap / TILE);  // < 2^31 tiles (host check)
       const int* trow = c.table ? c.table + static_cast<size_t>(b) * c.max_blocks : nullptr;
       // physical tile of sequence tile t, or -1 for an unusable block-table entry
-      auto phys_of = [&](int t) -> long {
+      auto phys_of = [&](int t) -> int {
         if (!trow) return seq_tile0 + t;
         const int blk = ld_uniform(trow + t);
         if (blk < 0 || blk >= c.num_blocks) return -1;
-        return static_cast<long>(blk) * H + h;
+        return blk * H + h;
       };
       // Per-channel keys: lane l folds the eight channels of QK MFMA block (g', j') = (blk / 4,
       // blk % 4), blk = l % 16, for head l / 16 (and + 4): channels 32 g' + kchan(j', 0..7), which
@@ -592,11 +595,16 @@ __global__ __launch_bounds__(256, NP == 1 ? 3 : 2) void decode_kernel(DecodePara
       bool bad_block = false;
       // Every unit issues the same loads (an unusable or absent tile reads tile 0 of the buffer
       // and is ignored), so the compiler can count outstanding loads exactly.
-      auto load_k = [&](int xx, long pA, long pB) {
-        pA = max(pA, 0L);
-        pB = max(pB, 0L);
-        load_words<KB>(c.kc + pA * TILE_BYTES + n * RBK + g * (RBK / 4), d.kw[0]);
-        load_words<KB>(c.kc + pB * TILE_BYTES + n * RBK + g * (RBK / 4), d.kw[1]);
+      // Loads address a wave-uniform tile base (scalar registers) plus a 32-bit lane offset
+      // that is fixed for the segment, so no per-lane 64-bit address arithmetic is needed.
+      const unsigned k_lane = n * RBK + g * (RBK / 4);
+      const unsigned v_lane = (g * (D / 8) + n) * VCH;
+      const unsigned ks_lane = cg * TILE + 4 * g;
+      auto load_k = [&](int xx, int pA, int pB) {
+        pA = max(pA, 0);
+        pB = max(pB, 0);
+        load_words<KB>(c.kc + static_cast<size_t>(pA) * TILE_BYTES + k_lane, d.kw[0]);
+        load_words<KB>(c.kc + static_cast<size_t>(pB) * TILE_BYTES + k_lane, d.kw[1]);
         if constexpr (KPC) {
           const size_t mi = kpc_meta((32 * xx) / kgroup);
           d.fs = load_meta8(c.ks, mi);
@@ -604,26 +612,25 @@ __global__ __launch_bounds__(256, NP == 1 ? 3 : 2) void decode_kernel(DecodePara
         } else {
 #pragma unroll
           for (int t = 0; t < 2; t++) {
-            const long pt = t ? pB : pA;
-            const size_t mi = (static_cast<size_t>(pt) * ngk + cg) * TILE + 4 * g;
-            d.ks[t] = *reinterpret_cast<const uint2*>(c.ks + mi);
-            if constexpr (ASYM) d.kz[t] = *reinterpret_cast<const uint2*>(c.kz + mi);
+            const size_t tb = static_cast<size_t>(t ? pB : pA) * ngk * TILE;
+            d.ks[t] = *reinterpret_cast<const uint2*>(c.ks + tb + ks_lane);
+            if constexpr (ASYM) d.kz[t] = *reinterpret_cast<const uint2*>(c.kz + tb + ks_lane);
           }
         }
       };
-      auto load_v = [&](long pA, long pB) {
-        pA = max(pA, 0L);
-        pB = max(pB, 0L);
-        load_words<KB>(c.vc + pA * TILE_BYTES + (g * (D / 8) + n) * VCH, d.vw[0]);
-        load_words<KB>(c.vc + pB * TILE_BYTES + (g * (D / 8) + n) * VCH, d.vw[1]);
+      auto load_v = [&](int pA, int pB) {
+        pA = max(pA, 0);
+        pB = max(pB, 0);
+        load_words<KB>(c.vc + static_cast<size_t>(pA) * TILE_BYTES + v_lane, d.vw[0]);
+        load_words<KB>(c.vc + static_cast<size_t>(pB) * TILE_BYTES + v_lane, d.vw[1]);
 #pragma unroll
         for (int t = 0; t < 2; t++) {
-          const long pt = t ? pB : pA;
+          const size_t tb = static_cast<size_t>(t ? pB : pA) * ngv * TILE;
 #pragma unroll
           for (int pp = 0; pp < NP; pp++) {
-            const size_t mi = (static_cast<size_t>(pt) * ngv + rgv[pp]) * TILE + 4 * g;
-            d.vs[pp][t] = *reinterpret_cast<const uint2*>(c.vs + mi);
-            if constexpr (ASYM) d.vz[pp][t] = *reinterpret_cast<const uint2*>(c.vz + mi);
+            const unsigned lo = rgv[pp] * TILE + 4 * g;
+            d.vs[pp][t] = *reinterpret_cast<const uint2*>(c.vs + tb + lo);
+            if constexpr (ASYM) d.vz[pp][t] = *reinterpret_cast<const uint2*>(c.vz + tb + lo);
           }
         }
       };
@@ -674,8 +681,8 @@ __global__ __launch_bounds__(256, NP == 1 ? 3 : 2) void decode_kernel(DecodePara
         wave_lds_sync();
       };
 
-      long pA = phys_of(2 * x);
-      long pB = (32 * x + 16 < nq) ? phys_of(2 * x + 1) : -1;
+      int pA = phys_of(2 * x);
+      int pB = (32 * x + 16 < nq) ? phys_of(2 * x + 1) : -1;
       load_k(x, pA, pB);
       load_v(pA, pB);
       for (; x < xq_end; x += WAVES) {
@@ -683,8 +690,8 @@ __global__ __launch_bounds__(256, NP == 1 ? 3 : 2) void decode_kernel(DecodePara
         const bool more = xn < xq_end;
         // after the last unit, reload the current tiles (cache hits) so the load count per
         // iteration stays fixed
-        const long nA = more ? phys_of(2 * xn) : pA;
-        const long nB = more ? ((32 * xn + 16 < nq) ? phys_of(2 * xn + 1) : -1) : pB;
+        const int nA = more ? phys_of(2 * xn) : pA;
+        const int nB = more ? ((32 * xn + 16 < nq) ? phys_of(2 * xn + 1) : -1) : pB;
         // valid tokens of tiles A and B (a tile whose block is unusable counts as empty)
         const int nvA = pA >= 0 ? min(16, nq - 32 * x) : 0;
         const int nvB = pB >= 0 ? min(16, nq - 32 * x - 16) : 0;
@@ -733,10 +740,10 @@ __global__ __launch_bounds__(256, NP == 1 ? 3 : 2) void decode_kernel(DecodePara
             for (int r = 0; r < 4; r++) s2[4 * t + r] = dq[t][r] + row_ror<G>(dq[t][r]) + zt;
           } else {
             const uint2 k2 = d.ks[t];
-            s2[4 * t + 0] = dq[t][0] * f16_lo(k2.x);
-            s2[4 * t + 1] = dq[t][1] * f16_hi(k2.x);
-            s2[4 * t + 2] = dq[t][2] * f16_lo(k2.y);
-            s2[4 * t + 3] = dq[t][3] * f16_hi(k2.y);
+            s2[4 * t + 0] = fmaf(dq[t][0], f16_lo(k2.x), 0.0f);
+            s2[4 * t + 1] = fmaf(dq[t][1], f16_hi(k2.x), 0.0f);
+            s2[4 * t + 2] = fmaf(dq[t][2], f16_lo(k2.y), 0.0f);
+            s2[4 * t + 3] = fmaf(dq[t][3], f16_hi(k2.y), 0.0f);
             if constexpr (ASYM) {
               const uint2 z2 = d.kz[t];
               s2[4 * t + 0] += f16_lo(z2.x) * qsum;
@@ -763,10 +770,10 @@ __global__ __launch_bounds__(256, NP == 1 ? 3 : 2) void decode_kernel(DecodePara
 #pragma unroll
           for (int t = 0; t < 2; t++) {
             const uint2 s2v = d.vs[pp][t];
-            ws[4 * t + 0] = s2[4 * t + 0] * f16_lo(s2v.x);
-            ws[4 * t + 1] = s2[4 * t + 1] * f16_hi(s2v.x);
-            ws[4 * t + 2] = s2[4 * t + 2] * f16_lo(s2v.y);
-            ws[4 * t + 3] = s2[4 * t + 3] * f16_hi(s2v.y);
+            ws[4 * t + 0] = fmaf(s2[4 * t + 0], f16_lo(s2v.x), 0.0f);
+            ws[4 * t + 1] = fmaf(s2[4 * t + 1], f16_hi(s2v.x), 0.0f);
+            ws[4 * t + 2] = fmaf(s2[4 * t + 2], f16_lo(s2v.y), 0.0f);
+            ws[4 * t + 3] = fmaf(s2[4 * t + 3], f16_hi(s2v.y), 0.0f);
             if constexpr (ASYM) {
               const uint2 z2v = d.vz[pp][t];
               const float zv[4] = {f16_lo(z2v.x), f16_hi(z2v.x), f16_lo(z2v.y), f16_hi(z2v.y)};

@@ -70,6 +70,10 @@ kvq_status check_cache(const kvq_cache* c) {
   if (c->fmt.k.scheme == KVQ_ASYM && !c->k_zero) return KVQ_EINVAL;
   if (c->fmt.v.scheme == KVQ_ASYM && !c->v_zero) return KVQ_EINVAL;
   if (c->fmt.residual > 0 && (!c->k_res || !c->v_res)) return KVQ_EINVAL;
+  // kernels index 16-slot tiles with 32-bit integers
+  const long tiles = c->block_table ? static_cast<long>(c->num_blocks) * c->n_kv_heads
+                                    : static_cast<long>(c->batch) * c->n_kv_heads * (c->capacity / TILE);
+  if (tiles >= (1L << 31)) return KVQ_ENOTSUP;
   const void* al[] = {c->k_codes, c->v_codes, c->k_scale, c->v_scale};
   for (const void* p : al)
     if (!aligned16(p)) return KVQ_EALIGN;
