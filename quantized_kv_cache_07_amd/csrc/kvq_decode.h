@@ -1000,34 +1000,41 @@ __device__ __forceinline__ int block_of(long long u, long long U, long long NB) 
 // output is merged by CG threads over interleaved partials, then across them in LDS.
 constexpr int COMBINE_THREADS = 1024;
 
-template <int G>
+// Merge the partials of one (sequence, kv head): grid (B * H, S) with S slices of its G x D
+// outputs.  A workgroup takes OPP = min(G D / S, 256) outputs per pass with CG = 1024 / OPP
+// threads each; thread (cgi, oi) folds partials kf + cgi, kf + cgi + CG, ... with the
+// log-sum-exp rule, and the OPP threads of a group read contiguous floats of one partial.
+// S is chosen on the host from the partials a segment has on average: many slices when few
+// segments are split many ways (one long sequence), one or two when many short segments are.
+template <int G, int S>
 __global__ __launch_bounds__(COMBINE_THREADS) void combine_kernel(DecodeParams p) {
-  constexpr int OUTS = G * D;
-  constexpr int PASS = OUTS < 256 ? OUTS : 256;  // outputs per pass
-  constexpr int CG = COMBINE_THREADS / PASS;     // threads per output
-  constexpr int NPASS = OUTS / PASS;
-  __shared__ float sm[CG][PASS], sl[CG][PASS], so[CG][PASS];
+  static_assert((G * D) % S == 0 && (G * D) / S >= 32, "combine slices");
+  __shared__ float sm[COMBINE_THREADS], sl[COMBINE_THREADS], so[COMBINE_THREADS];
   const int H = p.c.H, B = p.c.B;
   const int b = blockIdx.x / H, h = blockIdx.x % H;
+  constexpr int opb = (G * D) / S;
+  constexpr int opp = opb < 256 ? opb : 256;
+  constexpr int cg = COMBINE_THREADS / opp;
+  const int oi = threadIdx.x % opp, cgi = threadIdx.x / opp;
   const int* pre = p.ws_pre;
   const long long U = pre[B], NB = p.nblocks;
   const int ub = (pre[b + 1] - pre[b]) / H;
-  float* dst = p.out + (static_cast<size_t>(b) * p.Hq + static_cast<size_t>(h) * G) * D;
+  float* dst = p.out + (static_cast<size_t>(b) * p.Hq + static_cast<size_t>(h) * G) * D +
+               static_cast<size_t>(blockIdx.y) * opb;
   if (ub == 0) {
-    for (int o = threadIdx.x; o < OUTS; o += COMBINE_THREADS) dst[o] = 0.0f;
+    for (int o = threadIdx.x; o < opb; o += COMBINE_THREADS) dst[o] = 0.0f;
     return;
   }
   const long long us = pre[b] + static_cast<long long>(h) * ub, ue = us + ub;
   const int kf = block_of(us, U, NB), kl = block_of(ue - 1, U, NB);
   if (kf == kl) return;  // one workgroup saw the whole sequence and wrote the output
   const int s0 = ((static_cast<long long>(kf) * U) / NB == us) ? 0 : 1;
-  const int oi = threadIdx.x % PASS, cgi = threadIdx.x / PASS;
-  for (int pass = 0; pass < NPASS; pass++) {
-    const int o = pass * PASS + oi;
+  for (int o0 = 0; o0 < opb; o0 += opp) {
+    const int o = static_cast<int>(blockIdx.y) * opb + o0 + oi;
     const int oh = o / D, ch = o % D;
     float M = -FLT_MAX, L = 0.0f, O = 0.0f;
 #pragma unroll 4
-    for (int k = kf + cgi; k <= kl; k += CG) {
+    for (int k = kf + cgi; k <= kl; k += cg) {
       const float* pt =
           p.ws_part + ((static_cast<size_t>(k) * 2 + (k == kf ? s0 : 0)) * G + oh) * PART_STRIDE;
       const float m = pt[0], l = pt[1], v = pt[4 + ch];
@@ -1037,22 +1044,22 @@ __global__ __launch_bounds__(COMBINE_THREADS) void combine_kernel(DecodeParams p
       O = O * a + v * e;
       M = mn;
     }
-    sm[cgi][oi] = M;
-    sl[cgi][oi] = L;
-    so[cgi][oi] = O;
+    sm[threadIdx.x] = M;
+    sl[threadIdx.x] = L;
+    so[threadIdx.x] = O;
     __syncthreads();
     if (cgi == 0) {
       float Mt = -FLT_MAX;
 #pragma unroll
-      for (int q = 0; q < CG; q++) Mt = fmaxf(Mt, sm[q][oi]);
+      for (int q = 0; q < cg; q++) Mt = fmaxf(Mt, sm[q * opp + oi]);
       float Lt = 0.0f, Ot = 0.0f;
 #pragma unroll
-      for (int q = 0; q < CG; q++) {
-        const float e = __builtin_amdgcn_exp2f(sm[q][oi] - Mt);
-        Lt += e * sl[q][oi];
-        Ot += e * so[q][oi];
+      for (int q = 0; q < cg; q++) {
+        const float e = __builtin_amdgcn_exp2f(sm[q * opp + oi] - Mt);
+        Lt += e * sl[q * opp + oi];
+        Ot += e * so[q * opp + oi];
       }
-      dst[o] = (Lt > 0.0f) ? Ot / Lt : 0.0f;
+      dst[o0 + oi] = (Lt > 0.0f) ? Ot / Lt : 0.0f;
     }
     __syncthreads();
   }
@@ -1082,7 +1089,18 @@ hipError_t launch_decode_t(const DecodeParams& p0, hipStream_t s) {
   decode_kernel<KB, G, KPC, NP, ASYM><<<p.nblocks, 256, lds, s>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  combine_kernel<G><<<p.c.B * p.c.H, COMBINE_THREADS, 0, s>>>(p);
+  // slices: about one per 4 partials a segment has on average, 32 outputs per slice at most
+  const int avg = p.nblocks / (p.c.B * p.c.H);
+  int slices = 1;
+  while (slices < 16 && slices * 2 <= avg / 4 && (G * D) / (slices * 2) >= 32) slices *= 2;
+  const dim3 grid(p.c.B * p.c.H, slices);
+  switch (slices) {
+    case 1: combine_kernel<G, 1><<<grid, COMBINE_THREADS, 0, s>>>(p); break;
+    case 2: combine_kernel<G, 2><<<grid, COMBINE_THREADS, 0, s>>>(p); break;
+    case 4: combine_kernel<G, 4><<<grid, COMBINE_THREADS, 0, s>>>(p); break;
+    case 8: if constexpr (G >= 2) combine_kernel<G, 8><<<grid, COMBINE_THREADS, 0, s>>>(p); break;
+    default: if constexpr (G >= 4) combine_kernel<G, 16><<<grid, COMBINE_THREADS, 0, s>>>(p); break;
+  }
   return hipGetLastError();
 }
 

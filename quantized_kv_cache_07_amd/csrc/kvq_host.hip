@@ -135,7 +135,8 @@ WsLayout ws_layout(const kvq_cache* c, int n_q_heads, int max_tokens) {
     const long v = std::atol(e);
     if (v >= 1 && v <= 65536) nb = v;
   }
-  const long ub = units_bound(c, max_tokens);
+  // at most one unit per wave is left idle: small batches get fewer, fuller workgroups
+  const long ub = (units_bound(c, max_tokens) + 3) / 4;
   if (nb > ub) nb = ub;
   if (nb < 1) nb = 1;
   w.nblocks = static_cast<int>(nb);
