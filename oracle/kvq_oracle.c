@@ -26,6 +26,11 @@
  *   - a BF16 window of recent tokens, quantized and moved into the compressed cache when it fills
  *                                                  [P2, "Why some systems keep a full-precision window"]
  *   - block-table addressing of fixed-size blocks  [P2, "How this connects to paging and prefix caching"]
+ *   - bits = 16: the unquantized BF16 cache, the baseline the compressed formats are measured
+ *     against and the fallback kept beside them  [P2, "From BF16 to INT8, INT4, or even fewer
+ *     bits": two bytes per value; P3, "Step 3: Deploy a Fallback-Capable FP8 First" and
+ *     "Go-Live Checklist": a BF16 baseline and fallback].  Elements are stored as given, with no
+ *     scale; in the byte images they are 16-bit fields of the same K-row and V-tile layouts.
  *   - Attention(q_t, K, V) = softmax(q_t K^T / sqrt(d_h)) V, in fp64 on the dequantized values
  *                                                  [P2, "Why the KV cache grows so quickly", attention eq.]
  *
@@ -199,6 +204,7 @@ typedef struct {
   uint16_t *ks, *kz, *vs, *vz;     /* per-token [H][cap][d/G]; per-channel keys [H][cap/Gt][d] */
   uint16_t *kres, *vres;           /* [H][R][d] bf16 */
   int32_t n_quant, n_res;
+  uint16_t *kb, *vb;               /* bits 16: the stored bf16 elements [H][cap][d] */
 } orc_seq;
 
 enum { ORC_OK = 0, ORC_ERR_CAPACITY = 1, ORC_ERR_FORMAT = 2 };
@@ -215,6 +221,14 @@ static size_t meta_index(const orc_seq *s, const orc_side *sd, int h, int slot, 
 static void quantize_rows(orc_seq *s, int is_k, const uint16_t *rows, size_t tok_stride,
                           size_t head_stride, int n, int slot0) {
   const orc_side *sd = is_k ? &s->k : &s->v;
+  if (sd->bits == 16) { /* BF16 storage: the element itself, no scale */
+    uint16_t *E = is_k ? s->kb : s->vb;
+    for (int h = 0; h < s->H; h++)
+      for (int j = 0; j < n; j++)
+        memcpy(E + ((size_t)h * s->cap + slot0 + j) * s->d,
+               rows + (size_t)j * tok_stride + (size_t)h * head_stride, 2 * (size_t)s->d);
+    return;
+  }
   uint8_t *U = is_k ? s->ku : s->vu;
   uint16_t *S = is_k ? s->ks : s->vs;
   uint16_t *Z = is_k ? s->kz : s->vz;
@@ -313,12 +327,14 @@ int orc_append(orc_seq *s, const uint16_t *k_new, const uint16_t *v_new, int32_t
 /* ------------------------------------------------------------------------------------------ */
 
 static double khat(const orc_seq *s, int h, int slot, int c) {
+  if (s->k.bits == 16) return (double)orc_bf16_to_f32(s->kb[((size_t)h * s->cap + slot) * s->d + c]);
   uint8_t u = s->ku[((size_t)h * s->cap + slot) * s->d + c];
   size_t mi = meta_index(s, &s->k, h, slot, c);
   return orc_dequant(s->k.bits, s->k.scheme, u, s->ks[mi], s->k.scheme == ORC_ASYM ? s->kz[mi] : 0);
 }
 
 static double vhat(const orc_seq *s, int h, int slot, int c) {
+  if (s->v.bits == 16) return (double)orc_bf16_to_f32(s->vb[((size_t)h * s->cap + slot) * s->d + c]);
   uint8_t u = s->vu[((size_t)h * s->cap + slot) * s->d + c];
   size_t mi = meta_index(s, &s->v, h, slot, c);
   return orc_dequant(s->v.bits, s->v.scheme, u, s->vs[mi], s->v.scheme == ORC_ASYM ? s->vz[mi] : 0);
@@ -423,6 +439,16 @@ static uint8_t get_field(const uint8_t *base, int64_t bit, int bits) {
   return (uint8_t)((base[bit / 8] >> (bit % 8)) & ((1u << bits) - 1u));
 }
 
+/* 16-bit fields (BF16 storage) start on a byte boundary; little-endian. */
+static void put16(uint8_t *base, int64_t bit, uint16_t x) {
+  base[bit / 8] = (uint8_t)(x & 0xff);
+  base[bit / 8 + 1] = (uint8_t)(x >> 8);
+}
+
+static uint16_t get16(const uint8_t *base, int64_t bit) {
+  return (uint16_t)(base[bit / 8] | (base[bit / 8 + 1] << 8));
+}
+
 static int64_t tile_index(const orc_seq *s, int b, int h, int slot, const int32_t *table_row) {
   if (table_row) return (int64_t)table_row[slot / 16] * s->H + h;
   return ((int64_t)b * s->H + h) * (s->cap / 16) + slot / 16;
@@ -444,10 +470,17 @@ void orc_pack(const orc_seq *s, int32_t b, const int32_t *table_row, uint8_t *kc
       uint8_t *krow = kc + (tile * 16 + p % 16) * RBk;
       uint8_t *vtile = vc + tile * 16 * RBv;
       for (int c = 0; c < d; c++) {
-        put_field(krow, orc_k_bit(s->k.bits, c), s->k.bits, s->ku[((size_t)h * s->cap + p) * d + c]);
-        put_field(vtile, orc_v_bit(s->v.bits, d, p % 16, c), s->v.bits,
-                  s->vu[((size_t)h * s->cap + p) * d + c]);
+        size_t e = ((size_t)h * s->cap + p) * d + c;
+        if (s->k.bits == 16)
+          put16(krow, orc_k_bit(16, c), s->kb[e]);
+        else
+          put_field(krow, orc_k_bit(s->k.bits, c), s->k.bits, s->ku[e]);
+        if (s->v.bits == 16)
+          put16(vtile, orc_v_bit(16, d, p % 16, c), s->vb[e]);
+        else
+          put_field(vtile, orc_v_bit(s->v.bits, d, p % 16, c), s->v.bits, s->vu[e]);
       }
+      if (s->k.bits == 16) continue; /* no scales */
       if (s->k.axis == ORC_PER_TOKEN) {
         for (int g = 0; g < ngk; g++) {
           size_t mi = meta_index(s, &s->k, h, p, g * s->k.group);
@@ -461,7 +494,7 @@ void orc_pack(const orc_seq *s, int32_t b, const int32_t *table_row, uint8_t *kc
         if (s->v.scheme == ORC_ASYM) vzc[(tile * ngv + g) * 16 + p % 16] = s->vz[mi];
       }
     }
-    if (s->k.axis == ORC_PER_CHANNEL) {
+    if (s->k.bits != 16 && s->k.axis == ORC_PER_CHANNEL) {
       int Gt = s->k.group, ntau = s->n_quant / Gt;
       for (int tau = 0; tau < ntau; tau++)
         for (int c = 0; c < d; c++) {
@@ -492,9 +525,15 @@ void orc_unpack_codes(orc_seq *s, int32_t b, const int32_t *table_row, const uin
       const uint8_t *krow = kc + (tile * 16 + p % 16) * RBk;
       const uint8_t *vtile = vc + tile * 16 * RBv;
       for (int c = 0; c < d; c++) {
-        s->ku[((size_t)h * s->cap + p) * d + c] = get_field(krow, orc_k_bit(s->k.bits, c), s->k.bits);
-        s->vu[((size_t)h * s->cap + p) * d + c] =
-            get_field(vtile, orc_v_bit(s->v.bits, d, p % 16, c), s->v.bits);
+        size_t e = ((size_t)h * s->cap + p) * d + c;
+        if (s->k.bits == 16)
+          s->kb[e] = get16(krow, orc_k_bit(16, c));
+        else
+          s->ku[e] = get_field(krow, orc_k_bit(s->k.bits, c), s->k.bits);
+        if (s->v.bits == 16)
+          s->vb[e] = get16(vtile, orc_v_bit(16, d, p % 16, c));
+        else
+          s->vu[e] = get_field(vtile, orc_v_bit(s->v.bits, d, p % 16, c), s->v.bits);
       }
     }
 }
@@ -508,4 +547,4 @@ void orc_f16_to_f32_array(const uint16_t *x, float *y, int64_t n) {
   for (int64_t i = 0; i < n; i++) y[i] = orc_f16_to_f32(x[i]);
 }
 
-int32_t orc_abi_version(void) { return 1; }
+int32_t orc_abi_version(void) { return 2; }

@@ -165,7 +165,8 @@ class _Seq(ctypes.Structure):
                 ("ks", ctypes.c_void_p), ("kz", ctypes.c_void_p),
                 ("vs", ctypes.c_void_p), ("vz", ctypes.c_void_p),
                 ("kres", ctypes.c_void_p), ("vres", ctypes.c_void_p),
-                ("n_quant", ctypes.c_int32), ("n_res", ctypes.c_int32)]
+                ("n_quant", ctypes.c_int32), ("n_res", ctypes.c_int32),
+                ("kb", ctypes.c_void_p), ("vb", ctypes.c_void_p)]
 
 
 class OracleError(RuntimeError):
@@ -174,7 +175,8 @@ class OracleError(RuntimeError):
 
 class Sequence:
     """Logical cache of one sequence (all kv heads): one code byte per element plus fp16
-    metadata, and the BF16 window.  ``k_side``/``v_side`` are (bits, scheme, axis, group)."""
+    metadata, and the BF16 window.  ``k_side``/``v_side`` are (bits, scheme, axis, group);
+    bits 16 is the unquantized BF16 cache (elements kept in ``kb``/``vb``, no metadata)."""
 
     def __init__(self, k_side, v_side, n_kv_heads: int, residual: int, capacity: int,
                  d: int = D_HEAD):
@@ -183,6 +185,8 @@ class Sequence:
         H, cap = n_kv_heads, capacity
         self.ku = np.zeros((H, cap, d), np.uint8)
         self.vu = np.zeros((H, cap, d), np.uint8)
+        self.kb = np.zeros((H, cap, d) if self.k_side[0] == 16 else 1, np.uint16)
+        self.vb = np.zeros((H, cap, d) if self.v_side[0] == 16 else 1, np.uint16)
 
         def meta(side):
             bits, scheme, axis, group = side
@@ -197,7 +201,7 @@ class Sequence:
         self.vres = np.zeros((H, max(residual, 1), d), np.uint16)
         self._s = _Seq(_Side(*self.k_side), _Side(*self.v_side), d, H, residual, cap,
                        _p(self.ku), _p(self.vu), _p(self.ks), _p(self.kz), _p(self.vs),
-                       _p(self.vz), _p(self.kres), _p(self.vres), 0, 0)
+                       _p(self.vz), _p(self.kres), _p(self.vres), 0, 0, _p(self.kb), _p(self.vb))
 
     @property
     def n_quant(self) -> int:

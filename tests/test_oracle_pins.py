@@ -326,6 +326,9 @@ def python_reference_attention(seq, q_bits, sm_scale):
     Hq = q_bits.shape[0]
     qf = (q_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
+    def bf16(x):
+        return float((np.asarray(x, np.uint32) << 16).view(np.float32))
+
     def deq(u, s16, z16, bits, scheme):
         s = float(f16_np(s16))
         if scheme == 0:
@@ -345,10 +348,16 @@ def python_reference_attention(seq, q_bits, sm_scale):
         h = hq * H // Hq
         keys, vals = [], []
         for p in range(seq.n_quant):
-            keys.append([deq(seq.ku[h, p, c], *meta(seq.k_side, seq.ks, seq.kz, h, p, c), k_bits,
-                             k_scheme) for c in range(d)])
-            vals.append([deq(seq.vu[h, p, c], *meta(seq.v_side, seq.vs, seq.vz, h, p, c), v_bits,
-                             v_scheme) for c in range(d)])
+            if k_bits == 16:
+                keys.append([bf16(seq.kb[h, p, c]) for c in range(d)])
+            else:
+                keys.append([deq(seq.ku[h, p, c], *meta(seq.k_side, seq.ks, seq.kz, h, p, c),
+                                 k_bits, k_scheme) for c in range(d)])
+            if v_bits == 16:
+                vals.append([bf16(seq.vb[h, p, c]) for c in range(d)])
+            else:
+                vals.append([deq(seq.vu[h, p, c], *meta(seq.v_side, seq.vs, seq.vz, h, p, c),
+                                 v_bits, v_scheme) for c in range(d)])
         for r in range(seq.n_res):
             keys.append(list((seq.kres[h, r].astype(np.uint32) << 16).view(np.float32).astype(float)))
             vals.append(list((seq.vres[h, r].astype(np.uint32) << 16).view(np.float32).astype(float)))
@@ -366,6 +375,7 @@ def python_reference_attention(seq, q_bits, sm_scale):
     ((4, 0, 0, 64), (4, 0, 0, 64), 16, 45),
     ((2, 1, 1, 16), (2, 1, 0, 32), 32, 61),
     ((4, 1, 0, 32), (8, 1, 0, 64), 16, 33),
+    ((16, 0, 0, 128), (16, 0, 0, 128), 16, 37),
 ])
 def test_attention_brute_force_tiny(orc, case):
     """The oracle's attention over its own state equals a pure-Python fsum computation to
@@ -382,6 +392,73 @@ def test_attention_brute_force_tiny(orc, case):
     got = seq.attend(q, sm)
     ref = python_reference_attention(seq, q, sm)
     assert np.allclose(got, ref, rtol=2.0**-23, atol=1e-30)
+
+
+# ------------------------------------------------------------------------------------------
+# BF16 storage (bits 16): the unquantized baseline [P2, "From BF16 to INT8, INT4, or even fewer
+# bits"; P3, "Go-Live Checklist": a BF16 baseline and fallback]
+# ------------------------------------------------------------------------------------------
+
+BF16_SIDE = (16, 0, 0, 128)
+
+
+def test_bf16_storage_keeps_every_bit(orc):
+    H, T, R = 2, 77, 16
+    seq = orc.Sequence(BF16_SIDE, BF16_SIDE, H, R, capacity=128)
+    kv = bf16_values(RNG.standard_normal((2, T, H, 128)).astype(np.float32) * 100)
+    kb = (kv.view(np.uint32) >> 16).astype(np.uint16)
+    seq.append(kb[0], kb[1])
+    nq = seq.n_quant
+    assert nq == T - seq.n_res and seq.n_res == (T - 1) % R + 1
+    assert np.array_equal(seq.kb[:, :nq], kb[0, :nq].transpose(1, 0, 2))
+    assert np.array_equal(seq.vb[:, :nq], kb[1, :nq].transpose(1, 0, 2))
+
+
+def test_bf16_equals_int8_where_int8_is_exact(orc):
+    """Rows of integers in [-127, 127] that reach +-127 in every row: the INT8 per-token
+    quantizer (group 128) gets scale exactly 1 and reproduces them, so attention over the INT8
+    cache and over the BF16 cache sees identical values and must agree to the last bit."""
+    H, T, Hq = 2, 70, 4
+    x = RNG.integers(-127, 128, size=(2, T, H, 128)).astype(np.float32)
+    x[..., 5] = np.where(RNG.random((2, T, H)) < 0.5, 127.0, -127.0)
+    xb = (x.view(np.uint32) >> 16).astype(np.uint16)  # integers below 256 are exact in bf16
+    a = orc.Sequence(BF16_SIDE, BF16_SIDE, H, 0, capacity=128)
+    b = orc.Sequence((8, 0, 0, 128), (8, 0, 0, 128), H, 0, capacity=128)
+    a.append(xb[0], xb[1])
+    b.append(xb[0], xb[1])
+    assert np.all(b.ks[:, :T] == 0x3C00) and np.all(b.vs[:, :T] == 0x3C00)  # fp16 1.0
+    q = (bf16_values(RNG.standard_normal((Hq, 128)).astype(np.float32) * 0.01).view(np.uint32)
+         >> 16).astype(np.uint16)
+    assert np.array_equal(a.attend(q, 0.088), b.attend(q, 0.088))
+
+
+def test_bf16_layout_and_paged_roundtrip(orc):
+    vb = sorted(orc.v_bit(16, t, c) for t in range(16) for c in range(128))
+    assert vb == list(range(0, 16 * 128 * 16, 16))
+    # channel c of token t sits at byte 2 (4 (8 chunk + c % 8) + t % 4) of its tile
+    for t in range(16):
+        for c in range(128):
+            chunk = (t // 4) * 16 + c // 8
+            assert orc.v_bit(16, t, c) == 16 * (4 * (8 * chunk + c % 8) + t % 4)
+    H, T = 2, 90
+    seq = orc.Sequence(BF16_SIDE, BF16_SIDE, H, 0, capacity=128)
+    kv = bf16_values(RNG.standard_normal((2, T, H, 128)).astype(np.float32))
+    kb = (kv.view(np.uint32) >> 16).astype(np.uint16)
+    seq.append(kb[0], kb[1])
+    table = RNG.permutation(8).astype(np.int32)
+    im = orc.empty_images(BF16_SIDE, BF16_SIDE, 1, H, 0, num_blocks=8)
+    seq.pack(0, im, table)
+    # K rows are plain little-endian bf16 rows
+    for p_ in (0, 17, 89):
+        for h in range(H):
+            tile = table[p_ // 16] * H + h
+            row = im["k_codes"][(tile * 16 + p_ % 16) * 256:(tile * 16 + p_ % 16 + 1) * 256]
+            assert np.array_equal(row.view(np.uint16), kb[0, p_, h])
+    back = orc.Sequence(BF16_SIDE, BF16_SIDE, H, 0, capacity=128)
+    back.set_counters(T, 0)
+    back.unpack_codes(0, im, table)
+    assert np.array_equal(back.kb[:, :T], seq.kb[:, :T])
+    assert np.array_equal(back.vb[:, :T], seq.vb[:, :T])
 
 
 # ------------------------------------------------------------------------------------------
