@@ -90,8 +90,15 @@ enum {
   KVQ_BUF_K_ZERO = 4, KVQ_BUF_V_ZERO = 5, KVQ_BUF_K_RES = 6, KVQ_BUF_V_RES = 7
 };
 
+/* bits = 16 selects the unquantized BF16 cache, the baseline and fallback the compressed
+ * formats are measured against [P2, "From BF16 to INT8, INT4, or even fewer bits"; P3, "Step 3:
+ * Deploy a Fallback-Capable FP8 First", "Go-Live Checklist"]: both sides 16, scheme KVQ_SYM,
+ * axis KVQ_PER_TOKEN, group 128 (else KVQ_EINVAL).  Elements are stored as given -- K rows as
+ * bf16 rows, V in the same token-interleaved tile layout as the codes, two bytes per field --
+ * and there are no scale or zero buffers (kvq_buffer_bytes returns 0, the pointers may be
+ * NULL).  Stored bytes past a sequence's end are never read into a result. */
 typedef struct {
-  int32_t bits;   /* 2, 4 or 8 */
+  int32_t bits;   /* 2, 4 or 8; 16 = unquantized BF16 */
   int32_t scheme; /* KVQ_SYM or KVQ_ASYM */
   int32_t axis;   /* KVQ_PER_TOKEN or KVQ_PER_CHANNEL (keys only) */
   int32_t group;  /* PER_TOKEN: channels per group, 32, 64 or 128.
@@ -121,7 +128,7 @@ typedef struct {
   int32_t max_blocks; /* paged: row length of block_table; contiguous: 0 */
   const int32_t *block_table; /* paged: [batch][max_blocks] int32; contiguous: NULL */
   uint8_t *k_codes, *v_codes;   /* sized by kvq_buffer_bytes(), 16-byte aligned */
-  uint16_t *k_scale, *v_scale;  /* fp16 bit patterns */
+  uint16_t *k_scale, *v_scale;  /* fp16 bit patterns; NULL allowed for bits 16 */
   uint16_t *k_zero, *v_zero;    /* fp16 bit patterns; NULL for a KVQ_SYM side */
   uint16_t *k_res, *v_res;      /* bf16 window; NULL when residual == 0 */
   int32_t *n_quant, *n_res;     /* [batch] counters; zero for an empty cache */

@@ -259,6 +259,11 @@ def empty_images(k_side, v_side, batch: int, n_kv_heads: int, residual: int, cap
     for name, side in (("k", k_side), ("v", v_side)):
         bits, scheme, axis, group = side
         out[f"{name}_codes"] = np.zeros(tiles * TILE * d * bits // 8, np.uint8)
+        if bits == 16:  # BF16 storage has no metadata
+            out[f"{name}_scale"] = np.zeros(0, np.uint16)
+            out[f"{name}_zero"] = np.zeros(0, np.uint16)
+            out[f"{name}_res"] = np.zeros(batch * H * max(residual, 1) * d, np.uint16)
+            continue
         if axis == PER_TOKEN:
             n = tiles * (d // group) * TILE
         else:

@@ -154,6 +154,29 @@ __global__ __launch_bounds__(256) void quantize_kernel(CacheDev c, const uint16_
   }
   __syncthreads();
 
+  // BF16 storage (bits 16): the rows go in unchanged -- K row-major, V into the tile's
+  // token-interleaved layout (channel ch of tile row t at halfword 4 (8 chunk + ch % 8) + t % 4,
+  // chunk (t / 4) (D / 8) + ch / 8) -- and there is no metadata.
+  if (K.bits == 16) {
+    constexpr int PIECES = D * 2 / 16;
+    for (int it = tid; it < (hi - lo) * PIECES; it += blockDim.x) {
+      const int slot = lo + it / PIECES, piece = it % PIECES;
+      bool ok = true;
+      const long tile = tile_index(c, b, h, slot / TILE, ok);
+      reinterpret_cast<uint4*>(c.kc + (tile * TILE + slot % TILE) * (D * 2))[piece] =
+          reinterpret_cast<const uint4*>(&xs[slot - seg0][0][0])[piece];
+    }
+    for (int it = tid; it < (hi - lo) * D; it += blockDim.x) {
+      const int slot = lo + it / D, ch = it % D, tr = slot % TILE;
+      bool ok = true;
+      const long tile = tile_index(c, b, h, slot / TILE, ok);
+      const int chunk = (tr / 4) * (D / 8) + ch / 8;
+      reinterpret_cast<uint16_t*>(c.vc + tile * TILE * (D * 2))[(chunk * 8 + ch % 8) * 4 + tr % 4] =
+          xs[slot - seg0][1][ch];
+    }
+    return;
+  }
+
   // Phase 1a: per-token groups.  One wave per (slot, side) row; lane l holds channels 2l and
   // 2l + 1, and the group's maximum (or minimum and maximum) is reduced across its lanes.
   {

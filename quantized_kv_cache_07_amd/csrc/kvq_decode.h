@@ -112,6 +112,10 @@ template <int KB>
 __device__ __forceinline__ UnpackRegs unpack_regs() {
   UnpackRegs r;
   r.magic = 0x64006400u;
+  if constexpr (KB == 16) {  // BF16 storage: nothing to unpack
+    r.m_lo = r.m_hi = 0;
+    return r;
+  }
   asm volatile("" : "+v"(r.magic));
   if constexpr (KB == 8) {
     asm volatile("s_mov_b32 %0, 0x00ff00ff" : "=s"(r.m_lo));
@@ -137,7 +141,9 @@ __device__ __forceinline__ f16x2 upair(const uint32_t* w, int r, float off, cons
   constexpr int HH = 16 / KB;
   const uint32_t x = w[r / HH];
   const int k = r % HH;
-  if constexpr (KB == 8) {
+  if constexpr (KB == 16) {  // stored bf16 pairs are never unpacked (bf16 products read them)
+    return as_h2(x);
+  } else if constexpr (KB == 8) {
     const uint32_t s = k ? (x >> 8) : x;
     return as_h2((s & u.m_lo) | u.magic) - h2s(1024.0f + off);
   } else if constexpr (KB == 4) {
@@ -245,6 +251,7 @@ __device__ __forceinline__ u16x8 gather_kchan(const uint16_t* row, int j) {
     return __builtin_shufflevector(a, b, 0, 4, 1, 5, 2, 6, 3, 7);
   } else {
     const u16x8 a = *reinterpret_cast<const u16x8*>(row + 8 * j);
+    if constexpr (KB == 16) return a;
     if constexpr (KB == 4) return __builtin_shufflevector(a, a, 0, 4, 1, 5, 2, 6, 3, 7);
     else return __builtin_shufflevector(a, a, 0, 2, 1, 3, 4, 6, 5, 7);
   }
@@ -267,7 +274,13 @@ __device__ __forceinline__ uint2 ld_stream2(const void* p) {
 
 template <int KB>
 __device__ __forceinline__ void load_words(const uint8_t* ptr, uint32_t (&w)[KB]) {
-  if constexpr (KB == 8) {
+  if constexpr (KB == 16) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const uint4 a = ld_stream4(ptr + 16 * i);
+      w[4 * i] = a.x; w[4 * i + 1] = a.y; w[4 * i + 2] = a.z; w[4 * i + 3] = a.w;
+    }
+  } else if constexpr (KB == 8) {
     const uint4 a = ld_stream4(ptr);
     const uint4 b = ld_stream4(ptr + 16);
     w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
@@ -321,7 +334,7 @@ __device__ __forceinline__ int seq_units(const CacheDev& c, int max_tokens, int 
 }
 
 template <int KB, int G, bool KPC, int NP, bool ASYM>
-__global__ __launch_bounds__(256, NP == 1 ? 3 : 2) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const CacheDev& c = p.c;
   const int B = c.B, H = c.H;
@@ -388,7 +401,8 @@ __global__ __launch_bounds__(256, NP == 1 ? 3 : 2) void decode_kernel(DecodePara
   // Value codes enter PV raw (1024 + alpha u) when alpha depends only on the token position
   // (8- and 4-bit); the weights then carry 1 / alpha and one more product with vbias removes the
   // bias.  2-bit fields change alpha with the channel, so they are unpacked exactly instead.
-  constexpr bool VBF = KB != 2;
+  constexpr bool VBF = KB == 4 || KB == 8;
+  constexpr bool BF = KB == 16;  // unquantized BF16 storage: bf16 matrix products, no scales
   f16x8 vbias;
 #pragma unroll
   for (int i = 0; i < 8; i++)
@@ -432,10 +446,15 @@ __global__ __launch_bounds__(256, NP == 1 ? 3 : 2) void decode_kernel(DecodePara
 
     // ---- QK operand: f16 query, masked to the column's key group ----
     f16x8 qb[4];
+    bf16x8 qbf[4];                            // BF16 storage: the bf16 query as it is
     f32x4 dq0 = f32x4{0.f, 0.f, 0.f, 0.f};  // QK accumulator start of every tile
     float qsum = 0.0f;  // asymmetric per-token keys: sum of q over the column's group
     float zt = 0.0f;    // asymmetric per-channel keys: sum of q * zero over the key group
-    if constexpr (!KPC) {
+    if constexpr (BF) {
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        qbf[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qs + hh * D + 32 * g + 8 * j));
+    } else if constexpr (!KPC) {
       const bool in_grp = ((32 * g) / kgroup) == cg;
 #pragma unroll
       for (int j = 0; j < 4; j++) {
@@ -605,7 +624,8 @@ __global__ __launch_bounds__(256, NP == 1 ? 3 : 2) void decode_kernel(DecodePara
         pB = max(pB, 0);
         load_words<KB>(c.kc + static_cast<size_t>(pA) * TILE_BYTES + k_lane, d.kw[0]);
         load_words<KB>(c.kc + static_cast<size_t>(pB) * TILE_BYTES + k_lane, d.kw[1]);
-        if constexpr (KPC) {
+        if constexpr (BF) {
+        } else if constexpr (KPC) {
           const size_t mi = kpc_meta((32 * xx) / kgroup);
           d.fs = load_meta8(c.ks, mi);
           if constexpr (ASYM) d.fz = load_meta8(c.kz, mi);
@@ -623,6 +643,7 @@ __global__ __launch_bounds__(256, NP == 1 ? 3 : 2) void decode_kernel(DecodePara
         pB = max(pB, 0);
         load_words<KB>(c.vc + static_cast<size_t>(pA) * TILE_BYTES + v_lane, d.vw[0]);
         load_words<KB>(c.vc + static_cast<size_t>(pB) * TILE_BYTES + v_lane, d.vw[1]);
+        if constexpr (!BF)
 #pragma unroll
         for (int t = 0; t < 2; t++) {
           const size_t tb = static_cast<size_t>(t ? pB : pA) * ngv * TILE;
@@ -723,6 +744,14 @@ __global__ __launch_bounds__(256, NP == 1 ? 3 : 2) void decode_kernel(DecodePara
               dq[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop<KB>(d.kw[1], j, koff, ur), qb[j], dq[1], 0, 0, 0);
             }
           }
+        } else if constexpr (BF) {
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            const bf16x8 ka = __builtin_bit_cast(bf16x8, uint4{d.kw[0][4 * j], d.kw[0][4 * j + 1], d.kw[0][4 * j + 2], d.kw[0][4 * j + 3]});
+            const bf16x8 kb = __builtin_bit_cast(bf16x8, uint4{d.kw[1][4 * j], d.kw[1][4 * j + 1], d.kw[1][4 * j + 2], d.kw[1][4 * j + 3]});
+            dq[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qbf[j], dq[0], 0, 0, 0);
+            dq[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qbf[j], dq[1], 0, 0, 0);
+          }
         } else {
           dq[0] = dq0;
           dq[1] = dq0;
@@ -735,7 +764,10 @@ __global__ __launch_bounds__(256, NP == 1 ? 3 : 2) void decode_kernel(DecodePara
         float s2[8];
 #pragma unroll
         for (int t = 0; t < 2; t++) {
-          if constexpr (KPC) {
+          if constexpr (BF) {
+#pragma unroll
+            for (int r = 0; r < 4; r++) s2[4 * t + r] = dq[t][r];
+          } else if constexpr (KPC) {
 #pragma unroll
             for (int r = 0; r < 4; r++) s2[4 * t + r] = dq[t][r] + row_ror<G>(dq[t][r]) + zt;
           } else {
@@ -762,6 +794,48 @@ __global__ __launch_bounds__(256, NP == 1 ? 3 : 2) void decode_kernel(DecodePara
         // Rows 16 pp + n with part >= 2 are never read back, so they are left as computed.
         // A stand-in tile's scales may be anything: its tokens' products are selected away.
         const bool full = nvA == 16 && nvB == 16;
+        if constexpr (BF) {
+          // bf16 hi / lo parts of w (truncations; hi + lo carries 16 significant bits); a
+          // stand-in tile's tokens have w = 0 and its finite rows contribute nothing
+          bf16x8 pb;
+          uint32_t pk[4];
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            uint32_t e2[2];
+#pragma unroll
+            for (int k2 = 0; k2 < 2; k2++) {
+              const float wv = s2[2 * i + k2];
+              const float lo_v = wv - __uint_as_float(__float_as_uint(wv) & 0xFFFF0000u);
+              e2[k2] = __float_as_uint(rpart[0] == 1 ? lo_v : wv) >> 16;
+            }
+            pk[i] = e2[0] | (e2[1] << 16);
+          }
+          pb = __builtin_bit_cast(bf16x8, uint4{pk[0], pk[1], pk[2], pk[3]});
+          if (!full) {
+            // stored bytes past the sequence end (or of a stand-in tile) may be anything, and
+            // 0 * NaN is NaN: clear the lane's value halves of tokens it must not read
+#pragma unroll
+            for (int tt = 0; tt < 2; tt++) {
+              const int nv = tt ? nvB : nvA;
+#pragma unroll
+              for (int w = 0; w < 16; w++) {
+                // word w of the chunk holds tokens 2 (w % 2) and 2 (w % 2) + 1 of channel w / 2
+                const int r0 = 4 * g + 2 * (w % 2);
+                const uint32_t keep = (r0 < nv ? 0x0000FFFFu : 0u) | (r0 + 1 < nv ? 0xFFFF0000u : 0u);
+                d.vw[tt][w] &= keep;
+              }
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < 8; j++) {
+            const bf16x8 vb = __builtin_bit_cast(bf16x8, uint4{d.vw[0][2 * j], d.vw[0][2 * j + 1], d.vw[1][2 * j], d.vw[1][2 * j + 1]});
+            acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb, vb, acc[0][j], 0, 0, 0);
+          }
+          load_v(nA, nB);  // value registers are free again
+          pA = nA;
+          pB = nB;
+          continue;
+        }
         f16x8 pa[NP];
 #pragma unroll
         for (int pp = 0; pp < NP; pp++) {
@@ -1106,6 +1180,16 @@ hipError_t launch_decode_t(const DecodeParams& p0, hipStream_t s) {
 
 template <int KB, bool ASYM>
 hipError_t launch_decode_bits(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s) {
+  if constexpr (KB == 16) {  // BF16 storage: per-token rows only, at most 16 PV rows
+    if (kpc || NP != 1) return hipErrorInvalidValue;
+    switch (G) {
+      case 1: return launch_decode_t<16, 1, false, 1, false>(p, s);
+      case 2: return launch_decode_t<16, 2, false, 1, false>(p, s);
+      case 4: return launch_decode_t<16, 4, false, 1, false>(p, s);
+      case 8: return launch_decode_t<16, 8, false, 1, false>(p, s);
+      default: return hipErrorInvalidValue;
+    }
+  } else {
 #define KVQ_CASE(GG, NN)                                                        \
   if (G == GG && NP == NN)                                                      \
     return kpc ? launch_decode_t<KB, GG, true, NN, ASYM>(p, s)                 \
@@ -1117,7 +1201,8 @@ hipError_t launch_decode_bits(const DecodeParams& p, int G, int NP, bool kpc, hi
   KVQ_CASE(8, 1)
   KVQ_CASE(8, 2)
 #undef KVQ_CASE
-  return hipErrorInvalidValue;
+    return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace kvq

@@ -18,12 +18,17 @@ hipError_t launch_decode_b8s(const DecodeParams& p, int G, int NP, bool kpc, hip
 hipError_t launch_decode_b2a(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s);
 hipError_t launch_decode_b4a(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s);
 hipError_t launch_decode_b8a(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s);
+hipError_t launch_decode_b16(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s);
 
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 kvq_status check_side(const kvq_side& s, bool is_key, int residual) {
+  if (s.bits == 16) {  // unquantized BF16 storage: one "group" per row, no scale
+    if (s.scheme != KVQ_SYM || s.axis != KVQ_PER_TOKEN || s.group != D) return KVQ_EINVAL;
+    return KVQ_OK;
+  }
   if (s.bits != 2 && s.bits != 4 && s.bits != 8) return KVQ_ENOTSUP;
   if (s.scheme != KVQ_SYM && s.scheme != KVQ_ASYM) return KVQ_EINVAL;
   if (s.axis == KVQ_PER_TOKEN) {
@@ -64,8 +69,9 @@ kvq_status check_cache(const kvq_cache* c) {
     if (c->capacity < TILE || c->capacity % TILE != 0) return KVQ_EINVAL;
     if (c->fmt.k.axis == KVQ_PER_CHANNEL && c->capacity % c->fmt.k.group != 0) return KVQ_EINVAL;
   }
-  if (!c->k_codes || !c->v_codes || !c->k_scale || !c->v_scale || !c->n_quant || !c->n_res ||
-      !c->err)
+  const bool scaled = c->fmt.k.bits != 16;
+  if (!c->k_codes || !c->v_codes || (scaled && (!c->k_scale || !c->v_scale)) || !c->n_quant ||
+      !c->n_res || !c->err)
     return KVQ_EINVAL;
   if (c->fmt.k.scheme == KVQ_ASYM && !c->k_zero) return KVQ_EINVAL;
   if (c->fmt.v.scheme == KVQ_ASYM && !c->v_zero) return KVQ_EINVAL;
@@ -74,9 +80,11 @@ kvq_status check_cache(const kvq_cache* c) {
   const long tiles = c->block_table ? static_cast<long>(c->num_blocks) * c->n_kv_heads
                                     : static_cast<long>(c->batch) * c->n_kv_heads * (c->capacity / TILE);
   if (tiles >= (1L << 31)) return KVQ_ENOTSUP;
-  const void* al[] = {c->k_codes, c->v_codes, c->k_scale, c->v_scale};
+  const void* al[] = {c->k_codes, c->v_codes};
   for (const void* p : al)
     if (!aligned16(p)) return KVQ_EALIGN;
+  if ((c->k_scale && !aligned16(c->k_scale)) || (c->v_scale && !aligned16(c->v_scale)))
+    return KVQ_EALIGN;
   if ((c->k_zero && !aligned16(c->k_zero)) || (c->v_zero && !aligned16(c->v_zero)) ||
       (c->k_res && !aligned16(c->k_res)) || (c->v_res && !aligned16(c->v_res)))
     return KVQ_EALIGN;
@@ -216,6 +224,7 @@ size_t kvq_buffer_bytes(const kvq_format* fmt, int32_t batch, int32_t n_kv_heads
     case KVQ_BUF_V_SCALE:
     case KVQ_BUF_K_ZERO:
     case KVQ_BUF_V_ZERO: {
+      if (s.bits == 16) return 0;
       if ((which == KVQ_BUF_K_ZERO || which == KVQ_BUF_V_ZERO) && s.scheme != KVQ_ASYM) return 0;
       if (s.axis == KVQ_PER_TOKEN) return tiles * (D / s.group) * TILE * 2;
       if (paged || capacity % s.group) return 0;
@@ -302,6 +311,7 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int32_t n
   switch (cache->fmt.k.bits) {
     case 2: e = asym ? launch_decode_b2a(p, G, NP, kpc, st) : launch_decode_b2s(p, G, NP, kpc, st); break;
     case 4: e = asym ? launch_decode_b4a(p, G, NP, kpc, st) : launch_decode_b4s(p, G, NP, kpc, st); break;
+    case 16: e = launch_decode_b16(p, G, NP, kpc, st); break;
     default: e = asym ? launch_decode_b8a(p, G, NP, kpc, st) : launch_decode_b8s(p, G, NP, kpc, st); break;
   }
   return e == hipSuccess ? KVQ_OK : KVQ_ELAUNCH;

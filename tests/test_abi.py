@@ -39,7 +39,8 @@ def test_every_declared_symbol_is_exported(K):
 @pytest.mark.parametrize("k,v,R", [((4, 0, 0, 64), (4, 0, 0, 64), 0),
                                    ((8, 0, 0, 128), (8, 0, 0, 128), 16),
                                    ((2, 1, 1, 32), (2, 1, 0, 32), 128),
-                                   ((4, 1, 0, 32), (4, 1, 0, 32), 32)])
+                                   ((4, 1, 0, 32), (4, 1, 0, 32), 32),
+                                   ((16, 0, 0, 128), (16, 0, 0, 128), 16)])
 def test_buffer_sizes_match_the_storage_layout(K, orc, k, v, R):
     fmt = K.make_format(k, v, R)
     B, H = 3, 2
@@ -77,6 +78,11 @@ def test_worked_example_footprint(K):
     ((8, 0, 0, 64), (4, 0, 0, 64), 0, 2),     # K and V share one bit width
     ((4, 2, 0, 64), (4, 0, 0, 64), 0, 1),
     ((4, 0, 0, 64), (4, 0, 0, 64), 24, 1),    # window not a multiple of 16
+    ((16, 0, 0, 128), (16, 0, 0, 128), 0, 0),  # unquantized BF16 cache
+    ((16, 0, 0, 128), (16, 0, 0, 128), 32, 0),
+    ((16, 1, 0, 128), (16, 1, 0, 128), 0, 1),  # BF16 storage has no scheme ...
+    ((16, 0, 0, 64), (16, 0, 0, 64), 0, 1),    # ... and no groups
+    ((16, 0, 0, 128), (8, 0, 0, 128), 0, 2),   # K and V share one width
 ])
 def test_check_format(K, k, v, R, status):
     fmt = K.make_format(k, v, R)

@@ -24,6 +24,7 @@ ASYM4_32 = (4, 1, 0, 32)
 ASYM2_32 = (2, 1, 0, 32)
 KPC2 = (2, 1, 1, 32)
 KPC4S = (4, 0, 1, 16)
+BF16 = (16, 0, 0, 128)  # unquantized BF16 storage
 
 
 def announce(**kw):
@@ -50,6 +51,10 @@ CASES = [
     ("kpc4-sym-g16", KPC4S, SYM4, 2, 4, 1, 32, [100, 50], False),
     ("gqa8-int8", SYM8, SYM8, 1, 16, 2, 0, [600], False),
     ("gqa2-int4-paged", SYM4, SYM4, 2, 4, 2, 0, [300, 17], True),
+    ("bf16-gqa4-window", BF16, BF16, 2, 8, 2, 32, [777, 190], False),
+    ("bf16-mha-paged", BF16, BF16, 3, 4, 4, 0, [300, 17, 1031], True),
+    ("bf16-gqa8-paged-window", BF16, BF16, 1, 16, 2, 16, [600], True),
+    ("asym8-g64-paged", (8, 1, 0, 64), (8, 1, 0, 64), 2, 8, 2, 16, [500, 77], True),
 ]
 
 
