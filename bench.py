@@ -46,6 +46,8 @@ def side_token_bytes(side) -> float:
     bits, scheme, axis, group = side
     meta = 2 * (2 if scheme == 1 else 1)
     codes = HEAD_DIM * bits / 8
+    if bits == 16:  # unquantized BF16 rows carry no metadata
+        return codes
     if axis == 0:
         return codes + (HEAD_DIM // group) * meta
     return codes + HEAD_DIM * meta / group
@@ -323,6 +325,108 @@ def counter_traffic(workload: str):
 
 # ------------------------------------------------------------------------------------------
 
+# ------------------------------------------------------------------------------------------
+# Crossover sweep: unquantized BF16 against INT8 / INT4 / INT2 decode attention over context
+# length and batch [P2, "Why compression may also improve speed": saved memory traffic versus
+# quantization and dequantization overhead; at short contexts the overhead may win]
+# ------------------------------------------------------------------------------------------
+
+SWEEP_FORMATS = {
+    "bf16": (16, 0, 0, 128),
+    "int8-g128": (8, 0, 0, 128),
+    "int4-g64": (4, 0, 0, 64),
+    "int2-g32": (2, 0, 0, 32),
+}
+
+
+def sweep_crossover(batches, lengths, calls_per_graph: int = 20, replays: int = 5) -> list[dict]:
+    """Device time of one decode-attention call per (batch, context length, format), H_q = 32,
+    H_kv = 8, head_dim 128, contiguous caches without a window.  The calls are captured in a HIP
+    graph and replayed, so the time is the GPU's, not the host's launch rate; the first replay's
+    output is checked bit for bit against an eager call."""
+    import torch
+
+    import kvq_inputs as ki
+    from quantized_kv_cache_07_amd import kvq
+
+    rows = []
+    for B in batches:
+        for T in lengths:
+            base = None
+            for name, side in SWEEP_FORMATS.items():
+                w = ki.Workload(f"sweep-{name}", 11, B, 32, 8, T, ki.Side(*side), ki.Side(*side))
+                cap = -(-(T + 16) // 16) * 16
+                cache = kvq.Cache(side, side, B, 8, residual=0, capacity=cap)
+                k = torch.empty((B, T, 8, HEAD_DIM), dtype=torch.bfloat16, device="cuda")
+                v = torch.empty_like(k)
+                for b in range(B):
+                    kb, vb = ki.prefill_kv(w, b, T, device="cuda")
+                    k[b].copy_(kb)
+                    v[b].copy_(vb)
+                kvq.quantize_append(cache, k, v)
+                del k, v
+                q = ki.queries(w, 0, "cuda")
+                out = torch.empty((B, 32, HEAD_DIM), dtype=torch.float32, device="cuda")
+                ws = torch.empty(kvq.workspace_bytes(cache, 32, T), dtype=torch.uint8, device="cuda")
+                kvq.decode_attention(cache, q, T, out=out, workspace=ws)
+                torch.cuda.synchronize()
+                if kvq.read_error(cache):
+                    raise RuntimeError(f"device error in sweep {name} B={B} T={T}")
+                ref = out.clone()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for _ in range(calls_per_graph):
+                        kvq.decode_attention(cache, q, T, out=out, workspace=ws)
+                g.replay()
+                torch.cuda.synchronize()
+                if not torch.equal(out, ref):
+                    raise RuntimeError(f"graph replay differs from the eager call ({name} B={B} T={T})")
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(replays):
+                    g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / (replays * calls_per_graph)
+                nbytes = attention_bytes(w, [T] * B, [0] * B)
+                row = {"batch": B, "tokens": T, "format": name, "us_per_call": round(us, 2),
+                       "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                       "kv_tokens_per_s": round(B * T / (us * 1e-6), 1),
+                       "kv_bytes": int(nbytes)}
+                if name == "bf16":
+                    base = us
+                row["speedup_vs_bf16"] = round(base / us, 3)
+                rows.append(row)
+                print(json.dumps(row), flush=True)
+                del g, cache, ws, out
+                torch.cuda.empty_cache()
+    return rows
+
+
+def sweep_table(rows: list[dict], command: str) -> str:
+    fmts = list(SWEEP_FORMATS)
+    out = ["# Decode attention: BF16 against quantized caches (MI355X, one GPU)", "",
+           "Command (from the repository root on the GPU box):", "", f"    {command}", "",
+           "Device time of one `kvq_decode_attention` call (HIP-graph replay), H_q = 32, "
+           "H_kv = 8, head_dim 128, contiguous caches, no window; speed-up against the BF16 "
+           "cache in parentheses. Working sets below ~256 MB fit the Infinity Cache.", "",
+           "| batch | tokens | KV bytes (bf16) | " + " | ".join(f"{f} µs" for f in fmts) + " |",
+           "|---|---|---|" + "---|" * len(fmts)]
+    by = {}
+    for r in rows:
+        by.setdefault((r["batch"], r["tokens"]), {})[r["format"]] = r
+    for (B, T), d in sorted(by.items()):
+        cells = []
+        for f in fmts:
+            r = d.get(f)
+            cells.append("—" if r is None else
+                         (f"{r['us_per_call']:.1f}" if f == "bf16" else
+                          f"{r['us_per_call']:.1f} ({r['speedup_vs_bf16']:.2f}×)"))
+        kb = d["bf16"]["kv_bytes"] if "bf16" in d else 0
+        out.append(f"| {B} | {T} | {kb / 2**20:.1f} MiB | " + " | ".join(cells) + " |")
+    return "\n".join(out) + "\n"
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -337,6 +441,11 @@ def main() -> int:
     ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV",
                     help="print a text summary of a rocprofv3 --stats kernel table")
     ap.add_argument("--command", default="", help="the profiling command, recorded in summaries")
+    ap.add_argument("--sweep", choices=["crossover"],
+                    help="instead of the step benchmark: BF16 vs quantized decode-attention sweep")
+    ap.add_argument("--sweep-batches", default="1,16")
+    ap.add_argument("--sweep-lengths", default="512,2048,8192,32768,131072")
+    ap.add_argument("--sweep-out", default="", help="write the sweep's markdown table here")
     a = ap.parse_args()
     if a.summarize_counters:
         d = summarize_counters(*a.summarize_counters, a.workload, a.command)
@@ -362,6 +471,13 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if a.sweep == "crossover":
+        rows = sweep_crossover([int(x) for x in a.sweep_batches.split(",")],
+                               [int(x) for x in a.sweep_lengths.split(",")])
+        if a.sweep_out:
+            cmd = a.command or "python bench.py --sweep crossover"
+            open(a.sweep_out, "w").write(sweep_table(rows, cmd))
+        return 0
     dev = "cuda"
     n_total = a.warmup + a.steps
     print(f"[bench] setup {a.workload}", file=sys.stderr, flush=True)

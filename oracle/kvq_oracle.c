@@ -44,9 +44,12 @@
  *   tile        = 16 consecutive compressed token slots of one (sequence, kv head)
  *   tile index  contiguous: (b * H + h) * (cap / 16) + slot / 16
  *               paged:      block_table[b][slot / 16] * H + h      (block = 16 tokens)
- *   K codes     row-major: tile * 16 * RB + (slot % 16) * RB, RB = d * bits / 8; channel c of a row
- *               sits at bit c * bits (little-endian within each byte)
- *   V codes     token-interleaved inside the tile, see orc_v_bit()
+ *   K codes     slice (t, c / 32) of tile row t holds channels 32 (c / 32) .. + 31 at bit
+ *               (c % 32) * bits of the slice (little-endian within each byte), see orc_k_bit()
+ *   V codes     token-interleaved chunks of 4 tokens x 8 channels, see orc_v_bit()
+ *   slices      a tile is 64 slices of 4 * bits bytes, stored in pieces of S = min(16, 4 bits)
+ *               bytes: piece i of slice s at byte 64 S i + S s of the tile (slab i), so the
+ *               slices' piece i form one contiguous run (for bits <= 4 a slice is one piece)
  *   scales/zeros per-token groups: fp16 [tile][d / G][16]
  *               per-channel key groups: fp16 [b][h][cap / Gt][d]   (contiguous caches only)
  *   residual    bf16 [b][h][R][d]
@@ -408,24 +411,32 @@ void orc_attend_rows(const double *q, const double *kh, const double *vh, int32_
 /* Byte images in the storage layout (see the header comment).                                 */
 /* ------------------------------------------------------------------------------------------ */
 
-/* Bit offset of channel c inside a row-major K row. */
-int64_t orc_k_bit(int32_t bits, int32_t c) { return (int64_t)c * bits; }
+/* Bit offset, inside its tile, of bit `bit` of slice `slice` (see the header comment). */
+static int64_t slab_bit(int bits, int64_t slice, int64_t bit) {
+  int64_t S = 4 * bits < 16 ? 4 * bits : 16;
+  return 8 * (64 * S * (bit / (8 * S)) + S * slice) + bit % (8 * S);
+}
+
+/* Bit offset of (tile row t, channel c) inside a K tile: slice 4 t + c / 32, bit (c % 32) bits.
+ * For 2- and 4-bit codes this is the row-major order t * d * bits + c * bits. */
+int64_t orc_k_bit(int32_t bits, int32_t t, int32_t c) {
+  return slab_bit(bits, 4 * (int64_t)t + c / 32, (int64_t)(c % 32) * bits);
+}
 
 /* Bit offset of (tile row t in 0..15, channel c) inside a 16-token V tile of d channels.
- * The tile is 4 * (d / 8) chunks of 4 * bits bytes; chunk (t / 4) * (d / 8) + c / 8 holds the
+ * The tile is 4 * (d / 8) chunks (slices) of 4 * bits bytes; chunk (t / 4) * (d / 8) + c / 8 holds the
  * 8 channels c & ~7 .. (c & ~7) + 7 of the 4 tokens 4 (t / 4) .. 4 (t / 4) + 3.  Inside a
  * chunk, E = 32 / bits fields per 32-bit word; pair index r = 2 (c % 8) + (t % 4) / 2 picks
  * word r / (E / 2) and field r % (E / 2) in the low 16 bits for even t % 4, the same field of
  * the high 16 bits (+ E / 2) for odd t % 4. */
 int64_t orc_v_bit(int32_t bits, int32_t d, int32_t t, int32_t c) {
-  int64_t CB = 4 * bits;
   int64_t chunk = (int64_t)(t / 4) * (d / 8) + c / 8;
   int E = 32 / bits, Hh = E / 2;
   int tt = t % 4, jj = c % 8;
   int r = 2 * jj + tt / 2;
   int word = r / Hh, k = r % Hh;
   int field = k + Hh * (tt % 2);
-  return chunk * CB * 8 + (int64_t)word * 32 + (int64_t)field * bits;
+  return slab_bit(bits, chunk, (int64_t)word * 32 + (int64_t)field * bits);
 }
 
 static void put_field(uint8_t *base, int64_t bit, int bits, uint8_t code) {
@@ -467,14 +478,14 @@ void orc_pack(const orc_seq *s, int32_t b, const int32_t *table_row, uint8_t *kc
   for (int h = 0; h < s->H; h++) {
     for (int p = 0; p < s->n_quant; p++) {
       int64_t tile = tile_index(s, b, h, p, table_row);
-      uint8_t *krow = kc + (tile * 16 + p % 16) * RBk;
+      uint8_t *ktile = kc + tile * 16 * RBk;
       uint8_t *vtile = vc + tile * 16 * RBv;
       for (int c = 0; c < d; c++) {
         size_t e = ((size_t)h * s->cap + p) * d + c;
         if (s->k.bits == 16)
-          put16(krow, orc_k_bit(16, c), s->kb[e]);
+          put16(ktile, orc_k_bit(16, p % 16, c), s->kb[e]);
         else
-          put_field(krow, orc_k_bit(s->k.bits, c), s->k.bits, s->ku[e]);
+          put_field(ktile, orc_k_bit(s->k.bits, p % 16, c), s->k.bits, s->ku[e]);
         if (s->v.bits == 16)
           put16(vtile, orc_v_bit(16, d, p % 16, c), s->vb[e]);
         else
@@ -522,14 +533,14 @@ void orc_unpack_codes(orc_seq *s, int32_t b, const int32_t *table_row, const uin
   for (int h = 0; h < s->H; h++)
     for (int p = 0; p < s->n_quant; p++) {
       int64_t tile = tile_index(s, b, h, p, table_row);
-      const uint8_t *krow = kc + (tile * 16 + p % 16) * RBk;
+      const uint8_t *ktile = kc + tile * 16 * RBk;
       const uint8_t *vtile = vc + tile * 16 * RBv;
       for (int c = 0; c < d; c++) {
         size_t e = ((size_t)h * s->cap + p) * d + c;
         if (s->k.bits == 16)
-          s->kb[e] = get16(krow, orc_k_bit(16, c));
+          s->kb[e] = get16(ktile, orc_k_bit(16, p % 16, c));
         else
-          s->ku[e] = get_field(krow, orc_k_bit(s->k.bits, c), s->k.bits);
+          s->ku[e] = get_field(ktile, orc_k_bit(s->k.bits, p % 16, c), s->k.bits);
         if (s->v.bits == 16)
           s->vb[e] = get16(vtile, orc_v_bit(16, d, p % 16, c));
         else
@@ -547,4 +558,4 @@ void orc_f16_to_f32_array(const uint16_t *x, float *y, int64_t n) {
   for (int64_t i = 0; i < n; i++) y[i] = orc_f16_to_f32(x[i]);
 }
 
-int32_t orc_abi_version(void) { return 2; }
+int32_t orc_abi_version(void) { return 3; }

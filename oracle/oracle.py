@@ -68,7 +68,7 @@ def lib() -> ctypes.CDLL:
         L.orc_attend_rows.argtypes = [P, P, P, i32, i32, f64, P]
         L.orc_pack.argtypes = [P, i32, P, P, P, P, P, P, P, P, P]
         L.orc_unpack_codes.argtypes = [P, i32, P, P, P]
-        L.orc_k_bit.argtypes, L.orc_k_bit.restype = [i32, i32], i64
+        L.orc_k_bit.argtypes, L.orc_k_bit.restype = [i32, i32, i32], i64
         L.orc_v_bit.argtypes, L.orc_v_bit.restype = [i32, i32, i32, i32], i64
         _LIB = L
     return _LIB
@@ -141,8 +141,9 @@ def attend_rows(q, khat, vhat, sm_scale: float) -> np.ndarray:
     return out
 
 
-def k_bit(bits: int, c: int) -> int:
-    return lib().orc_k_bit(bits, c)
+def k_bit(bits: int, t: int, c: int) -> int:
+    """Bit offset of (tile row t, channel c) inside a K tile."""
+    return lib().orc_k_bit(bits, t, c)
 
 
 def v_bit(bits: int, t: int, c: int, d: int = D_HEAD) -> int:

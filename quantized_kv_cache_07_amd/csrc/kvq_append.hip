@@ -154,25 +154,27 @@ __global__ __launch_bounds__(256) void quantize_kernel(CacheDev c, const uint16_
   }
   __syncthreads();
 
-  // BF16 storage (bits 16): the rows go in unchanged -- K row-major, V into the tile's
-  // token-interleaved layout (channel ch of tile row t at halfword 4 (8 chunk + ch % 8) + t % 4,
-  // chunk (t / 4) (D / 8) + ch / 8) -- and there is no metadata.
+  // BF16 storage (bits 16): the elements go in unchanged, into the same slice layout as codes
+  // (K: channels 8 p .. 8 p + 7 of row t are piece p % 4 of slice 4 t + p / 4; V: channel ch of
+  // row t is halfword 4 (ch % 8) + t % 4 of chunk (t / 4) (D / 8) + ch / 8), and there is no
+  // metadata.
   if (K.bits == 16) {
     constexpr int PIECES = D * 2 / 16;
     for (int it = tid; it < (hi - lo) * PIECES; it += blockDim.x) {
-      const int slot = lo + it / PIECES, piece = it % PIECES;
+      const int slot = lo + it / PIECES, pc = it % PIECES;
       bool ok = true;
       const long tile = tile_index(c, b, h, slot / TILE, ok);
-      reinterpret_cast<uint4*>(c.kc + (tile * TILE + slot % TILE) * (D * 2))[piece] =
-          reinterpret_cast<const uint4*>(&xs[slot - seg0][0][0])[piece];
+      const long off = slab_byte(16, 4 * (slot % TILE) + pc / 4, 128 * (pc % 4));
+      *reinterpret_cast<uint4*>(c.kc + tile * TILE * (D * 2) + off) =
+          reinterpret_cast<const uint4*>(&xs[slot - seg0][0][0])[pc];
     }
     for (int it = tid; it < (hi - lo) * D; it += blockDim.x) {
       const int slot = lo + it / D, ch = it % D, tr = slot % TILE;
       bool ok = true;
       const long tile = tile_index(c, b, h, slot / TILE, ok);
       const int chunk = (tr / 4) * (D / 8) + ch / 8;
-      reinterpret_cast<uint16_t*>(c.vc + tile * TILE * (D * 2))[(chunk * 8 + ch % 8) * 4 + tr % 4] =
-          xs[slot - seg0][1][ch];
+      const long off = slab_byte(16, chunk, 16 * (4 * (ch % 8) + tr % 4));
+      *reinterpret_cast<uint16_t*>(c.vc + tile * TILE * (D * 2) + off) = xs[slot - seg0][1][ch];
     }
     return;
   }
@@ -274,8 +276,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(CacheDev c, const uint16_
       uint32_t word = 0;
       for (int f = 0; f < E; f++)
         word |= static_cast<uint32_t>(lk[slot - seg0][w * E + f]) << (f * K.bits);
-      uint32_t* dst = reinterpret_cast<uint32_t*>(c.kc + (tile * TILE + slot % TILE) * RB) + w;
-      *dst = word;
+      // word w of row t: channels w E .. w E + E - 1, slice 4 t + w E / 32
+      const long off = slab_byte(K.bits, 4 * (slot % TILE) + (w * E) / 32, ((w * E) % 32) * K.bits);
+      *reinterpret_cast<uint32_t*>(c.kc + tile * TILE * RB + off) = word;
     }
   }
   // Phase 2b: V tiles, one 32-bit word per item; words shared with slots outside [lo, hi)
@@ -301,7 +304,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(CacheDev c, const uint16_
           mask |= ((1u << V.bits) - 1u) << (f * V.bits);
         }
       }
-      uint32_t* dst = reinterpret_cast<uint32_t*>(c.vc + tile * tile_bytes) + q;
+      // word q of the chunk sequence: word q % bits of chunk q / bits
+      uint32_t* dst = reinterpret_cast<uint32_t*>(c.vc + tile * tile_bytes +
+                                                  slab_byte(V.bits, q / V.bits, 32 * (q % V.bits)));
       if (mask != 0xFFFFFFFFu) val = (*dst & ~mask) | val;
       *dst = val;
     }

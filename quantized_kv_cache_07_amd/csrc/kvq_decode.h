@@ -272,17 +272,19 @@ __device__ __forceinline__ uint2 ld_stream2(const void* p) {
   return uint2{v[0], v[1]};
 }
 
+// A lane's slice of a tile (4 KB bytes) at `ptr`; 8- and 16-bit slices are stored as 16-byte
+// pieces one 1 KiB slab apart, so each load instruction of a wave reads 1 KiB contiguously.
 template <int KB>
 __device__ __forceinline__ void load_words(const uint8_t* ptr, uint32_t (&w)[KB]) {
   if constexpr (KB == 16) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const uint4 a = ld_stream4(ptr + 16 * i);
+      const uint4 a = ld_stream4(ptr + 1024 * i);
       w[4 * i] = a.x; w[4 * i + 1] = a.y; w[4 * i + 2] = a.z; w[4 * i + 3] = a.w;
     }
   } else if constexpr (KB == 8) {
     const uint4 a = ld_stream4(ptr);
-    const uint4 b = ld_stream4(ptr + 16);
+    const uint4 b = ld_stream4(ptr + 1024);
     w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
     w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
   } else if constexpr (KB == 4) {
@@ -409,9 +411,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
     vbias[i] = static_cast<_Float16>(-(1024.0f + static_cast<float>(velem_alpha<KB>(0, i)) * voff));
   const int hh = n % G;          // query head of QK column n and of PV row 16 pp + n
   const int cg = (n / G) % ngk;  // key group (or hi/lo part) of QK column n
-  constexpr int RBK = D * KB / 8;
   constexpr long TILE_BYTES = static_cast<long>(TILE) * D * KB / 8;
-  constexpr int VCH = 4 * KB;  // bytes of a lane's value chunk
 
   int u = u0;
   bool first_seg = true;
@@ -616,8 +616,9 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
       // and is ignored), so the compiler can count outstanding loads exactly.
       // Loads address a wave-uniform tile base (scalar registers) plus a 32-bit lane offset
       // that is fixed for the segment, so no per-lane 64-bit address arithmetic is needed.
-      const unsigned k_lane = n * RBK + g * (RBK / 4);
-      const unsigned v_lane = (g * (D / 8) + n) * VCH;
+      constexpr unsigned SP = (4 * KB < 16) ? 4 * KB : 16;  // bytes of a slice piece
+      const unsigned k_lane = SP * (4 * n + g);                // slice 4 n + g (token n)
+      const unsigned v_lane = SP * (16 * g + n);               // chunk 16 g + n
       const unsigned ks_lane = cg * TILE + 4 * g;
       auto load_k = [&](int xx, int pA, int pB) {
         pA = max(pA, 0);

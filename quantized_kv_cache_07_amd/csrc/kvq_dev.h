@@ -75,6 +75,15 @@ constexpr int PART_STRIDE = D + 4;
 // n_new single-token appends each flushing a full window before copying the token in.
 enum { MODE_APPEND = 0, MODE_FLUSH = 1 };
 
+// Storage slices: a tile is 64 lane-sized slices of 4 * bits bytes (K: 32 channels of one row,
+// slice 4 t + c / 32; V: a chunk of 4 tokens x 8 channels), stored in pieces of
+// S = min(16, 4 bits) bytes, piece i of slice s at byte 64 S i + S s (slab i).  A wave reading
+// piece i of all slices reads one contiguous 64 S-byte run.  Byte of bit `bit` of slice `s`:
+__device__ __forceinline__ long slab_byte(int bits, int s, int bit) {
+  const int S = (4 * bits < 16) ? 4 * bits : 16;
+  return 64L * S * (bit / (8 * S)) + static_cast<long>(S) * s + (bit % (8 * S)) / 8;
+}
+
 __device__ __forceinline__ void step_counts(int mode, int R, int nr, int n_new, int& F,
                                             int& total, int& nr_after) {
   if (R == 0) nr = 0;

@@ -95,7 +95,7 @@ def _check_codes(st, cache, w, samples):
                     for i in range(group):
                         c = g * group + i
                         if side == "k":
-                            got = _field(codes_buf[(tile * 16 + slot % 16) * rb:], oracle.k_bit(bits, c), bits)
+                            got = _field(codes_buf[tile * 16 * rb:], oracle.k_bit(bits, slot % 16, c), bits)
                         else:
                             got = _field(codes_buf[tile * 16 * rb:], oracle.v_bit(bits, slot % 16, c), bits)
                         assert got == u[i], (side, b, h, slot, c, got, int(u[i]))
@@ -113,7 +113,7 @@ def _check_codes(st, cache, w, samples):
                     assert sc[mi] == s16, ("k", b, h, slot, c, "per-channel scale")
                     if z16 is not None:
                         assert zc[mi] == z16, ("k", b, h, slot, c, "per-channel zero")
-                    got = _field(codes_buf[(tile * 16 + slot % 16) * rb:], oracle.k_bit(bits, c), bits)
+                    got = _field(codes_buf[tile * 16 * rb:], oracle.k_bit(bits, slot % 16, c), bits)
                     assert got == u[slot % group], ("k", b, h, slot, c, got, int(u[slot % group]))
 
 

@@ -433,13 +433,16 @@ def test_bf16_equals_int8_where_int8_is_exact(orc):
 
 
 def test_bf16_layout_and_paged_roundtrip(orc):
-    vb = sorted(orc.v_bit(16, t, c) for t in range(16) for c in range(128))
-    assert vb == list(range(0, 16 * 128 * 16, 16))
-    # channel c of token t sits at byte 2 (4 (8 chunk + c % 8) + t % 4) of its tile
+    # V: element (t, c) is halfword 4 (c % 8) + t % 4 of chunk (t / 4) 16 + c / 8, whose 16-byte
+    # piece i lives in slab i (1 KiB) at 16 chunk; K: channels 8 p .. 8 p + 7 of row t form
+    # piece p % 4 of slice 4 t + p / 4
     for t in range(16):
         for c in range(128):
             chunk = (t // 4) * 16 + c // 8
-            assert orc.v_bit(16, t, c) == 16 * (4 * (8 * chunk + c % 8) + t % 4)
+            hb = 2 * (4 * (c % 8) + t % 4)
+            assert orc.v_bit(16, t, c) == 8 * (1024 * (hb // 16) + 16 * chunk + hb % 16)
+            p_ = c // 8
+            assert orc.k_bit(16, t, c) == 8 * (1024 * (p_ % 4) + 16 * (4 * t + p_ // 4) + 2 * (c % 8))
     H, T = 2, 90
     seq = orc.Sequence(BF16_SIDE, BF16_SIDE, H, 0, capacity=128)
     kv = bf16_values(RNG.standard_normal((2, T, H, 128)).astype(np.float32))
@@ -448,12 +451,14 @@ def test_bf16_layout_and_paged_roundtrip(orc):
     table = RNG.permutation(8).astype(np.int32)
     im = orc.empty_images(BF16_SIDE, BF16_SIDE, 1, H, 0, num_blocks=8)
     seq.pack(0, im, table)
-    # K rows are plain little-endian bf16 rows
+    # every K element is its bf16 bit pattern, little-endian, at the slab offset
     for p_ in (0, 17, 89):
         for h in range(H):
             tile = table[p_ // 16] * H + h
-            row = im["k_codes"][(tile * 16 + p_ % 16) * 256:(tile * 16 + p_ % 16 + 1) * 256]
-            assert np.array_equal(row.view(np.uint16), kb[0, p_, h])
+            img = im["k_codes"][tile * 4096:(tile + 1) * 4096]
+            got = [int(img[orc.k_bit(16, p_ % 16, c) // 8]) | int(img[orc.k_bit(16, p_ % 16, c) // 8 + 1]) << 8
+                   for c in range(128)]
+            assert got == [int(x) for x in kb[0, p_, h]]
     back = orc.Sequence(BF16_SIDE, BF16_SIDE, H, 0, capacity=128)
     back.set_counters(T, 0)
     back.unpack_codes(0, im, table)
@@ -520,15 +525,21 @@ def test_per_channel_key_groups_follow_definition(orc):
 # [P2, "How this connects to paging and prefix caching": block tables]
 # ------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("bits", [8, 4, 2])
+@pytest.mark.parametrize("bits", [16, 8, 4, 2])
 def test_layout_is_a_bijection(orc, bits):
+    S = min(16, 4 * bits)  # bytes of a slice piece; slab i holds piece i of all 64 slices
     vb = sorted(orc.v_bit(bits, t, c) for t in range(16) for c in range(128))
     assert vb == list(range(0, 16 * 128 * bits, bits))
+    kb = sorted(orc.k_bit(bits, t, c) for t in range(16) for c in range(128))
+    assert kb == list(range(0, 16 * 128 * bits, bits))
     for t in range(16):
-        for c in range(128):  # chunk (t/4)*16 + c/8 holds channels c&~7.., tokens 4(t/4)..
-            chunk = orc.v_bit(bits, t, c) // (32 * bits)
-            assert chunk == (t // 4) * 16 + c // 8
-    assert [orc.k_bit(bits, c) for c in range(128)] == list(range(0, 128 * bits, bits))
+        for c in range(128):
+            # V: slice (t/4)*16 + c/8 holds channels c&~7.., tokens 4(t/4)..; K: slice 4t + c/32
+            vbyte, kbyte = orc.v_bit(bits, t, c) // 8, orc.k_bit(bits, t, c) // 8
+            assert (vbyte % (64 * S)) // S == (t // 4) * 16 + c // 8
+            assert (kbyte % (64 * S)) // S == 4 * t + c // 32
+            if bits <= 4:  # one piece per slice: K rows are plain row-major rows
+                assert orc.k_bit(bits, t, c) == (t * 128 + c) * bits
 
 
 @pytest.mark.parametrize("k_side,v_side", [((4, 0, 0, 64), (4, 0, 0, 64)),
