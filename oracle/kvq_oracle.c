@@ -26,6 +26,11 @@
  *   - a BF16 window of recent tokens, quantized and moved into the compressed cache when it fills
  *                                                  [P2, "Why some systems keep a full-precision window"]
  *   - block-table addressing of fixed-size blocks  [P2, "How this connects to paging and prefix caching"]
+ *   - FP8 (scheme 2): elements stored as OCP FP8 E4M3 with one fp32 scale per tensor or per
+ *     attention head, supplied by the caller  [P3, "Step 3: Deploy a Fallback-Capable FP8
+ *     First": FP8 KV cache with per-tensor and per-attention-head scales; "FP8 / INT8:
+ *     Engineering Baseline"].  Reading: code = E4M3(x / s), x / s an IEEE fp32 division, the
+ *     nearest E4M3 value with ties to the even code, saturating at +-448; x^ = s * E4M3 value.
  *   - bits = 16: the unquantized BF16 cache, the baseline the compressed formats are measured
  *     against and the fallback kept beside them  [P2, "From BF16 to INT8, INT4, or even fewer
  *     bits": two bytes per value; P3, "Step 3: Deploy a Fallback-Capable FP8 First" and
@@ -61,8 +66,11 @@
 
 #define ORC_SYM 0
 #define ORC_ASYM 1
+#define ORC_FP8 2
 #define ORC_PER_TOKEN 0
 #define ORC_PER_CHANNEL 1
+#define ORC_PER_TENSOR 2
+#define ORC_PER_HEAD 3
 
 /* ------------------------------------------------------------------------------------------ */
 /* Scalar conversions, written from the IEEE-754 / bfloat16 definitions.                       */
@@ -185,6 +193,38 @@ void orc_quant_asym(const float *x, int n, int bits, uint16_t *scale16, uint16_t
 }
 
 /* Reconstruction, evaluated exactly in fp64: symmetric s * q, asymmetric s * u + z. */
+/* OCP FP8 E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent 0 is subnormal
+ * (m / 8 * 2^-6); no infinities; S.1111.111 is NaN.  Value of a code, exactly. */
+double orc_e4m3_value(uint8_t code) {
+  int s = code >> 7, e = (code >> 3) & 15, m = code & 7;
+  double v;
+  if (e == 15 && m == 7)
+    v = NAN;
+  else if (e == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp((double)(8 + m), e - 10);
+  return s ? -v : v;
+}
+
+/* The E4M3 code nearest to y (ties: the code with an even mantissa), by search over every
+ * finite non-negative code; |y| >= 448 saturates to +-448.  The sign of y is kept (-0 -> 0x80). */
+uint8_t orc_e4m3_encode(float y) {
+  double a = fabs((double)y);
+  uint8_t sign = signbit(y) ? 0x80 : 0;
+  if (a >= 448.0) return sign | 0x7E;
+  int best = 0;
+  double bd = INFINITY;
+  for (int c = 0; c <= 0x7E; c++) {
+    double d = fabs(orc_e4m3_value((uint8_t)c) - a);
+    if (d < bd || (d == bd && (c & 1) == 0)) {
+      bd = d;
+      best = c;
+    }
+  }
+  return (uint8_t)(sign | best);
+}
+
 double orc_dequant(int bits, int scheme, uint8_t code, uint16_t s16, uint16_t z16) {
   double s = (double)orc_f16_to_f32(s16);
   if (scheme == ORC_SYM) return s * (double)((int)code - (1 << (bits - 1)));
@@ -208,6 +248,7 @@ typedef struct {
   uint16_t *kres, *vres;           /* [H][R][d] bf16 */
   int32_t n_quant, n_res;
   uint16_t *kb, *vb;               /* bits 16: the stored bf16 elements [H][cap][d] */
+  float *kf8, *vf8;                /* FP8: the scale of each kv head [H] (per tensor: all equal) */
 } orc_seq;
 
 enum { ORC_OK = 0, ORC_ERR_CAPACITY = 1, ORC_ERR_FORMAT = 2 };
@@ -233,6 +274,16 @@ static void quantize_rows(orc_seq *s, int is_k, const uint16_t *rows, size_t tok
     return;
   }
   uint8_t *U = is_k ? s->ku : s->vu;
+  if (sd->scheme == ORC_FP8) { /* one scale per head (or tensor), elementwise codes */
+    const float *F = is_k ? s->kf8 : s->vf8;
+    for (int h = 0; h < s->H; h++)
+      for (int j = 0; j < n; j++)
+        for (int c = 0; c < s->d; c++) {
+          float x = orc_bf16_to_f32(rows[(size_t)j * tok_stride + (size_t)h * head_stride + c]);
+          U[((size_t)h * s->cap + slot0 + j) * s->d + c] = orc_e4m3_encode(x / F[h]);
+        }
+    return;
+  }
   uint16_t *S = is_k ? s->ks : s->vs;
   uint16_t *Z = is_k ? s->kz : s->vz;
   int d = s->d;
@@ -332,6 +383,7 @@ int orc_append(orc_seq *s, const uint16_t *k_new, const uint16_t *v_new, int32_t
 static double khat(const orc_seq *s, int h, int slot, int c) {
   if (s->k.bits == 16) return (double)orc_bf16_to_f32(s->kb[((size_t)h * s->cap + slot) * s->d + c]);
   uint8_t u = s->ku[((size_t)h * s->cap + slot) * s->d + c];
+  if (s->k.scheme == ORC_FP8) return (double)s->kf8[h] * orc_e4m3_value(u);
   size_t mi = meta_index(s, &s->k, h, slot, c);
   return orc_dequant(s->k.bits, s->k.scheme, u, s->ks[mi], s->k.scheme == ORC_ASYM ? s->kz[mi] : 0);
 }
@@ -339,6 +391,7 @@ static double khat(const orc_seq *s, int h, int slot, int c) {
 static double vhat(const orc_seq *s, int h, int slot, int c) {
   if (s->v.bits == 16) return (double)orc_bf16_to_f32(s->vb[((size_t)h * s->cap + slot) * s->d + c]);
   uint8_t u = s->vu[((size_t)h * s->cap + slot) * s->d + c];
+  if (s->v.scheme == ORC_FP8) return (double)s->vf8[h] * orc_e4m3_value(u);
   size_t mi = meta_index(s, &s->v, h, slot, c);
   return orc_dequant(s->v.bits, s->v.scheme, u, s->vs[mi], s->v.scheme == ORC_ASYM ? s->vz[mi] : 0);
 }
@@ -491,7 +544,7 @@ void orc_pack(const orc_seq *s, int32_t b, const int32_t *table_row, uint8_t *kc
         else
           put_field(vtile, orc_v_bit(s->v.bits, d, p % 16, c), s->v.bits, s->vu[e]);
       }
-      if (s->k.bits == 16) continue; /* no scales */
+      if (s->k.bits == 16 || s->k.scheme == ORC_FP8) continue; /* no per-slot metadata */
       if (s->k.axis == ORC_PER_TOKEN) {
         for (int g = 0; g < ngk; g++) {
           size_t mi = meta_index(s, &s->k, h, p, g * s->k.group);
@@ -505,7 +558,7 @@ void orc_pack(const orc_seq *s, int32_t b, const int32_t *table_row, uint8_t *kc
         if (s->v.scheme == ORC_ASYM) vzc[(tile * ngv + g) * 16 + p % 16] = s->vz[mi];
       }
     }
-    if (s->k.bits != 16 && s->k.axis == ORC_PER_CHANNEL) {
+    if (s->k.bits != 16 && s->k.scheme != ORC_FP8 && s->k.axis == ORC_PER_CHANNEL) {
       int Gt = s->k.group, ntau = s->n_quant / Gt;
       for (int tau = 0; tau < ntau; tau++)
         for (int c = 0; c < d; c++) {
@@ -554,8 +607,12 @@ void orc_f32_to_f16_array(const float *x, uint16_t *y, int64_t n) {
   for (int64_t i = 0; i < n; i++) y[i] = orc_f32_to_f16(x[i]);
 }
 
+void orc_e4m3_encode_array(const float *x, uint8_t *y, int64_t n) {
+  for (int64_t i = 0; i < n; i++) y[i] = orc_e4m3_encode(x[i]);
+}
+
 void orc_f16_to_f32_array(const uint16_t *x, float *y, int64_t n) {
   for (int64_t i = 0; i < n; i++) y[i] = orc_f16_to_f32(x[i]);
 }
 
-int32_t orc_abi_version(void) { return 3; }
+int32_t orc_abi_version(void) { return 4; }

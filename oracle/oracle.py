@@ -23,8 +23,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "kvq_oracle.c")
 SO = os.path.join(HERE, "libkvq_oracle.so")
 
-SYM, ASYM = 0, 1
-PER_TOKEN, PER_CHANNEL = 0, 1
+SYM, ASYM, FP8 = 0, 1, 2
+PER_TOKEN, PER_CHANNEL, PER_TENSOR, PER_HEAD = 0, 1, 2, 3
 D_HEAD = 128
 TILE = 16
 
@@ -69,6 +69,9 @@ def lib() -> ctypes.CDLL:
         L.orc_pack.argtypes = [P, i32, P, P, P, P, P, P, P, P, P]
         L.orc_unpack_codes.argtypes = [P, i32, P, P, P]
         L.orc_k_bit.argtypes, L.orc_k_bit.restype = [i32, i32, i32], i64
+        L.orc_e4m3_encode.argtypes, L.orc_e4m3_encode.restype = [f32], ctypes.c_uint8
+        L.orc_e4m3_value.argtypes, L.orc_e4m3_value.restype = [ctypes.c_uint8], f64
+        L.orc_e4m3_encode_array.argtypes = [P, P, i64]
         L.orc_v_bit.argtypes, L.orc_v_bit.restype = [i32, i32, i32, i32], i64
         _LIB = L
     return _LIB
@@ -141,6 +144,21 @@ def attend_rows(q, khat, vhat, sm_scale: float) -> np.ndarray:
     return out
 
 
+def e4m3_encode(y: float) -> int:
+    return lib().orc_e4m3_encode(float(y))
+
+
+def e4m3_encode_array(y) -> np.ndarray:
+    y = np.ascontiguousarray(y, np.float32)
+    out = np.zeros(y.shape, np.uint8)
+    lib().orc_e4m3_encode_array(_p(y), _p(out), y.size)
+    return out
+
+
+def e4m3_value(code: int) -> float:
+    return lib().orc_e4m3_value(code)
+
+
 def k_bit(bits: int, t: int, c: int) -> int:
     """Bit offset of (tile row t, channel c) inside a K tile."""
     return lib().orc_k_bit(bits, t, c)
@@ -167,7 +185,8 @@ class _Seq(ctypes.Structure):
                 ("vs", ctypes.c_void_p), ("vz", ctypes.c_void_p),
                 ("kres", ctypes.c_void_p), ("vres", ctypes.c_void_p),
                 ("n_quant", ctypes.c_int32), ("n_res", ctypes.c_int32),
-                ("kb", ctypes.c_void_p), ("vb", ctypes.c_void_p)]
+                ("kb", ctypes.c_void_p), ("vb", ctypes.c_void_p),
+                ("kf8", ctypes.c_void_p), ("vf8", ctypes.c_void_p)]
 
 
 class OracleError(RuntimeError):
@@ -180,7 +199,7 @@ class Sequence:
     bits 16 is the unquantized BF16 cache (elements kept in ``kb``/``vb``, no metadata)."""
 
     def __init__(self, k_side, v_side, n_kv_heads: int, residual: int, capacity: int,
-                 d: int = D_HEAD):
+                 d: int = D_HEAD, k_fp8_scale=None, v_fp8_scale=None):
         self.k_side, self.v_side = tuple(k_side), tuple(v_side)
         self.H, self.R, self.cap, self.d = n_kv_heads, residual, capacity, d
         H, cap = n_kv_heads, capacity
@@ -189,8 +208,20 @@ class Sequence:
         self.kb = np.zeros((H, cap, d) if self.k_side[0] == 16 else 1, np.uint16)
         self.vb = np.zeros((H, cap, d) if self.v_side[0] == 16 else 1, np.uint16)
 
+        def fp8_scales(side, given):
+            # FP8: the caller's scale per tensor (one value) or per kv head, as float32 [H]
+            if side[1] != FP8:
+                return np.ones(1, np.float32)
+            g = np.atleast_1d(np.asarray(given, np.float32))
+            return np.ascontiguousarray(np.broadcast_to(g, (H,)) if g.size == 1 else g, np.float32)
+
+        self.kf8 = fp8_scales(self.k_side, k_fp8_scale)
+        self.vf8 = fp8_scales(self.v_side, v_fp8_scale)
+
         def meta(side):
             bits, scheme, axis, group = side
+            if scheme == FP8:  # no per-slot metadata
+                return np.zeros(1, np.uint16), np.zeros(1, np.uint16)
             shape = (H, cap, d // group) if axis == PER_TOKEN else (H, cap // group, d)
             s = np.zeros(shape, np.uint16)
             z = np.zeros(shape, np.uint16) if scheme == ASYM else np.zeros(1, np.uint16)
@@ -202,7 +233,8 @@ class Sequence:
         self.vres = np.zeros((H, max(residual, 1), d), np.uint16)
         self._s = _Seq(_Side(*self.k_side), _Side(*self.v_side), d, H, residual, cap,
                        _p(self.ku), _p(self.vu), _p(self.ks), _p(self.kz), _p(self.vs),
-                       _p(self.vz), _p(self.kres), _p(self.vres), 0, 0, _p(self.kb), _p(self.vb))
+                       _p(self.vz), _p(self.kres), _p(self.vres), 0, 0, _p(self.kb), _p(self.vb),
+                       _p(self.kf8), _p(self.vf8))
 
     @property
     def n_quant(self) -> int:
@@ -260,6 +292,12 @@ def empty_images(k_side, v_side, batch: int, n_kv_heads: int, residual: int, cap
     for name, side in (("k", k_side), ("v", v_side)):
         bits, scheme, axis, group = side
         out[f"{name}_codes"] = np.zeros(tiles * TILE * d * bits // 8, np.uint8)
+        if scheme == FP8:  # the caller's fp32 scales: one per tensor or per kv head
+            out[f"{name}_codes"] = np.zeros(tiles * TILE * d, np.uint8)
+            out[f"{name}_scale"] = np.zeros(0, np.uint16)
+            out[f"{name}_zero"] = np.zeros(0, np.uint16)
+            out[f"{name}_res"] = np.zeros(batch * H * max(residual, 1) * d, np.uint16)
+            continue
         if bits == 16:  # BF16 storage has no metadata
             out[f"{name}_scale"] = np.zeros(0, np.uint16)
             out[f"{name}_zero"] = np.zeros(0, np.uint16)

@@ -467,6 +467,76 @@ def test_bf16_layout_and_paged_roundtrip(orc):
 
 
 # ------------------------------------------------------------------------------------------
+# FP8 E4M3 with per-tensor / per-head scales [P3, "Step 3: Deploy a Fallback-Capable FP8 First"]
+# ------------------------------------------------------------------------------------------
+
+def torch_e4m3(x):
+    import torch
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3_values_match_torch(orc):
+    import torch
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    got = np.array([orc.e4m3_value(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2  # 0x7F, 0xFF
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert orc.e4m3_value(0x7E) == 448.0 and orc.e4m3_value(0x01) == 2.0**-9
+
+
+def test_e4m3_encode_matches_torch_cast_exhaustively(orc):
+    """Every finite bf16 value below 464 in magnitude (torch's cast turns larger ones into NaN;
+    here they saturate to +-448), plus random fp32 values around every binade."""
+    b = np.arange(65536, dtype=np.uint32)
+    x = (b << 16).view(np.float32)
+    x = x[np.isfinite(x) & (np.abs(x) < 464)]
+    assert np.array_equal(orc.e4m3_encode_array(x), torch_e4m3(x))
+    y = (RNG.standard_normal(200000) * np.exp2(RNG.integers(-12, 9, 200000))).astype(np.float32)
+    y = y[np.abs(y) < 464]
+    assert np.array_equal(orc.e4m3_encode_array(y), torch_e4m3(y))
+    big = np.array([448.0, 463.9, 464.0, 1e4, 3e38, -500.0], np.float32)
+    assert list(orc.e4m3_encode_array(big)) == [0x7E] * 5 + [0xFE]
+
+
+def test_fp8_cache_follows_definition_and_attention(orc):
+    """Per-head scales: head h stores E4M3(x / s_h) (numpy fp32 division, torch's cast); the
+    oracle's attention equals a pure-Python fsum over s_h * E4M3 value."""
+    import torch
+    H, Hq, T, R = 2, 4, 45, 16
+    ks, vs = np.array([0.02, 0.5], np.float32), np.array([0.01, 0.75], np.float32)
+    side_k, side_v = (8, 2, 3, 0), (8, 2, 3, 0)
+    seq = orc.Sequence(side_k, side_v, H, R, capacity=128, k_fp8_scale=ks, v_fp8_scale=vs)
+    kv = bf16_values(RNG.standard_normal((2, T, H, 128)).astype(np.float32))
+    kbits = (kv.view(np.uint32) >> 16).astype(np.uint16)
+    seq.append(kbits[0], kbits[1])
+    nq = seq.n_quant
+    for h in range(H):
+        assert np.array_equal(seq.ku[h, :nq], torch_e4m3(kv[0, :nq, h] / ks[h]))
+        assert np.array_equal(seq.vu[h, :nq], torch_e4m3(kv[1, :nq, h] / vs[h]))
+    q = (bf16_values(RNG.standard_normal((Hq, 128)).astype(np.float32)).view(np.uint32) >> 16)
+    q = q.astype(np.uint16)
+    sm = float(np.float32(1 / math.sqrt(128)))
+    got = seq.attend(q, sm)
+    dec = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    qf = (q.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for hq in range(Hq):
+        h = hq * H // Hq
+        keys = [list(float(ks[h]) * dec[seq.ku[h, p]]) for p in range(nq)]
+        vals = [list(float(vs[h]) * dec[seq.vu[h, p]]) for p in range(nq)]
+        for r in range(seq.n_res):
+            keys.append(list((seq.kres[h, r].astype(np.uint32) << 16).view(np.float32).astype(float)))
+            vals.append(list((seq.vres[h, r].astype(np.uint32) << 16).view(np.float32).astype(float)))
+        scores = [math.fsum(qf[hq, c] * kk[c] for c in range(128)) * sm for kk in keys]
+        m = max(scores)
+        w = [math.exp(s - m) for s in scores]
+        l = math.fsum(w)
+        ref = [math.fsum(w[t] * vals[t][c] for t in range(len(w))) / l for c in range(128)]
+        assert np.allclose(got[hq], ref, rtol=2.0**-23, atol=1e-30)
+
+
+# ------------------------------------------------------------------------------------------
 # Window state machine [P2, "Why some systems keep a full-precision window"]
 # ------------------------------------------------------------------------------------------
 
