@@ -70,12 +70,22 @@ typedef enum {
  * round() is half away from zero; x / s is an IEEE fp32 division by the stored fp16 scale;
  * the fp32 scale is rounded once to fp16 (nearest even).  A group whose scale is 0 stores
  * code 0 (symmetric) or u = 0 (asymmetric). */
-enum { KVQ_SYM = 0, KVQ_ASYM = 1 };
+enum { KVQ_SYM = 0, KVQ_ASYM = 1, KVQ_FP8 = 2 };
 
 /* Grouping direction [P2, "Why scales and groups matter"; P3, "Why Can't You Quantize the KV
  * Cache Like Ordinary Activations?"]: one scale (and zero-point) per group of `group` channels
  * of one token, or, for keys only, per channel over `group` consecutive tokens. */
-enum { KVQ_PER_TOKEN = 0, KVQ_PER_CHANNEL = 1 };
+enum { KVQ_PER_TOKEN = 0, KVQ_PER_CHANNEL = 1, KVQ_PER_TENSOR = 2, KVQ_PER_HEAD = 3 };
+
+/* KVQ_FP8: elements stored as OCP FP8 E4M3 bytes with one fp32 scale per tensor (axis
+ * KVQ_PER_TENSOR) or per kv head (KVQ_PER_HEAD) [P3, "Step 3: Deploy a Fallback-Capable FP8
+ * First": per-tensor and per-attention-head scales; "FP8 / INT8: Engineering Baseline"]:
+ * code = E4M3(x / s) with x / s an IEEE fp32 division, rounded to the nearest E4M3 value (ties to
+ * the even code) and saturated at +-448; x^ = s * E4M3 value.  bits 8, group 0 (else
+ * KVQ_EINVAL); both sides FP8, each with its own axis.  k_scale / v_scale then point to float32
+ * scales (1 or n_kv_heads of them, kvq_buffer_bytes gives the size) that the caller sets before
+ * the first append and keeps for the cache's lifetime; the library only reads them.  The codes
+ * use the 8-bit layout.  There are no zero buffers. */
 
 /* Device error bits. */
 enum {

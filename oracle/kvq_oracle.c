@@ -526,8 +526,10 @@ void orc_pack(const orc_seq *s, int32_t b, const int32_t *table_row, uint8_t *kc
               uint16_t *vres_img) {
   int d = s->d;
   int64_t RBk = d * s->k.bits / 8, RBv = d * s->v.bits / 8;
-  int ngk = (s->k.axis == ORC_PER_TOKEN) ? d / s->k.group : 0;
-  int ngv = d / s->v.group;
+  /* per-slot metadata groups; FP8 and BF16 rows have none */
+  int meta = s->k.scheme != ORC_FP8 && s->k.bits != 16;
+  int ngk = (meta && s->k.axis == ORC_PER_TOKEN) ? d / s->k.group : 0;
+  int ngv = meta ? d / s->v.group : 0;
   for (int h = 0; h < s->H; h++) {
     for (int p = 0; p < s->n_quant; p++) {
       int64_t tile = tile_index(s, b, h, p, table_row);

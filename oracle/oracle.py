@@ -212,7 +212,7 @@ class Sequence:
             # FP8: the caller's scale per tensor (one value) or per kv head, as float32 [H]
             if side[1] != FP8:
                 return np.ones(1, np.float32)
-            g = np.atleast_1d(np.asarray(given, np.float32))
+            g = np.atleast_1d(np.asarray(1.0 if given is None else given, np.float32))
             return np.ascontiguousarray(np.broadcast_to(g, (H,)) if g.size == 1 else g, np.float32)
 
         self.kf8 = fp8_scales(self.k_side, k_fp8_scale)

@@ -77,6 +77,20 @@ __device__ __forceinline__ void quant_asym(Get get, int n, int bits, uint16_t& s
   z16out = __half_as_ushort(zh);
 }
 
+// OCP FP8 E4M3 code of y: the nearest E4M3 value (ties to the even code, i.e. round-half-even
+// on the integer significand), saturating at +-448; the sign is kept (-0 -> 0x80).
+__device__ __forceinline__ uint8_t e4m3_rne_sat(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fabsf(y);
+  if (!(a < 448.0f)) return static_cast<uint8_t>(sign | 0x7Eu);
+  if (a < 0.015625f)  // below 2^-6: subnormal codes m 2^-9, m = 0..8 (8 is the smallest normal)
+    return static_cast<uint8_t>(sign | static_cast<uint32_t>(rintf(a * 512.0f)));
+  const int e = static_cast<int>((__float_as_uint(a) >> 23) & 0xFFu) - 127;  // -6 .. 8
+  const float m8 = rintf(a * __uint_as_float(static_cast<uint32_t>(127 + 3 - e) << 23));  // 8..16
+  const int code = ((e + 7) << 3) + (static_cast<int>(m8) - 8);  // 16 carries into the exponent
+  return static_cast<uint8_t>(sign | static_cast<uint32_t>(code > 0x7E ? 0x7E : code));
+}
+
 // Row j of the slots this call moves into the compressed cache: the window rows first, then
 // the new rows.
 __device__ __forceinline__ const uint16_t* pending_row(const CacheDev& c, const uint16_t* fresh,
@@ -135,8 +149,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(CacheDev c, const uint16_
   if (!s_ok) return;
 
   const SideDev K = c.k, V = c.v;
-  const int ngk = (K.axis == KVQ_PER_TOKEN) ? D / K.group : 0;
-  const int ngv = D / V.group;
+  const bool fp8 = K.scheme == KVQ_FP8;  // both sides share the scheme
+  const int ngk = (!fp8 && K.axis == KVQ_PER_TOKEN) ? D / K.group : 0;
+  const int ngv = fp8 ? 0 : D / V.group;
 
   // Phase 0: the pending bf16 rows of this segment into LDS (16-byte pieces).
   {
@@ -179,9 +194,21 @@ __global__ __launch_bounds__(256) void quantize_kernel(CacheDev c, const uint16_
     return;
   }
 
+  // FP8: every element is E4M3(x / s) with the side's scale for this kv head (or tensor).
+  if (fp8) {
+    const float* fks = reinterpret_cast<const float*>(c.ks);
+    const float* fvs = reinterpret_cast<const float*>(c.vs);
+    const float sk = fks[K.axis == KVQ_PER_HEAD ? h : 0], sv = fvs[V.axis == KVQ_PER_HEAD ? h : 0];
+    for (int it = tid; it < (hi - lo) * 2 * D; it += blockDim.x) {
+      const int j = lo - seg0 + it / (2 * D), side = (it / D) % 2, ch = it % D;
+      const float x = bf16_to_f32(xs[j][side][ch]);
+      (side ? lv : lk)[j][ch] = e4m3_rne_sat(x / (side ? sv : sk));
+    }
+  }
+
   // Phase 1a: per-token groups.  One wave per (slot, side) row; lane l holds channels 2l and
   // 2l + 1, and the group's maximum (or minimum and maximum) is reduced across its lanes.
-  {
+  if (!fp8) {
     const int wave = tid >> 6, lane = tid & 63;
     const bool k_pt = K.axis == KVQ_PER_TOKEN;
     const int nside = k_pt ? 2 : 1;  // per-channel keys are quantized in phase 1b
@@ -251,7 +278,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(CacheDev c, const uint16_
 
   // Phase 1b: per-channel keys: the segment is exactly one group of S tokens (lo == seg0, hi ==
   // seg0 + S: flushes move whole windows, R is a multiple of the group); a thread per channel.
-  if (K.axis == KVQ_PER_CHANNEL) {
+  if (!fp8 && K.axis == KVQ_PER_CHANNEL) {
     for (int ch = tid; ch < D; ch += blockDim.x) {
       auto get = [&](int j) { return bf16_to_f32(xs[j][0][ch]); };
       uint16_t s16 = 0, z16 = 0;
@@ -311,7 +338,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(CacheDev c, const uint16_
       *dst = val;
     }
   }
-  // Phase 2c: metadata.
+  // Phase 2c: metadata (none for FP8: its scales are the caller's).
+  if (fp8) return;
   if (K.axis == KVQ_PER_TOKEN) {
     for (int it = tid; it < (hi - lo) * ngk; it += blockDim.x) {
       const int slot = lo + it / ngk, g = it % ngk;

@@ -214,6 +214,18 @@ __device__ __forceinline__ f16x8 vop_raw(const uint32_t* wa, const uint32_t* wb,
                                          rawpair<KB>(wb, 2 * j, u), rawpair<KB>(wb, 2 * j + 1, u)});
 }
 
+// FP8 E4M3 bytes to exact f16 (every E4M3 value is an f16 value): bytes (0, 1) and (2, 3) of
+// each word, in that order.
+__device__ __forceinline__ f16x8 f8_to_f16x8(uint32_t w0, uint32_t w1) {
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+  const f16x4 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+  const f16x4 cd = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+  return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // QK A operand of MFMA j: pairs 4 j .. 4 j + 3 of the lane's key slice.
 template <int KB>
 __device__ __forceinline__ f16x8 kop(const uint32_t* w, int j, float off, const UnpackRegs& u) {
@@ -335,8 +347,10 @@ __device__ __forceinline__ int seq_units(const CacheDev& c, int max_tokens, int 
   return (nq + 31) / 32 + (nr + 31) / 32;
 }
 
-template <int KB, int G, bool KPC, int NP, bool ASYM>
+template <int KB, int G, bool KPC, int NP, int SCH>
 __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_kernel(DecodeParams p) {
+  constexpr bool ASYM = SCH == KVQ_ASYM;
+  constexpr bool F8 = SCH == KVQ_FP8;  // E4M3 bytes, one scale per kv head (or tensor) per side
   extern __shared__ __align__(16) unsigned char smem[];
   const CacheDev& c = p.c;
   const int B = c.B, H = c.H;
@@ -395,7 +409,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
     return;
   }
 
-  const int kgroup = c.k.group, vgroup = c.v.group;
+  const int kgroup = (F8 || KB == 16) ? D : c.k.group, vgroup = (F8 || KB == 16) ? D : c.v.group;
   const int ngk = KPC ? 2 : D / kgroup;  // QK columns per head: key groups, or hi/lo parts
   const int ngv = D / vgroup;
   constexpr float koff = ASYM ? 0.0f : static_cast<float>(1 << (KB - 1));
@@ -403,7 +417,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
   // Value codes enter PV raw (1024 + alpha u) when alpha depends only on the token position
   // (8- and 4-bit); the weights then carry 1 / alpha and one more product with vbias removes the
   // bias.  2-bit fields change alpha with the channel, so they are unpacked exactly instead.
-  constexpr bool VBF = KB == 4 || KB == 8;
+  constexpr bool VBF = (KB == 4 || KB == 8) && !F8;
   constexpr bool BF = KB == 16;  // unquantized BF16 storage: bf16 matrix products, no scales
   f16x8 vbias;
 #pragma unroll
@@ -450,10 +464,22 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
     f32x4 dq0 = f32x4{0.f, 0.f, 0.f, 0.f};  // QK accumulator start of every tile
     float qsum = 0.0f;  // asymmetric per-token keys: sum of q over the column's group
     float zt = 0.0f;    // asymmetric per-channel keys: sum of q * zero over the key group
+    float f8k = 1.0f, f8v = 1.0f;  // FP8: the key and value scales of kv head h
     if constexpr (BF) {
 #pragma unroll
       for (int j = 0; j < 4; j++)
         qbf[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qs + hh * D + 32 * g + 8 * j));
+    } else if constexpr (F8) {
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const u16x8 raw = *reinterpret_cast<const u16x8*>(qs + hh * D + 32 * g + 8 * j);
+#pragma unroll
+        for (int i = 0; i < 8; i++) qb[j][i] = static_cast<_Float16>(bf16_to_f32(raw[i]));
+      }
+      const int32_t* fks = reinterpret_cast<const int32_t*>(c.ks);
+      const int32_t* fvs = reinterpret_cast<const int32_t*>(c.vs);
+      f8k = __int_as_float(ld_uniform(fks + (c.k.axis == KVQ_PER_HEAD ? h : 0)));
+      f8v = __int_as_float(ld_uniform(fvs + (c.v.axis == KVQ_PER_HEAD ? h : 0)));
     } else if constexpr (!KPC) {
       const bool in_grp = ((32 * g) / kgroup) == cg;
 #pragma unroll
@@ -625,7 +651,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
         pB = max(pB, 0);
         load_words<KB>(c.kc + static_cast<size_t>(pA) * TILE_BYTES + k_lane, d.kw[0]);
         load_words<KB>(c.kc + static_cast<size_t>(pB) * TILE_BYTES + k_lane, d.kw[1]);
-        if constexpr (BF) {
+        if constexpr (BF || F8) {
         } else if constexpr (KPC) {
           const size_t mi = kpc_meta((32 * xx) / kgroup);
           d.fs = load_meta8(c.ks, mi);
@@ -644,7 +670,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
         pB = max(pB, 0);
         load_words<KB>(c.vc + static_cast<size_t>(pA) * TILE_BYTES + v_lane, d.vw[0]);
         load_words<KB>(c.vc + static_cast<size_t>(pB) * TILE_BYTES + v_lane, d.vw[1]);
-        if constexpr (!BF)
+        if constexpr (!BF && !F8)
 #pragma unroll
         for (int t = 0; t < 2; t++) {
           const size_t tb = static_cast<size_t>(t ? pB : pA) * ngv * TILE;
@@ -745,6 +771,12 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
               dq[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop<KB>(d.kw[1], j, koff, ur), qb[j], dq[1], 0, 0, 0);
             }
           }
+        } else if constexpr (F8) {
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            dq[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f8_to_f16x8(d.kw[0][2 * j], d.kw[0][2 * j + 1]), qb[j], dq[0], 0, 0, 0);
+            dq[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f8_to_f16x8(d.kw[1][2 * j], d.kw[1][2 * j + 1]), qb[j], dq[1], 0, 0, 0);
+          }
         } else if constexpr (BF) {
 #pragma unroll
           for (int j = 0; j < 4; j++) {
@@ -768,6 +800,9 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
           if constexpr (BF) {
 #pragma unroll
             for (int r = 0; r < 4; r++) s2[4 * t + r] = dq[t][r];
+          } else if constexpr (F8) {
+#pragma unroll
+            for (int r = 0; r < 4; r++) s2[4 * t + r] = dq[t][r] * f8k;
           } else if constexpr (KPC) {
 #pragma unroll
             for (int r = 0; r < 4; r++) s2[4 * t + r] = dq[t][r] + row_ror<G>(dq[t][r]) + zt;
@@ -844,6 +879,13 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
           float ws[8];
 #pragma unroll
           for (int t = 0; t < 2; t++) {
+            if constexpr (F8) {
+              // the head's value scale; P element order follows the converted bytes of a V
+              // word, tokens (0, 2, 1, 3) of each tile
+#pragma unroll
+              for (int r = 0; r < 4; r++) ws[4 * t + r] = s2[4 * t + ((r == 1) ? 2 : (r == 2) ? 1 : r)] * f8v;
+              continue;
+            }
             const uint2 s2v = d.vs[pp][t];
             ws[4 * t + 0] = fmaf(s2[4 * t + 0], f16_lo(s2v.x), 0.0f);
             ws[4 * t + 1] = fmaf(s2[4 * t + 1], f16_hi(s2v.x), 0.0f);
@@ -863,7 +905,10 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
           }
           if (!full) {
 #pragma unroll
-            for (int i = 0; i < 8; i++) ws[i] = (s2[i] != 0.0f) ? ws[i] : 0.0f;
+            for (int i = 0; i < 8; i++) {
+              const int si = F8 ? (i & 4) + (((i & 3) == 1) ? 2 : ((i & 3) == 2) ? 1 : (i & 3)) : i;
+              ws[i] = (s2[si] != 0.0f) ? ws[i] : 0.0f;
+            }
           }
           uint32_t pk[4];
 #pragma unroll
@@ -886,6 +931,12 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
 #pragma unroll
             for (int pp = 0; pp < NP; pp++)
               acc[pp][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[pp], vbias, acc[pp][j], 0, 0, 0);
+          } else if constexpr (F8) {
+            // word j of each tile's chunk: channel 8 n + j of tokens (0, 2, 1, 3)
+            const f16x8 vb = f8_to_f16x8(d.vw[0][j], d.vw[1][j]);
+#pragma unroll
+            for (int pp = 0; pp < NP; pp++)
+              acc[pp][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[pp], vb, acc[pp][j], 0, 0, 0);
           } else {
             const f16x8 vb = vop<KB>(d.vw[0], d.vw[1], j, voff, ur);
 #pragma unroll
@@ -1142,26 +1193,26 @@ __global__ __launch_bounds__(COMBINE_THREADS) void combine_kernel(DecodeParams p
 
 // Workgroups of decode_kernel that are resident at once on the current device.  Each workgroup
 // owns 1/NB of the units, so the grid must never exceed what runs concurrently.
-template <int KB, int G, bool KPC, int NP, bool ASYM>
+template <int KB, int G, bool KPC, int NP, int SCH>
 int decode_resident_blocks(size_t lds) {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<KB, G, KPC, NP, ASYM>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<KB, G, KPC, NP, SCH>,
                                                    256, lds) != hipSuccess)
     return 0;
   return cus * per_cu;
 }
 
-template <int KB, int G, bool KPC, int NP, bool ASYM>
+template <int KB, int G, bool KPC, int NP, int SCH>
 hipError_t launch_decode_t(const DecodeParams& p0, hipStream_t s) {
   DecodeParams p = p0;
   const size_t lds = DecodeLds::bytes(p.c.B);
-  const int resident = decode_resident_blocks<KB, G, KPC, NP, ASYM>(lds);
+  const int resident = decode_resident_blocks<KB, G, KPC, NP, SCH>(lds);
   if (resident <= 0) return hipErrorInvalidConfiguration;
   if (p.nblocks > resident) p.nblocks = resident;
-  decode_kernel<KB, G, KPC, NP, ASYM><<<p.nblocks, 256, lds, s>>>(p);
+  decode_kernel<KB, G, KPC, NP, SCH><<<p.nblocks, 256, lds, s>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // slices: about one per 4 partials a segment has on average, 32 outputs per slice at most
@@ -1179,22 +1230,22 @@ hipError_t launch_decode_t(const DecodeParams& p0, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int KB, bool ASYM>
+template <int KB, int SCH>
 hipError_t launch_decode_bits(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s) {
-  if constexpr (KB == 16) {  // BF16 storage: per-token rows only, at most 16 PV rows
+  if constexpr (KB == 16 || SCH == KVQ_FP8) {  // whole-row formats: at most 16 PV rows
     if (kpc || NP != 1) return hipErrorInvalidValue;
     switch (G) {
-      case 1: return launch_decode_t<16, 1, false, 1, false>(p, s);
-      case 2: return launch_decode_t<16, 2, false, 1, false>(p, s);
-      case 4: return launch_decode_t<16, 4, false, 1, false>(p, s);
-      case 8: return launch_decode_t<16, 8, false, 1, false>(p, s);
+      case 1: return launch_decode_t<KB, 1, false, 1, SCH>(p, s);
+      case 2: return launch_decode_t<KB, 2, false, 1, SCH>(p, s);
+      case 4: return launch_decode_t<KB, 4, false, 1, SCH>(p, s);
+      case 8: return launch_decode_t<KB, 8, false, 1, SCH>(p, s);
       default: return hipErrorInvalidValue;
     }
   } else {
 #define KVQ_CASE(GG, NN)                                                        \
   if (G == GG && NP == NN)                                                      \
-    return kpc ? launch_decode_t<KB, GG, true, NN, ASYM>(p, s)                 \
-               : launch_decode_t<KB, GG, false, NN, ASYM>(p, s);
+    return kpc ? launch_decode_t<KB, GG, true, NN, SCH>(p, s)                  \
+               : launch_decode_t<KB, GG, false, NN, SCH>(p, s);
   KVQ_CASE(1, 1)
   KVQ_CASE(2, 1)
   KVQ_CASE(4, 1)

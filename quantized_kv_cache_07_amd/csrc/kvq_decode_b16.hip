@@ -5,6 +5,6 @@
 
 namespace kvq {
 hipError_t launch_decode_b16(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s) {
-  return launch_decode_bits<16, false>(p, G, NP, kpc, s);
+  return launch_decode_bits<16, KVQ_SYM>(p, G, NP, kpc, s);
 }
 }  // namespace kvq

@@ -5,7 +5,7 @@
 namespace kvq {
 
 hipError_t launch_decode_b2s(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s) {
-  return launch_decode_bits<2, false>(p, G, NP, kpc, s);
+  return launch_decode_bits<2, KVQ_SYM>(p, G, NP, kpc, s);
 }
 
 }  // namespace kvq

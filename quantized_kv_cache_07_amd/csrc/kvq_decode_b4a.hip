@@ -5,7 +5,7 @@
 namespace kvq {
 
 hipError_t launch_decode_b4a(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s) {
-  return launch_decode_bits<4, true>(p, G, NP, kpc, s);
+  return launch_decode_bits<4, KVQ_ASYM>(p, G, NP, kpc, s);
 }
 
 }  // namespace kvq

@@ -19,12 +19,18 @@ hipError_t launch_decode_b2a(const DecodeParams& p, int G, int NP, bool kpc, hip
 hipError_t launch_decode_b4a(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s);
 hipError_t launch_decode_b8a(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s);
 hipError_t launch_decode_b16(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s);
+hipError_t launch_decode_b8f(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s);
 
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 kvq_status check_side(const kvq_side& s, bool is_key, int residual) {
+  if (s.scheme == KVQ_FP8) {  // E4M3 bytes, one fp32 scale per tensor or kv head
+    if (s.bits != 8 || (s.axis != KVQ_PER_TENSOR && s.axis != KVQ_PER_HEAD) || s.group != 0)
+      return KVQ_EINVAL;
+    return KVQ_OK;
+  }
   if (s.bits == 16) {  // unquantized BF16 storage: one "group" per row, no scale
     if (s.scheme != KVQ_SYM || s.axis != KVQ_PER_TOKEN || s.group != D) return KVQ_EINVAL;
     return KVQ_OK;
@@ -225,6 +231,10 @@ size_t kvq_buffer_bytes(const kvq_format* fmt, int32_t batch, int32_t n_kv_heads
     case KVQ_BUF_K_ZERO:
     case KVQ_BUF_V_ZERO: {
       if (s.bits == 16) return 0;
+      if (s.scheme == KVQ_FP8) {
+        if (which == KVQ_BUF_K_ZERO || which == KVQ_BUF_V_ZERO) return 0;
+        return (s.axis == KVQ_PER_HEAD ? static_cast<size_t>(n_kv_heads) : 1) * sizeof(float);
+      }
       if ((which == KVQ_BUF_K_ZERO || which == KVQ_BUF_V_ZERO) && s.scheme != KVQ_ASYM) return 0;
       if (s.axis == KVQ_PER_TOKEN) return tiles * (D / s.group) * TILE * 2;
       if (paged || capacity % s.group) return 0;
@@ -279,11 +289,15 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int32_t n
   const int G = n_q_heads / cache->n_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return KVQ_ENOTSUP;
   const bool kpc = cache->fmt.k.axis == KVQ_PER_CHANNEL;
-  if (!kpc && (D / cache->fmt.k.group) * G > 16) return KVQ_ENOTSUP;
+  // groups per row: FP8 and BF16 rows have one scale (or none) for all 128 channels
+  const bool whole_row = cache->fmt.k.scheme == KVQ_FP8 || cache->fmt.k.bits == 16;
+  const int kgroup = whole_row ? D : cache->fmt.k.group;
+  const int vgroup = whole_row ? D : cache->fmt.v.group;
+  if (!kpc && (D / kgroup) * G > 16) return KVQ_ENOTSUP;
   if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVQ_EALIGN;
   const WsLayout w = ws_layout(cache, n_q_heads, max_tokens);
   if (workspace_bytes < w.total) return KVQ_ENOSPACE;
-  const int ngv = D / cache->fmt.v.group;
+  const int ngv = D / vgroup;
   const int rows = 2 * G * ngv;  // PV rows: (hi/lo part, value group, query head)
   if (rows > 32) return KVQ_ENOTSUP;
   const int NP = rows > 16 ? 2 : 1;
@@ -312,7 +326,11 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int32_t n
     case 2: e = asym ? launch_decode_b2a(p, G, NP, kpc, st) : launch_decode_b2s(p, G, NP, kpc, st); break;
     case 4: e = asym ? launch_decode_b4a(p, G, NP, kpc, st) : launch_decode_b4s(p, G, NP, kpc, st); break;
     case 16: e = launch_decode_b16(p, G, NP, kpc, st); break;
-    default: e = asym ? launch_decode_b8a(p, G, NP, kpc, st) : launch_decode_b8s(p, G, NP, kpc, st); break;
+    case 8:
+      e = cache->fmt.k.scheme == KVQ_FP8 ? launch_decode_b8f(p, G, NP, kpc, st)
+          : asym ? launch_decode_b8a(p, G, NP, kpc, st) : launch_decode_b8s(p, G, NP, kpc, st);
+      break;
+    default: return KVQ_ENOTSUP;  // unreachable: check_cache accepted the width
   }
   return e == hipSuccess ? KVQ_OK : KVQ_ELAUNCH;
 }

@@ -34,6 +34,9 @@ EXPORTS = ["kvq_buffer_bytes", "kvq_check_format", "kvq_quantize_append", "kvq_f
            "kvq_measure_copy"]
 
 
+SCHEME_FP8 = 2  # KVQ_FP8
+
+
 class KvqError(RuntimeError):
     def __init__(self, status: int, what: str):
         super().__init__(f"{what}: {STATUS.get(status, status)}")
@@ -117,7 +120,9 @@ class Cache:
 
     def __init__(self, k, v, batch: int, n_kv_heads: int, residual: int = 0, capacity: int = 0,
                  block_table: torch.Tensor | None = None, num_blocks: int = 0,
-                 device="cuda"):
+                 device="cuda", fp8_scales=None):
+        """fp8_scales: for FP8 sides, (k_scales, v_scales), each one value (per tensor) or
+        n_kv_heads values (per head); copied into the float32 scale buffers."""
         self.fmt = make_format(k, v, residual)
         st = lib.kvq_check_format(ctypes.byref(self.fmt))
         _check(st, "format")
@@ -144,6 +149,12 @@ class Cache:
         self.v_zero = buf(BUF_V_ZERO, torch.int16)
         self.k_res = buf(BUF_K_RES, torch.int16)
         self.v_res = buf(BUF_V_RES, torch.int16)
+        if k[1] == SCHEME_FP8:
+            if fp8_scales is None:
+                raise ValueError("an FP8 cache needs its scales (fp8_scales=(k, v))")
+            for buf_, vals in ((self.k_scale, fp8_scales[0]), (self.v_scale, fp8_scales[1])):
+                f = buf_.view(torch.float32)
+                f.copy_(torch.as_tensor(vals, dtype=torch.float32).reshape(-1).expand(f.numel()))
         self.n_quant = torch.zeros(batch, dtype=torch.int32, device=device)
         self.n_res = torch.zeros(batch, dtype=torch.int32, device=device)
         self.err = torch.zeros(1, dtype=torch.int32, device=device)
@@ -183,7 +194,12 @@ class Cache:
             d.block_table = None
             for name in names:
                 t = getattr(self, name)
-                setattr(d, name, None if t is None else t.view(self.batch, -1)[seq].data_ptr())
+                shared = name in ("k_scale", "v_scale") and \
+                    (self.k_side if name[0] == "k" else self.v_side)[1] == SCHEME_FP8
+                if t is None or shared:  # FP8 scales belong to the whole cache
+                    setattr(d, name, _ptr(t))
+                else:
+                    setattr(d, name, t.view(self.batch, -1)[seq].data_ptr())
         return d
 
     def sequence(self, seq: int) -> CacheDesc:

@@ -40,7 +40,8 @@ def test_every_declared_symbol_is_exported(K):
                                    ((8, 0, 0, 128), (8, 0, 0, 128), 16),
                                    ((2, 1, 1, 32), (2, 1, 0, 32), 128),
                                    ((4, 1, 0, 32), (4, 1, 0, 32), 32),
-                                   ((16, 0, 0, 128), (16, 0, 0, 128), 16)])
+                                   ((16, 0, 0, 128), (16, 0, 0, 128), 16),
+                                   ((8, 2, 3, 0), (8, 2, 2, 0), 16)])
 def test_buffer_sizes_match_the_storage_layout(K, orc, k, v, R):
     fmt = K.make_format(k, v, R)
     B, H = 3, 2
@@ -52,7 +53,11 @@ def test_buffer_sizes_match_the_storage_layout(K, orc, k, v, R):
                                       "v_zero", "k_res", "v_res"]):
             got = K.lib.kvq_buffer_bytes(ctypes.byref(fmt), B, H, cap, nblk, which)
             side = k if name[0] == "k" else v
-            if name.endswith("zero") and side[1] == 0:
+            if side[1] == 2 and name.endswith("scale"):  # FP8: fp32 scale per head or tensor
+                assert got == 4 * (H if side[2] == 3 else 1)
+            elif side[1] == 2 and name.endswith("zero"):
+                assert got == 0
+            elif name.endswith("zero") and side[1] == 0:
                 assert got == 0
             elif name.endswith("res") and R == 0:
                 assert got == 0
@@ -83,6 +88,11 @@ def test_worked_example_footprint(K):
     ((16, 1, 0, 128), (16, 1, 0, 128), 0, 1),  # BF16 storage has no scheme ...
     ((16, 0, 0, 64), (16, 0, 0, 64), 0, 1),    # ... and no groups
     ((16, 0, 0, 128), (8, 0, 0, 128), 0, 2),   # K and V share one width
+    ((8, 2, 3, 0), (8, 2, 2, 0), 16, 0),       # FP8 E4M3: per-head keys, per-tensor values
+    ((8, 2, 0, 0), (8, 2, 0, 0), 0, 1),        # FP8 scales are per tensor or per head
+    ((8, 2, 3, 64), (8, 2, 3, 0), 0, 1),       # ... with no group
+    ((4, 2, 3, 0), (4, 2, 3, 0), 0, 1),        # ... on 8-bit codes
+    ((8, 2, 3, 0), (8, 0, 0, 128), 0, 2),      # K and V share one scheme
 ])
 def test_check_format(K, k, v, R, status):
     fmt = K.make_format(k, v, R)

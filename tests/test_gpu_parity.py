@@ -25,6 +25,8 @@ ASYM2_32 = (2, 1, 0, 32)
 KPC2 = (2, 1, 1, 32)
 KPC4S = (4, 0, 1, 16)
 BF16 = (16, 0, 0, 128)  # unquantized BF16 storage
+FP8H = (8, 2, 3, 0)     # FP8 E4M3, one scale per kv head
+FP8T = (8, 2, 2, 0)     # FP8 E4M3, one scale per tensor
 
 
 def announce(**kw):
@@ -55,6 +57,9 @@ CASES = [
     ("bf16-mha-paged", BF16, BF16, 3, 4, 4, 0, [300, 17, 1031], True),
     ("bf16-gqa8-paged-window", BF16, BF16, 1, 16, 2, 16, [600], True),
     ("asym8-g64-paged", (8, 1, 0, 64), (8, 1, 0, 64), 2, 8, 2, 16, [500, 77], True),
+    ("fp8-head-gqa4-window", FP8H, FP8H, 2, 16, 4, 32, [777, 190], False),
+    ("fp8-tensor-paged-mha", FP8T, FP8T, 3, 4, 4, 0, [300, 17, 1031], True),
+    ("fp8-mixed-axes-gqa8-paged", FP8H, FP8T, 1, 16, 2, 16, [600], True),
 ]
 
 

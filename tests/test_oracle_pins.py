@@ -613,7 +613,8 @@ def test_layout_is_a_bijection(orc, bits):
 
 
 @pytest.mark.parametrize("k_side,v_side", [((4, 0, 0, 64), (4, 0, 0, 64)),
-                                           ((2, 1, 0, 32), (8, 1, 0, 128))])
+                                           ((2, 1, 0, 32), (8, 1, 0, 128)),
+                                           ((8, 2, 3, 0), (8, 2, 2, 0))])
 def test_paged_pack_roundtrip_any_block_permutation(orc, k_side, v_side):
     H, R, T = 2, 16, 150
     seq = orc.Sequence(k_side, v_side, H, R, capacity=256)
