@@ -46,7 +46,7 @@ def side_token_bytes(side) -> float:
     bits, scheme, axis, group = side
     meta = 2 * (2 if scheme == 1 else 1)
     codes = HEAD_DIM * bits / 8
-    if bits == 16:  # unquantized BF16 rows carry no metadata
+    if bits == 16 or scheme == 2:  # BF16 rows and FP8 (scales per head / tensor): no per-row metadata
         return codes
     if axis == 0:
         return codes + (HEAD_DIM // group) * meta
@@ -333,6 +333,7 @@ def counter_traffic(workload: str):
 
 SWEEP_FORMATS = {
     "bf16": (16, 0, 0, 128),
+    "fp8-head": (8, 2, 3, 0),
     "int8-g128": (8, 0, 0, 128),
     "int4-g64": (4, 0, 0, 64),
     "int2-g32": (2, 0, 0, 32),
@@ -356,7 +357,9 @@ def sweep_crossover(batches, lengths, calls_per_graph: int = 20, replays: int = 
             for name, side in SWEEP_FORMATS.items():
                 w = ki.Workload(f"sweep-{name}", 11, B, 32, 8, T, ki.Side(*side), ki.Side(*side))
                 cap = -(-(T + 16) // 16) * 16
-                cache = kvq.Cache(side, side, B, 8, residual=0, capacity=cap)
+                # FP8: per-head scales of the N(0, 1) inputs, amax / 448 with amax ~ 5
+                f8 = {"fp8_scales": ([5.0 / 448] * 8, [5.0 / 448] * 8)} if side[1] == 2 else {}
+                cache = kvq.Cache(side, side, B, 8, residual=0, capacity=cap, **f8)
                 k = torch.empty((B, T, 8, HEAD_DIM), dtype=torch.bfloat16, device="cuda")
                 v = torch.empty_like(k)
                 for b in range(B):
