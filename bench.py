@@ -326,9 +326,9 @@ def counter_traffic(workload: str):
 # ------------------------------------------------------------------------------------------
 
 # ------------------------------------------------------------------------------------------
-# Crossover sweep: unquantized BF16 against INT8 / INT4 / INT2 decode attention over context
-# length and batch [P2, "Why compression may also improve speed": saved memory traffic versus
-# quantization and dequantization overhead; at short contexts the overhead may win]
+# Crossover sweep: unquantized BF16 against FP8 / INT8 / INT4 / INT2 decode attention over context
+# length and batch [P2, "Why compression may also improve speed": fewer bytes to stream against
+# the instructions spent decoding them, with short contexts where decoding can cost more]
 # ------------------------------------------------------------------------------------------
 
 SWEEP_FORMATS = {
