@@ -79,7 +79,7 @@ enum { KVQ_PER_TOKEN = 0, KVQ_PER_CHANNEL = 1, KVQ_PER_TENSOR = 2, KVQ_PER_HEAD 
 
 /* KVQ_FP8: elements stored as OCP FP8 E4M3 bytes with one fp32 scale per tensor (axis
  * KVQ_PER_TENSOR) or per kv head (KVQ_PER_HEAD) [P3, "Step 3: Deploy a Fallback-Capable FP8
- * First": per-tensor and per-attention-head scales; "FP8 / INT8: Engineering Baseline"]:
+ * First": FP8 caches scaled per tensor or per attention head; "FP8 / INT8: Engineering Baseline"]:
  * code = E4M3(x / s) with x / s an IEEE fp32 division, rounded to the nearest E4M3 value (ties to
  * the even code) and saturated at +-448; x^ = s * E4M3 value.  bits 8, group 0 (else
  * KVQ_EINVAL); both sides FP8, each with its own axis.  k_scale / v_scale then point to float32

@@ -23,12 +23,12 @@
  *                                                  [P2 same section, last paragraph; P3 "Why Can't
  *                                                   You Quantize the KV Cache Like Ordinary Activations?"]
  *   - fp16 scale                                   [P2, "Worked example", one two-byte FP16 scale]
- *   - a BF16 window of recent tokens, quantized and moved into the compressed cache when it fills
+ *   - a BF16 window of recent tokens; once it holds R tokens they are quantized into the main cache
  *                                                  [P2, "Why some systems keep a full-precision window"]
  *   - block-table addressing of fixed-size blocks  [P2, "How this connects to paging and prefix caching"]
  *   - FP8 (scheme 2): elements stored as OCP FP8 E4M3 with one fp32 scale per tensor or per
  *     attention head, supplied by the caller  [P3, "Step 3: Deploy a Fallback-Capable FP8
- *     First": FP8 KV cache with per-tensor and per-attention-head scales; "FP8 / INT8:
+ *     First": FP8 caches scaled per tensor or per attention head; "FP8 / INT8:
  *     Engineering Baseline"].  Reading: code = E4M3(x / s), x / s an IEEE fp32 division, the
  *     nearest E4M3 value with ties to the even code, saturating at +-448; x^ = s * E4M3 value.
  *   - bits = 16: the unquantized BF16 cache, the baseline the compressed formats are measured

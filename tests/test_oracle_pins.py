@@ -272,7 +272,7 @@ def test_outlier_vector_single_scale_vs_groups(orc):
     assert list(u2.astype(int) - 2) == [0, 0, 0, 0, 1]
     _, u8 = orc.quant_sym(x, 8)
     assert list(u8.astype(int) - 128) == [1, -1, 2, 2, 127]
-    sA, uA = orc.quant_sym(x[:4], 4)  # group A: small values, small scale
+    sA, uA = orc.quant_sym(x[:4], 4)  # first group: small magnitudes, hence a small scale
     qA = uA.astype(int) - 8
     assert list(qA) == [2, -4, 7, 5]
     err_single = np.abs(orc.dequant(4, 0, u[:4], s16) - x[:4])
