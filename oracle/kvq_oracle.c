@@ -56,7 +56,10 @@
  *               bytes: piece i of slice s at byte 64 S i + S s of the tile (slab i), so the
  *               slices' piece i form one contiguous run (for bits <= 4 a slice is one piece)
  *   scales/zeros per-token groups: fp16 [tile][d / G][16]
- *               per-channel key groups: fp16 [b][h][cap / Gt][d]   (contiguous caches only)
+ *               per-channel key groups: contiguous fp16 [b][h][cap / Gt][d]; paged fp16
+ *               [block][h][d], the row of key group tau kept with the block that holds the
+ *               group's first token (block_table[b][tau * Gt / 16]), so blocks shared between
+ *               sequences carry their groups' metadata with them
  *   residual    bf16 [b][h][R][d]
  */
 #include <math.h>
@@ -565,7 +568,8 @@ void orc_pack(const orc_seq *s, int32_t b, const int32_t *table_row, uint8_t *kc
       for (int tau = 0; tau < ntau; tau++)
         for (int c = 0; c < d; c++) {
           size_t mi = meta_index(s, &s->k, h, tau * Gt, c);
-          size_t img = (((size_t)b * s->H + h) * (s->cap / Gt) + tau) * d + c;
+          size_t img = table_row ? ((size_t)table_row[tau * Gt / 16] * s->H + h) * d + c
+                                 : (((size_t)b * s->H + h) * (s->cap / Gt) + tau) * d + c;
           ksc[img] = s->ks[mi];
           if (s->k.scheme == ORC_ASYM) kzc[img] = s->kz[mi];
         }

@@ -305,6 +305,8 @@ def empty_images(k_side, v_side, batch: int, n_kv_heads: int, residual: int, cap
             continue
         if axis == PER_TOKEN:
             n = tiles * (d // group) * TILE
+        elif num_blocks:  # paged per-channel keys: one metadata row per (block, head)
+            n = num_blocks * H * d
         else:
             n = batch * H * (capacity // group) * d
         out[f"{name}_scale"] = np.zeros(n, np.uint16)

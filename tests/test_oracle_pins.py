@@ -637,3 +637,31 @@ def test_paged_pack_roundtrip_any_block_permutation(orc, k_side, v_side):
                    for j in range(nblk)]
         imgs.append(np.concatenate(logical))
     assert np.array_equal(imgs[0], imgs[1])  # same logical content under either permutation
+
+
+@pytest.mark.parametrize("gt", [16, 32, 64])
+def test_paged_per_channel_metadata_travels_with_the_group_block(orc, gt):
+    """Paged per-channel keys: key group tau's scale/zero row is stored with the physical block
+    of the group's first token, whatever the block permutation [P2, "How this connects to paging
+    and prefix caching"; P3, "Why Can't You Quantize the KV Cache Like Ordinary Activations?"]."""
+    H, R, T = 2, 64, 300
+    k_side, v_side = (2, 1, 1, gt), (2, 1, 0, 32)
+    seq = orc.Sequence(k_side, v_side, H, R, capacity=512)
+    kv = bf16_values(RNG.standard_normal((2, T, H, 128)).astype(np.float32))
+    kb = (kv.view(np.uint32) >> 16).astype(np.uint16)
+    seq.append(kb[0], kb[1])
+    nblk = 32
+    table = RNG.permutation(nblk).astype(np.int32)
+    im = orc.empty_images(k_side, v_side, 1, H, R, num_blocks=nblk)
+    assert im["k_scale"].size == nblk * H * 128
+    seq.pack(0, im, table)
+    for tau in range(seq.n_quant // gt):
+        blk = table[tau * gt // 16]
+        for h in range(H):
+            row = slice((blk * H + h) * 128, (blk * H + h + 1) * 128)
+            assert np.array_equal(im["k_scale"][row], seq.ks[h, tau])
+            assert np.array_equal(im["k_zero"][row], seq.kz[h, tau])
+    back = orc.Sequence(k_side, v_side, H, R, capacity=512)
+    back.set_counters(seq.n_quant, 0)
+    back.unpack_codes(0, im, table)
+    assert np.array_equal(back.ku[:, :seq.n_quant], seq.ku[:, :seq.n_quant])
