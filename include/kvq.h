@@ -29,17 +29,25 @@
  *   tile        16 consecutive compressed token slots of one (sequence, kv head).
  *   tile index  contiguous: (b * H_kv + h) * (capacity / 16) + slot / 16
  *               paged:      block_table[b][slot / 16] * H_kv + h     (a block holds 16 tokens)
- *   K codes     row-major: byte (tile * 16 + slot % 16) * RB, RB = head_dim * bits / 8; channel c
- *               of a row at bit c * bits (little-endian inside each byte).
- *   V codes     token-interleaved inside each tile: the tile is (head_dim / 8) * 4 chunks of
- *               4 * bits bytes; chunk (t / 4) * (head_dim / 8) + c / 8 holds channels
- *               8 * (c / 8) .. + 7 of the tile rows 4 * (t / 4) .. + 3.  Inside a chunk, with
+ *   slices      a tile is 64 slices of 4 * bits bytes (one per lane of the wave that reads it),
+ *               stored in pieces of S = min(16, 4 * bits) bytes: piece i of slice s (its bits
+ *               8 S i .. 8 S (i + 1) - 1) sits at byte 64 S i + S s of the tile.  2- and 4-bit
+ *               slices are one piece; 8-bit slices two and 16-bit slices four, 1 KiB apart.
+ *   K codes     slice 4 * t + c / 32 holds channels 32 * (c / 32) .. + 31 of tile row t, channel
+ *               c at bit (c % 32) * bits of the slice (little-endian inside each byte); for 2-
+ *               and 4-bit codes this is plain row-major order.
+ *   V codes     token-interleaved: slice (chunk) (t / 4) * (head_dim / 8) + c / 8 holds channels
+ *               8 * (c / 8) .. + 7 of tile rows 4 * (t / 4) .. + 3.  Inside a chunk, with
  *               E = 32 / bits fields per 32-bit word and r = 2 * (c % 8) + (t % 4) / 2, element
  *               (t, c) is field (r % (E/2)) + (E/2) * (t % 2) of word r / (E/2).
  *   codes       offset binary: symmetric q in [-Q, Q] is stored as q + 2^(bits-1); asymmetric
- *               codes are stored as they are (0 .. 2^bits - 1).
- *   scales/zeros fp16.  Per-token groups: [tile][head_dim / group][16].  Per-channel key groups
- *               (contiguous caches only): [b][h][capacity / group][head_dim].
+ *               codes are stored as they are (0 .. 2^bits - 1); FP8 codes are E4M3 bytes; bits
+ *               16 stores the bf16 elements.
+ *   scales/zeros fp16.  Per-token groups: [tile][head_dim / group][16].  Per-channel key groups:
+ *               contiguous [b][h][capacity / group][head_dim]; paged [block][h][head_dim], the
+ *               row of key group tau kept with the block of its first token,
+ *               block_table[b][tau * group / 16] (other blocks' rows are unused).  FP8: fp32
+ *               [1] or [n_kv_heads], the caller's.
  *   window      bf16 [b][h][residual][head_dim].
  *   counters    n_quant[b] compressed tokens, n_res[b] window tokens (int32, device).
  */
@@ -126,6 +134,10 @@ typedef struct {
  * otherwise [P2, "How this connects to paging and prefix caching"]: each sequence's
  * compressed slots live in 16-token blocks of a shared pool, found through its row of the
  * block table.  Blocks that a call writes must belong to that sequence alone.
+ * Prefix sharing: a sequence may start its table with blocks another sequence already wrote
+ * (a shared, already-quantized prefix).  The caller then sets its counters to n_quant = the
+ * prefix length (a multiple of 16 and of a per-channel key group) and n_res = 0; calls only
+ * write slots >= n_quant, so shared blocks are read, never written.
  * Calls return KVQ_ENOTSUP when batch * n_kv_heads > 65535 or when a buffer would hold 2^31 or
  * more 16-slot tiles (batch * n_kv_heads * capacity / 16, or num_blocks * n_kv_heads). */
 typedef struct {
@@ -153,7 +165,8 @@ size_t kvq_buffer_bytes(const kvq_format *fmt, int32_t batch, int32_t n_kv_heads
 
 /* Check a format without a cache: KVQ_OK, KVQ_EINVAL or KVQ_ENOTSUP.  Supported: head_dim 128;
  * bits 2/4/8 and one scheme, the same for K and V; per-token groups 32/64/128; per-channel
- * grouping for keys only, with residual > 0 divisible by the group.  Pure host code. */
+ * grouping for keys only (contiguous or paged), with residual > 0 divisible by the group;
+ * FP8 and bits 16 as described above.  Pure host code. */
 kvq_status kvq_check_format(const kvq_format *fmt);
 
 /* Append n_new >= 1 new tokens to every sequence of the batch.

@@ -350,9 +350,13 @@ __global__ __launch_bounds__(256) void quantize_kernel(CacheDev c, const uint16_
       if (K.scheme == KVQ_ASYM) c.kz[idx] = mk_z[(slot - seg0) * 4 + g];
     }
   } else {
+    // the group's row: per (sequence, head) in order, or with the block of its first token
     const int tau = seg0 / S;
+    bool ok = true;
+    const size_t row = c.table ? static_cast<size_t>(tile_index(c, b, h, seg0 / TILE, ok))
+                               : (static_cast<size_t>(b) * c.H + h) * (c.cap / S) + tau;
     for (int ch = tid; ch < D; ch += blockDim.x) {
-      const size_t idx = ((static_cast<size_t>(b) * c.H + h) * (c.cap / S) + tau) * D + ch;
+      const size_t idx = row * D + ch;
       c.ks[idx] = pc_s[ch];
       if (K.scheme == KVQ_ASYM) c.kz[idx] = pc_z[ch];
     }

@@ -611,8 +611,14 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
       const int fold_blk = lane & 15;
       const int fold_c0 = (KB == 2) ? 32 * (fold_blk / 4) + 16 * ((fold_blk % 4) / 2) + 4 * (fold_blk % 2)
                                     : 8 * fold_blk;
+      // per-channel key group tau's metadata row: contiguous [b][h][cap / Gt], paged with the
+      // block of the group's first token (an unusable entry reads row 0; the block error is
+      // reported where the codes are read)
       auto kpc_meta = [&](int tau) -> size_t {
-        return ((static_cast<size_t>(b) * H + h) * (c.cap / kgroup) + tau) * D + fold_c0;
+        if (!trow) return ((static_cast<size_t>(b) * H + h) * (c.cap / kgroup) + tau) * D + fold_c0;
+        const int blk = ld_uniform(trow + (tau * kgroup) / TILE);
+        const int pb_ = (blk < 0 || blk >= c.num_blocks) ? 0 : blk;
+        return (static_cast<size_t>(pb_) * H + h) * D + fold_c0;
       };
       auto load_meta8 = [&](const uint16_t* base, size_t mi) -> uint4 {
         if constexpr (KB == 2) {

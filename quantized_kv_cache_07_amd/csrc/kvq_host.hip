@@ -70,7 +70,6 @@ kvq_status check_cache(const kvq_cache* c) {
   if (static_cast<long>(c->batch) * c->n_kv_heads > 65535) return KVQ_ENOTSUP;
   if (c->block_table) {
     if (c->num_blocks < 1 || c->max_blocks < 1) return KVQ_EINVAL;
-    if (c->fmt.k.axis == KVQ_PER_CHANNEL) return KVQ_ENOTSUP;
   } else {
     if (c->capacity < TILE || c->capacity % TILE != 0) return KVQ_EINVAL;
     if (c->fmt.k.axis == KVQ_PER_CHANNEL && c->capacity % c->fmt.k.group != 0) return KVQ_EINVAL;
@@ -237,7 +236,8 @@ size_t kvq_buffer_bytes(const kvq_format* fmt, int32_t batch, int32_t n_kv_heads
       }
       if ((which == KVQ_BUF_K_ZERO || which == KVQ_BUF_V_ZERO) && s.scheme != KVQ_ASYM) return 0;
       if (s.axis == KVQ_PER_TOKEN) return tiles * (D / s.group) * TILE * 2;
-      if (paged || capacity % s.group) return 0;
+      if (paged) return static_cast<size_t>(num_blocks) * n_kv_heads * D * 2;  // per block
+      if (capacity % s.group) return 0;
       return static_cast<size_t>(batch) * n_kv_heads * (capacity / s.group) * D * 2;
     }
     case KVQ_BUF_K_RES:

@@ -60,6 +60,9 @@ CASES = [
     ("fp8-head-gqa4-window", FP8H, FP8H, 2, 16, 4, 32, [777, 190], False),
     ("fp8-tensor-paged-mha", FP8T, FP8T, 3, 4, 4, 0, [300, 17, 1031], True),
     ("fp8-mixed-axes-gqa8-paged", FP8H, FP8T, 1, 16, 2, 16, [600], True),
+    ("kivi-int2-paged", KPC2, ASYM2_32, 2, 8, 2, 128, [700, 1300], True),
+    ("kpc4-sym-g16-paged", KPC4S, SYM4, 2, 4, 1, 32, [100, 50], True),
+    ("kpc4-asym-g64-paged", (4, 1, 1, 64), (4, 1, 0, 32), 1, 8, 2, 64, [500], True),
 ]
 
 
@@ -144,3 +147,55 @@ def test_device_faults_leave_other_sequences_intact():
     torch.cuda.synchronize()
     assert K.read_error(pr2.cache) & K.ERR_CAPACITY
     assert pr2.cache.n_quant.cpu().tolist() == [16, 6]
+
+
+def test_prefix_shared_blocks_are_read_not_written():
+    """Prefix sharing through the block table [P2, "How this connects to paging and prefix
+    caching"]: sequence 1 maps sequence 0's first P/16 physical blocks (its compressed prefix,
+    per-channel key metadata included) and sets its counters to (P, 0); then both sequences
+    take their own single-token steps, with window flushes.  Codes, metadata and windows equal
+    two oracle sequences (the second = the same P tokens, flushed, then its own tokens), the
+    shared blocks never change, and both attention outputs match."""
+    announce(test="prefix_sharing")
+    K = kc.kvq()
+    k_side, v_side, R, H, Hq, P = KPC2, ASYM2_32, 64, 2, 8, 256
+    w = kc.ki.Workload("share", 21, 2, Hq, H, P + 10, kc.ki.Side(*k_side), kc.ki.Side(*v_side),
+                       residual=R, paged=True)
+    nbs = (P + 10 + R + 160) // 16 + 1  # logical blocks per sequence
+    pool = 2 * nbs
+    perm = np.random.default_rng(3).permutation(pool).astype(np.int32)
+    table = np.full((2, nbs), -1, np.int32)
+    table[0] = perm[:nbs]
+    table[1, :P // 16] = table[0, :P // 16]  # shared prefix blocks
+    table[1, P // 16:] = perm[nbs:2 * nbs - P // 16]
+    cache = K.Cache(k_side, v_side, 2, H, residual=R, block_table=torch.from_numpy(table),
+                    num_blocks=pool)
+    k, v = kc.ki.prefill_kv(w, 0, P + 10)
+    K.quantize_append(cache, k[None].cuda().contiguous(), v[None].cuda().contiguous(),
+                      desc=cache.sequence(0))
+    torch.cuda.synchronize()
+    assert cache.n_quant.tolist() == [P, 0] and cache.n_res.tolist() == [10, 0]
+    cache.n_quant[1] = P  # sequence 1 adopts the compressed prefix
+    s0 = kc.oracle.Sequence(k_side, v_side, H, R, nbs * 16)
+    s1 = kc.oracle.Sequence(k_side, v_side, H, R, nbs * 16)
+    s0.append(kc.ki.bf16_bits(k), kc.ki.bf16_bits(v))
+    s1.append(kc.ki.bf16_bits(k[:P]), kc.ki.bf16_bits(v[:P]))
+    s1.flush()
+    assert (s1.n_quant, s1.n_res) == (P, 0)
+    shared = [int(bk) for bk in table[0, :P // 16]]
+    tile_bytes = 16 * 128 * k_side[0] // 8
+
+    def shared_bytes():
+        kcodes = cache.k_codes.cpu().numpy().reshape(pool * H, tile_bytes)
+        ks = kc._u16(cache.k_scale).reshape(pool, H, 128)
+        return [kcodes[[bk * H + h for bk in shared for h in range(H)]].copy(), ks[shared].copy()]
+
+    before = shared_bytes()
+    pr = kc.Pair(w, cache, [s0, s1], [P + 10, P], table, pool, 0)
+    for _ in range(90):  # each sequence flushes its window once, into its own blocks
+        kc.step(pr)
+    kc.compare_state(pr)
+    after = shared_bytes()
+    assert all(np.array_equal(x, y) for x, y in zip(before, after))
+    assert cache.n_quant.tolist() == [s0.n_quant, s1.n_quant] == [P + R, P + R]
+    kc.compare_attention(pr)
