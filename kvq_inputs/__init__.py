@@ -151,6 +151,12 @@ CONFIGS = {
                    description="KIVI-style 2-bit asymmetric: batch 16, H_q=32, H_kv=8, T=32768, "
                                "keys per-channel over 32 tokens, values per-token groups of 32, "
                                "BF16 window 128, key outlier channels x15"),
+    "c4p": Workload("c4p", 4, 16, 32, 8, 32768, Side(2, ASYM, PER_CHANNEL, 32), Side(2, ASYM, PER_TOKEN, 32),
+                    residual=128, k_outlier_channels=4, k_outlier_scale=15.0, step_append=True,
+                    paged=True,
+                    description="KIVI-style 2-bit asymmetric, paged: the c4 batch (same inputs) "
+                                "in 16-token blocks of a shuffled pool, per-channel key metadata "
+                                "kept with each group's first block"),
     "c5": Workload("c5", 5, 64, 32, 8, 131072, Side(4, SYM, PER_TOKEN, 64), Side(4, SYM, PER_TOKEN, 64),
                    residual=128, paged=True, step_append=True, mixed_lengths=True,
                    description="paged mixed batch: 64 sequences, lengths log-uniform in "

@@ -109,7 +109,11 @@ def _check_codes(st, cache, w, samples):
                         s16, z16, u = oracle.quant_asym(col[:, c].copy(), bits)
                     else:
                         (s16, u), z16 = oracle.quant_sym(col[:, c].copy(), bits), None
-                    mi = ((b * cache.n_kv_heads + h) * (cache.capacity // group) + tau) * d + c
+                    if cache.paged:  # the row kept with the block of the group's first token
+                        blk = int(cache.block_table[b, tau * group // 16].item())
+                        mi = (blk * cache.n_kv_heads + h) * d + c
+                    else:
+                        mi = ((b * cache.n_kv_heads + h) * (cache.capacity // group) + tau) * d + c
                     assert sc[mi] == s16, ("k", b, h, slot, c, "per-channel scale")
                     if z16 is not None:
                         assert zc[mi] == z16, ("k", b, h, slot, c, "per-channel zero")
@@ -145,14 +149,14 @@ def _attention_samples(w, lens):
     order = sorted(range(w.batch), key=lambda b: lens[b])
     if w.name == "c5":
         return [order[0], order[1], order[len(order) // 2]]
-    if w.name == "c4":
+    if w.name in ("c4", "c4p"):
         return [3]
     if w.name == "c3":
         return [0, 17]
     return list(range(w.batch))
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c4p", "c5"])
 def test_full_size_workload(name):
     st, w, cache, got, qb, nq_dev, nr_dev = _run(name)
     rng = np.random.default_rng(1234 + int(name[1]))
