@@ -400,10 +400,12 @@ static double vhat(const orc_seq *s, int h, int slot, int c) {
 }
 
 /* q: [Hq][d] bf16, out: [Hq][d] fp32.  Query head hq reads kv head floor(hq * H / Hq).  The
- * attended sequence is the compressed tokens 0..n_quant-1 followed by the window rows
+ * attended sequence is the first T of: the compressed tokens 0..n_quant-1, then the window rows
  * 0..n_res-1.  score_t = (sum_i q_i k^_ti) * sm_scale; o = sum_t e^(score_t - max) v^_t / sum. */
-void orc_attend(const orc_seq *s, const uint16_t *q, int32_t Hq, float sm_scale, float *out) {
-  int d = s->d, T = s->n_quant + s->n_res;
+static void attend_first(const orc_seq *s, const uint16_t *q, int32_t Hq, float sm_scale,
+                         float *out, int T) {
+  int d = s->d;
+  if (T < 0) T = 0;
   double *sc = (double *)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
   double *qd = (double *)malloc(sizeof(double) * (size_t)d);
   double *o = (double *)malloc(sizeof(double) * (size_t)d);
@@ -439,6 +441,24 @@ void orc_attend(const orc_seq *s, const uint16_t *q, int32_t Hq, float sm_scale,
   free(sc);
   free(qd);
   free(o);
+}
+
+/* Single-query decode: the query attends every cached token. */
+void orc_attend(const orc_seq *s, const uint16_t *q, int32_t Hq, float sm_scale, float *out) {
+  attend_first(s, q, Hq, sm_scale, out, s->n_quant + s->n_res);
+}
+
+/* Multi-query decode (speculative rows or a prefill chunk): the last n_q cached tokens are the
+ * queries' own, and query i (0-based, q [n_q][Hq][d], out [n_q][Hq][d]) attends the tokens up
+ * to and including its own, the first T - n_q + i + 1 of them (causal).  A query with no token
+ * before it outputs zeros.  [P2, "Why the KV cache grows so quickly", attention equation, per
+ * query row; P3, "Step 3: Deploy a Fallback-Capable FP8 First": prefill-heavy workloads] */
+void orc_attend_mq(const orc_seq *s, const uint16_t *q, int32_t n_q, int32_t Hq, float sm_scale,
+                   float *out) {
+  int T = s->n_quant + s->n_res;
+  for (int i = 0; i < n_q; i++)
+    attend_first(s, q + (size_t)i * Hq * s->d, Hq, sm_scale, out + (size_t)i * Hq * s->d,
+                 T - n_q + i + 1);
 }
 
 /* Same, but on already dequantized fp64 rows khat/vhat [T][d] (used by the pins). */

@@ -65,6 +65,7 @@ def lib() -> ctypes.CDLL:
         L.orc_flush.argtypes = [P]
         L.orc_flush.restype = ctypes.c_int
         L.orc_attend.argtypes = [P, P, i32, f32, P]
+        L.orc_attend_mq.argtypes = [P, P, i32, i32, f32, P]
         L.orc_attend_rows.argtypes = [P, P, P, i32, i32, f64, P]
         L.orc_pack.argtypes = [P, i32, P, P, P, P, P, P, P, P, P]
         L.orc_unpack_codes.argtypes = [P, i32, P, P, P]
@@ -266,6 +267,15 @@ class Sequence:
         q = np.ascontiguousarray(q, dtype=np.uint16)
         out = np.zeros(q.shape, np.float32)
         lib().orc_attend(ctypes.byref(self._s), _p(q), q.shape[0], float(sm_scale), _p(out))
+        return out
+
+    def attend_mq(self, q: np.ndarray, sm_scale: float) -> np.ndarray:
+        """q: bf16 bits [n_q][Hq][d] for the last n_q cached tokens -> fp32 [n_q][Hq][d];
+        query i attends the first T - n_q + i + 1 tokens (causal)."""
+        q = np.ascontiguousarray(q, dtype=np.uint16)
+        out = np.zeros(q.shape, np.float32)
+        lib().orc_attend_mq(ctypes.byref(self._s), _p(q), q.shape[0], q.shape[1],
+                            float(sm_scale), _p(out))
         return out
 
     def pack(self, b: int, images: dict, table_row: np.ndarray | None = None) -> None:

@@ -665,3 +665,29 @@ def test_paged_per_channel_metadata_travels_with_the_group_block(orc, gt):
     back.set_counters(seq.n_quant, 0)
     back.unpack_codes(0, im, table)
     assert np.array_equal(back.ku[:, :seq.n_quant], seq.ku[:, :seq.n_quant])
+
+
+@pytest.mark.parametrize("k_side,v_side", [((4, 0, 0, 64), (4, 0, 0, 64)),
+                                           ((16, 0, 0, 128), (16, 0, 0, 128))])
+def test_multi_query_is_causal_single_query_over_prefixes(orc, k_side, v_side):
+    """Multi-query decode: query i of the last n_q tokens equals single-query decode over a
+    sequence that holds only the first T - n_q + i + 1 tokens (without a window the codes of a
+    token do not depend on what follows, so the prefixes are the same cache state)."""
+    H, Hq, T, nq = 2, 8, 75, 6
+    kv = bf16_values(RNG.standard_normal((2, T, H, 128)).astype(np.float32))
+    kb = (kv.view(np.uint32) >> 16).astype(np.uint16)
+    full = orc.Sequence(k_side, v_side, H, 0, capacity=128)
+    full.append(kb[0], kb[1])
+    q = (bf16_values(RNG.standard_normal((nq, Hq, 128)).astype(np.float32)).view(np.uint32) >> 16)
+    q = q.astype(np.uint16)
+    got = full.attend_mq(q, 0.088)
+    for i in range(nq):
+        pre = orc.Sequence(k_side, v_side, H, 0, capacity=128)
+        pre.append(kb[0, :T - nq + i + 1], kb[1, :T - nq + i + 1])
+        assert np.array_equal(got[i], pre.attend(q[i], 0.088))
+    assert np.array_equal(full.attend_mq(q[-1:], 0.088)[0], full.attend(q[-1], 0.088))
+    # a query before the first token attends nothing
+    tiny = orc.Sequence(k_side, v_side, H, 0, capacity=128)
+    tiny.append(kb[0, :2], kb[1, :2])
+    out = tiny.attend_mq(q[:4], 0.088)
+    assert np.all(out[0] == 0) and np.all(out[1] == 0) and np.any(out[3] != 0)
