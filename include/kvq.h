@@ -215,6 +215,29 @@ kvq_status kvq_decode_attention(const kvq_cache *cache, const void *q, int32_t n
                                 float sm_scale, int32_t max_tokens, float *out, void *workspace,
                                 size_t workspace_bytes, void *stream);
 
+/* Workspace bytes kvq_decode_attention_mq() needs for n_q query tokens per sequence;
+ * kvq_decode_workspace_bytes(c, hq, mt) equals kvq_decode_workspace_bytes_mq(c, hq, 1, mt).
+ * 0 for invalid arguments (n_q < 1 or n_q > max_tokens included).  Pure host arithmetic. */
+size_t kvq_decode_workspace_bytes_mq(const kvq_cache *cache, int32_t n_q_heads, int32_t n_q,
+                                     int32_t max_tokens);
+
+/* Multi-query decode attention (speculative rows, a prefill chunk) over the same cache: the
+ * last n_q cached tokens of every sequence are the queries' own tokens (append them first), and
+ * query i attends the tokens up to and including its own, the first n_quant + n_res - n_q + i + 1
+ * of the sequence (causal; a query with no such token gets zeros) [P2, "Why the KV cache grows
+ * so quickly", attention equation, one row per query; P3, "Step 3: Deploy a Fallback-Capable FP8
+ * First": prefill-heavy workloads gain least].  The K/V tiles streamed from HBM are dequantized
+ * once per block of query rows and multiplied against all of them on the matrix cores.
+ *   q:   bf16 [batch][n_q][n_q_heads][head_dim], device, 16-byte aligned
+ *   out: fp32 [batch][n_q][n_q_heads][head_dim], device
+ *   n_q: 1 .. max_tokens; n_q = 1 is kvq_decode_attention.
+ *   workspace: >= kvq_decode_workspace_bytes_mq(cache, n_q_heads, n_q, max_tokens) bytes
+ * Other arguments, errors and device faults as kvq_decode_attention.  Launches two kernels. */
+kvq_status kvq_decode_attention_mq(const kvq_cache *cache, const void *q, int32_t n_q,
+                                   int32_t n_q_heads, float sm_scale, int32_t max_tokens,
+                                   float *out, void *workspace, size_t workspace_bytes,
+                                   void *stream);
+
 /* Synchronise `stream`, copy the device error word into *host_err and return KVQ_EDEVICE if
  * any bit is set, KVQ_OK otherwise.  The word is not cleared. */
 kvq_status kvq_read_error(const kvq_cache *cache, int32_t *host_err, void *stream);

@@ -29,6 +29,7 @@
 #pragma once
 
 #include <cfloat>
+#include <climits>
 #include <type_traits>
 
 #include "kvq_dev.h"
@@ -347,8 +348,10 @@ __device__ __forceinline__ int seq_units(const CacheDev& c, int max_tokens, int 
   return (nq + 31) / 32 + (nr + 31) / 32;
 }
 
-template <int KB, int G, bool KPC, int NP, int SCH>
+template <int KB, int G, bool KPC, int NP, int SCH, bool MQ>
 __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_kernel(DecodeParams p) {
+  // multi-query geometry; single-query instantiations fold it to constants
+  const int nqt = MQ ? p.nqt : 1, qbs = MQ ? p.qbs : 1, nqb = MQ ? p.nqb : 1, gkv = MQ ? p.gkv : G;
   constexpr bool ASYM = SCH == KVQ_ASYM;
   constexpr bool F8 = SCH == KVQ_FP8;  // E4M3 bytes, one scale per kv head (or tensor) per side
   extern __shared__ __align__(16) unsigned char smem[];
@@ -376,7 +379,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
       if (un < 0) {
         if (blockIdx.x == 0) atomicOr(c.err, KVQ_ERR_TOKENS);
       } else {
-        s += un * H;
+        s += un * H * nqb;
       }
     }
     scan[tid] = s;
@@ -390,7 +393,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
     int run = scan[tid] - s;
     for (int i = tid * per; i < min(B, (tid + 1) * per); i++) {
       pre[i] = run;
-      run += max(seq_units(c, p.max_tokens, i), 0) * H;
+      run += max(seq_units(c, p.max_tokens, i), 0) * H * nqb;
     }
     if (tid == 255) pre[B] = scan[255];
     __syncthreads();
@@ -430,7 +433,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
   int u = u0;
   bool first_seg = true;
   while (u < u1) {
-    // ---- locate the segment: sequence b, kv head h, first unit kk ----
+    // ---- locate the segment: sequence b, kv head h, query block qblk, first unit kk ----
     int lo = 0, hi = B - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -438,9 +441,10 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
     }
     const int b = uni(lo);
     const int pb0 = uni(pre[b]);
-    const int ub = uni((pre[b + 1] - pb0) / H);
-    const int h = (u - pb0) / ub, kk = (u - pb0) % ub;
-    const int seg_abs_end = pb0 + (h + 1) * ub;
+    const int ub = uni((pre[b + 1] - pb0) / (H * nqb));
+    const int sidx = (u - pb0) / ub, kk = (u - pb0) % ub;
+    const int h = sidx / nqb, qblk = sidx % nqb;
+    const int seg_abs_end = pb0 + (sidx + 1) * ub;
     const int uend = min(u1, seg_abs_end);
     const bool complete = (kk == 0) && (uend == seg_abs_end);
     const int slot = first_seg ? 0 : 1;
@@ -449,14 +453,23 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
     const int uq = (nq + 31) / 32;
     const int xend = kk + (uend - u);
 
-    // ---- stage the GQA group's query rows (bf16) ----
+    // ---- stage the segment's G query rows (bf16): row v = query token qblk * qbs + v / gkv,
+    // query head h * gkv + v % gkv; rows past the last query token are zero ----
     __syncthreads();
     if (tid < G * (D / 8)) {
-      const uint4* src = reinterpret_cast<const uint4*>(
-          p.q + (static_cast<size_t>(b) * p.Hq + static_cast<size_t>(h) * G) * D);
-      reinterpret_cast<uint4*>(qs)[tid] = src[tid];
+      const int v = tid / (D / 8), qg = qblk * qbs + v / gkv;
+      uint4 val = uint4{0u, 0u, 0u, 0u};
+      if (qg < nqt)
+        val = reinterpret_cast<const uint4*>(
+            p.q + ((static_cast<size_t>(b) * nqt + qg) * p.Hq +
+                   static_cast<size_t>(h) * gkv + v % gkv) * D)[tid % (D / 8)];
+      reinterpret_cast<uint4*>(qs)[tid] = val;
     }
     __syncthreads();
+    // causal limit (multi-query): the block's first query token sees the first lim_min cached
+    // tokens (the query tokens are the last nqt), column n's token lim_min + hh / gkv of them;
+    // single-query decode has no limit
+    const int lim_min = MQ ? uni(nq + nr - nqt + qblk * qbs + 1) : INT_MAX;
 
     // ---- QK operand: f16 query, masked to the column's key group ----
     f16x8 qb[4];
@@ -531,12 +544,18 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
     // at a finite sentinel, so empty waves never form inf - inf.
     // With vfold, element i's weight comes out divided by alpha_i of the value codes it meets
     // (the raw-code PV operand), which only shifts its exponent.
-    auto softmax = [&](float (&s2)[8], int nvA, int nvB, auto vfold) {
+    auto softmax = [&](float (&s2)[8], int nvA, int nvB, auto vfold, int tok0) {
       const bool full = nvA == 16 && nvB == 16;
       if (!full) {
 #pragma unroll
         for (int i = 0; i < 8; i++)
           if (4 * g + (i & 3) >= (i < 4 ? nvA : nvB)) s2[i] = -INFINITY;
+      }
+      if (tok0 + 32 > lim_min) {  // tokens at or past a column's limit are hidden
+        const int lim = lim_min + hh / gkv;
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+          if (tok0 + 16 * (i >> 2) + 4 * g + (i & 3) >= lim) s2[i] = -INFINITY;
       }
       const float m01 = max3f(s2[0], s2[1], s2[2]);
       const float m02 = max3f(s2[3], s2[4], s2[5]);
@@ -830,7 +849,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
         if constexpr (!KPC) fold_cols8(s2);
         load_k(more ? xn : x, nA, nB);  // key registers are free again
 
-        softmax(s2, nvA, nvB, std::integral_constant<bool, VBF>{});  // s2: weights / alpha
+        softmax(s2, nvA, nvB, std::integral_constant<bool, VBF>{}, 32 * x);  // s2: weights / alpha
 
         // ---- P rows (hi / lo f16 parts of w * s_v) and PV ----
         // Rows 16 pp + n with part >= 2 are never read back, so they are left as computed.
@@ -988,7 +1007,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
           for (int r = 0; r < 4; r++) s2[4 * t + r] = dq[r];
         }
         fold_cols8(s2);
-        softmax(s2, nvA, nvB, std::false_type{});
+        softmax(s2, nvA, nvB, std::false_type{}, nq + r0);
         // P rows: bf16 hi / lo parts of w (truncation; hi + lo carries 16 significant bits)
         bf16x8 pb[NP];
 #pragma unroll
@@ -1105,8 +1124,10 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
 #pragma unroll
       for (int wv = 0; wv < WAVES; wv++) L += e[oi][wv] * lw[wv * 8 + oh];
       if (complete) {
-        p.out[(static_cast<size_t>(b) * p.Hq + static_cast<size_t>(h) * G + oh) * D + ch] =
-            (L > 0.0f) ? O[oi] / L : 0.0f;
+        const int qg = qblk * qbs + oh / gkv;
+        if (qg < nqt)
+          p.out[((static_cast<size_t>(b) * nqt + qg) * p.Hq + static_cast<size_t>(h) * gkv +
+                 oh % gkv) * D + ch] = (L > 0.0f) ? O[oi] / L : 0.0f;
       } else {
         float* part =
             p.ws_part + ((static_cast<size_t>(blockIdx.x) * 2 + slot) * G + oh) * PART_STRIDE;
@@ -1143,21 +1164,29 @@ __global__ __launch_bounds__(COMBINE_THREADS) void combine_kernel(DecodeParams p
   static_assert((G * D) % S == 0 && (G * D) / S >= 32, "combine slices");
   __shared__ float sm[COMBINE_THREADS], sl[COMBINE_THREADS], so[COMBINE_THREADS];
   const int H = p.c.H, B = p.c.B;
-  const int b = blockIdx.x / H, h = blockIdx.x % H;
+  const int SEGS = H * p.nqb;  // segments per sequence: (kv head, query block)
+  const int b = blockIdx.x / SEGS, sidx = blockIdx.x % SEGS;
+  const int h = sidx / p.nqb, qblk = sidx % p.nqb;
   constexpr int opb = (G * D) / S;
   constexpr int opp = opb < 256 ? opb : 256;
   constexpr int cg = COMBINE_THREADS / opp;
   const int oi = threadIdx.x % opp, cgi = threadIdx.x / opp;
   const int* pre = p.ws_pre;
   const long long U = pre[B], NB = p.nblocks;
-  const int ub = (pre[b + 1] - pre[b]) / H;
-  float* dst = p.out + (static_cast<size_t>(b) * p.Hq + static_cast<size_t>(h) * G) * D +
-               static_cast<size_t>(blockIdx.y) * opb;
+  const int ub = (pre[b + 1] - pre[b]) / SEGS;
+  // output element o of the segment's G x D block (row o / D: query token, query head)
+  auto dst = [&](int o) -> float* {
+    const int row = o / D, qg = qblk * p.qbs + row / p.gkv;
+    if (qg >= p.nqt) return nullptr;
+    return p.out + ((static_cast<size_t>(b) * p.nqt + qg) * p.Hq + static_cast<size_t>(h) * p.gkv +
+                    row % p.gkv) * D + o % D;
+  };
   if (ub == 0) {
-    for (int o = threadIdx.x; o < opb; o += COMBINE_THREADS) dst[o] = 0.0f;
+    for (int o = threadIdx.x; o < opb; o += COMBINE_THREADS)
+      if (float* d = dst(static_cast<int>(blockIdx.y) * opb + o)) *d = 0.0f;
     return;
   }
-  const long long us = pre[b] + static_cast<long long>(h) * ub, ue = us + ub;
+  const long long us = pre[b] + static_cast<long long>(sidx) * ub, ue = us + ub;
   const int kf = block_of(us, U, NB), kl = block_of(ue - 1, U, NB);
   if (kf == kl) return;  // one workgroup saw the whole sequence and wrote the output
   const int s0 = ((static_cast<long long>(kf) * U) / NB == us) ? 0 : 1;
@@ -1191,7 +1220,7 @@ __global__ __launch_bounds__(COMBINE_THREADS) void combine_kernel(DecodeParams p
         Lt += e * sl[q * opp + oi];
         Ot += e * so[q * opp + oi];
       }
-      dst[o0 + oi] = (Lt > 0.0f) ? Ot / Lt : 0.0f;
+      if (float* d = dst(o)) *d = (Lt > 0.0f) ? Ot / Lt : 0.0f;
     }
     __syncthreads();
   }
@@ -1199,33 +1228,33 @@ __global__ __launch_bounds__(COMBINE_THREADS) void combine_kernel(DecodeParams p
 
 // Workgroups of decode_kernel that are resident at once on the current device.  Each workgroup
 // owns 1/NB of the units, so the grid must never exceed what runs concurrently.
-template <int KB, int G, bool KPC, int NP, int SCH>
+template <int KB, int G, bool KPC, int NP, int SCH, bool MQ>
 int decode_resident_blocks(size_t lds) {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<KB, G, KPC, NP, SCH>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<KB, G, KPC, NP, SCH, MQ>,
                                                    256, lds) != hipSuccess)
     return 0;
   return cus * per_cu;
 }
 
-template <int KB, int G, bool KPC, int NP, int SCH>
+template <int KB, int G, bool KPC, int NP, int SCH, bool MQ>
 hipError_t launch_decode_t(const DecodeParams& p0, hipStream_t s) {
   DecodeParams p = p0;
   const size_t lds = DecodeLds::bytes(p.c.B);
-  const int resident = decode_resident_blocks<KB, G, KPC, NP, SCH>(lds);
+  const int resident = decode_resident_blocks<KB, G, KPC, NP, SCH, MQ>(lds);
   if (resident <= 0) return hipErrorInvalidConfiguration;
   if (p.nblocks > resident) p.nblocks = resident;
-  decode_kernel<KB, G, KPC, NP, SCH><<<p.nblocks, 256, lds, s>>>(p);
+  decode_kernel<KB, G, KPC, NP, SCH, MQ><<<p.nblocks, 256, lds, s>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // slices: about one per 4 partials a segment has on average, 32 outputs per slice at most
-  const int avg = p.nblocks / (p.c.B * p.c.H);
+  const int avg = p.nblocks / (p.c.B * p.c.H * p.nqb);
   int slices = 1;
   while (slices < 16 && slices * 2 <= avg / 4 && (G * D) / (slices * 2) >= 32) slices *= 2;
-  const dim3 grid(p.c.B * p.c.H, slices);
+  const dim3 grid(p.c.B * p.c.H * p.nqb, slices);
   switch (slices) {
     case 1: combine_kernel<G, 1><<<grid, COMBINE_THREADS, 0, s>>>(p); break;
     case 2: combine_kernel<G, 2><<<grid, COMBINE_THREADS, 0, s>>>(p); break;
@@ -1236,22 +1265,22 @@ hipError_t launch_decode_t(const DecodeParams& p0, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int KB, int SCH>
-hipError_t launch_decode_bits(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s) {
+template <int KB, int SCH, bool MQ>
+hipError_t launch_decode_mq(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s) {
   if constexpr (KB == 16 || SCH == KVQ_FP8) {  // whole-row formats: at most 16 PV rows
     if (kpc || NP != 1) return hipErrorInvalidValue;
     switch (G) {
-      case 1: return launch_decode_t<KB, 1, false, 1, SCH>(p, s);
-      case 2: return launch_decode_t<KB, 2, false, 1, SCH>(p, s);
-      case 4: return launch_decode_t<KB, 4, false, 1, SCH>(p, s);
-      case 8: return launch_decode_t<KB, 8, false, 1, SCH>(p, s);
+      case 1: return launch_decode_t<KB, 1, false, 1, SCH, MQ>(p, s);
+      case 2: return launch_decode_t<KB, 2, false, 1, SCH, MQ>(p, s);
+      case 4: return launch_decode_t<KB, 4, false, 1, SCH, MQ>(p, s);
+      case 8: return launch_decode_t<KB, 8, false, 1, SCH, MQ>(p, s);
       default: return hipErrorInvalidValue;
     }
   } else {
 #define KVQ_CASE(GG, NN)                                                        \
   if (G == GG && NP == NN)                                                      \
-    return kpc ? launch_decode_t<KB, GG, true, NN, SCH>(p, s)                  \
-               : launch_decode_t<KB, GG, false, NN, SCH>(p, s);
+    return kpc ? launch_decode_t<KB, GG, true, NN, SCH, MQ>(p, s)              \
+               : launch_decode_t<KB, GG, false, NN, SCH, MQ>(p, s);
   KVQ_CASE(1, 1)
   KVQ_CASE(2, 1)
   KVQ_CASE(4, 1)
@@ -1261,6 +1290,14 @@ hipError_t launch_decode_bits(const DecodeParams& p, int G, int NP, bool kpc, hi
 #undef KVQ_CASE
     return hipErrorInvalidValue;
   }
+}
+
+// Single-query decode and multi-query decode are separate instantiations, so the single-query
+// kernel carries none of the query-block bookkeeping.
+template <int KB, int SCH>
+hipError_t launch_decode_bits(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s) {
+  return p.nqt > 1 ? launch_decode_mq<KB, SCH, true>(p, G, NP, kpc, s)
+                   : launch_decode_mq<KB, SCH, false>(p, G, NP, kpc, s);
 }
 
 }  // namespace kvq

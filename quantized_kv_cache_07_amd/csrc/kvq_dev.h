@@ -60,12 +60,16 @@ __device__ __forceinline__ long tile_index(const CacheDev& c, int b, int h, int 
 // Decode-attention launch parameters.
 struct DecodeParams {
   CacheDev c;
-  const uint16_t* q;  // [B][Hq][D] bf16
-  float* out;         // [B][Hq][D] fp32
+  const uint16_t* q;  // [B][nqt][Hq][D] bf16
+  float* out;         // [B][nqt][Hq][D] fp32
   int32_t* ws_pre;    // [B + 1] prefix over sequences of work units (all kv heads)
   float* ws_part;     // [nblocks][2][G][PART_STRIDE] partial (max, sum, pad, pad, o[D])
   int Hq, max_tokens, nblocks;
   float sm_log2;      // sm_scale * log2(e)
+  // Queries per sequence: nqt query tokens, the last nqt cached tokens (1: single-query decode).
+  // A segment is one (sequence, kv head, query block) whose G rows are qbs query tokens x gkv
+  // query heads (G = qbs * gkv); nqb = ceil(nqt / qbs) query blocks per (sequence, kv head).
+  int nqt, qbs, nqb, gkv;
 };
 
 constexpr int PART_STRIDE = D + 4;

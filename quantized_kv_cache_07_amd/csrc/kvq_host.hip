@@ -129,7 +129,8 @@ CacheDev to_dev(const kvq_cache* c) {
 // contiguous range of units.  The workspace holds the unit prefix sum and two partial slots
 // per workgroup.
 struct WsLayout {
-  int G, nblocks;
+  int G, nblocks;  // G: rows of a segment (query tokens per block x query heads per kv head)
+  int qbs, nqb;    // query tokens per block, query blocks per (sequence, kv head)
   size_t pre_off, part_off, total;
 };
 
@@ -140,16 +141,34 @@ long units_bound(const kvq_cache* c, int max_tokens) {
 
 int device_cus();
 
-WsLayout ws_layout(const kvq_cache* c, int n_q_heads, int max_tokens) {
+// Query tokens per segment for multi-query decode: the largest power of two (at most the
+// next power of two >= n_q) that keeps the segment within 8 rows, 16 QK columns (one per key
+// group and row) and 32 PV rows (hi / lo part, value group, row).
+int query_block(const kvq_cache* c, int gkv, int n_q) {
+  if (n_q <= 1) return 1;
+  const bool whole_row = c->fmt.k.scheme == KVQ_FP8 || c->fmt.k.bits == 16;
+  const bool kpc = c->fmt.k.axis == KVQ_PER_CHANNEL;
+  const int ngk = kpc ? 2 : whole_row ? 1 : D / c->fmt.k.group;
+  const int ngv = whole_row ? 1 : D / c->fmt.v.group;
+  int qbs = 1;
+  while (qbs < n_q && gkv * qbs * 2 <= 8 && ngk * gkv * qbs * 2 <= 16 && 2 * ngv * gkv * qbs * 2 <= 32)
+    qbs *= 2;
+  return qbs;
+}
+
+WsLayout ws_layout(const kvq_cache* c, int n_q_heads, int max_tokens, int n_q = 1) {
   WsLayout w;
-  w.G = n_q_heads / c->n_kv_heads;
+  const int gkv = n_q_heads / c->n_kv_heads;
+  w.qbs = query_block(c, gkv, n_q);
+  w.nqb = (n_q + w.qbs - 1) / w.qbs;
+  w.G = gkv * w.qbs;
   long nb = static_cast<long>(device_cus()) * 4;
   if (const char* e = std::getenv("KVQ_DECODE_BLOCKS")) {
     const long v = std::atol(e);
     if (v >= 1 && v <= 65536) nb = v;
   }
   // at most one unit per wave is left idle: small batches get fewer, fuller workgroups
-  const long ub = (units_bound(c, max_tokens) + 3) / 4;
+  const long ub = (units_bound(c, max_tokens) * w.nqb + 3) / 4;
   if (nb > ub) nb = ub;
   if (nb < 1) nb = 1;
   w.nblocks = static_cast<int>(nb);
@@ -273,35 +292,50 @@ kvq_status kvq_flush_residual(const kvq_cache* cache, void* stream) {
 }
 
 size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t n_q_heads, int32_t max_tokens) {
-  if (check_cache(cache) != KVQ_OK || n_q_heads < 1 || max_tokens < 1 ||
-      n_q_heads % cache->n_kv_heads)
+  return kvq_decode_workspace_bytes_mq(cache, n_q_heads, 1, max_tokens);
+}
+
+size_t kvq_decode_workspace_bytes_mq(const kvq_cache* cache, int32_t n_q_heads, int32_t n_q,
+                                     int32_t max_tokens) {
+  if (check_cache(cache) != KVQ_OK || n_q_heads < 1 || max_tokens < 1 || n_q < 1 ||
+      n_q > max_tokens || n_q_heads % cache->n_kv_heads)
     return 0;
-  return ws_layout(cache, n_q_heads, max_tokens).total;
+  return ws_layout(cache, n_q_heads, max_tokens, n_q).total;
 }
 
 kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int32_t n_q_heads,
                                 float sm_scale, int32_t max_tokens, float* out, void* workspace,
                                 size_t workspace_bytes, void* stream) {
+  return kvq_decode_attention_mq(cache, q, 1, n_q_heads, sm_scale, max_tokens, out, workspace,
+                                 workspace_bytes, stream);
+}
+
+kvq_status kvq_decode_attention_mq(const kvq_cache* cache, const void* q, int32_t n_q,
+                                   int32_t n_q_heads, float sm_scale, int32_t max_tokens,
+                                   float* out, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
   kvq_status s = check_cache(cache);
   if (s != KVQ_OK) return s;
   if (!q || !out || !workspace || n_q_heads < 1 || max_tokens < 1) return KVQ_EINVAL;
+  if (n_q < 1 || n_q > max_tokens) return KVQ_EINVAL;
   if (n_q_heads % cache->n_kv_heads) return KVQ_EINVAL;
-  const int G = n_q_heads / cache->n_kv_heads;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return KVQ_ENOTSUP;
+  const int gkv = n_q_heads / cache->n_kv_heads;
+  if (gkv != 1 && gkv != 2 && gkv != 4 && gkv != 8) return KVQ_ENOTSUP;
   const bool kpc = cache->fmt.k.axis == KVQ_PER_CHANNEL;
   // groups per row: FP8 and BF16 rows have one scale (or none) for all 128 channels
   const bool whole_row = cache->fmt.k.scheme == KVQ_FP8 || cache->fmt.k.bits == 16;
   const int kgroup = whole_row ? D : cache->fmt.k.group;
   const int vgroup = whole_row ? D : cache->fmt.v.group;
-  if (!kpc && (D / kgroup) * G > 16) return KVQ_ENOTSUP;
+  if (!kpc && (D / kgroup) * gkv > 16) return KVQ_ENOTSUP;
   if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVQ_EALIGN;
-  const WsLayout w = ws_layout(cache, n_q_heads, max_tokens);
+  const WsLayout w = ws_layout(cache, n_q_heads, max_tokens, n_q);
   if (workspace_bytes < w.total) return KVQ_ENOSPACE;
+  const int G = w.G;
   const int ngv = D / vgroup;
-  const int rows = 2 * G * ngv;  // PV rows: (hi/lo part, value group, query head)
+  const int rows = 2 * G * ngv;  // PV rows: (hi/lo part, value group, row)
   if (rows > 32) return KVQ_ENOTSUP;
   const int NP = rows > 16 ? 2 : 1;
-  if (units_bound(cache, max_tokens) * 64 >= (1L << 31)) return KVQ_ENOTSUP;
+  if (units_bound(cache, max_tokens) * w.nqb * 64 >= (1L << 31)) return KVQ_ENOTSUP;
 
   DecodeParams p;
   p.c = to_dev(cache);
@@ -314,11 +348,15 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int32_t n
   p.max_tokens = max_tokens;
   p.nblocks = w.nblocks;
   p.sm_log2 = sm_scale * 1.4426950408889634f;
+  p.nqt = n_q;
+  p.qbs = w.qbs;
+  p.nqb = w.nqb;
+  p.gkv = gkv;
 
   if (std::getenv("KVQ_DEBUG"))
-    fprintf(stderr, "[kvq] decode B=%d H=%d G=%d bits=%d NP=%d kpc=%d blocks=%d ws=%zu\n",
-            cache->batch, cache->n_kv_heads, G, cache->fmt.k.bits, NP, kpc ? 1 : 0, w.nblocks,
-            w.total);
+    fprintf(stderr, "[kvq] decode B=%d H=%d G=%d (n_q %d, %d per block) bits=%d NP=%d kpc=%d blocks=%d ws=%zu\n",
+            cache->batch, cache->n_kv_heads, G, n_q, w.qbs, cache->fmt.k.bits, NP, kpc ? 1 : 0,
+            w.nblocks, w.total);
   const hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
   const bool asym = cache->fmt.k.scheme == KVQ_ASYM;

@@ -29,7 +29,8 @@ STATUS = {0: "KVQ_OK", 1: "KVQ_EINVAL", 2: "KVQ_ENOTSUP", 3: "KVQ_EALIGN", 4: "K
 
 # Every function declared in include/kvq.h and include/kvq_measure.h.
 EXPORTS = ["kvq_buffer_bytes", "kvq_check_format", "kvq_quantize_append", "kvq_flush_residual",
-           "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_read_error",
+           "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_decode_workspace_bytes_mq",
+           "kvq_decode_attention_mq", "kvq_read_error",
            "kvq_status_str", "kvq_measure_read", "kvq_measure_read_sink_floats",
            "kvq_measure_copy"]
 
@@ -79,6 +80,9 @@ def _load() -> ctypes.CDLL:
     L.kvq_decode_workspace_bytes.argtypes = [P, i32, i32]
     L.kvq_decode_workspace_bytes.restype = sz
     L.kvq_decode_attention.argtypes = [P, P, i32, f32, i32, P, P, sz, P]
+    L.kvq_decode_workspace_bytes_mq.argtypes = [P, i32, i32, i32]
+    L.kvq_decode_workspace_bytes_mq.restype = sz
+    L.kvq_decode_attention_mq.argtypes = [P, P, i32, i32, f32, i32, P, P, sz, P]
     L.kvq_read_error.argtypes = [P, P, P]
     L.kvq_status_str.argtypes = [ctypes.c_int]
     L.kvq_status_str.restype = ctypes.c_char_p
@@ -86,7 +90,8 @@ def _load() -> ctypes.CDLL:
     L.kvq_measure_read_sink_floats.restype = i32
     L.kvq_measure_copy.argtypes = [P, P, sz, P]
     for f in ("kvq_check_format", "kvq_quantize_append", "kvq_flush_residual",
-              "kvq_decode_attention", "kvq_read_error", "kvq_measure_read", "kvq_measure_copy"):
+              "kvq_decode_attention", "kvq_decode_attention_mq", "kvq_read_error",
+              "kvq_measure_read", "kvq_measure_copy"):
         getattr(L, f).restype = ctypes.c_int
     return L
 
@@ -243,6 +248,33 @@ def decode_attention(cache: Cache, q: torch.Tensor, max_tokens: int, out: torch.
                                   max_tokens, out.data_ptr(), workspace.data_ptr(),
                                   workspace.numel(), _stream(stream))
     _check(st, "kvq_decode_attention")
+    return out
+
+
+def workspace_bytes_mq(cache: Cache, n_q_heads: int, n_q: int, max_tokens: int) -> int:
+    return lib.kvq_decode_workspace_bytes_mq(ctypes.byref(cache.desc), n_q_heads, n_q, max_tokens)
+
+
+def decode_attention_mq(cache: Cache, q: torch.Tensor, max_tokens: int,
+                        out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                        sm_scale: float | None = None, stream=None) -> torch.Tensor:
+    """q: bf16 [batch][n_q][H_q][128], the queries of each sequence's last n_q cached tokens
+    -> fp32 [batch][n_q][H_q][128] (causal)."""
+    assert q.dtype == torch.bfloat16 and q.is_contiguous() and q.dim() == 4
+    nq, hq = q.shape[1], q.shape[2]
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    need = workspace_bytes_mq(cache, hq, nq, max_tokens)
+    if need == 0:
+        raise KvqError(1, "kvq_decode_workspace_bytes_mq")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = lib.kvq_decode_attention_mq(ctypes.byref(cache.desc), q.data_ptr(), nq, hq,
+                                     float(sm_scale), max_tokens, out.data_ptr(),
+                                     workspace.data_ptr(), workspace.numel(), _stream(stream))
+    _check(st, "kvq_decode_attention_mq")
     return out
 
 

@@ -167,3 +167,27 @@ def compare_attention(pr: Pair, q_seed_step: int = 0, max_tokens: int | None = N
     assert ok.all(), (f"attention: {int((~ok).sum())} of {ok.size} outside tolerance; "
                       f"max abs err {err.max():.3e} at {np.unravel_index(err.argmax(), err.shape)}")
     return float(err.max()), got
+
+
+def mq_queries(pr: Pair, n_q: int, q_seed_step: int = 7):
+    """bf16 [B][n_q][H_q][128] queries for the last n_q cached tokens of every sequence."""
+    dev = pr.cache.n_quant.device
+    return torch.stack([ki.queries(pr.w, q_seed_step + i, dev) for i in range(n_q)], dim=1).contiguous()
+
+
+def compare_attention_mq(pr: Pair, n_q: int, q_seed_step: int = 7, max_tokens: int | None = None):
+    """Multi-query decode of the last n_q cached tokens against the oracle (causal)."""
+    K = kvq()
+    q = mq_queries(pr, n_q, q_seed_step)
+    mt = max_tokens or max(s.n_quant + s.n_res for s in pr.seqs)
+    out = K.decode_attention_mq(pr.cache, q, max_tokens=mt, sm_scale=SM_SCALE)
+    torch.cuda.synchronize()
+    assert K.read_error(pr.cache) == 0
+    got = out.cpu().numpy()
+    qb = ki.bf16_bits(q)
+    ref = np.stack([s.attend_mq(qb[b], SM_SCALE) for b, s in enumerate(pr.seqs)])
+    err = np.abs(got - ref)
+    ok = err <= ATOL + RTOL * np.abs(ref)
+    assert ok.all(), (f"multi-query attention: {int((~ok).sum())} of {ok.size} outside tolerance; "
+                      f"max abs err {err.max():.3e} at {np.unravel_index(err.argmax(), err.shape)}")
+    return float(err.max()), got

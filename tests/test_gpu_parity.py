@@ -199,3 +199,42 @@ def test_prefix_shared_blocks_are_read_not_written():
     assert all(np.array_equal(x, y) for x, y in zip(before, after))
     assert cache.n_quant.tolist() == [s0.n_quant, s1.n_quant] == [P + R, P + R]
     kc.compare_attention(pr)
+
+
+MQ_CASES = [
+    # name, k, v, B, Hq, H, R, lens, paged, n_q (queries per sequence)
+    ("mq-int4-gqa4-window", SYM4, SYM4, 2, 8, 2, 32, [777, 190], False, 16),
+    ("mq-int8-mha-paged", SYM8, SYM8, 3, 4, 4, 0, [300, 17, 1031], True, 5),
+    ("mq-kivi-int2", KPC2, ASYM2_32, 2, 8, 2, 128, [700, 1300], False, 8),
+    ("mq-fp8-gqa8-paged", FP8H, FP8H, 1, 16, 2, 16, [600], True, 3),
+    ("mq-bf16-gqa2", BF16, BF16, 2, 4, 2, 0, [333, 64], False, 16),
+]
+
+
+@pytest.mark.parametrize("name,k,v,B,Hq,H,R,lens,paged,nq", MQ_CASES, ids=[c[0] for c in MQ_CASES])
+def test_multi_query_decode(name, k, v, B, Hq, H, R, lens, paged, nq):
+    """Multi-query decode: append the n_q query tokens (single-token steps, so windows flush
+    where due), then attend with each query seeing the tokens up to its own."""
+    announce(test="multi_query", name=name)
+    pr = kc.build_pair(k, v, B, Hq, H, R, lens, paged=paged, seed=zlib.crc32(name.encode()) % 1000,
+                       extra_tokens=64 + nq)
+    for _ in range(nq):
+        kc.step(pr)
+    kc.compare_state(pr)
+    kc.compare_attention_mq(pr, nq)
+
+
+def test_multi_query_edges():
+    """n_q = 1 is single-query decode bit for bit; queries that precede every cached token of
+    their sequence (a sequence shorter than n_q) get zeros."""
+    announce(test="multi_query_edges")
+    K = kc.kvq()
+    pr = kc.build_pair(SYM4, SYM4, 3, 8, 2, 16, [50, 3, 200], seed=31, extra_tokens=80)
+    q1 = kc.mq_queries(pr, 1)
+    mt = max(s.n_quant + s.n_res for s in pr.seqs)
+    a = K.decode_attention_mq(pr.cache, q1, max_tokens=mt, sm_scale=kc.SM_SCALE)
+    b_ = K.decode_attention(pr.cache, q1[:, 0].contiguous(), max_tokens=mt, sm_scale=kc.SM_SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(a[:, 0], b_)
+    _, got = kc.compare_attention_mq(pr, 6)
+    assert np.all(got[1, :3] == 0) and np.any(got[1, 3] != 0)  # sequence 1 holds 3 tokens
