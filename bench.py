@@ -406,6 +406,87 @@ def sweep_crossover(batches, lengths, calls_per_graph: int = 20, replays: int = 
     return rows
 
 
+def sweep_multiquery(batch: int, tokens: int, nqs, calls_per_graph: int = 10,
+                     replays: int = 5) -> list[dict]:
+    """Device time of one multi-query decode call (n_q query tokens per sequence, causal, the
+    last n_q cached tokens) per format, against n_q single-query calls, H_q = 32, H_kv = 8,
+    contiguous caches of `tokens` tokens without a window (HIP-graph replay)."""
+    import torch
+
+    import kvq_inputs as ki
+    from quantized_kv_cache_07_amd import kvq
+
+    rows = []
+    for name, side in SWEEP_FORMATS.items():
+        w = ki.Workload(f"mq-{name}", 13, batch, 32, 8, tokens, ki.Side(*side), ki.Side(*side))
+        cap = -(-(tokens + 16) // 16) * 16
+        f8 = {"fp8_scales": ([5.0 / 448] * 8, [5.0 / 448] * 8)} if side[1] == 2 else {}
+        cache = kvq.Cache(side, side, batch, 8, residual=0, capacity=cap, **f8)
+        for b in range(batch):
+            k, v = ki.prefill_kv(w, b, tokens, device="cuda")
+            kvq.quantize_append(cache, k[None].contiguous(), v[None].contiguous(), desc=cache.sequence(b))
+        single = None
+        for nq in nqs:
+            q = torch.stack([ki.queries(w, i, "cuda") for i in range(nq)], dim=1).contiguous()
+            out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+            ws = torch.empty(kvq.workspace_bytes_mq(cache, 32, nq, tokens), dtype=torch.uint8,
+                             device="cuda")
+            kvq.decode_attention_mq(cache, q, tokens, out=out, workspace=ws)
+            torch.cuda.synchronize()
+            if kvq.read_error(cache):
+                raise RuntimeError(f"device error in multi-query sweep {name} n_q={nq}")
+            ref = out.clone()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(calls_per_graph):
+                    kvq.decode_attention_mq(cache, q, tokens, out=out, workspace=ws)
+            g.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(out, ref):
+                raise RuntimeError(f"graph replay differs from the eager call ({name} n_q={nq})")
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(replays):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (replays * calls_per_graph)
+            if nq == 1:
+                single = us
+            row = {"format": name, "batch": batch, "tokens": tokens, "n_q": nq,
+                   "us_per_call": round(us, 2),
+                   "query_tokens_per_s": round(batch * nq / (us * 1e-6), 1),
+                   "vs_separate_calls": round(nq * single / us, 3) if single else None,
+                   "cache_gbs": round(attention_bytes(w, [tokens] * batch, [0] * batch) / (us * 1e-6) / 1e9, 1)}
+            rows.append(row)
+            print(json.dumps(row), flush=True)
+            del g
+        del cache
+        torch.cuda.empty_cache()
+    return rows
+
+
+def multiquery_table(rows: list[dict], command: str) -> str:
+    fmts = list(SWEEP_FORMATS)
+    B, T = rows[0]["batch"], rows[0]["tokens"]
+    out = ["# Multi-query decode over the quantized cache (MI355X, one GPU)", "",
+           "Command (from the repository root on the GPU box):", "", f"    {command}", "",
+           f"Device time of one causal multi-query `kvq_decode_attention_mq` call (HIP-graph "
+           f"replay), batch {B}, {T} cached tokens per sequence, H_q = 32, H_kv = 8, contiguous, "
+           f"no window; in parentheses the speed-up over n_q single-query calls.", "",
+           "| n_q | " + " | ".join(f"{f} µs" for f in fmts) + " |", "|---|" + "---|" * len(fmts)]
+    by = {}
+    for r in rows:
+        by.setdefault(r["n_q"], {})[r["format"]] = r
+    for nq, d in sorted(by.items()):
+        cells = []
+        for f in fmts:
+            r = d.get(f)
+            cells.append("—" if r is None else f"{r['us_per_call']:.1f} ({r['vs_separate_calls']:.2f}×)")
+        out.append(f"| {nq} | " + " | ".join(cells) + " |")
+    return "\n".join(out) + "\n"
+
+
 def sweep_table(rows: list[dict], command: str) -> str:
     fmts = list(SWEEP_FORMATS)
     out = ["# Decode attention: BF16 against quantized caches (MI355X, one GPU)", "",
@@ -444,7 +525,7 @@ def main() -> int:
     ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV",
                     help="print a text summary of a rocprofv3 --stats kernel table")
     ap.add_argument("--command", default="", help="the profiling command, recorded in summaries")
-    ap.add_argument("--sweep", choices=["crossover"],
+    ap.add_argument("--sweep", choices=["crossover", "multiquery"],
                     help="instead of the step benchmark: BF16 vs quantized decode-attention sweep")
     ap.add_argument("--sweep-batches", default="1,16")
     ap.add_argument("--sweep-lengths", default="512,2048,8192,32768,131072")
@@ -474,6 +555,11 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if a.sweep == "multiquery":
+        rows = sweep_multiquery(16, 32768, [1, 2, 4, 8, 16])
+        if a.sweep_out:
+            open(a.sweep_out, "w").write(multiquery_table(rows, a.command or "python bench.py --sweep multiquery"))
+        return 0
     if a.sweep == "crossover":
         rows = sweep_crossover([int(x) for x in a.sweep_batches.split(",")],
                                [int(x) for x in a.sweep_lengths.split(",")])
