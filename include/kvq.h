@@ -43,7 +43,11 @@
  *   codes       offset binary: symmetric q in [-Q, Q] is stored as q + 2^(bits-1); asymmetric
  *               codes are stored as they are (0 .. 2^bits - 1); FP8 codes are E4M3 bytes; bits
  *               16 stores the bf16 elements.
- *   scales/zeros fp16.  Per-token groups: [tile][head_dim / group][16].  Per-channel key groups:
+ *   scales/zeros fp16.  Per-token groups: [tile][head_dim / group][16]; when both sides use
+ *               per-token groups they share one record per tile in k_scale (and k_zero):
+ *               [tile][head_dim / k_group + head_dim / v_group][16], the key rows then the value
+ *               rows, so a tile's rows are one contiguous run (one 128-byte line for 4-bit groups
+ *               of 64); v_scale / v_zero are then unused (NULL, 0 bytes).  Per-channel key groups:
  *               contiguous [b][h][capacity / group][head_dim]; paged [block][h][head_dim], the
  *               row of key group tau kept with the block of its first token,
  *               block_table[b][tau * group / 16] (other blocks' rows are unused).  FP8: fp32

@@ -55,7 +55,9 @@
  *   slices      a tile is 64 slices of 4 * bits bytes, stored in pieces of S = min(16, 4 bits)
  *               bytes: piece i of slice s at byte 64 S i + S s of the tile (slab i), so the
  *               slices' piece i form one contiguous run (for bits <= 4 a slice is one piece)
- *   scales/zeros per-token groups: fp16 [tile][d / G][16]
+ *   scales/zeros per-token groups: fp16 [tile][d / G][16]; when both sides use per-token groups
+ *               they share one record per tile in the key buffers, [tile][d/Gk + d/Gv][16]:
+ *               the key rows, then the value rows (one 128-byte line for 4-bit groups of 64)
  *               per-channel key groups: contiguous fp16 [b][h][cap / Gt][d]; paged fp16
  *               [block][h][d], the row of key group tau kept with the block that holds the
  *               group's first token (block_table[b][tau * Gt / 16]), so blocks shared between
@@ -570,17 +572,22 @@ void orc_pack(const orc_seq *s, int32_t b, const int32_t *table_row, uint8_t *kc
           put_field(vtile, orc_v_bit(s->v.bits, d, p % 16, c), s->v.bits, s->vu[e]);
       }
       if (s->k.bits == 16 || s->k.scheme == ORC_FP8) continue; /* no per-slot metadata */
-      if (s->k.axis == ORC_PER_TOKEN) {
+      /* shared record: key rows then value rows of each tile in the key buffers */
+      int shared = s->k.axis == ORC_PER_TOKEN;
+      int rows = shared ? ngk + ngv : ngv;
+      uint16_t *vs_img = shared ? ksc : vsc, *vz_img = shared ? kzc : vzc;
+      int v0 = shared ? ngk : 0;
+      if (shared) {
         for (int g = 0; g < ngk; g++) {
           size_t mi = meta_index(s, &s->k, h, p, g * s->k.group);
-          ksc[(tile * ngk + g) * 16 + p % 16] = s->ks[mi];
-          if (s->k.scheme == ORC_ASYM) kzc[(tile * ngk + g) * 16 + p % 16] = s->kz[mi];
+          ksc[(tile * rows + g) * 16 + p % 16] = s->ks[mi];
+          if (s->k.scheme == ORC_ASYM) kzc[(tile * rows + g) * 16 + p % 16] = s->kz[mi];
         }
       }
       for (int g = 0; g < ngv; g++) {
         size_t mi = meta_index(s, &s->v, h, p, g * s->v.group);
-        vsc[(tile * ngv + g) * 16 + p % 16] = s->vs[mi];
-        if (s->v.scheme == ORC_ASYM) vzc[(tile * ngv + g) * 16 + p % 16] = s->vz[mi];
+        vs_img[(tile * rows + v0 + g) * 16 + p % 16] = s->vs[mi];
+        if (s->v.scheme == ORC_ASYM) vz_img[(tile * rows + v0 + g) * 16 + p % 16] = s->vz[mi];
       }
     }
     if (s->k.bits != 16 && s->k.scheme != ORC_FP8 && s->k.axis == ORC_PER_CHANNEL) {

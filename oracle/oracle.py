@@ -315,12 +315,14 @@ def empty_images(k_side, v_side, batch: int, n_kv_heads: int, residual: int, cap
             continue
         if axis == PER_TOKEN:
             n = tiles * (d // group) * TILE
+            if k_side[2] == PER_TOKEN:  # both per-token: one record per tile in the key buffers
+                n = tiles * (d // k_side[3] + d // v_side[3]) * TILE if name == "k" else 0
         elif num_blocks:  # paged per-channel keys: one metadata row per (block, head)
             n = num_blocks * H * d
         else:
             n = batch * H * (capacity // group) * d
         out[f"{name}_scale"] = np.zeros(n, np.uint16)
-        out[f"{name}_zero"] = np.zeros(n if scheme == ASYM else 1, np.uint16)
+        out[f"{name}_zero"] = np.zeros(n if scheme == ASYM else (1 if n else 0), np.uint16)
         out[f"{name}_res"] = np.zeros(batch * H * max(residual, 1) * d, np.uint16)
     return out
 

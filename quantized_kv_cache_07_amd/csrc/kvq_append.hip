@@ -345,7 +345,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(CacheDev c, const uint16_
       const int slot = lo + it / ngk, g = it % ngk;
       bool ok = true;
       const long tile = tile_index(c, b, h, slot / TILE, ok);
-      const size_t idx = (static_cast<size_t>(tile) * ngk + g) * TILE + slot % TILE;
+      const size_t idx = static_cast<size_t>(tile) * c.ks_tile + g * TILE + slot % TILE;
       c.ks[idx] = mk_s[(slot - seg0) * 4 + g];
       if (K.scheme == KVQ_ASYM) c.kz[idx] = mk_z[(slot - seg0) * 4 + g];
     }
@@ -365,7 +365,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(CacheDev c, const uint16_
     const int slot = lo + it / ngv, g = it % ngv;
     bool ok = true;
     const long tile = tile_index(c, b, h, slot / TILE, ok);
-    const size_t idx = (static_cast<size_t>(tile) * ngv + g) * TILE + slot % TILE;
+    const size_t idx = static_cast<size_t>(tile) * c.vs_tile + g * TILE + slot % TILE;
     c.vs[idx] = mv_s[(slot - seg0) * 4 + g];
     if (V.scheme == KVQ_ASYM) c.vz[idx] = mv_z[(slot - seg0) * 4 + g];
   }

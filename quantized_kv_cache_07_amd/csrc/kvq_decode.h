@@ -684,7 +684,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
         } else {
 #pragma unroll
           for (int t = 0; t < 2; t++) {
-            const size_t tb = static_cast<size_t>(t ? pB : pA) * ngk * TILE;
+            const size_t tb = static_cast<size_t>(t ? pB : pA) * c.ks_tile;
             d.ks[t] = *reinterpret_cast<const uint2*>(c.ks + tb + ks_lane);
             if constexpr (ASYM) d.kz[t] = *reinterpret_cast<const uint2*>(c.kz + tb + ks_lane);
           }
@@ -698,7 +698,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
         if constexpr (!BF && !F8)
 #pragma unroll
         for (int t = 0; t < 2; t++) {
-          const size_t tb = static_cast<size_t>(t ? pB : pA) * ngv * TILE;
+          const size_t tb = static_cast<size_t>(t ? pB : pA) * c.vs_tile;
 #pragma unroll
           for (int pp = 0; pp < NP; pp++) {
             const unsigned lo = rgv[pp] * TILE + 4 * g;

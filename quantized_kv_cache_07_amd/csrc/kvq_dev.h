@@ -34,6 +34,10 @@ struct CacheDev {
   int32_t* n_quant;
   int32_t* n_res;
   int32_t* err;
+  // Per-token scale (and zero) rows: fp16 elements from one tile's rows to the next.  When both
+  // sides use per-token groups they share one record per tile in the key buffers (key rows,
+  // then value rows) and vs / vz point at the value rows of tile 0.
+  int ks_tile, vs_tile;
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

@@ -25,6 +25,13 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Both sides use per-token groups: their scale (and zero) rows share one record per tile in
+// the key buffers, so the rows of a tile are one contiguous run (one 128-byte line for 4-bit
+// groups of 64) instead of two half-used lines.
+bool shared_scale_records(const kvq_format& f) {
+  return f.k.bits != 16 && f.k.scheme != KVQ_FP8 && f.k.axis == KVQ_PER_TOKEN;
+}
+
 kvq_status check_side(const kvq_side& s, bool is_key, int residual) {
   if (s.scheme == KVQ_FP8) {  // E4M3 bytes, one fp32 scale per tensor or kv head
     if (s.bits != 8 || (s.axis != KVQ_PER_TENSOR && s.axis != KVQ_PER_HEAD) || s.group != 0)
@@ -75,11 +82,12 @@ kvq_status check_cache(const kvq_cache* c) {
     if (c->fmt.k.axis == KVQ_PER_CHANNEL && c->capacity % c->fmt.k.group != 0) return KVQ_EINVAL;
   }
   const bool scaled = c->fmt.k.bits != 16;
-  if (!c->k_codes || !c->v_codes || (scaled && (!c->k_scale || !c->v_scale)) || !c->n_quant ||
-      !c->n_res || !c->err)
+  const bool shared = shared_scale_records(c->fmt);  // value rows live in the key buffers
+  if (!c->k_codes || !c->v_codes || (scaled && !c->k_scale) ||
+      (scaled && !shared && !c->v_scale) || !c->n_quant || !c->n_res || !c->err)
     return KVQ_EINVAL;
   if (c->fmt.k.scheme == KVQ_ASYM && !c->k_zero) return KVQ_EINVAL;
-  if (c->fmt.v.scheme == KVQ_ASYM && !c->v_zero) return KVQ_EINVAL;
+  if (c->fmt.v.scheme == KVQ_ASYM && !shared && !c->v_zero) return KVQ_EINVAL;
   if (c->fmt.residual > 0 && (!c->k_res || !c->v_res)) return KVQ_EINVAL;
   // kernels index 16-slot tiles with 32-bit integers
   const long tiles = c->block_table ? static_cast<long>(c->num_blocks) * c->n_kv_heads
@@ -116,6 +124,19 @@ CacheDev to_dev(const kvq_cache* c) {
   d.vs = c->v_scale;
   d.kz = c->k_zero;
   d.vz = c->v_zero;
+  d.ks_tile = d.vs_tile = 0;
+  const bool rows = c->fmt.k.bits != 16 && c->fmt.k.scheme != KVQ_FP8;  // per-slot scale rows
+  if (rows) {
+    const int ngv = D / c->fmt.v.group;
+    if (shared_scale_records(c->fmt)) {
+      const int ngk = D / c->fmt.k.group;
+      d.ks_tile = d.vs_tile = (ngk + ngv) * TILE;
+      d.vs = c->k_scale + ngk * TILE;
+      d.vz = c->k_zero ? c->k_zero + ngk * TILE : nullptr;
+    } else {
+      d.vs_tile = ngv * TILE;
+    }
+  }
   d.kres = c->k_res;
   d.vres = c->v_res;
   d.n_quant = c->n_quant;
@@ -254,6 +275,10 @@ size_t kvq_buffer_bytes(const kvq_format* fmt, int32_t batch, int32_t n_kv_heads
         return (s.axis == KVQ_PER_HEAD ? static_cast<size_t>(n_kv_heads) : 1) * sizeof(float);
       }
       if ((which == KVQ_BUF_K_ZERO || which == KVQ_BUF_V_ZERO) && s.scheme != KVQ_ASYM) return 0;
+      if (shared_scale_records(*fmt)) {  // one record per tile in the key buffers
+        if (which == KVQ_BUF_V_SCALE || which == KVQ_BUF_V_ZERO) return 0;
+        return tiles * (D / fmt->k.group + D / fmt->v.group) * TILE * 2;
+      }
       if (s.axis == KVQ_PER_TOKEN) return tiles * (D / s.group) * TILE * 2;
       if (paged) return static_cast<size_t>(num_blocks) * n_kv_heads * D * 2;  // per block
       if (capacity % s.group) return 0;

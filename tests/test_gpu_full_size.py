@@ -67,7 +67,7 @@ def _check_codes(st, cache, w, samples):
     kc = cache.k_codes.cpu().numpy()
     vc = cache.v_codes.cpu().numpy()
     ks = cache.k_scale.cpu().numpy().view(np.uint16)
-    vs = cache.v_scale.cpu().numpy().view(np.uint16)
+    vs = None if cache.v_scale is None else cache.v_scale.cpu().numpy().view(np.uint16)
     kz = None if cache.k_zero is None else cache.k_zero.cpu().numpy().view(np.uint16)
     vz = None if cache.v_zero is None else cache.v_zero.cpu().numpy().view(np.uint16)
     d = 128
@@ -88,7 +88,13 @@ def _check_codes(st, cache, w, samples):
                         z16 = None
                     else:
                         s16, z16, u = oracle.quant_asym(xs, bits)
-                    mi = (tile * ng + g) * 16 + slot % 16
+                    # both sides per-token: one record per tile in the key buffers
+                    ngk_, ngv_ = d // w.k.group, d // w.v.group
+                    if w.k.axis == ki.PER_TOKEN:
+                        sc, zc = ks, kz
+                        mi = (tile * (ngk_ + ngv_) + (0 if side == "k" else ngk_) + g) * 16 + slot % 16
+                    else:
+                        mi = (tile * ng + g) * 16 + slot % 16
                     assert sc[mi] == s16, (side, b, h, slot, g, "scale")
                     if z16 is not None:
                         assert zc[mi] == z16, (side, b, h, slot, g, "zero")
