@@ -30,6 +30,7 @@
 
 #include <cfloat>
 #include <climits>
+#include <mutex>
 #include <type_traits>
 
 #include "kvq_dev.h"
@@ -1227,17 +1228,29 @@ __global__ __launch_bounds__(COMBINE_THREADS) void combine_kernel(DecodeParams p
 }
 
 // Workgroups of decode_kernel that are resident at once on the current device.  Each workgroup
-// owns 1/NB of the units, so the grid must never exceed what runs concurrently.
+// owns 1/NB of the units, so the grid must never exceed what runs concurrently.  The answer
+// depends on the device and the LDS size alone and is cached per instantiation.
 template <int KB, int G, bool KPC, int NP, int SCH, bool MQ>
 int decode_resident_blocks(size_t lds) {
+  static std::mutex mu;
+  static int cached_dev = -1, cached_blocks = 0;
+  static size_t cached_lds = 0;
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
+  {
+    std::lock_guard<std::mutex> g(mu);
+    if (dev == cached_dev && lds == cached_lds) return cached_blocks;
+  }
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<KB, G, KPC, NP, SCH, MQ>,
                                                    256, lds) != hipSuccess)
     return 0;
-  return cus * per_cu;
+  std::lock_guard<std::mutex> g(mu);
+  cached_dev = dev;
+  cached_lds = lds;
+  cached_blocks = cus * per_cu;
+  return cached_blocks;
 }
 
 template <int KB, int G, bool KPC, int NP, int SCH, bool MQ>
