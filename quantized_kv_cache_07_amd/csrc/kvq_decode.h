@@ -454,18 +454,119 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
     const int uq = (nq + 31) / 32;
     const int xend = kk + (uend - u);
 
-    // ---- stage the segment's G query rows (bf16): row v = query token qblk * qbs + v / gkv,
-    // query head h * gkv + v % gkv; rows past the last query token are zero ----
-    __syncthreads();
-    if (tid < G * (D / 8)) {
+    // ---- issue the segment's first loads before staging its query: the query rows, the
+    // block-table entries and the first unit's codes and scales are in flight together ----
+    uint4 qval = uint4{0u, 0u, 0u, 0u};  // query row v = query token qblk * qbs + v / gkv,
+    if (tid < G * (D / 8)) {             // query head h * gkv + v % gkv (zero past the last)
       const int v = tid / (D / 8), qg = qblk * qbs + v / gkv;
-      uint4 val = uint4{0u, 0u, 0u, 0u};
       if (qg < nqt)
-        val = reinterpret_cast<const uint4*>(
+        qval = reinterpret_cast<const uint4*>(
             p.q + ((static_cast<size_t>(b) * nqt + qg) * p.Hq +
                    static_cast<size_t>(h) * gkv + v % gkv) * D)[tid % (D / 8)];
-      reinterpret_cast<uint4*>(qs)[tid] = val;
     }
+    int x = kk + wave;
+    const int xq_end = min(xend, uq);
+
+    // PV row roles: row 16 pp + n is (part, value group, head hh)
+    int rpart[NP], rgv[NP];
+#pragma unroll
+    for (int pp = 0; pp < NP; pp++) {
+      const int row = 16 * pp + n;
+      rpart[pp] = row / (G * ngv);
+      rgv[pp] = (row / G) % ngv;
+    }
+
+    const int seq_tile0 = (b * H + h) * (c.cap / TILE);  // < 2^31 tiles (host check)
+    const int* trow = c.table ? c.table + static_cast<size_t>(b) * c.max_blocks : nullptr;
+    // physical tile of sequence tile t, or -1 for an unusable block-table entry
+    auto phys_of = [&](int t) -> int {
+      if (!trow) return seq_tile0 + t;
+      const int blk = ld_uniform(trow + t);
+      if (blk < 0 || blk >= c.num_blocks) return -1;
+      return blk * H + h;
+    };
+    // Per-channel keys: lane l folds the eight channels of QK MFMA block (g', j') = (blk / 4,
+    // blk % 4), blk = l % 16, for head l / 16 (and + 4): channels 32 g' + kchan(j', 0..7), which
+    // are the run 8 blk .. 8 blk + 7 (8- and 4-bit) or two runs of four (2-bit).
+    const int fold_blk = lane & 15;
+    const int fold_c0 = (KB == 2) ? 32 * (fold_blk / 4) + 16 * ((fold_blk % 4) / 2) + 4 * (fold_blk % 2)
+                                  : 8 * fold_blk;
+    // per-channel key group tau's metadata row: contiguous [b][h][cap / Gt], paged with the
+    // block of the group's first token (an unusable entry reads row 0; the block error is
+    // reported where the codes are read)
+    auto kpc_meta = [&](int tau) -> size_t {
+      if (!trow) return ((static_cast<size_t>(b) * H + h) * (c.cap / kgroup) + tau) * D + fold_c0;
+      const int blk = ld_uniform(trow + (tau * kgroup) / TILE);
+      const int pb_ = (blk < 0 || blk >= c.num_blocks) ? 0 : blk;
+      return (static_cast<size_t>(pb_) * H + h) * D + fold_c0;
+    };
+    auto load_meta8 = [&](const uint16_t* base, size_t mi) -> uint4 {
+      if constexpr (KB == 2) {
+        const uint2 a = *reinterpret_cast<const uint2*>(base + mi);
+        const uint2 bb = *reinterpret_cast<const uint2*>(base + mi + 8);
+        return uint4{a.x, a.y, bb.x, bb.y};
+      } else {
+        return *reinterpret_cast<const uint4*>(base + mi);
+      }
+    };
+    UnitData<KB, NP, KPC, ASYM> d{};
+    const UnpackRegs ur = unpack_regs<KB>();
+    bool bad_block = false;
+    // Every unit issues the same loads (an unusable or absent tile reads tile 0 of the buffer
+    // and is ignored), so the compiler can count outstanding loads exactly.
+    // Loads address a wave-uniform tile base (scalar registers) plus a 32-bit lane offset
+    // that is fixed for the segment, so no per-lane 64-bit address arithmetic is needed.
+    constexpr unsigned SP = (4 * KB < 16) ? 4 * KB : 16;  // bytes of a slice piece
+    const unsigned k_lane = SP * (4 * n + g);                // slice 4 n + g (token n)
+    const unsigned v_lane = SP * (16 * g + n);               // chunk 16 g + n
+    const unsigned ks_lane = cg * TILE + 4 * g;
+    auto load_k = [&](int xx, int pA, int pB) {
+      pA = max(pA, 0);
+      pB = max(pB, 0);
+      load_words<KB>(c.kc + static_cast<size_t>(pA) * TILE_BYTES + k_lane, d.kw[0]);
+      load_words<KB>(c.kc + static_cast<size_t>(pB) * TILE_BYTES + k_lane, d.kw[1]);
+      if constexpr (BF || F8) {
+      } else if constexpr (KPC) {
+        const size_t mi = kpc_meta((32 * xx) / kgroup);
+        d.fs = load_meta8(c.ks, mi);
+        if constexpr (ASYM) d.fz = load_meta8(c.kz, mi);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+          const size_t tb = static_cast<size_t>(t ? pB : pA) * c.ks_tile;
+          d.ks[t] = *reinterpret_cast<const uint2*>(c.ks + tb + ks_lane);
+          if constexpr (ASYM) d.kz[t] = *reinterpret_cast<const uint2*>(c.kz + tb + ks_lane);
+        }
+      }
+    };
+    auto load_v = [&](int pA, int pB) {
+      pA = max(pA, 0);
+      pB = max(pB, 0);
+      load_words<KB>(c.vc + static_cast<size_t>(pA) * TILE_BYTES + v_lane, d.vw[0]);
+      load_words<KB>(c.vc + static_cast<size_t>(pB) * TILE_BYTES + v_lane, d.vw[1]);
+      if constexpr (!BF && !F8)
+#pragma unroll
+      for (int t = 0; t < 2; t++) {
+        const size_t tb = static_cast<size_t>(t ? pB : pA) * c.vs_tile;
+#pragma unroll
+        for (int pp = 0; pp < NP; pp++) {
+          const unsigned lo = rgv[pp] * TILE + 4 * g;
+          d.vs[pp][t] = *reinterpret_cast<const uint2*>(c.vs + tb + lo);
+          if constexpr (ASYM) d.vz[pp][t] = *reinterpret_cast<const uint2*>(c.vz + tb + lo);
+        }
+      }
+    };
+    int pA = -1, pB = -1;
+    if (x < xq_end) {
+      pA = phys_of(2 * x);
+      pB = (32 * x + 16 < nq) ? phys_of(2 * x + 1) : -1;
+      load_k(x, pA, pB);
+      load_v(pA, pB);
+    }
+
+    // ---- stage the segment's G query rows (bf16) ----
+    __syncthreads();
+    if (tid < G * (D / 8)) reinterpret_cast<uint4*>(qs)[tid] = qval;
     __syncthreads();
     // causal limit (multi-query): the block's first query token sees the first lim_min cached
     // tokens (the query tokens are the last nqt), column n's token lim_min + hh / gkv of them;
@@ -530,15 +631,6 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
     float zacc[NP];
 #pragma unroll
     for (int pp = 0; pp < NP; pp++) zacc[pp] = 0.0f;
-
-    // PV row roles: row 16 pp + n is (part, value group, head hh)
-    int rpart[NP], rgv[NP];
-#pragma unroll
-    for (int pp = 0; pp < NP; pp++) {
-      const int row = 16 * pp + n;
-      rpart[pp] = row / (G * ngv);
-      rgv[pp] = (row / G) % ngv;
-    }
 
     // ---- online softmax over the 8 raw scores of a pair; returns the weights in s2 ----
     // m_run is in log2 units; weights are exp2(score * sm_log2 - m_run).  The running max starts
@@ -611,44 +703,8 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
       }
     };
 
-    int x = kk + wave;
-    const int xq_end = min(xend, uq);
-
     // ---------------------------- compressed units ----------------------------
     if (x < xq_end) {
-      const int seq_tile0 = (b * H + h) * (c.cap / TILE);  // < 2^31 tiles (host check)
-      const int* trow = c.table ? c.table + static_cast<size_t>(b) * c.max_blocks : nullptr;
-      // physical tile of sequence tile t, or -1 for an unusable block-table entry
-      auto phys_of = [&](int t) -> int {
-        if (!trow) return seq_tile0 + t;
-        const int blk = ld_uniform(trow + t);
-        if (blk < 0 || blk >= c.num_blocks) return -1;
-        return blk * H + h;
-      };
-      // Per-channel keys: lane l folds the eight channels of QK MFMA block (g', j') = (blk / 4,
-      // blk % 4), blk = l % 16, for head l / 16 (and + 4): channels 32 g' + kchan(j', 0..7), which
-      // are the run 8 blk .. 8 blk + 7 (8- and 4-bit) or two runs of four (2-bit).
-      const int fold_blk = lane & 15;
-      const int fold_c0 = (KB == 2) ? 32 * (fold_blk / 4) + 16 * ((fold_blk % 4) / 2) + 4 * (fold_blk % 2)
-                                    : 8 * fold_blk;
-      // per-channel key group tau's metadata row: contiguous [b][h][cap / Gt], paged with the
-      // block of the group's first token (an unusable entry reads row 0; the block error is
-      // reported where the codes are read)
-      auto kpc_meta = [&](int tau) -> size_t {
-        if (!trow) return ((static_cast<size_t>(b) * H + h) * (c.cap / kgroup) + tau) * D + fold_c0;
-        const int blk = ld_uniform(trow + (tau * kgroup) / TILE);
-        const int pb_ = (blk < 0 || blk >= c.num_blocks) ? 0 : blk;
-        return (static_cast<size_t>(pb_) * H + h) * D + fold_c0;
-      };
-      auto load_meta8 = [&](const uint16_t* base, size_t mi) -> uint4 {
-        if constexpr (KB == 2) {
-          const uint2 a = *reinterpret_cast<const uint2*>(base + mi);
-          const uint2 bb = *reinterpret_cast<const uint2*>(base + mi + 8);
-          return uint4{a.x, a.y, bb.x, bb.y};
-        } else {
-          return *reinterpret_cast<const uint4*>(base + mi);
-        }
-      };
       // the query of the folding lane's channels, in MFMA element order, as f32 (per segment)
       float qfold[(G + 3) / 4][8];
       if constexpr (KPC) {
@@ -661,53 +717,6 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
         }
       }
 
-      UnitData<KB, NP, KPC, ASYM> d{};
-      const UnpackRegs ur = unpack_regs<KB>();
-      bool bad_block = false;
-      // Every unit issues the same loads (an unusable or absent tile reads tile 0 of the buffer
-      // and is ignored), so the compiler can count outstanding loads exactly.
-      // Loads address a wave-uniform tile base (scalar registers) plus a 32-bit lane offset
-      // that is fixed for the segment, so no per-lane 64-bit address arithmetic is needed.
-      constexpr unsigned SP = (4 * KB < 16) ? 4 * KB : 16;  // bytes of a slice piece
-      const unsigned k_lane = SP * (4 * n + g);                // slice 4 n + g (token n)
-      const unsigned v_lane = SP * (16 * g + n);               // chunk 16 g + n
-      const unsigned ks_lane = cg * TILE + 4 * g;
-      auto load_k = [&](int xx, int pA, int pB) {
-        pA = max(pA, 0);
-        pB = max(pB, 0);
-        load_words<KB>(c.kc + static_cast<size_t>(pA) * TILE_BYTES + k_lane, d.kw[0]);
-        load_words<KB>(c.kc + static_cast<size_t>(pB) * TILE_BYTES + k_lane, d.kw[1]);
-        if constexpr (BF || F8) {
-        } else if constexpr (KPC) {
-          const size_t mi = kpc_meta((32 * xx) / kgroup);
-          d.fs = load_meta8(c.ks, mi);
-          if constexpr (ASYM) d.fz = load_meta8(c.kz, mi);
-        } else {
-#pragma unroll
-          for (int t = 0; t < 2; t++) {
-            const size_t tb = static_cast<size_t>(t ? pB : pA) * c.ks_tile;
-            d.ks[t] = *reinterpret_cast<const uint2*>(c.ks + tb + ks_lane);
-            if constexpr (ASYM) d.kz[t] = *reinterpret_cast<const uint2*>(c.kz + tb + ks_lane);
-          }
-        }
-      };
-      auto load_v = [&](int pA, int pB) {
-        pA = max(pA, 0);
-        pB = max(pB, 0);
-        load_words<KB>(c.vc + static_cast<size_t>(pA) * TILE_BYTES + v_lane, d.vw[0]);
-        load_words<KB>(c.vc + static_cast<size_t>(pB) * TILE_BYTES + v_lane, d.vw[1]);
-        if constexpr (!BF && !F8)
-#pragma unroll
-        for (int t = 0; t < 2; t++) {
-          const size_t tb = static_cast<size_t>(t ? pB : pA) * c.vs_tile;
-#pragma unroll
-          for (int pp = 0; pp < NP; pp++) {
-            const unsigned lo = rgv[pp] * TILE + 4 * g;
-            d.vs[pp][t] = *reinterpret_cast<const uint2*>(c.vs + tb + lo);
-            if constexpr (ASYM) d.vz[pp][t] = *reinterpret_cast<const uint2*>(c.vz + tb + lo);
-          }
-        }
-      };
       // per-channel keys: fold one key group's scales (and zero-points) into the query
       auto kpc_fold = [&](uint4 fs, uint4 fz) {
         // metadata words hold the lane's 8 channels in natural order; element i of the MFMA
@@ -755,10 +764,6 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
         wave_lds_sync();
       };
 
-      int pA = phys_of(2 * x);
-      int pB = (32 * x + 16 < nq) ? phys_of(2 * x + 1) : -1;
-      load_k(x, pA, pB);
-      load_v(pA, pB);
       for (; x < xq_end; x += WAVES) {
         const int xn = x + WAVES;
         const bool more = xn < xq_end;
