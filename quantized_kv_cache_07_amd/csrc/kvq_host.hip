@@ -156,7 +156,9 @@ struct WsLayout {
 };
 
 long units_bound(const kvq_cache* c, int max_tokens) {
-  const long per_seq = (static_cast<long>(max_tokens) + 31) / 32 + 1;
+  // compressed and window units of a sequence: at most one more than ceil(max_tokens / 32)
+  // when a window exists (the two parts round up separately)
+  const long per_seq = (static_cast<long>(max_tokens) + 31) / 32 + (c->fmt.residual > 0 ? 1 : 0);
   return static_cast<long>(c->batch) * c->n_kv_heads * per_seq;
 }
 
