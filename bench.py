@@ -342,7 +342,7 @@ def counter_traffic(workload: str):
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
-    if d.get("kvq_decode_hip_sha256_16") != decode_source_hash():
+    if d.get("kvq_decode_h_sha256_16") != decode_source_hash():
         return None
     return d.get("bytes_per_launch")
 
