@@ -333,7 +333,9 @@ struct DecodeLds {
   static constexpr int zw = lw + WAVES * 8 * 4;                   // [WAVES][32] f32
   static constexpr int ztw = zw + WAVES * 32 * 4;                 // [WAVES][8] f32
   static constexpr int qs = ztw + WAVES * 8 * 4;                  // [8][D] bf16
-  static constexpr int pre = qs + 8 * D * 2;                      // [B + 1] int
+  static constexpr int ustat = qs + 8 * D * 2;                    // [WAVES][3] int: min, max,
+                                                                  // count of units (> 0)
+  static constexpr int pre = ustat + WAVES * 3 * 4;               // [B + 1] int
   // per-channel key folding buffer [WAVES][2][8][D] f16 overlays `red` (never live together)
   static constexpr int kf = red;
   static_assert(WAVES * 2 * 8 * D * 2 <= WAVES * 16 * RED_STRIDE * 4, "kf overlay");
@@ -347,6 +349,19 @@ __device__ __forceinline__ int seq_units(const CacheDev& c, int max_tokens, int 
       (c.table && (nq + TILE - 1) / TILE > c.max_blocks) || nq > max_tokens - nr)
     return -1;
   return (nq + 31) / 32 + (nr + 31) / 32;
+}
+
+// Ranges actually used of nb workgroups over S segments.  When every segment has the same number
+// of units, ranges that end on segment boundaries save a segment restart and a partial per
+// workgroup: nb rounded down to a multiple of S (each segment split m ways), or S / k with k | S
+// (k whole segments per range), whichever aligned count is largest, if it keeps at least half of
+// the workgroups.  Otherwise all nb ranges (Stream-K over the unit sequence).
+__device__ __forceinline__ int aligned_ranges(int nb, int S, bool uniform) {
+  if (!uniform || S <= 0) return nb;
+  if (S <= nb) return (nb / S) * S;
+  int k = (S + nb - 1) / nb;
+  while (S % k) k++;
+  return (S / k >= (nb + 1) / 2) ? S / k : nb;
 }
 
 template <int KB, int G, bool KPC, int NP, int SCH, bool MQ>
@@ -368,20 +383,36 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
   float* ztw = reinterpret_cast<float*>(smem + DecodeLds::ztw);
   uint16_t* qs = reinterpret_cast<uint16_t*>(smem + DecodeLds::qs);
   int* pre = reinterpret_cast<int*>(smem + DecodeLds::pre);
+  int* ustat = reinterpret_cast<int*>(smem + DecodeLds::ustat);
   uint16_t* kf = reinterpret_cast<uint16_t*>(smem + DecodeLds::kf) + wave * 2 * 8 * D;
 
   // ---- units per sequence, prefix sum (every workgroup; workgroup 0 publishes it) ----
   {
     const int per = (B + 255) / 256;
     int* scan = reinterpret_cast<int*>(red);
-    int s = 0;
+    int s = 0, umin = INT_MAX, umax = 0, useq = 0;
     for (int i = tid * per; i < min(B, (tid + 1) * per); i++) {
       const int un = seq_units(c, p.max_tokens, i);
       if (un < 0) {
         if (blockIdx.x == 0) atomicOr(c.err, KVQ_ERR_TOKENS);
       } else {
         s += un * H * nqb;
+        if (un > 0) {
+          umin = min(umin, un);
+          umax = max(umax, un);
+          useq++;
+        }
       }
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+      umin = min(umin, __shfl_xor(umin, off));
+      umax = max(umax, __shfl_xor(umax, off));
+      useq += __shfl_xor(useq, off);
+    }
+    if (lane == 0) {
+      ustat[3 * wave] = umin;
+      ustat[3 * wave + 1] = umax;
+      ustat[3 * wave + 2] = useq;
     }
     scan[tid] = s;
     __syncthreads();
@@ -398,12 +429,24 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
     }
     if (tid == 255) pre[B] = scan[255];
     __syncthreads();
-    if (blockIdx.x == 0)
-      for (int i = tid; i <= B; i += 256) p.ws_pre[i] = pre[i];
   }
 
   const int U = uni(pre[B]);
-  const long long NBl = gridDim.x;
+  // ranges in use (the combine reads the count back): segment-aligned for uniform batches
+  int umin = ustat[0], umax = ustat[1], useq = ustat[2];
+#pragma unroll
+  for (int w = 1; w < WAVES; w++) {
+    umin = min(umin, ustat[3 * w]);
+    umax = max(umax, ustat[3 * w + 1]);
+    useq += ustat[3 * w + 2];
+  }
+  const int nbe = uni(aligned_ranges(gridDim.x, useq * H * nqb, umin == umax));
+  if (blockIdx.x == 0) {
+    for (int i = tid; i <= B; i += 256) p.ws_pre[i] = pre[i];
+    if (tid == 0) p.ws_pre[B + 1] = nbe;
+  }
+  if (static_cast<int>(blockIdx.x) >= nbe) return;
+  const long long NBl = nbe;
   const int u0 = static_cast<int>((static_cast<long long>(blockIdx.x) * U) / NBl);
   const int u1 = static_cast<int>((static_cast<long long>(blockIdx.x + 1) * U) / NBl);
   if (u0 == u1) {
@@ -1178,7 +1221,7 @@ __global__ __launch_bounds__(COMBINE_THREADS) void combine_kernel(DecodeParams p
   constexpr int cg = COMBINE_THREADS / opp;
   const int oi = threadIdx.x % opp, cgi = threadIdx.x / opp;
   const int* pre = p.ws_pre;
-  const long long U = pre[B], NB = p.nblocks;
+  const long long U = pre[B], NB = pre[B + 1];  // ranges the decode launch used
   const int ub = (pre[b + 1] - pre[b]) / SEGS;
   // output element o of the segment's G x D block (row o / D: query token, query head)
   auto dst = [&](int o) -> float* {

@@ -66,7 +66,8 @@ struct DecodeParams {
   CacheDev c;
   const uint16_t* q;  // [B][nqt][Hq][D] bf16
   float* out;         // [B][nqt][Hq][D] fp32
-  int32_t* ws_pre;    // [B + 1] prefix over sequences of work units (all kv heads)
+  int32_t* ws_pre;    // [B + 1] prefix over sequences of work units (all kv heads), then
+                      // the number of unit ranges in use
   float* ws_part;     // [nblocks][2][G][PART_STRIDE] partial (max, sum, pad, pad, o[D])
   int Hq, max_tokens, nblocks;
   float sm_log2;      // sm_scale * log2(e)

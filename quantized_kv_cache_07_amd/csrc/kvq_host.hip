@@ -197,7 +197,7 @@ WsLayout ws_layout(const kvq_cache* c, int n_q_heads, int max_tokens, int n_q = 
   if (nb < 1) nb = 1;
   w.nblocks = static_cast<int>(nb);
   w.pre_off = 0;
-  w.part_off = ((static_cast<size_t>(c->batch) + 1) * 4 + 255) & ~static_cast<size_t>(255);
+  w.part_off = ((static_cast<size_t>(c->batch) + 2) * 4 + 255) & ~static_cast<size_t>(255);
   w.total = w.part_off + static_cast<size_t>(w.nblocks) * 2 * w.G * PART_STRIDE * 4;
   return w;
 }
