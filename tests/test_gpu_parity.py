@@ -105,6 +105,30 @@ def test_window_edge_states():
     kc.compare_attention(pr)
 
 
+# Uniform batches use segment-aligned unit ranges; a forced grid size drives each choice:
+# segments split m ways, k whole segments per range (k dividing S), and the fall-back to plain
+# ranges when no aligned count keeps half of the workgroups.
+ALIGN_CASES = [
+    # name, k, v, B, Hq, H, R, lens, workgroups
+    ("segments-split-2-ways", SYM4, SYM4, 2, 8, 4, 0, [700, 700], 20),
+    ("two-segments-per-range", SYM4, SYM4, 2, 8, 4, 0, [700, 700], 7),
+    ("four-segments-per-range-window", SYM8, SYM8, 2, 4, 4, 32, [650, 650], 3),
+    ("prime-segment-count-falls-back", SYM4, SYM4, 7, 2, 1, 0, [300] * 7, 5),
+    ("uniform-with-empty-sequence", SYM4, SYM4, 3, 8, 2, 0, [0, 500, 500], 5),
+    ("ragged-keeps-plain-ranges", SYM4, SYM4, 3, 8, 2, 0, [100, 500, 500], 5),
+]
+
+
+@pytest.mark.parametrize("name,k,v,B,Hq,H,R,lens,nb", ALIGN_CASES, ids=[c[0] for c in ALIGN_CASES])
+def test_unit_range_choices(name, k, v, B, Hq, H, R, lens, nb, monkeypatch):
+    announce(test="unit_range_choices", name=name, workgroups=nb)
+    monkeypatch.setenv("KVQ_DECODE_BLOCKS", str(nb))
+    pr = kc.build_pair(k, v, B, Hq, H, R, lens, seed=zlib.crc32(name.encode()) % 1000)
+    kc.compare_attention(pr)
+    kc.step(pr, flush_first=False)
+    kc.compare_attention(pr, q_seed_step=1)
+
+
 def test_empty_sequence_gives_zeros():
     announce(test="empty_sequence")
     pr = kc.build_pair(SYM8, SYM8, 3, 2, 2, 0, [0, 40, 0])
