@@ -205,6 +205,13 @@ __device__ __forceinline__ constexpr int velem_alpha(int j, int i) {
   return pair_alpha<KB>((2 * j + (i / 2) % 2) % (16 / KB));
 }
 
+// 1 / alpha of natural channel k (0..7) of a per-channel folding lane's block in QK column block
+// jp: natural channels k and k + 4 are the two halves of pair (4 jp + k % 4) mod 16 / KB
+template <int KB>
+__device__ __forceinline__ float fold_inv_alpha(int jp, int k) {
+  return 1.0f / static_cast<float>(pair_alpha<KB>((4 * jp + (k & 3)) % (16 / KB)));
+}
+
 template <int KB>
 __device__ __forceinline__ f16x8 kop_raw(const uint32_t* w, int j, const UnpackRegs& u) {
   return __builtin_bit_cast(f16x8, uint4{rawpair<KB>(w, 4 * j, u), rawpair<KB>(w, 4 * j + 1, u),
@@ -312,14 +319,20 @@ __device__ __forceinline__ void load_words(const uint8_t* ptr, uint32_t (&w)[KB]
 
 // ---- per-unit register data ----------------------------------------------------------------
 
+// PV row blocks and the value-scale rows a lane needs.  Rows are (hi/lo part, value group, query
+// head); with two row blocks there are exactly 16 (group, head) rows, so block pp is part pp and
+// both blocks read the same value group: one set of scale rows serves both.
+template <int NP>
+constexpr int scale_rows() { return NP == 2 ? 1 : NP; }
+
 template <int KB, int NP, bool KPC, bool ASYM>
 struct UnitData {
   uint32_t kw[2][KB];  // key slices of tiles A and B (token n, channels 32 g .. 32 g + 31)
   uint32_t vw[2][KB];  // value chunks of tiles A and B (tokens 4 g .. 4 g + 3, channels 8 n ..)
   uint2 ks[2];         // per-token keys: scale of tokens 4 g .. 4 g + 3 (column's group)
   uint2 kz[2];         // per-token asymmetric keys: zero-points
-  uint2 vs[NP][2];     // value scales of tokens 4 g .. 4 g + 3 (row's group), tiles A, B
-  uint2 vz[NP][2];     // asymmetric values: zero-points
+  uint2 vs[scale_rows<NP>()][2];  // value scales of tokens 4 g .. 4 g + 3 (row's group), tiles A, B
+  uint2 vz[scale_rows<NP>()][2];  // asymmetric values: zero-points
   uint4 fs, fz;        // per-channel keys: scale / zero of the folding lane's 8 channels
 };
 
@@ -592,7 +605,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
       for (int t = 0; t < 2; t++) {
         const size_t tb = static_cast<size_t>(t ? pB : pA) * c.vs_tile;
 #pragma unroll
-        for (int pp = 0; pp < NP; pp++) {
+        for (int pp = 0; pp < scale_rows<NP>(); pp++) {
           const unsigned lo = rgv[pp] * TILE + 4 * g;
           d.vs[pp][t] = *reinterpret_cast<const uint2*>(c.vs + tb + lo);
           if constexpr (ASYM) d.vz[pp][t] = *reinterpret_cast<const uint2*>(c.vz + tb + lo);
@@ -760,12 +773,28 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
         }
       }
 
-      // per-channel keys: fold one key group's scales (and zero-points) into the query
+      // Raw key codes read as 1024 + alpha u: the folded query carries 1 / alpha of each
+      // channel (a power of two), applied to the folding lane's 8 scales as they arrive.
+      f16x2 ia2[4];
+      if constexpr (KPC) {
+#pragma unroll
+        for (int w = 0; w < 4; w++)
+          ia2[w] = f16x2{static_cast<_Float16>(fold_inv_alpha<KB>(fold_blk % 4, 2 * w)),
+                         static_cast<_Float16>(fold_inv_alpha<KB>(fold_blk % 4, 2 * w + 1))};
+      }
+
+      // per-channel keys: fold one key group's scales (and zero-points) into the query, then
+      // start the group's QK accumulator at minus the bias of the raw codes (plus, for
+      // asymmetric keys, the zero-point term sum_i q_i z_i in the hi column)
       auto kpc_fold = [&](uint4 fs, uint4 fz) {
         // metadata words hold the lane's 8 channels in natural order; element i of the MFMA
         // block is natural index nat(i)
-        const uint32_t sw[4] = {fs.x, fs.y, fs.z, fs.w};
+        uint32_t sw[4] = {fs.x, fs.y, fs.z, fs.w};
         const uint32_t zwd[4] = {fz.x, fz.y, fz.z, fz.w};
+        if constexpr (KB != 8) {
+#pragma unroll
+          for (int w = 0; w < 4; w++) sw[w] = h2_bits(as_h2(sw[w]) * ia2[w]);
+        }
         auto nat = [](int i) { return (KB == 8) ? ((i & 4) | ((i & 1) << 1) | ((i >> 1) & 1)) : ((i >> 1) | ((i & 1) << 2)); };
 #pragma unroll
         for (int r0 = 0; r0 < G; r0 += 4) {
@@ -805,6 +834,20 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
           qb[j] = *reinterpret_cast<const f16x8*>(kf + (cg * 8 + hh) * D + 8 * (4 * g + j));
         if constexpr (ASYM) zt = ztw[wave * 8 + hh];
         wave_lds_sync();
+        dq0 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          f16x8 bias;
+#pragma unroll
+          for (int i = 0; i < 8; i++)
+            bias[i] = static_cast<_Float16>(-(1024.0f + static_cast<float>(kelem_alpha<KB>(j, i)) * koff));
+          dq0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(bias, qb[j], dq0, 0, 0, 0);
+        }
+        if constexpr (ASYM) {
+          const float zc = (cg == 0) ? zt : 0.0f;
+#pragma unroll
+          for (int r = 0; r < 4; r++) dq0[r] += zc;
+        }
       };
 
       for (; x < xq_end; x += WAVES) {
@@ -827,22 +870,26 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
         if constexpr (KPC) {
           if (kgroup == 16 && nvB > 0) {
             // tile B opens its own key group: finish tile A with the current fold first
+            dq[0] = dq0;
 #pragma unroll
             for (int j = 0; j < 4; j++)
-              dq[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop<KB>(d.kw[0], j, koff, ur), qb[j], dq[0], 0, 0, 0);
+              dq[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop_raw<KB>(d.kw[0], j, ur), qb[j], dq[0], 0, 0, 0);
             const size_t mi = kpc_meta(2 * x + 1);
             const uint4 fs2 = load_meta8(c.ks, mi);
             uint4 fz2 = uint4{0, 0, 0, 0};
             if constexpr (ASYM) fz2 = load_meta8(c.kz, mi);
             kpc_fold(fs2, fz2);
+            dq[1] = dq0;
 #pragma unroll
             for (int j = 0; j < 4; j++)
-              dq[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop<KB>(d.kw[1], j, koff, ur), qb[j], dq[1], 0, 0, 0);
+              dq[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop_raw<KB>(d.kw[1], j, ur), qb[j], dq[1], 0, 0, 0);
           } else {
+            dq[0] = dq0;
+            dq[1] = dq0;
 #pragma unroll
             for (int j = 0; j < 4; j++) {
-              dq[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop<KB>(d.kw[0], j, koff, ur), qb[j], dq[0], 0, 0, 0);
-              dq[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop<KB>(d.kw[1], j, koff, ur), qb[j], dq[1], 0, 0, 0);
+              dq[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop_raw<KB>(d.kw[0], j, ur), qb[j], dq[0], 0, 0, 0);
+              dq[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop_raw<KB>(d.kw[1], j, ur), qb[j], dq[1], 0, 0, 0);
             }
           }
         } else if constexpr (F8) {
@@ -879,7 +926,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
             for (int r = 0; r < 4; r++) s2[4 * t + r] = dq[t][r] * f8k;
           } else if constexpr (KPC) {
 #pragma unroll
-            for (int r = 0; r < 4; r++) s2[4 * t + r] = dq[t][r] + row_ror<G>(dq[t][r]) + zt;
+            for (int r = 0; r < 4; r++) s2[4 * t + r] = dq[t][r] + row_ror<G>(dq[t][r]);
           } else {
             const uint2 k2 = d.ks[t];
             s2[4 * t + 0] = fmaf(dq[t][0], f16_lo(k2.x), 0.0f);
@@ -946,9 +993,11 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
           pB = nB;
           continue;
         }
+        // With two row blocks, block 0 takes the hi parts and block 1 the lo parts of the same
+        // products w * s_v, formed once; with one block each lane's row picks its own part.
         f16x8 pa[NP];
 #pragma unroll
-        for (int pp = 0; pp < NP; pp++) {
+        for (int pp = 0; pp < scale_rows<NP>(); pp++) {
           const float sel = (rpart[pp] == 1) ? 1.0f : 0.0f;
           float ws[8];
 #pragma unroll
@@ -967,12 +1016,16 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
             ws[4 * t + 3] = fmaf(s2[4 * t + 3], f16_hi(s2v.y), 0.0f);
             if constexpr (ASYM) {
               const uint2 z2v = d.vz[pp][t];
-              const float zv[4] = {f16_lo(z2v.x), f16_hi(z2v.x), f16_lo(z2v.y), f16_hi(z2v.y)};
+              float zv[4] = {f16_lo(z2v.x), f16_hi(z2v.x), f16_lo(z2v.y), f16_hi(z2v.y)};
+              if (!full) {  // a token past the end may sit on a stand-in tile with any zero-point
+#pragma unroll
+                for (int r = 0; r < 4; r++) zv[r] = (s2[4 * t + r] != 0.0f) ? zv[r] : 0.0f;
+              }
               float zp = 0.0f;
 #pragma unroll
               for (int r = 0; r < 4; r++) {
                 const float wa = VBF ? s2[4 * t + r] * static_cast<float>(velem_alpha<KB>(0, r)) : s2[4 * t + r];
-                zp += (full || s2[4 * t + r] != 0.0f) ? wa * zv[r] : 0.0f;
+                zp = fmaf(wa, zv[r], zp);
               }
               zacc[pp] += zp;
             }
@@ -984,15 +1037,22 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
               ws[i] = (s2[si] != 0.0f) ? ws[i] : 0.0f;
             }
           }
-          uint32_t pk[4];
+          uint32_t pk[4], pl[4];
 #pragma unroll
           for (int i = 0; i < 4; i++) {
             const f16x2 hi2 = pkrtz(ws[2 * i], ws[2 * i + 1]);
-            const float r0 = fmaf(-sel, static_cast<float>(hi2[0]), ws[2 * i]);
-            const float r1 = fmaf(-sel, static_cast<float>(hi2[1]), ws[2 * i + 1]);
-            pk[i] = h2_bits(pkrtz(r0, r1));
+            if constexpr (NP == 2) {
+              pk[i] = h2_bits(hi2);
+              pl[i] = h2_bits(pkrtz(ws[2 * i] - static_cast<float>(hi2[0]),
+                                    ws[2 * i + 1] - static_cast<float>(hi2[1])));
+            } else {
+              const float r0 = fmaf(-sel, static_cast<float>(hi2[0]), ws[2 * i]);
+              const float r1 = fmaf(-sel, static_cast<float>(hi2[1]), ws[2 * i + 1]);
+              pk[i] = h2_bits(pkrtz(r0, r1));
+            }
           }
           pa[pp] = __builtin_bit_cast(f16x8, uint4{pk[0], pk[1], pk[2], pk[3]});
+          if constexpr (NP == 2) pa[1] = __builtin_bit_cast(f16x8, uint4{pl[0], pl[1], pl[2], pl[3]});
         }
 #pragma unroll
         for (int j = 0; j < 8; j++) {

@@ -63,6 +63,11 @@ CASES = [
     ("kivi-int2-paged", KPC2, ASYM2_32, 2, 8, 2, 128, [700, 1300], True),
     ("kpc4-sym-g16-paged", KPC4S, SYM4, 2, 4, 1, 32, [100, 50], True),
     ("kpc4-asym-g64-paged", (4, 1, 1, 64), (4, 1, 0, 32), 1, 8, 2, 64, [500], True),
+    # two PV row blocks (hi and lo parts of one set of value-group rows), symmetric and GQA-8
+    ("int4-g32-gqa4-two-row-blocks", (4, 0, 0, 32), (4, 0, 0, 32), 2, 8, 2, 0, [345, 1200], False),
+    ("kpc8-asym-gqa8-two-row-blocks", (8, 1, 1, 32), (8, 1, 0, 64), 1, 16, 2, 64, [900], False),
+    # symmetric 2-bit per-channel keys: raw codes with every field scale 1..256 and a bias
+    ("kpc2-sym-g64", (2, 0, 1, 64), (2, 0, 0, 32), 2, 4, 2, 128, [500, 260], False),
 ]
 
 
