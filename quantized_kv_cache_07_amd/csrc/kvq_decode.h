@@ -70,7 +70,7 @@ template <int S>
 __device__ __forceinline__ float row_ror(float x) {
   static_assert(S >= 1 && S <= 15, "row_ror");
   return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x120 + S, 0xF, 0xF, false));
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x120 + S, 0xF, 0xF, true));
 }
 
 // Values every lane of a wave agrees on, made scalar (the compiler cannot see it for LDS loads).
@@ -635,6 +635,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
     f32x4 dq0 = f32x4{0.f, 0.f, 0.f, 0.f};  // QK accumulator start of every tile
     float qsum = 0.0f;  // asymmetric per-token keys: sum of q over the column's group
     float zt = 0.0f;    // asymmetric per-channel keys: sum of q * zero over the key group
+    float ztc = 0.0f;   // zt in the hi column of each head, 0 in the lo column
     float f8k = 1.0f, f8v = 1.0f;  // FP8: the key and value scales of kv head h
     if constexpr (BF) {
 #pragma unroll
@@ -801,12 +802,12 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
           const int hw = r0 + (lane >> 4);
           float zp = 0.0f;
           if (hw < G) {
-            float pv[8];
+            float pv[8], sv[8];
 #pragma unroll
             for (int i = 0; i < 8; i++) {
               const int k = nat(i);
-              const float sv = (k & 1) ? f16_hi(sw[k / 2]) : f16_lo(sw[k / 2]);
-              pv[i] = qfold[r0 / 4][i] * sv;  // exact: 8-bit x 11-bit significands
+              sv[i] = (k & 1) ? f16_hi(sw[k / 2]) : f16_lo(sw[k / 2]);
+              pv[i] = fmaf(qfold[r0 / 4][i], sv[i], 0.0f);  // exact: 8-bit x 11-bit significands
               if constexpr (ASYM) zp += qfold[r0 / 4][i] * ((k & 1) ? f16_hi(zwd[k / 2]) : f16_lo(zwd[k / 2]));
             }
             uint32_t hw4[4], lw4[4];
@@ -814,8 +815,9 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
             for (int i = 0; i < 4; i++) {
               const f16x2 hi2 = pkrtz(pv[2 * i], pv[2 * i + 1]);
               hw4[i] = h2_bits(hi2);
-              lw4[i] = h2_bits(pkrtz(pv[2 * i] - static_cast<float>(hi2[0]),
-                                     pv[2 * i + 1] - static_cast<float>(hi2[1])));
+              // q s - hi, exact, in one fused op on the f16 operands
+              lw4[i] = h2_bits(pkrtz(fmaf(qfold[r0 / 4][2 * i], sv[2 * i], -static_cast<float>(hi2[0])),
+                                     fmaf(qfold[r0 / 4][2 * i + 1], sv[2 * i + 1], -static_cast<float>(hi2[1]))));
             }
             *reinterpret_cast<uint4*>(kf + hw * D + 8 * fold_blk) = uint4{hw4[0], hw4[1], hw4[2], hw4[3]};
             *reinterpret_cast<uint4*>(kf + (8 + hw) * D + 8 * fold_blk) = uint4{lw4[0], lw4[1], lw4[2], lw4[3]};
@@ -843,11 +845,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
             bias[i] = static_cast<_Float16>(-(1024.0f + static_cast<float>(kelem_alpha<KB>(j, i)) * koff));
           dq0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(bias, qb[j], dq0, 0, 0, 0);
         }
-        if constexpr (ASYM) {
-          const float zc = (cg == 0) ? zt : 0.0f;
-#pragma unroll
-          for (int r = 0; r < 4; r++) dq0[r] += zc;
-        }
+        if constexpr (ASYM) ztc = (cg == 0) ? zt : 0.0f;
       };
 
       for (; x < xq_end; x += WAVES) {
@@ -924,9 +922,9 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
           } else if constexpr (F8) {
 #pragma unroll
             for (int r = 0; r < 4; r++) s2[4 * t + r] = dq[t][r] * f8k;
-          } else if constexpr (KPC) {
+          } else if constexpr (KPC) {  // hi + lo columns are summed below; zt once, in the hi one
 #pragma unroll
-            for (int r = 0; r < 4; r++) s2[4 * t + r] = dq[t][r] + row_ror<G>(dq[t][r]);
+            for (int r = 0; r < 4; r++) s2[4 * t + r] = dq[t][r] + ztc;
           } else {
             const uint2 k2 = d.ks[t];
             s2[4 * t + 0] = fmaf(dq[t][0], f16_lo(k2.x), 0.0f);
@@ -942,7 +940,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
             }
           }
         }
-        if constexpr (!KPC) fold_cols8(s2);
+        fold_cols8(s2);
         load_k(more ? xn : x, nA, nB);  // key registers are free again
 
         softmax(s2, nvA, nvB, std::integral_constant<bool, VBF>{}, 32 * x);  // s2: weights / alpha
