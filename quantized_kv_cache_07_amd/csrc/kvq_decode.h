@@ -107,7 +107,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 struct UnpackRegs {
   uint32_t magic;       // VGPR: 0x64006400, f16 1024.0 in both halves
   uint32_t m_lo, m_hi;  // SGPRs: masks of the fields a pair needs (per bit width)
-  uint32_t m2[5];       // 2-bit codes: 0x00030003 << 2k, k = 0..4
+  uint32_t m2[4];       // 2-bit codes: 0x00030003 << 2k, k = 0..3
 };
 
 template <int KB>
@@ -130,48 +130,40 @@ __device__ __forceinline__ UnpackRegs unpack_regs() {
     asm volatile("s_mov_b32 %0, 0x000c000c" : "=s"(r.m2[1]));
     asm volatile("s_mov_b32 %0, 0x00300030" : "=s"(r.m2[2]));
     asm volatile("s_mov_b32 %0, 0x00c000c0" : "=s"(r.m2[3]));
-    asm volatile("s_mov_b32 %0, 0x03000300" : "=s"(r.m2[4]));
     r.m_lo = r.m_hi = 0;
   }
   return r;
 }
 
-// A word holds E = 32 / KB fields; pair k (0 <= k < E/2) is (field k, field k + E/2), returned
-// as the exact f16 values (u - off).  Pair index r = word * (E/2) + k.
-template <int KB>
-__device__ __forceinline__ f16x2 upair(const uint32_t* w, int r, float off, const UnpackRegs& u) {
-  constexpr int HH = 16 / KB;
-  const uint32_t x = w[r / HH];
-  const int k = r % HH;
-  if constexpr (KB == 16) {  // stored bf16 pairs are never unpacked (bf16 products read them)
-    return as_h2(x);
-  } else if constexpr (KB == 8) {
-    const uint32_t s = k ? (x >> 8) : x;
-    return as_h2((s & u.m_lo) | u.magic) - h2s(1024.0f + off);
-  } else if constexpr (KB == 4) {
-    const uint32_t s = (k >= 2) ? (x >> 8) : x;
-    if ((k & 1) == 0) return as_h2((s & u.m_lo) | u.magic) - h2s(1024.0f + off);
-    return __builtin_elementwise_fma(as_h2((s & u.m_hi) | u.magic), h2s(0.0625f),
-                                     h2s(-(64.0f + off)));
-  } else {
-    static_assert(KB == 2, "bits");
-    // field k sits at bit 2k (k < 5) or, after a shift by 10, at bit 2 (k - 5); the masked
-    // code reads as 1024 + 2^sh u, and one fma takes it to u - off
-    const uint32_t s = (k >= 5) ? (x >> 10) : x;
-    const int sh = (k >= 5) ? 2 * (k - 5) : 2 * k;
-    const float scl = 1.0f / static_cast<float>(1 << sh);
-    const f16x2 v = as_h2((s & u.m2[sh / 2]) | u.magic);
-    if (sh == 0) return v - h2s(1024.0f + off);
-    return __builtin_elementwise_fma(v, h2s(scl), h2s(-(1024.0f * scl + off)));
-  }
-}
+// A word holds E = 32 / KB fields; pair k (0 <= k < E/2) is (field k, field k + E/2): the
+// same field of the word's two 16-bit halves, so one mask under an f16 exponent turns a pair into
+// two f16 values.  2-bit pairs 4..7 are taken from the word shifted right by 8.
 
 // Scale of pair k's fields in the bias-free form: the masked field reads as 1024 + alpha u.
 template <int KB>
 __device__ __forceinline__ constexpr int pair_alpha(int k) {
   if constexpr (KB == 8) return 1;
   else if constexpr (KB == 4) return (k & 1) ? 16 : 1;
-  else return 1 << (2 * (k >= 5 ? k - 5 : k));
+  else return 1 << (2 * (k & 3));
+}
+
+// Pair r as two f16 subnormals alpha u 2^-24 (the masked fields under a zero exponent; one
+// and).  The matrix cores take f16 subnormal operands exactly, so these products need no bias
+// removal: the other operand carries 1 / alpha and the result is scaled by 2^24 afterwards.
+template <int KB>
+__device__ __forceinline__ uint32_t subpair(const uint32_t* w, int r, const UnpackRegs& u) {
+  constexpr int HH = 16 / KB;
+  const uint32_t x = w[r / HH];
+  const int k = r % HH;
+  if constexpr (KB == 8) {
+    return (k ? (x >> 8) : x) & u.m_lo;
+  } else if constexpr (KB == 4) {
+    const uint32_t s = (k >= 2) ? (x >> 8) : x;
+    return s & ((k & 1) ? u.m_hi : u.m_lo);
+  } else {
+    const uint32_t s = (k >= 4) ? (x >> 8) : x;
+    return s & u.m2[k & 3];
+  }
 }
 
 // Pair r as the raw f16 values 1024 + alpha u (one and-or, no bias removal).  The bias is
@@ -179,19 +171,7 @@ __device__ __forceinline__ constexpr int pair_alpha(int k) {
 // operand holding -(1024 + alpha off) cancels the rest.
 template <int KB>
 __device__ __forceinline__ uint32_t rawpair(const uint32_t* w, int r, const UnpackRegs& u) {
-  constexpr int HH = 16 / KB;
-  const uint32_t x = w[r / HH];
-  const int k = r % HH;
-  if constexpr (KB == 8) {
-    return ((k ? (x >> 8) : x) & u.m_lo) | u.magic;
-  } else if constexpr (KB == 4) {
-    const uint32_t s = (k >= 2) ? (x >> 8) : x;
-    return (s & ((k & 1) ? u.m_hi : u.m_lo)) | u.magic;
-  } else {
-    const uint32_t s = (k >= 5) ? (x >> 10) : x;
-    const int sh = (k >= 5) ? 2 * (k - 5) : 2 * k;
-    return (s & u.m2[sh / 2]) | u.magic;
-  }
+  return subpair<KB>(w, r, u) | u.magic;
 }
 
 // alpha of element i of QK MFMA j (pair 4 j + i / 2) and of element i of a PV B operand
@@ -218,9 +198,19 @@ __device__ __forceinline__ f16x8 kop_raw(const uint32_t* w, int j, const UnpackR
                                          rawpair<KB>(w, 4 * j + 2, u), rawpair<KB>(w, 4 * j + 3, u)});
 }
 template <int KB>
-__device__ __forceinline__ f16x8 vop_raw(const uint32_t* wa, const uint32_t* wb, int j, const UnpackRegs& u) {
-  return __builtin_bit_cast(f16x8, uint4{rawpair<KB>(wa, 2 * j, u), rawpair<KB>(wa, 2 * j + 1, u),
-                                         rawpair<KB>(wb, 2 * j, u), rawpair<KB>(wb, 2 * j + 1, u)});
+__device__ __forceinline__ f16x8 kop_sub(const uint32_t* w, int j, const UnpackRegs& u) {
+  return __builtin_bit_cast(f16x8, uint4{subpair<KB>(w, 4 * j, u), subpair<KB>(w, 4 * j + 1, u),
+                                         subpair<KB>(w, 4 * j + 2, u), subpair<KB>(w, 4 * j + 3, u)});
+}
+template <int KB>
+__device__ __forceinline__ f16x8 vop_sub(const uint32_t* wa, const uint32_t* wb, int j, const UnpackRegs& u) {
+  return __builtin_bit_cast(f16x8, uint4{subpair<KB>(wa, 2 * j, u), subpair<KB>(wa, 2 * j + 1, u),
+                                         subpair<KB>(wb, 2 * j, u), subpair<KB>(wb, 2 * j + 1, u)});
+}
+// alpha of value MFMA j's channel factor (element i's alpha is vchan_alpha(j) * vtok_alpha(i))
+template <int KB>
+__device__ __forceinline__ constexpr int vchan_alpha(int j) {
+  return velem_alpha<KB>(j, 0);
 }
 
 // FP8 E4M3 bytes to exact f16 (every E4M3 value is an f16 value): bytes (0, 1) and (2, 3) of
@@ -233,24 +223,6 @@ __device__ __forceinline__ f16x8 f8_to_f16x8(uint32_t w0, uint32_t w1) {
   const f16x4 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3);
   const f16x4 cd = __builtin_shufflevector(c, d, 0, 1, 2, 3);
   return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// QK A operand of MFMA j: pairs 4 j .. 4 j + 3 of the lane's key slice.
-template <int KB>
-__device__ __forceinline__ f16x8 kop(const uint32_t* w, int j, float off, const UnpackRegs& u) {
-  const uint4 v = uint4{h2_bits(upair<KB>(w, 4 * j, off, u)), h2_bits(upair<KB>(w, 4 * j + 1, off, u)),
-                        h2_bits(upair<KB>(w, 4 * j + 2, off, u)), h2_bits(upair<KB>(w, 4 * j + 3, off, u))};
-  return __builtin_bit_cast(f16x8, v);
-}
-
-// PV B operand of MFMA j (channel 8 n + j): tokens 4 g .. 4 g + 3 of tile A, then of tile B
-// (value pairs 2 j and 2 j + 1 hold tokens (0, 1) and (2, 3) of channel j).
-template <int KB>
-__device__ __forceinline__ f16x8 vop(const uint32_t* wa, const uint32_t* wb, int j, float off,
-                                     const UnpackRegs& u) {
-  const uint4 v = uint4{h2_bits(upair<KB>(wa, 2 * j, off, u)), h2_bits(upair<KB>(wa, 2 * j + 1, off, u)),
-                        h2_bits(upair<KB>(wb, 2 * j, off, u)), h2_bits(upair<KB>(wb, 2 * j + 1, off, u))};
-  return __builtin_bit_cast(f16x8, v);
 }
 
 // Channel (0..31 inside a lane's 32-channel key slice) of element i of QK MFMA j: element i is
@@ -474,15 +446,14 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
   const int ngv = D / vgroup;
   constexpr float koff = ASYM ? 0.0f : static_cast<float>(1 << (KB - 1));
   constexpr float voff = koff;
-  // Value codes enter PV raw (1024 + alpha u) when alpha depends only on the token position
-  // (8- and 4-bit); the weights then carry 1 / alpha and one more product with vbias removes the
-  // bias.  2-bit fields change alpha with the channel, so they are unpacked exactly instead.
-  constexpr bool VBF = (KB == 4 || KB == 8) && !F8;
+  // Integer value codes enter PV as f16 subnormals alpha u 2^-24 (one and per pair).  alpha is
+  // a token-position factor VT (at i % 4 >= 2; the weights come out of the exponential divided
+  // by it) times a channel factor of MFMA j, removed with the 2^24 when the compressed units are
+  // done.  The offset of symmetric codes (-off times the sum of w s_v) is accumulated apart (zo).
+  constexpr bool VBF = !F8 && KB != 16;
+  constexpr float VLG = KB == 4 ? 4.0f : KB == 2 ? 2.0f : 0.0f;  // log2 VT
+  constexpr float VT = KB == 4 ? 16.0f : KB == 2 ? 4.0f : 1.0f;
   constexpr bool BF = KB == 16;  // unquantized BF16 storage: bf16 matrix products, no scales
-  f16x8 vbias;
-#pragma unroll
-  for (int i = 0; i < 8; i++)
-    vbias[i] = static_cast<_Float16>(-(1024.0f + static_cast<float>(velem_alpha<KB>(0, i)) * voff));
   const int hh = n % G;          // query head of QK column n and of PV row 16 pp + n
   const int cg = (n / G) % ngk;  // key group (or hi/lo part) of QK column n
   constexpr long TILE_BYTES = static_cast<long>(TILE) * D * KB / 8;
@@ -685,6 +656,15 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
     for (int pp = 0; pp < NP; pp++)
 #pragma unroll
       for (int j = 0; j < 8; j++) acc[pp][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // symmetric subnormal value codes: -off times the sum of each row's products, one product
+    // per unit against a constant operand, the same for every channel
+    f32x4 zo[NP];
+#pragma unroll
+    for (int pp = 0; pp < NP; pp++) zo[pp] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f16x8 voffop;
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+      voffop[i] = static_cast<_Float16>(-voff * ((i & 2) ? VT : 1.0f) * 0x1p-24f);
     float zacc[NP];
 #pragma unroll
     for (int pp = 0; pp < NP; pp++) zacc[pp] = 0.0f;
@@ -732,18 +712,20 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
           for (int pp = 0; pp < NP; pp++)
 #pragma unroll
             for (int j = 0; j < 8; j++) acc[pp][j][r] *= a;
+#pragma unroll
+          for (int pp = 0; pp < NP; pp++) zo[pp][r] *= a;
         }
         m_run = mn;
       }
-      constexpr bool A16 = decltype(vfold)::value && KB == 4;  // alpha 16 at i % 4 >= 2
+      constexpr bool AT = decltype(vfold)::value && VT > 1.0f;  // factor VT at i % 4 >= 2
 #pragma unroll
       for (int i = 0; i < 8; i++) {
-        const float a = (A16 && (i & 2)) ? 4.0f : 0.0f;  // log2 alpha_i
+        const float a = (AT && (i & 2)) ? VLG : 0.0f;  // log2 of element i's token factor
         s2[i] = __builtin_amdgcn_exp2f(fmaf(s2[i], p.sm_log2, -m_run - a));  // -inf -> 0
       }
       const float l1 = (s2[0] + s2[1]) + (s2[4] + s2[5]);
       const float l16 = (s2[2] + s2[3]) + (s2[6] + s2[7]);
-      l_run += A16 ? fmaf(l16, 16.0f, l1) : l1 + l16;
+      l_run += AT ? fmaf(l16, VT, l1) : l1 + l16;
     };
 
     // sum the per-group (or hi/lo) columns of one head, for 8 scores at once
@@ -836,14 +818,18 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
           qb[j] = *reinterpret_cast<const f16x8*>(kf + (cg * 8 + hh) * D + 8 * (4 * g + j));
         if constexpr (ASYM) zt = ztw[wave * 8 + hh];
         wave_lds_sync();
+        // subnormal key codes alpha u 2^-24: symmetric codes start at minus the offset,
+        // -off alpha 2^-24 against the same operand; asymmetric ones need no start
         dq0 = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (!ASYM) {
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-          f16x8 bias;
+          for (int j = 0; j < 4; j++) {
+            f16x8 bias;
 #pragma unroll
-          for (int i = 0; i < 8; i++)
-            bias[i] = static_cast<_Float16>(-(1024.0f + static_cast<float>(kelem_alpha<KB>(j, i)) * koff));
-          dq0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(bias, qb[j], dq0, 0, 0, 0);
+            for (int i = 0; i < 8; i++)
+              bias[i] = static_cast<_Float16>(-static_cast<float>(kelem_alpha<KB>(j, i)) * koff * 0x1p-24f);
+            dq0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(bias, qb[j], dq0, 0, 0, 0);
+          }
         }
         if constexpr (ASYM) ztc = (cg == 0) ? zt : 0.0f;
       };
@@ -871,7 +857,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
             dq[0] = dq0;
 #pragma unroll
             for (int j = 0; j < 4; j++)
-              dq[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop_raw<KB>(d.kw[0], j, ur), qb[j], dq[0], 0, 0, 0);
+              dq[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop_sub<KB>(d.kw[0], j, ur), qb[j], dq[0], 0, 0, 0);
             const size_t mi = kpc_meta(2 * x + 1);
             const uint4 fs2 = load_meta8(c.ks, mi);
             uint4 fz2 = uint4{0, 0, 0, 0};
@@ -880,14 +866,14 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
             dq[1] = dq0;
 #pragma unroll
             for (int j = 0; j < 4; j++)
-              dq[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop_raw<KB>(d.kw[1], j, ur), qb[j], dq[1], 0, 0, 0);
+              dq[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop_sub<KB>(d.kw[1], j, ur), qb[j], dq[1], 0, 0, 0);
           } else {
             dq[0] = dq0;
             dq[1] = dq0;
 #pragma unroll
             for (int j = 0; j < 4; j++) {
-              dq[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop_raw<KB>(d.kw[0], j, ur), qb[j], dq[0], 0, 0, 0);
-              dq[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop_raw<KB>(d.kw[1], j, ur), qb[j], dq[1], 0, 0, 0);
+              dq[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop_sub<KB>(d.kw[0], j, ur), qb[j], dq[0], 0, 0, 0);
+              dq[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop_sub<KB>(d.kw[1], j, ur), qb[j], dq[1], 0, 0, 0);
             }
           }
         } else if constexpr (F8) {
@@ -924,7 +910,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
             for (int r = 0; r < 4; r++) s2[4 * t + r] = dq[t][r] * f8k;
           } else if constexpr (KPC) {  // hi + lo columns are summed below; zt once, in the hi one
 #pragma unroll
-            for (int r = 0; r < 4; r++) s2[4 * t + r] = dq[t][r] + ztc;
+            for (int r = 0; r < 4; r++) s2[4 * t + r] = fmaf(dq[t][r], 0x1p24f, ztc);
           } else {
             const uint2 k2 = d.ks[t];
             s2[4 * t + 0] = fmaf(dq[t][0], f16_lo(k2.x), 0.0f);
@@ -1055,22 +1041,21 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
 #pragma unroll
         for (int j = 0; j < 8; j++) {
           if constexpr (VBF) {
-            // raw codes 1024 + alpha u against weights / alpha, then the bias: -(1024 + alpha off)
-            const f16x8 vb = vop_raw<KB>(d.vw[0], d.vw[1], j, ur);
+            // subnormal codes alpha u 2^-24 against weights / token factor
+            const f16x8 vb = vop_sub<KB>(d.vw[0], d.vw[1], j, ur);
 #pragma unroll
             for (int pp = 0; pp < NP; pp++)
               acc[pp][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[pp], vb, acc[pp][j], 0, 0, 0);
+            if constexpr (!ASYM) {
+              if (j == 0) {
 #pragma unroll
-            for (int pp = 0; pp < NP; pp++)
-              acc[pp][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[pp], vbias, acc[pp][j], 0, 0, 0);
+                for (int pp = 0; pp < NP; pp++)
+                  zo[pp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[pp], voffop, zo[pp], 0, 0, 0);
+              }
+            }
           } else if constexpr (F8) {
             // word j of each tile's chunk: channel 8 n + j of tokens (0, 2, 1, 3)
             const f16x8 vb = f8_to_f16x8(d.vw[0][j], d.vw[1][j]);
-#pragma unroll
-            for (int pp = 0; pp < NP; pp++)
-              acc[pp][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[pp], vb, acc[pp][j], 0, 0, 0);
-          } else {
-            const f16x8 vb = vop<KB>(d.vw[0], d.vw[1], j, voff, ur);
 #pragma unroll
             for (int pp = 0; pp < NP; pp++)
               acc[pp][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[pp], vb, acc[pp][j], 0, 0, 0);
@@ -1081,6 +1066,18 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
         pB = nB;
       }
       if (bad_block && lane == 0) atomicOr(c.err, KVQ_ERR_BLOCK);
+    }
+    // the compressed units' products are in units of 2^-24 / (channel factor of MFMA j); the
+    // window rows below add true values
+    if constexpr (VBF) {
+#pragma unroll
+      for (int pp = 0; pp < NP; pp++)
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+#pragma unroll
+          for (int r = 0; r < 4; r++)
+            acc[pp][j][r] = fmaf(acc[pp][j][r], 16777216.0f / static_cast<float>(vchan_alpha<KB>(j)),
+                                 ASYM ? 0.0f : zo[pp][r] * 16777216.0f);
     }
 
     // ---------------------------- BF16 window units ----------------------------
