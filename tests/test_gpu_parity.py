@@ -68,6 +68,12 @@ CASES = [
     ("kpc8-asym-gqa8-two-row-blocks", (8, 1, 1, 32), (8, 1, 0, 64), 1, 16, 2, 64, [900], False),
     # symmetric 2-bit per-channel keys: raw codes with every field scale 1..256 and a bias
     ("kpc2-sym-g64", (2, 0, 1, 64), (2, 0, 0, 32), 2, 4, 2, 128, [500, 260], False),
+    # value codes as f16 subnormals: every bit width and scheme, one and two row blocks, GQA 1..8
+    ("asym2-g64-per-token-keys", (2, 1, 0, 64), (2, 1, 0, 64), 2, 8, 2, 32, [613, 97], True),
+    ("int2-mha-g128", (2, 0, 0, 128), (2, 0, 0, 128), 2, 4, 4, 0, [1000, 33], False),
+    ("int2-g64-gqa8-two-row-blocks", (2, 0, 0, 64), (2, 0, 0, 64), 1, 16, 2, 16, [1200], False),
+    ("int8-g32-gqa4-two-row-blocks", (8, 0, 0, 32), (8, 0, 0, 32), 2, 8, 2, 0, [321, 1029], True),
+    ("asym8-g128-gqa2", (8, 1, 0, 128), (8, 1, 0, 128), 2, 4, 2, 64, [700, 65], False),
 ]
 
 
