@@ -310,6 +310,7 @@ struct UnitData {
 
 // ---- the kernel ----------------------------------------------------------------------------
 
+template <int MQ>
 struct DecodeLds {
   // byte offsets inside the dynamic LDS block
   static constexpr int red = 0;                                   // [WAVES][16][RED_STRIDE] f32
@@ -317,8 +318,9 @@ struct DecodeLds {
   static constexpr int lw = mw + WAVES * 8 * 4;                   // [WAVES][8] f32
   static constexpr int zw = lw + WAVES * 8 * 4;                   // [WAVES][32] f32
   static constexpr int ztw = zw + WAVES * 32 * 4;                 // [WAVES][8] f32
-  static constexpr int qs = ztw + WAVES * 8 * 4;                  // [8][D] bf16
-  static constexpr int ustat = qs + 8 * D * 2;                    // [WAVES][3] int: min, max,
+  static constexpr int QB = MQ == 2 ? WAVES : 1;                  // query-row blocks
+  static constexpr int qs = ztw + WAVES * 8 * 4;                  // [QB][8][D] bf16
+  static constexpr int ustat = qs + QB * 8 * D * 2;               // [WAVES][3] int: min, max,
                                                                   // count of units (> 0)
   static constexpr int pre = ustat + WAVES * 3 * 4;               // [B + 1] int
   // per-channel key folding buffer [WAVES][2][8][D] f16 overlays `red` (never live together)
@@ -349,10 +351,14 @@ __device__ __forceinline__ int aligned_ranges(int nb, int S, bool uniform) {
   return (S / k >= (nb + 1) / 2) ? S / k : nb;
 }
 
-template <int KB, int G, bool KPC, int NP, int SCH, bool MQ>
-__global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_kernel(DecodeParams p) {
+template <int KB, int G, bool KPC, int NP, int SCH, int MQ>
+__global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2) ? 3 : 2) void decode_kernel(DecodeParams p) {
   // multi-query geometry; single-query instantiations fold it to constants
   const int nqt = MQ ? p.nqt : 1, qbs = MQ ? p.qbs : 1, nqb = MQ ? p.nqb : 1, gkv = MQ ? p.gkv : G;
+  // query blocks per segment, one per wave (1: the waves interleave the units of one block),
+  // and segments per (sequence, kv head)
+  constexpr int qpw = MQ == 2 ? WAVES : 1;
+  const int nqs = MQ ? p.nqs : 1;
   constexpr bool ASYM = SCH == KVQ_ASYM;
   constexpr bool F8 = SCH == KVQ_FP8;  // E4M3 bytes, one scale per kv head (or tensor) per side
   extern __shared__ __align__(16) unsigned char smem[];
@@ -361,15 +367,15 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
   const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63;
   const int g = lane >> 4, n = lane & 15;
 
-  float* red = reinterpret_cast<float*>(smem + DecodeLds::red);
-  float* mw = reinterpret_cast<float*>(smem + DecodeLds::mw);
-  float* lw = reinterpret_cast<float*>(smem + DecodeLds::lw);
-  float* zw = reinterpret_cast<float*>(smem + DecodeLds::zw);
-  float* ztw = reinterpret_cast<float*>(smem + DecodeLds::ztw);
-  uint16_t* qs = reinterpret_cast<uint16_t*>(smem + DecodeLds::qs);
-  int* pre = reinterpret_cast<int*>(smem + DecodeLds::pre);
-  int* ustat = reinterpret_cast<int*>(smem + DecodeLds::ustat);
-  uint16_t* kf = reinterpret_cast<uint16_t*>(smem + DecodeLds::kf) + wave * 2 * 8 * D;
+  float* red = reinterpret_cast<float*>(smem + DecodeLds<MQ>::red);
+  float* mw = reinterpret_cast<float*>(smem + DecodeLds<MQ>::mw);
+  float* lw = reinterpret_cast<float*>(smem + DecodeLds<MQ>::lw);
+  float* zw = reinterpret_cast<float*>(smem + DecodeLds<MQ>::zw);
+  float* ztw = reinterpret_cast<float*>(smem + DecodeLds<MQ>::ztw);
+  uint16_t* qs = reinterpret_cast<uint16_t*>(smem + DecodeLds<MQ>::qs);
+  int* pre = reinterpret_cast<int*>(smem + DecodeLds<MQ>::pre);
+  int* ustat = reinterpret_cast<int*>(smem + DecodeLds<MQ>::ustat);
+  uint16_t* kf = reinterpret_cast<uint16_t*>(smem + DecodeLds<MQ>::kf) + wave * 2 * 8 * D;
 
   // ---- units per sequence, prefix sum (every workgroup; workgroup 0 publishes it) ----
   {
@@ -381,7 +387,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
       if (un < 0) {
         if (blockIdx.x == 0) atomicOr(c.err, KVQ_ERR_TOKENS);
       } else {
-        s += un * H * nqb;
+        s += un * H * nqs;
         if (un > 0) {
           umin = min(umin, un);
           umax = max(umax, un);
@@ -410,7 +416,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
     int run = scan[tid] - s;
     for (int i = tid * per; i < min(B, (tid + 1) * per); i++) {
       pre[i] = run;
-      run += max(seq_units(c, p.max_tokens, i), 0) * H * nqb;
+      run += max(seq_units(c, p.max_tokens, i), 0) * H * nqs;
     }
     if (tid == 255) pre[B] = scan[255];
     __syncthreads();
@@ -425,7 +431,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
     umax = max(umax, ustat[3 * w + 1]);
     useq += ustat[3 * w + 2];
   }
-  const int nbe = uni(aligned_ranges(gridDim.x, useq * H * nqb, umin == umax));
+  const int nbe = uni(aligned_ranges(gridDim.x, useq * H * nqs, umin == umax));
   if (blockIdx.x == 0) {
     for (int i = tid; i <= B; i += 256) p.ws_pre[i] = pre[i];
     if (tid == 0) p.ws_pre[B + 1] = nbe;
@@ -436,8 +442,8 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
   const int u1 = static_cast<int>((static_cast<long long>(blockIdx.x + 1) * U) / NBl);
   if (u0 == u1) {
     // An empty range still owns slot 0, which the combine may read: make it neutral.
-    float* part = p.ws_part + static_cast<size_t>(blockIdx.x) * 2 * G * PART_STRIDE;
-    for (int i = tid; i < G * PART_STRIDE; i += 256) part[i] = (i % PART_STRIDE == 0) ? -FLT_MAX : 0.0f;
+    float* part = p.ws_part + static_cast<size_t>(blockIdx.x) * 2 * qpw * G * PART_STRIDE;
+    for (int i = tid; i < qpw * G * PART_STRIDE; i += 256) part[i] = (i % PART_STRIDE == 0) ? -FLT_MAX : 0.0f;
     return;
   }
 
@@ -469,9 +475,11 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
     }
     const int b = uni(lo);
     const int pb0 = uni(pre[b]);
-    const int ub = uni((pre[b + 1] - pb0) / (H * nqb));
+    const int ub = uni((pre[b + 1] - pb0) / (H * nqs));
     const int sidx = (u - pb0) / ub, kk = (u - pb0) % ub;
-    const int h = sidx / nqb, qblk = sidx % nqb;
+    const int h = sidx / nqs, qgrp = sidx % nqs;
+    const int qi = (qpw > 1) ? wave : 0;  // this wave's query block within the segment
+    const int qblk = qgrp * qpw + qi;
     const int seg_abs_end = pb0 + (sidx + 1) * ub;
     const int uend = min(u1, seg_abs_end);
     const bool complete = (kk == 0) && (uend == seg_abs_end);
@@ -483,15 +491,26 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
 
     // ---- issue the segment's first loads before staging its query: the query rows, the
     // block-table entries and the first unit's codes and scales are in flight together ----
-    uint4 qval = uint4{0u, 0u, 0u, 0u};  // query row v = query token qblk * qbs + v / gkv,
-    if (tid < G * (D / 8)) {             // query head h * gkv + v % gkv (zero past the last)
-      const int v = tid / (D / 8), qg = qblk * qbs + v / gkv;
-      if (qg < nqt)
-        qval = reinterpret_cast<const uint4*>(
-            p.q + ((static_cast<size_t>(b) * nqt + qg) * p.Hq +
-                   static_cast<size_t>(h) * gkv + v % gkv) * D)[tid % (D / 8)];
+    // query row v of block bi = query token (qgrp qpw + bi) qbs + v / gkv, query head
+    // h gkv + v % gkv (zero past the last); up to two 16-byte pieces per thread
+    constexpr int QPC = MQ == 2 ? 2 : 1;
+    uint4 qval[QPC];
+#pragma unroll
+    for (int k = 0; k < QPC; k++) {
+      qval[k] = uint4{0u, 0u, 0u, 0u};
+      const int piece = tid + 256 * k;
+      if (piece < qpw * G * (D / 8)) {
+        const int row = piece / (D / 8), bi = row / G, v = row % G;
+        const int qg = (qgrp * qpw + bi) * qbs + v / gkv;
+        if (qg < nqt)
+          qval[k] = reinterpret_cast<const uint4*>(
+              p.q + ((static_cast<size_t>(b) * nqt + qg) * p.Hq +
+                     static_cast<size_t>(h) * gkv + v % gkv) * D)[piece % (D / 8)];
+      }
     }
-    int x = kk + wave;
+    // with one block per wave every wave walks all units; a wave past the last block idles
+    const int xstep = (qpw > 1) ? 1 : WAVES;
+    int x = (qpw > 1) ? ((qblk < nqb) ? kk : xend) : kk + wave;
     const int xq_end = min(xend, uq);
 
     // PV row roles: row 16 pp + n is (part, value group, head hh)
@@ -593,8 +612,16 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
 
     // ---- stage the segment's G query rows (bf16) ----
     __syncthreads();
-    if (tid < G * (D / 8)) reinterpret_cast<uint4*>(qs)[tid] = qval;
+#pragma unroll
+    for (int k = 0; k < QPC; k++) {
+      const int piece = tid + 256 * k;
+      if (piece < qpw * G * (D / 8)) {
+        const int row = piece / (D / 8);
+        reinterpret_cast<uint4*>(qs + ((row / G) * 8 + row % G) * D)[piece % (D / 8)] = qval[k];
+      }
+    }
     __syncthreads();
+    const uint16_t* qsw = qs + qi * 8 * D;  // this wave's query rows
     // causal limit (multi-query): the block's first query token sees the first lim_min cached
     // tokens (the query tokens are the last nqt), column n's token lim_min + hh / gkv of them;
     // single-query decode has no limit
@@ -611,11 +638,11 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
     if constexpr (BF) {
 #pragma unroll
       for (int j = 0; j < 4; j++)
-        qbf[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qs + hh * D + 32 * g + 8 * j));
+        qbf[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qsw + hh * D + 32 * g + 8 * j));
     } else if constexpr (F8) {
 #pragma unroll
       for (int j = 0; j < 4; j++) {
-        const u16x8 raw = *reinterpret_cast<const u16x8*>(qs + hh * D + 32 * g + 8 * j);
+        const u16x8 raw = *reinterpret_cast<const u16x8*>(qsw + hh * D + 32 * g + 8 * j);
 #pragma unroll
         for (int i = 0; i < 8; i++) qb[j][i] = static_cast<_Float16>(bf16_to_f32(raw[i]));
       }
@@ -627,7 +654,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
       const bool in_grp = ((32 * g) / kgroup) == cg;
 #pragma unroll
       for (int j = 0; j < 4; j++) {
-        const u16x8 raw = gather_kchan<KB>(qs + hh * D + 32 * g, j);
+        const u16x8 raw = gather_kchan<KB>(qsw + hh * D + 32 * g, j);
 #pragma unroll
         for (int i = 0; i < 8; i++) {
           const float x = in_grp ? bf16_to_f32(raw[i]) : 0.0f;
@@ -750,7 +777,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
 #pragma unroll
         for (int r0 = 0; r0 < G; r0 += 4) {
           const int hw = min(r0 + (lane >> 4), G - 1);
-          const u16x8 q8 = gather_kchan<KB>(qs + hw * D + 32 * (fold_blk / 4), fold_blk % 4);
+          const u16x8 q8 = gather_kchan<KB>(qsw + hw * D + 32 * (fold_blk / 4), fold_blk % 4);
 #pragma unroll
           for (int i = 0; i < 8; i++) qfold[r0 / 4][i] = bf16_to_f32(q8[i]);
         }
@@ -834,8 +861,8 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
         if constexpr (ASYM) ztc = (cg == 0) ? zt : 0.0f;
       };
 
-      for (; x < xq_end; x += WAVES) {
-        const int xn = x + WAVES;
+      for (; x < xq_end; x += xstep) {
+        const int xn = x + xstep;
         const bool more = xn < xq_end;
         // after the last unit, reload the current tiles (cache hits) so the load count per
         // iteration stays fixed
@@ -1087,13 +1114,13 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
       const bool keep = KPC ? (cg == 0) : (((32 * g) / kgroup) == cg);
 #pragma unroll
       for (int j = 0; j < 4; j++) {
-        u16x8 raw = *reinterpret_cast<const u16x8*>(qs + hh * D + 32 * g + 8 * j);
+        u16x8 raw = *reinterpret_cast<const u16x8*>(qsw + hh * D + 32 * g + 8 * j);
         if (!keep) raw = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
         qw[j] = __builtin_bit_cast(bf16x8, raw);
       }
       const uint16_t* kr = c.kres + (static_cast<size_t>(b) * H + h) * c.R * D;
       const uint16_t* vr = c.vres + (static_cast<size_t>(b) * H + h) * c.R * D;
-      for (; x < xend; x += WAVES) {
+      for (; x < xend; x += xstep) {
         const int r0 = 32 * (x - uq);
         const int nvA = min(16, nr - r0), nvB = max(0, min(16, nr - r0 - 16));
         float s2[8];
@@ -1175,6 +1202,56 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16) ? 3 : 2) void decode_ker
     if (lane < 16) {
 #pragma unroll
       for (int pp = 0; pp < NP; pp++) zw[wave * 32 + 16 * pp + lane] = zs[pp];
+    }
+    if constexpr (MQ == 2) {
+      // one query block per wave: each wave normalises (or writes the partial of) its own
+      // block from its own rows of the merge buffer, no merge across waves
+      constexpr int NOW = (G * D) / 64;  // outputs per lane
+      float Ow[NOW];
+#pragma unroll
+      for (int pp = 0; pp < NP; pp++) {
+        wave_lds_sync();  // the previous pass's reads (or the m / l / z stores) are done
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+#pragma unroll
+          for (int r = 0; r < 4; r++) red[(wave * 16 + 4 * g + r) * RED_STRIDE + 8 * n + j] = acc[pp][j][r];
+        wave_lds_sync();
+#pragma unroll
+        for (int oi = 0; oi < NOW; oi++) {
+          const int o = lane + 64 * oi;
+          const int oh = o / D, ch = o % D;
+          const int gv = ch / vgroup;
+          if (pp == 0) Ow[oi] = ASYM ? zw[wave * 32 + gv * G + oh] : 0.0f;
+#pragma unroll
+          for (int part = 0; part < 2; part++) {
+            const int row = (part * ngv + gv) * G + oh;
+            if (row / 16 == pp) Ow[oi] += red[(wave * 16 + row % 16) * RED_STRIDE + ch];
+          }
+        }
+      }
+#pragma unroll
+      for (int oi = 0; oi < NOW; oi++) {
+        const int o = lane + 64 * oi;
+        const int oh = o / D, ch = o % D;
+        const float L = lw[wave * 8 + oh];
+        if (complete) {
+          const int qg = qblk * qbs + oh / gkv;
+          if (qg < nqt)
+            p.out[((static_cast<size_t>(b) * nqt + qg) * p.Hq + static_cast<size_t>(h) * gkv +
+                   oh % gkv) * D + ch] = (L > 0.0f) ? Ow[oi] / L : 0.0f;
+        } else {
+          float* part = p.ws_part +
+                        (((static_cast<size_t>(blockIdx.x) * 2 + slot) * qpw + qi) * G + oh) * PART_STRIDE;
+          if (ch == 0) {
+            part[0] = mw[wave * 8 + oh];
+            part[1] = L;
+          }
+          part[4 + ch] = Ow[oi];
+        }
+      }
+      u = uend;
+      first_seg = false;
+      continue;
     }
     constexpr int NO = (G * D + 255) / 256;
     float O[NO], Mx[NO], e[NO][WAVES];
@@ -1268,16 +1345,19 @@ __global__ __launch_bounds__(COMBINE_THREADS) void combine_kernel(DecodeParams p
   static_assert((G * D) % S == 0 && (G * D) / S >= 32, "combine slices");
   __shared__ float sm[COMBINE_THREADS], sl[COMBINE_THREADS], so[COMBINE_THREADS];
   const int H = p.c.H, B = p.c.B;
-  const int SEGS = H * p.nqb;  // segments per sequence: (kv head, query block)
-  const int b = blockIdx.x / SEGS, sidx = blockIdx.x % SEGS;
-  const int h = sidx / p.nqb, qblk = sidx % p.nqb;
+  // one workgroup per (sequence, kv head, query block); the decode segment holding the block is
+  // (kv head, group of qpw blocks), the block's partials sit at position qi of each slot
+  const int QB = H * p.nqb;
+  const int b = blockIdx.x / QB, hq = blockIdx.x % QB;
+  const int h = hq / p.nqb, qblk = hq % p.nqb;
+  const int qpw = p.qpw, qi = qblk % qpw, sidx = h * p.nqs + qblk / qpw;
   constexpr int opb = (G * D) / S;
   constexpr int opp = opb < 256 ? opb : 256;
   constexpr int cg = COMBINE_THREADS / opp;
   const int oi = threadIdx.x % opp, cgi = threadIdx.x / opp;
   const int* pre = p.ws_pre;
   const long long U = pre[B], NB = pre[B + 1];  // ranges the decode launch used
-  const int ub = (pre[b + 1] - pre[b]) / SEGS;
+  const int ub = (pre[b + 1] - pre[b]) / (H * p.nqs);
   // output element o of the segment's G x D block (row o / D: query token, query head)
   auto dst = [&](int o) -> float* {
     const int row = o / D, qg = qblk * p.qbs + row / p.gkv;
@@ -1301,7 +1381,7 @@ __global__ __launch_bounds__(COMBINE_THREADS) void combine_kernel(DecodeParams p
 #pragma unroll 4
     for (int k = kf + cgi; k <= kl; k += cg) {
       const float* pt =
-          p.ws_part + ((static_cast<size_t>(k) * 2 + (k == kf ? s0 : 0)) * G + oh) * PART_STRIDE;
+          p.ws_part + (((static_cast<size_t>(k) * 2 + (k == kf ? s0 : 0)) * qpw + qi) * G + oh) * PART_STRIDE;
       const float m = pt[0], l = pt[1], v = pt[4 + ch];
       const float mn = fmaxf(M, m);
       const float a = __builtin_amdgcn_exp2f(M - mn), e = __builtin_amdgcn_exp2f(m - mn);
@@ -1333,7 +1413,7 @@ __global__ __launch_bounds__(COMBINE_THREADS) void combine_kernel(DecodeParams p
 // Workgroups of decode_kernel that are resident at once on the current device.  Each workgroup
 // owns 1/NB of the units, so the grid must never exceed what runs concurrently.  The answer
 // depends on the device and the LDS size alone and is cached per instantiation.
-template <int KB, int G, bool KPC, int NP, int SCH, bool MQ>
+template <int KB, int G, bool KPC, int NP, int SCH, int MQ>
 int decode_resident_blocks(size_t lds) {
   static std::mutex mu;
   static int cached_dev = -1, cached_blocks = 0;
@@ -1356,10 +1436,10 @@ int decode_resident_blocks(size_t lds) {
   return cached_blocks;
 }
 
-template <int KB, int G, bool KPC, int NP, int SCH, bool MQ>
+template <int KB, int G, bool KPC, int NP, int SCH, int MQ>
 hipError_t launch_decode_t(const DecodeParams& p0, hipStream_t s) {
   DecodeParams p = p0;
-  const size_t lds = DecodeLds::bytes(p.c.B);
+  const size_t lds = DecodeLds<MQ>::bytes(p.c.B);
   const int resident = decode_resident_blocks<KB, G, KPC, NP, SCH, MQ>(lds);
   if (resident <= 0) return hipErrorInvalidConfiguration;
   if (p.nblocks > resident) p.nblocks = resident;
@@ -1367,7 +1447,7 @@ hipError_t launch_decode_t(const DecodeParams& p0, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // slices: about one per 4 partials a segment has on average, 32 outputs per slice at most
-  const int avg = p.nblocks / (p.c.B * p.c.H * p.nqb);
+  const int avg = p.nblocks / (p.c.B * p.c.H * p.nqs);
   int slices = 1;
   while (slices < 16 && slices * 2 <= avg / 4 && (G * D) / (slices * 2) >= 32) slices *= 2;
   const dim3 grid(p.c.B * p.c.H * p.nqb, slices);
@@ -1381,7 +1461,7 @@ hipError_t launch_decode_t(const DecodeParams& p0, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int KB, int SCH, bool MQ>
+template <int KB, int SCH, int MQ>
 hipError_t launch_decode_mq(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s) {
   if constexpr (KB == 16 || SCH == KVQ_FP8) {  // whole-row formats: at most 16 PV rows
     if (kpc || NP != 1) return hipErrorInvalidValue;
@@ -1408,12 +1488,14 @@ hipError_t launch_decode_mq(const DecodeParams& p, int G, int NP, bool kpc, hipS
   }
 }
 
-// Single-query decode and multi-query decode are separate instantiations, so the single-query
-// kernel carries none of the query-block bookkeeping.
+// Single-query decode and the two multi-query modes are separate instantiations, so the
+// single-query kernel carries none of the query-block bookkeeping: mode 1 has the waves of a
+// workgroup interleave the units of one query block, mode 2 gives each wave its own block.
 template <int KB, int SCH>
 hipError_t launch_decode_bits(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s) {
-  return p.nqt > 1 ? launch_decode_mq<KB, SCH, true>(p, G, NP, kpc, s)
-                   : launch_decode_mq<KB, SCH, false>(p, G, NP, kpc, s);
+  if (p.nqt <= 1) return launch_decode_mq<KB, SCH, 0>(p, G, NP, kpc, s);
+  return p.qpw > 1 ? launch_decode_mq<KB, SCH, 2>(p, G, NP, kpc, s)
+                   : launch_decode_mq<KB, SCH, 1>(p, G, NP, kpc, s);
 }
 
 }  // namespace kvq

@@ -68,13 +68,16 @@ struct DecodeParams {
   float* out;         // [B][nqt][Hq][D] fp32
   int32_t* ws_pre;    // [B + 1] prefix over sequences of work units (all kv heads), then
                       // the number of unit ranges in use
-  float* ws_part;     // [nblocks][2][G][PART_STRIDE] partial (max, sum, pad, pad, o[D])
+  float* ws_part;     // [nblocks][2][qpw][G][PART_STRIDE] partial (max, sum, pad, pad, o[D])
   int Hq, max_tokens, nblocks;
   float sm_log2;      // sm_scale * log2(e)
   // Queries per sequence: nqt query tokens, the last nqt cached tokens (1: single-query decode).
-  // A segment is one (sequence, kv head, query block) whose G rows are qbs query tokens x gkv
-  // query heads (G = qbs * gkv); nqb = ceil(nqt / qbs) query blocks per (sequence, kv head).
-  int nqt, qbs, nqb, gkv;
+  // A query block has G rows, qbs query tokens x gkv query heads (G = qbs * gkv); there are
+  // nqb = ceil(nqt / qbs) blocks per (sequence, kv head).  A segment is one (sequence, kv head,
+  // group of qpw blocks): with qpw = 4 each wave of a workgroup takes one block and all waves
+  // walk the same units (the codes are fetched once for four blocks); with qpw = 1 the waves
+  // interleave the units of one block.  nqs = ceil(nqb / qpw) segments per (sequence, kv head).
+  int nqt, qbs, nqb, gkv, qpw, nqs;
 };
 
 constexpr int PART_STRIDE = D + 4;

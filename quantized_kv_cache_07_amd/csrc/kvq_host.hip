@@ -152,6 +152,7 @@ CacheDev to_dev(const kvq_cache* c) {
 struct WsLayout {
   int G, nblocks;  // G: rows of a segment (query tokens per block x query heads per kv head)
   int qbs, nqb;    // query tokens per block, query blocks per (sequence, kv head)
+  int qpw, nqs;    // query blocks per segment (one per wave, or 1), segments per (seq, kv head)
   size_t pre_off, part_off, total;
 };
 
@@ -185,6 +186,10 @@ WsLayout ws_layout(const kvq_cache* c, int n_q_heads, int max_tokens, int n_q = 
   w.qbs = query_block(c, gkv, n_q);
   w.nqb = (n_q + w.qbs - 1) / w.qbs;
   w.G = gkv * w.qbs;
+  // four or more blocks: one per wave, so the waves of a workgroup read the same codes (with
+  // fewer, waves would idle; the waves then interleave the units of one block instead)
+  w.qpw = w.nqb >= 4 ? 4 : 1;
+  w.nqs = (w.nqb + w.qpw - 1) / w.qpw;
   long nb = static_cast<long>(device_cus()) * 4;
   if (const char* e = std::getenv("KVQ_DECODE_BLOCKS")) {
     const long v = std::atol(e);
@@ -192,13 +197,15 @@ WsLayout ws_layout(const kvq_cache* c, int n_q_heads, int max_tokens, int n_q = 
   }
   // small batches get fewer, fuller workgroups: about two units per wave (on the 8 K-token
   // worked example 12.7 us per call against 16.0 us at one unit per wave and 14.1 us at four)
-  const long ub = (units_bound(c, max_tokens) * w.nqb + 7) / 8;
+  // (each wave walks every unit of its range when the waves take separate blocks)
+  const long ub = w.qpw > 1 ? (units_bound(c, max_tokens) * w.nqs + 1) / 2
+                            : (units_bound(c, max_tokens) * w.nqb + 7) / 8;
   if (nb > ub) nb = ub;
   if (nb < 1) nb = 1;
   w.nblocks = static_cast<int>(nb);
   w.pre_off = 0;
   w.part_off = ((static_cast<size_t>(c->batch) + 2) * 4 + 255) & ~static_cast<size_t>(255);
-  w.total = w.part_off + static_cast<size_t>(w.nblocks) * 2 * w.G * PART_STRIDE * 4;
+  w.total = w.part_off + static_cast<size_t>(w.nblocks) * 2 * w.qpw * w.G * PART_STRIDE * 4;
   return w;
 }
 
@@ -380,6 +387,8 @@ kvq_status kvq_decode_attention_mq(const kvq_cache* cache, const void* q, int32_
   p.qbs = w.qbs;
   p.nqb = w.nqb;
   p.gkv = gkv;
+  p.qpw = w.qpw;
+  p.nqs = w.nqs;
 
   if (std::getenv("KVQ_DEBUG"))
     fprintf(stderr, "[kvq] decode B=%d H=%d G=%d (n_q %d, %d per block) bits=%d NP=%d kpc=%d blocks=%d ws=%zu\n",

@@ -243,6 +243,10 @@ MQ_CASES = [
     ("mq-kivi-int2", KPC2, ASYM2_32, 2, 8, 2, 128, [700, 1300], False, 8),
     ("mq-fp8-gqa8-paged", FP8H, FP8H, 1, 16, 2, 16, [600], True, 3),
     ("mq-bf16-gqa2", BF16, BF16, 2, 4, 2, 0, [333, 64], False, 16),
+    # one query block per wave, with idle waves in the last group and a sequence shorter than n_q
+    ("mq-int4-gqa4-ragged-idle-waves", SYM4, SYM4, 3, 8, 2, 16, [50, 3, 200], False, 13),
+    ("mq-int4-paged-idle-waves", SYM4, SYM4, 2, 8, 2, 32, [900, 70], True, 9),
+    ("mq-int8-g32-two-row-blocks", (8, 0, 0, 32), (8, 0, 0, 32), 2, 8, 2, 0, [400, 1100], False, 12),
 ]
 
 
