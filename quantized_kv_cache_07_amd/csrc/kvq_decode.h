@@ -1,4 +1,4 @@
-// kvq_decode.h -- single-query decode attention over the quantized cache (gfx950 kernels).
+// kvq_decode.h -- decode attention over the quantized cache (gfx950 kernels).
 //
 //   out[b][hq] = softmax(sm_scale * q K^T) V          [P2 = llmdaily.org "KV-cache quantization --
 //   making long-context inference fit in memory", "Why the KV cache grows so quickly", attention
@@ -13,18 +13,24 @@
 // unit whatever the length mix.  Inside a workgroup the four waves interleave the units of each
 // (sequence, kv head) segment; at a segment end the waves merge in LDS and the workgroup writes
 // either the normalised output (the segment was the whole sequence) or a partial (max, sum,
-// o[128]) that combine_kernel merges with a log-sum-exp rescale.
+// o[128]) that combine_kernel merges with a log-sum-exp rescale.  Multi-query decode with four
+// or more query blocks per (sequence, kv head) gives each wave its own block instead, all four
+// walking the same units (mode 2).
 //
 // One unit on one wave (lane = 16 g + n):
 //   QK^T  4 MFMA 16x16x32 f16 per tile: D[token][col] = sum_k A[token][k] B[k][col], A = key
-//         codes of token n turned into exact f16 integers (0x6400 exponent trick), B = the query
-//         rows of the GQA group, one column per (key group, query head) with the other groups'
-//         channels zeroed, so per-token group scales apply to the products; per-channel key
-//         scales are folded into the query (hi + lo f16 parts) once per key group.
+//         codes of token n as f16 operands (a masked field under the exponent of 1024, or, for
+//         per-channel keys, under a zero exponent: an exact subnormal), B = the query rows of
+//         the GQA group divided by each field's power-of-two position factor, one column per
+//         (key group, query head) with the other groups' channels zeroed, so per-token group
+//         scales apply to the products; per-channel key scales are folded into the query (hi +
+//         lo f16 parts) once per key group.
 //   softmax  online, in log2 units; the running max is only raised when a score exceeds it by
 //         more than 8 (weights stay <= 2^8), so the accumulator is rarely rescaled.
-//   PV    8 MFMA 16x16x32 f16 per pair and row block: D[row][ch] = sum_t P[row][t] V[t][ch] with
-//         rows (hi/lo part, value group, query head) of w * s_v, 32 tokens (both tiles) deep.
+//   PV    8 MFMA 16x16x32 f16 per row block: D[row][ch] = sum_t P[row][t] V[t][ch] with rows
+//         (hi/lo part, value group, query head) of w * s_v, 32 tokens (both tiles) deep; value
+//         codes enter as f16 subnormals (one AND per two codes), the symmetric offset as one
+//         more product per unit.
 //   Codes of the next unit are loaded as soon as the current ones are consumed.
 #pragma once
 
