@@ -1336,20 +1336,20 @@ __device__ __forceinline__ int block_of(long long u, long long U, long long NB) 
 }
 
 // Merge the partials of each (sequence, kv head) that more than one workgroup worked on; write
-// zeros for empty sequences.  One workgroup of 1024 threads per (sequence, kv head): each
-// output is merged by CG threads over interleaved partials, then across them in LDS.
-constexpr int COMBINE_THREADS = 1024;
-
-// Merge the partials of one (sequence, kv head): grid (B * H, S) with S slices of its G x D
-// outputs.  A workgroup takes OPP = min(G D / S, 256) outputs per pass with CG = 1024 / OPP
+// zeros for empty sequences.  Each output is merged by CG threads over interleaved partials,
+// then across them in LDS.
+//
+// Grid (B * H * query blocks, S) with S slices of a block's G x D outputs; T threads per
+// workgroup.  A workgroup takes OPP = min(G D / S, 256) outputs per pass with CG = T / OPP
 // threads each; thread (cgi, oi) folds partials kf + cgi, kf + cgi + CG, ... with the
 // log-sum-exp rule, and the OPP threads of a group read contiguous floats of one partial.
-// S is chosen on the host from the partials a segment has on average: many slices when few
-// segments are split many ways (one long sequence), one or two when many short segments are.
-template <int G, int S>
-__global__ __launch_bounds__(COMBINE_THREADS) void combine_kernel(DecodeParams p) {
+// S and T are chosen on the host from the partials a segment has on average: many slices and
+// 1024 threads when few segments are split many ways (one long sequence), one slice of 256
+// threads when many short segments have a partial or two each (a smaller launch).
+template <int G, int S, int T>
+__global__ __launch_bounds__(T) void combine_kernel(DecodeParams p) {
   static_assert((G * D) % S == 0 && (G * D) / S >= 32, "combine slices");
-  __shared__ float sm[COMBINE_THREADS], sl[COMBINE_THREADS], so[COMBINE_THREADS];
+  __shared__ float sm[T], sl[T], so[T];
   const int H = p.c.H, B = p.c.B;
   // one workgroup per (sequence, kv head, query block); the decode segment holding the block is
   // (kv head, group of qpw blocks), the block's partials sit at position qi of each slot
@@ -1359,7 +1359,7 @@ __global__ __launch_bounds__(COMBINE_THREADS) void combine_kernel(DecodeParams p
   const int qpw = p.qpw, qi = qblk % qpw, sidx = h * p.nqs + qblk / qpw;
   constexpr int opb = (G * D) / S;
   constexpr int opp = opb < 256 ? opb : 256;
-  constexpr int cg = COMBINE_THREADS / opp;
+  constexpr int cg = T / opp;
   const int oi = threadIdx.x % opp, cgi = threadIdx.x / opp;
   const int* pre = p.ws_pre;
   const long long U = pre[B], NB = pre[B + 1];  // ranges the decode launch used
@@ -1372,7 +1372,7 @@ __global__ __launch_bounds__(COMBINE_THREADS) void combine_kernel(DecodeParams p
                     row % p.gkv) * D + o % D;
   };
   if (ub == 0) {
-    for (int o = threadIdx.x; o < opb; o += COMBINE_THREADS)
+    for (int o = threadIdx.x; o < opb; o += T)
       if (float* d = dst(static_cast<int>(blockIdx.y) * opb + o)) *d = 0.0f;
     return;
   }
@@ -1457,12 +1457,13 @@ hipError_t launch_decode_t(const DecodeParams& p0, hipStream_t s) {
   int slices = 1;
   while (slices < 16 && slices * 2 <= avg / 4 && (G * D) / (slices * 2) >= 32) slices *= 2;
   const dim3 grid(p.c.B * p.c.H * p.nqb, slices);
-  switch (slices) {
-    case 1: combine_kernel<G, 1><<<grid, COMBINE_THREADS, 0, s>>>(p); break;
-    case 2: combine_kernel<G, 2><<<grid, COMBINE_THREADS, 0, s>>>(p); break;
-    case 4: combine_kernel<G, 4><<<grid, COMBINE_THREADS, 0, s>>>(p); break;
-    case 8: if constexpr (G >= 2) combine_kernel<G, 8><<<grid, COMBINE_THREADS, 0, s>>>(p); break;
-    default: if constexpr (G >= 4) combine_kernel<G, 16><<<grid, COMBINE_THREADS, 0, s>>>(p); break;
+  switch (avg < 8 ? 0 : slices) {  // 0: one slice, 256 threads for short partial chains
+    case 0: combine_kernel<G, 1, 256><<<grid, 256, 0, s>>>(p); break;
+    case 1: combine_kernel<G, 1, 1024><<<grid, 1024, 0, s>>>(p); break;
+    case 2: combine_kernel<G, 2, 1024><<<grid, 1024, 0, s>>>(p); break;
+    case 4: combine_kernel<G, 4, 1024><<<grid, 1024, 0, s>>>(p); break;
+    case 8: if constexpr (G >= 2) combine_kernel<G, 8, 1024><<<grid, 1024, 0, s>>>(p); break;
+    default: if constexpr (G >= 4) combine_kernel<G, 16, 1024><<<grid, 1024, 0, s>>>(p); break;
   }
   return hipGetLastError();
 }
