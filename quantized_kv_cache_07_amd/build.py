@@ -1,7 +1,9 @@
 """Build libkvq.so in place: hipcc for gfx950, one object per source, compiled in parallel.
 
 Flags: -O3, no fast-math (HIP's default correctly rounded fp32 division is kept), and packed
-fp32 arithmetic disabled (-Xclang -target-feature -Xclang -packed-fp32-ops).
+fp32 arithmetic disabled (-Xclang -target-feature -Xclang -packed-fp32-ops).  f16 denormals must
+stay enabled (the default): the decode kernels feed code fields to the matrix cores as exact f16
+subnormals, so no denormal-flushing option may be added here.
 """
 from __future__ import annotations
 
