@@ -579,7 +579,10 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2) ? 3 : 2) void
       load_words<KB>(c.kc + static_cast<size_t>(pB) * TILE_BYTES + k_lane, d.kw[1]);
       if constexpr (BF || F8) {
       } else if constexpr (KPC) {
-        const size_t mi = kpc_meta((32 * xx) / kgroup);
+        // a paged key group of 16 or 32 tokens starts at this unit's tile A, whose block then
+        // holds the group's metadata row: no second block-table read
+        const size_t mi = (trow && kgroup <= 2 * TILE) ? static_cast<size_t>(pA) * D + fold_c0
+                                                       : kpc_meta((32 * xx) / kgroup);
         d.fs = load_meta8(c.ks, mi);
         if constexpr (ASYM) d.fz = load_meta8(c.kz, mi);
       } else {
@@ -891,7 +894,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2) ? 3 : 2) void
 #pragma unroll
             for (int j = 0; j < 4; j++)
               dq[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop_sub<KB>(d.kw[0], j, ur), qb[j], dq[0], 0, 0, 0);
-            const size_t mi = kpc_meta(2 * x + 1);
+            const size_t mi = trow ? static_cast<size_t>(max(pB, 0)) * D + fold_c0 : kpc_meta(2 * x + 1);
             const uint4 fs2 = load_meta8(c.ks, mi);
             uint4 fz2 = uint4{0, 0, 0, 0};
             if constexpr (ASYM) fz2 = load_meta8(c.kz, mi);
