@@ -324,7 +324,7 @@ struct DecodeLds {
   static constexpr int lw = mw + WAVES * 8 * 4;                   // [WAVES][8] f32
   static constexpr int zw = lw + WAVES * 8 * 4;                   // [WAVES][32] f32
   static constexpr int ztw = zw + WAVES * 32 * 4;                 // [WAVES][8] f32
-  static constexpr int QB = MQ == 2 ? WAVES : 1;                  // query-row blocks
+  static constexpr int QB = MQ == 2 ? 4 : MQ == 3 ? 2 : 1;        // query-row blocks
   static constexpr int qs = ztw + WAVES * 8 * 4;                  // [QB][8][D] bf16
   static constexpr int ustat = qs + QB * 8 * D * 2;               // [WAVES][3] int: min, max,
                                                                   // count of units (> 0)
@@ -358,12 +358,13 @@ __device__ __forceinline__ int aligned_ranges(int nb, int S, bool uniform) {
 }
 
 template <int KB, int G, bool KPC, int NP, int SCH, int MQ>
-__global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2) ? 3 : 2) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 3 : 2) void decode_kernel(DecodeParams p) {
   // multi-query geometry; single-query instantiations fold it to constants
   const int nqt = MQ ? p.nqt : 1, qbs = MQ ? p.qbs : 1, nqb = MQ ? p.nqb : 1, gkv = MQ ? p.gkv : G;
   // query blocks per segment, one per wave (1: the waves interleave the units of one block),
   // and segments per (sequence, kv head)
-  constexpr int qpw = MQ == 2 ? WAVES : 1;
+  constexpr int qpw = MQ == 2 ? 4 : MQ == 3 ? 2 : 1;
+  constexpr int WPQ = WAVES / qpw;  // waves per query block
   const int nqs = MQ ? p.nqs : 1;
   constexpr bool ASYM = SCH == KVQ_ASYM;
   constexpr bool F8 = SCH == KVQ_FP8;  // E4M3 bytes, one scale per kv head (or tensor) per side
@@ -484,7 +485,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2) ? 3 : 2) void
     const int ub = uni((pre[b + 1] - pb0) / (H * nqs));
     const int sidx = (u - pb0) / ub, kk = (u - pb0) % ub;
     const int h = sidx / nqs, qgrp = sidx % nqs;
-    const int qi = (qpw > 1) ? wave : 0;  // this wave's query block within the segment
+    const int qi = wave / WPQ;  // this wave's query block within the segment
     const int qblk = qgrp * qpw + qi;
     const int seg_abs_end = pb0 + (sidx + 1) * ub;
     const int uend = min(u1, seg_abs_end);
@@ -514,9 +515,9 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2) ? 3 : 2) void
                      static_cast<size_t>(h) * gkv + v % gkv) * D)[piece % (D / 8)];
       }
     }
-    // with one block per wave every wave walks all units; a wave past the last block idles
-    const int xstep = (qpw > 1) ? 1 : WAVES;
-    int x = (qpw > 1) ? ((qblk < nqb) ? kk : xend) : kk + wave;
+    // the WPQ waves of a block interleave its units; waves past the last block idle
+    const int xstep = WPQ;
+    int x = (qblk < nqb) ? kk + wave % WPQ : xend;
     const int xq_end = min(xend, uq);
 
     // PV row roles: row 16 pp + n is (part, value group, head hh)
@@ -1262,8 +1263,9 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2) ? 3 : 2) void
       first_seg = false;
       continue;
     }
-    constexpr int NO = (G * D + 255) / 256;
-    float O[NO], Mx[NO], e[NO][WAVES];
+    // merge the WPQ waves of each of the qpw blocks (one block of all four waves unless mode 3)
+    constexpr int NO = (qpw * G * D + 255) / 256;
+    float O[NO], Mx[NO], e[NO][WPQ];
 #pragma unroll
     for (int pp = 0; pp < NP; pp++) {
       if (pp > 0) __syncthreads();
@@ -1275,24 +1277,25 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2) ? 3 : 2) void
 #pragma unroll
       for (int oi = 0; oi < NO; oi++) {
         const int o = tid + 256 * oi;
-        if (o >= G * D) continue;
-        const int oh = o / D, ch = o % D;
+        if (o >= qpw * G * D) continue;
+        const int qo = o / (G * D), oh = (o % (G * D)) / D, ch = o % D;  // block, row, channel
+        const int w0 = qo * WPQ;                                           // its first wave
         const int gv = ch / vgroup;
         if (pp == 0) {
           float M = -FLT_MAX;
 #pragma unroll
-          for (int wv = 0; wv < WAVES; wv++) M = fmaxf(M, mw[wv * 8 + oh]);
+          for (int k = 0; k < WPQ; k++) M = fmaxf(M, mw[(w0 + k) * 8 + oh]);
           Mx[oi] = M;
           O[oi] = 0.0f;
 #pragma unroll
-          for (int wv = 0; wv < WAVES; wv++) {
-            const float mv = mw[wv * 8 + oh];
-            e[oi][wv] = __builtin_amdgcn_exp2f(mv - M);  // waves without tokens hold -FLT_MAX
+          for (int k = 0; k < WPQ; k++) {
+            const float mv = mw[(w0 + k) * 8 + oh];
+            e[oi][k] = __builtin_amdgcn_exp2f(mv - M);  // waves without tokens hold -FLT_MAX
           }
           if constexpr (ASYM) {
             const int row0 = gv * G + oh;
 #pragma unroll
-            for (int wv = 0; wv < WAVES; wv++) O[oi] += e[oi][wv] * zw[wv * 32 + row0];
+            for (int k = 0; k < WPQ; k++) O[oi] += e[oi][k] * zw[(w0 + k) * 32 + row0];
           }
         }
 #pragma unroll
@@ -1300,27 +1303,28 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2) ? 3 : 2) void
           const int row = (part * ngv + gv) * G + oh;
           if (row / 16 != pp) continue;
 #pragma unroll
-          for (int wv = 0; wv < WAVES; wv++)
-            O[oi] += e[oi][wv] * red[(wv * 16 + row % 16) * RED_STRIDE + ch];
+          for (int k = 0; k < WPQ; k++)
+            O[oi] += e[oi][k] * red[((w0 + k) * 16 + row % 16) * RED_STRIDE + ch];
         }
       }
     }
 #pragma unroll
     for (int oi = 0; oi < NO; oi++) {
       const int o = tid + 256 * oi;
-      if (o >= G * D) continue;
-      const int oh = o / D, ch = o % D;
+      if (o >= qpw * G * D) continue;
+      const int qo = o / (G * D), oh = (o % (G * D)) / D, ch = o % D;
+      const int w0 = qo * WPQ;
       float L = 0.0f;
 #pragma unroll
-      for (int wv = 0; wv < WAVES; wv++) L += e[oi][wv] * lw[wv * 8 + oh];
+      for (int k = 0; k < WPQ; k++) L += e[oi][k] * lw[(w0 + k) * 8 + oh];
       if (complete) {
-        const int qg = qblk * qbs + oh / gkv;
+        const int qg = (qgrp * qpw + qo) * qbs + oh / gkv;
         if (qg < nqt)
           p.out[((static_cast<size_t>(b) * nqt + qg) * p.Hq + static_cast<size_t>(h) * gkv +
                  oh % gkv) * D + ch] = (L > 0.0f) ? O[oi] / L : 0.0f;
       } else {
-        float* part =
-            p.ws_part + ((static_cast<size_t>(blockIdx.x) * 2 + slot) * G + oh) * PART_STRIDE;
+        float* part = p.ws_part +
+                      (((static_cast<size_t>(blockIdx.x) * 2 + slot) * qpw + qo) * G + oh) * PART_STRIDE;
         if (ch == 0) {
           part[0] = Mx[oi];
           part[1] = L;
@@ -1498,14 +1502,18 @@ hipError_t launch_decode_mq(const DecodeParams& p, int G, int NP, bool kpc, hipS
   }
 }
 
-// Single-query decode and the two multi-query modes are separate instantiations, so the
-// single-query kernel carries none of the query-block bookkeeping: mode 1 has the waves of a
-// workgroup interleave the units of one query block, mode 2 gives each wave its own block.
+// Single-query decode and the three multi-query modes are separate instantiations, so the
+// single-query kernel carries none of the query-block bookkeeping: mode 1 has the four waves of
+// a workgroup interleave the units of one query block, mode 3 gives two blocks two waves each,
+// mode 2 gives each wave its own block.
 template <int KB, int SCH>
 hipError_t launch_decode_bits(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s) {
   if (p.nqt <= 1) return launch_decode_mq<KB, SCH, 0>(p, G, NP, kpc, s);
-  return p.qpw > 1 ? launch_decode_mq<KB, SCH, 2>(p, G, NP, kpc, s)
-                   : launch_decode_mq<KB, SCH, 1>(p, G, NP, kpc, s);
+  switch (p.qpw) {
+    case 4: return launch_decode_mq<KB, SCH, 2>(p, G, NP, kpc, s);
+    case 2: return launch_decode_mq<KB, SCH, 3>(p, G, NP, kpc, s);
+    default: return launch_decode_mq<KB, SCH, 1>(p, G, NP, kpc, s);
+  }
 }
 
 }  // namespace kvq

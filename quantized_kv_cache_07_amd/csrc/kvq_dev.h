@@ -75,8 +75,9 @@ struct DecodeParams {
   // A query block has G rows, qbs query tokens x gkv query heads (G = qbs * gkv); there are
   // nqb = ceil(nqt / qbs) blocks per (sequence, kv head).  A segment is one (sequence, kv head,
   // group of qpw blocks): with qpw = 4 each wave of a workgroup takes one block and all waves
-  // walk the same units (the codes are fetched once for four blocks); with qpw = 1 the waves
-  // interleave the units of one block.  nqs = ceil(nqb / qpw) segments per (sequence, kv head).
+  // walk the same units (the codes are fetched once for four blocks), with qpw = 2 two waves
+  // share each of two blocks, with qpw = 1 the four waves interleave the units of one block.
+  // nqs = ceil(nqb / qpw) segments per (sequence, kv head).
   int nqt, qbs, nqb, gkv, qpw, nqs;
 };
 

@@ -186,9 +186,9 @@ WsLayout ws_layout(const kvq_cache* c, int n_q_heads, int max_tokens, int n_q = 
   w.qbs = query_block(c, gkv, n_q);
   w.nqb = (n_q + w.qbs - 1) / w.qbs;
   w.G = gkv * w.qbs;
-  // four or more blocks: one per wave, so the waves of a workgroup read the same codes (with
-  // fewer, waves would idle; the waves then interleave the units of one block instead)
-  w.qpw = w.nqb >= 4 ? 4 : 1;
+  // several blocks share a segment, so the waves of a workgroup read the same codes: four blocks
+  // one per wave, or two blocks of two waves each (with more blocks than waves would idle)
+  w.qpw = w.nqb >= 4 ? 4 : w.nqb >= 2 ? 2 : 1;
   w.nqs = (w.nqb + w.qpw - 1) / w.qpw;
   long nb = static_cast<long>(device_cus()) * 4;
   if (const char* e = std::getenv("KVQ_DECODE_BLOCKS")) {
@@ -197,9 +197,9 @@ WsLayout ws_layout(const kvq_cache* c, int n_q_heads, int max_tokens, int n_q = 
   }
   // small batches get fewer, fuller workgroups: about two units per wave (on the 8 K-token
   // worked example 12.7 us per call against 16.0 us at one unit per wave and 14.1 us at four)
-  // (each wave walks every unit of its range when the waves take separate blocks)
-  const long ub = w.qpw > 1 ? (units_bound(c, max_tokens) * w.nqs + 1) / 2
-                            : (units_bound(c, max_tokens) * w.nqb + 7) / 8;
+  // (the 4 / qpw waves of a block share its units)
+  const long wpq = 4 / w.qpw;
+  const long ub = (units_bound(c, max_tokens) * w.nqs + 2 * wpq - 1) / (2 * wpq);
   if (nb > ub) nb = ub;
   if (nb < 1) nb = 1;
   w.nblocks = static_cast<int>(nb);

@@ -247,6 +247,10 @@ MQ_CASES = [
     ("mq-int4-gqa4-ragged-idle-waves", SYM4, SYM4, 3, 8, 2, 16, [50, 3, 200], False, 13),
     ("mq-int4-paged-idle-waves", SYM4, SYM4, 2, 8, 2, 32, [900, 70], True, 9),
     ("mq-int8-g32-two-row-blocks", (8, 0, 0, 32), (8, 0, 0, 32), 2, 8, 2, 0, [400, 1100], False, 12),
+    # two query blocks of two waves each (2 or 3 blocks per sequence and kv head)
+    ("mq-int4-gqa4-two-blocks", SYM4, SYM4, 2, 8, 2, 32, [777, 190], False, 4),
+    ("mq-kivi-int2-three-blocks", KPC2, ASYM2_32, 2, 8, 2, 128, [700, 1300], False, 3),
+    ("mq-asym4-paged-two-blocks", ASYM4_32, ASYM4_32, 2, 4, 2, 16, [250, 999], True, 3),
 ]
 
 
