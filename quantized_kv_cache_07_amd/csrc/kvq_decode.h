@@ -13,9 +13,9 @@
 // unit whatever the length mix.  Inside a workgroup the four waves interleave the units of each
 // (sequence, kv head) segment; at a segment end the waves merge in LDS and the workgroup writes
 // either the normalised output (the segment was the whole sequence) or a partial (max, sum,
-// o[128]) that combine_kernel merges with a log-sum-exp rescale.  Multi-query decode with four
-// or more query blocks per (sequence, kv head) gives each wave its own block instead, all four
-// walking the same units (mode 2).
+// o[128]) that combine_kernel merges with a log-sum-exp rescale.  Multi-query decode with two or
+// more query blocks per (sequence, kv head) puts two (mode 3: two waves each) or four (mode 2:
+// one wave each) blocks in a segment, their waves walking the same units.
 //
 // One unit on one wave (lane = 16 g + n):
 //   QK^T  4 MFMA 16x16x32 f16 per tile: D[token][col] = sum_k A[token][k] B[k][col], A = key
