@@ -309,8 +309,24 @@ __global__ __launch_bounds__(256) void quantize_kernel(CacheDev c, const uint16_
     }
   }
   // Phase 2b: V tiles, one 32-bit word per item; words shared with slots outside [lo, hi)
-  // keep those slots' bits (read-modify-write by the single owner of the tile).
-  {
+  // keep those slots' bits (read-modify-write by the single owner of the tile).  8-bit codes
+  // are whole bytes: a tile the range covers only in part gets byte stores instead, with no
+  // read of the words it shares with other slots.
+  const bool v_bytes = V.bits == 8 && (lo % TILE != 0 || hi % TILE != 0);
+  if (v_bytes) {
+    const long tile_bytes = static_cast<long>(TILE) * D;
+    for (int it = tid; it < (hi - lo) * D; it += blockDim.x) {
+      const int slot = lo + it / D, ch = it % D, t = slot % TILE;
+      bool ok = true;
+      const long tile = tile_index(c, b, h, slot / TILE, ok);
+      // inverse of v_field_owner for 8-bit fields: chunk, word in the chunk, field in the word
+      const int chunk = (t / 4) * (D / 8) + ch / 8;
+      const int r = 2 * (ch % 8) + (t % 4) / 2;
+      const int fld = r % 2 + 2 * (t % 2);
+      c.vc[tile * tile_bytes + slab_byte(8, chunk, 32 * (r / 2) + 8 * fld)] = lv[slot - seg0][ch];
+    }
+  }
+  if (!v_bytes) {
     const int E = 32 / V.bits;
     const int words = (D / 8) * 4 * V.bits;  // per tile
     const int t_first = seg0 / TILE, n_tiles = S / TILE;
@@ -432,7 +448,8 @@ hipError_t launch_append(const CacheDev& c, const uint16_t* knew, const uint16_t
   // - 1) / R) <= R floor((R + n_new - 1) / R)
   const int f_max = (mode == MODE_FLUSH) ? c.R
                     : (c.R == 0 ? n_new : c.R * ((c.R + n_new - 1) / c.R));
-  const int segs = (f_max + S - 1) / S + 1;
+  // S-slot segments a range of f_max slots can touch, wherever it starts
+  const int segs = (f_max + S - 2) / S + 1;
   dim3 grid(segs, c.B * c.H);
   switch (S) {
     case 16: quantize_kernel<16><<<grid, 256, 0, stream>>>(c, knew, vnew, n_new, mode); break;
