@@ -332,7 +332,9 @@ struct DecodeLds {
   // per-channel key folding buffer [WAVES][2][8][D] f16 overlays `red` (never live together)
   static constexpr int kf = red;
   static_assert(WAVES * 2 * 8 * D * 2 <= WAVES * 16 * RED_STRIDE * 4, "kf overlay");
-  static size_t bytes(int B) { return static_cast<size_t>(pre) + 4 * static_cast<size_t>(B + 1); }
+  // then [B][2] int: each sequence's counters (n_quant, n_res) as the prologue read them
+  __host__ __device__ static size_t cnt(int B) { return static_cast<size_t>(pre) + 4 * static_cast<size_t>(B + 1); }
+  static size_t bytes(int B) { return cnt(B) + 8 * static_cast<size_t>(B); }
 };
 
 // Work units of one sequence (per kv head), or -1 when its counters are out of range.
@@ -381,6 +383,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
   float* ztw = reinterpret_cast<float*>(smem + DecodeLds<MQ>::ztw);
   uint16_t* qs = reinterpret_cast<uint16_t*>(smem + DecodeLds<MQ>::qs);
   int* pre = reinterpret_cast<int*>(smem + DecodeLds<MQ>::pre);
+  int* cnt = reinterpret_cast<int*>(smem + DecodeLds<MQ>::cnt(c.B));
   int* ustat = reinterpret_cast<int*>(smem + DecodeLds<MQ>::ustat);
   uint16_t* kf = reinterpret_cast<uint16_t*>(smem + DecodeLds<MQ>::kf) + wave * 2 * 8 * D;
 
@@ -391,6 +394,8 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
     int s = 0, umin = INT_MAX, umax = 0, useq = 0;
     for (int i = tid * per; i < min(B, (tid + 1) * per); i++) {
       const int un = seq_units(c, p.max_tokens, i);
+      cnt[2 * i] = c.n_quant[i];  // kept for the segment starts (the loads above hit the cache)
+      cnt[2 * i + 1] = c.R > 0 ? c.n_res[i] : 0;
       if (un < 0) {
         if (blockIdx.x == 0) atomicOr(c.err, KVQ_ERR_TOKENS);
       } else {
@@ -491,8 +496,8 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
     const int uend = min(u1, seg_abs_end);
     const bool complete = (kk == 0) && (uend == seg_abs_end);
     const int slot = first_seg ? 0 : 1;
-    const int nq = ld_uniform(c.n_quant + b);
-    const int nr = c.R > 0 ? ld_uniform(c.n_res + b) : 0;
+    const int nq = uni(cnt[2 * b]);
+    const int nr = uni(cnt[2 * b + 1]);
     const int uq = (nq + 31) / 32;
     const int xend = kk + (uend - u);
 
