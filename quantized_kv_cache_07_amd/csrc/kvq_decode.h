@@ -388,7 +388,39 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
   uint16_t* kf = reinterpret_cast<uint16_t*>(smem + DecodeLds<MQ>::kf) + wave * 2 * 8 * D;
 
   // ---- units per sequence, prefix sum (every workgroup; workgroup 0 publishes it) ----
-  {
+  if (B <= 64) {
+    // one wave: lane i takes sequence i, an in-register scan, one barrier
+    if (wave == 0) {
+      int un = 0;
+      if (lane < B) {
+        un = seq_units(c, p.max_tokens, lane);
+        cnt[2 * lane] = c.n_quant[lane];
+        cnt[2 * lane + 1] = c.R > 0 ? c.n_res[lane] : 0;
+        if (un < 0 && blockIdx.x == 0) atomicOr(c.err, KVQ_ERR_TOKENS);
+      }
+      const int own = max(un, 0) * H * nqs;
+      int incl = own;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(incl, off);
+        if (lane >= off) incl += t;
+      }
+      if (lane < B) pre[lane] = incl - own;
+      if (lane == 63) pre[B] = incl;
+      int umin = (un > 0) ? un : INT_MAX, umax = max(un, 0), useq = (un > 0) ? 1 : 0;
+      for (int off = 32; off > 0; off >>= 1) {
+        umin = min(umin, __shfl_xor(umin, off));
+        umax = max(umax, __shfl_xor(umax, off));
+        useq += __shfl_xor(useq, off);
+      }
+      if (lane < WAVES) {  // this wave's totals in slot 0, neutral ones for the others
+        ustat[3 * lane] = lane == 0 ? umin : INT_MAX;
+        ustat[3 * lane + 1] = lane == 0 ? umax : 0;
+        ustat[3 * lane + 2] = lane == 0 ? useq : 0;
+      }
+    }
+    __syncthreads();
+  } else {
     const int per = (B + 255) / 256;
     int* scan = reinterpret_cast<int*>(red);
     int s = 0, umin = INT_MAX, umax = 0, useq = 0;

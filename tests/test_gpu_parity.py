@@ -74,6 +74,8 @@ CASES = [
     ("int2-g64-gqa8-two-row-blocks", (2, 0, 0, 64), (2, 0, 0, 64), 1, 16, 2, 16, [1200], False),
     ("int8-g32-gqa4-two-row-blocks", (8, 0, 0, 32), (8, 0, 0, 32), 2, 8, 2, 0, [321, 1029], True),
     ("asym8-g128-gqa2", (8, 1, 0, 128), (8, 1, 0, 128), 2, 4, 2, 64, [700, 65], False),
+    # more sequences than one wave scans (the prologue's workgroup-wide prefix sum)
+    ("int4-batch70-ragged", SYM4, SYM4, 70, 4, 2, 16, [20 + (37 * i) % 113 for i in range(70)], True),
 ]
 
 
