@@ -145,3 +145,19 @@ def test_binding_refuses_to_run_without_library(tmp_path, monkeypatch):
     with pytest.raises(ImportError):
         mod._load()
     importlib.reload(mod)
+
+
+def test_multi_query_workspace_grows_with_the_blocks_a_segment_holds(K):
+    """Multi-query decode sizes its partial slots by the query blocks one segment holds: one
+    block (the waves interleave its units), two blocks of two waves, or four of one wave each.
+    Per workgroup a slot pair holds qpw x G rows of 132 floats."""
+    L = K.lib
+    d = fake_cache(K)  # INT4 group 64, H_kv = 2, GQA-4 with 8 query heads: G = 8 rows per block
+    one = L.kvq_decode_workspace_bytes(ctypes.byref(d), 8, 1000)
+    assert L.kvq_decode_workspace_bytes_mq(ctypes.byref(d), 8, 1, 1000) == one
+    sizes = {nq: L.kvq_decode_workspace_bytes_mq(ctypes.byref(d), 8, nq, 1000)
+             for nq in (2, 4, 6, 8, 16)}
+    assert all(v > 0 for v in sizes.values())
+    # n_q = 2 is one block of two tokens; 4 and 6 are two or three blocks (two per segment),
+    # 8 and 16 four or more (four per segment): the per-workgroup slots grow 1 : 2 : 4
+    assert sizes[4] > sizes[2] and sizes[8] > sizes[4]
