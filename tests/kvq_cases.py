@@ -151,12 +151,13 @@ def compare_state(pr: Pair) -> None:
                 assert np.array_equal(got[b, :, :nr[b]], ref[b, :, :nr[b]]), f"{name} seq {b}"
 
 
-def compare_attention(pr: Pair, q_seed_step: int = 0, max_tokens: int | None = None):
+def compare_attention(pr: Pair, q_seed_step: int = 0, max_tokens: int | None = None,
+                      workspace: torch.Tensor | None = None):
     K = kvq()
     dev = pr.cache.n_quant.device
     q = ki.queries(pr.w, q_seed_step, dev)
     mt = max_tokens or max(s.n_quant + s.n_res for s in pr.seqs) or 1
-    out = K.decode_attention(pr.cache, q, max_tokens=mt, sm_scale=SM_SCALE)
+    out = K.decode_attention(pr.cache, q, max_tokens=mt, sm_scale=SM_SCALE, workspace=workspace)
     torch.cuda.synchronize()
     assert K.read_error(pr.cache) == 0
     got = out.cpu().numpy()
@@ -175,12 +176,13 @@ def mq_queries(pr: Pair, n_q: int, q_seed_step: int = 7):
     return torch.stack([ki.queries(pr.w, q_seed_step + i, dev) for i in range(n_q)], dim=1).contiguous()
 
 
-def compare_attention_mq(pr: Pair, n_q: int, q_seed_step: int = 7, max_tokens: int | None = None):
+def compare_attention_mq(pr: Pair, n_q: int, q_seed_step: int = 7, max_tokens: int | None = None,
+                         workspace: torch.Tensor | None = None):
     """Multi-query decode of the last n_q cached tokens against the oracle (causal)."""
     K = kvq()
     q = mq_queries(pr, n_q, q_seed_step)
     mt = max_tokens or max(s.n_quant + s.n_res for s in pr.seqs)
-    out = K.decode_attention_mq(pr.cache, q, max_tokens=mt, sm_scale=SM_SCALE)
+    out = K.decode_attention_mq(pr.cache, q, max_tokens=mt, sm_scale=SM_SCALE, workspace=workspace)
     torch.cuda.synchronize()
     assert K.read_error(pr.cache) == 0
     got = out.cpu().numpy()

@@ -142,6 +142,35 @@ def test_unit_range_choices(name, k, v, B, Hq, H, R, lens, nb, monkeypatch):
     kc.compare_attention(pr, q_seed_step=1)
 
 
+def test_more_workgroups_than_units(monkeypatch):
+    """A max_tokens far above the lengths sizes the grid for units that do not exist: most unit
+    ranges are empty, and the empty ones that start inside a segment count in a neutral partial."""
+    announce(test="more_workgroups_than_units")
+    monkeypatch.setenv("KVQ_DECODE_BLOCKS", "64")
+    pr = kc.build_pair(SYM4, SYM4, 2, 8, 2, 0, [100, 40], seed=31)
+    kc.compare_attention(pr, max_tokens=4096)
+    pr = kc.build_pair(SYM4, SYM4, 2, 8, 2, 32, [130, 7], seed=32)
+    kc.compare_attention_mq(pr, 9, max_tokens=4096)
+
+
+def test_workspace_needs_no_initialisation():
+    """One workspace filled with garbage serves calls of different shapes in a row: nothing in
+    it is read before the call writes it."""
+    announce(test="workspace_reuse")
+    K = kc.kvq()
+    a = kc.build_pair(SYM4, SYM4, 3, 8, 2, 0, [900, 40, 333], seed=5)
+    b = kc.build_pair(KPC2, ASYM2_32, 2, 8, 2, 128, [700, 1300], seed=6)
+    c = kc.build_pair(SYM4, SYM4, 2, 8, 2, 32, [777, 190], seed=7)
+    mt = lambda pr: max(s.n_quant + s.n_res for s in pr.seqs)
+    need = max(K.workspace_bytes(a.cache, 8, mt(a)), K.workspace_bytes(b.cache, 8, mt(b)),
+               K.workspace_bytes_mq(c.cache, 8, 9, mt(c)))
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        kc.compare_attention(a, q_seed_step=rep, workspace=ws)
+        kc.compare_attention(b, q_seed_step=rep, workspace=ws)
+        kc.compare_attention_mq(c, 9, workspace=ws)
+
+
 def test_empty_sequence_gives_zeros():
     announce(test="empty_sequence")
     pr = kc.build_pair(SYM8, SYM8, 3, 2, 2, 0, [0, 40, 0])
