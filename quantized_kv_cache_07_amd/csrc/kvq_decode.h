@@ -10,7 +10,8 @@
 // rows of one (sequence, kv head).  Units are numbered sequence by sequence, kv head by kv head,
 // from a prefix sum every workgroup rebuilds from the device counters (no host sync).  Workgroup
 // k of NB owns the contiguous unit range [k U / NB, (k+1) U / NB): the load is balanced to one
-// unit whatever the length mix.  Inside a workgroup the four waves interleave the units of each
+// unit whatever the length mix.  A window unit counts window_weight units (about its bytes
+// against a compressed unit's), so ranges that hold many sequence ends carry no more bytes.  Inside a workgroup the four waves interleave the units of each
 // (sequence, kv head) segment; at a segment end the waves merge in LDS and the workgroup writes
 // either the normalised output (the segment was the whole sequence) or a partial (max, sum,
 // o[128]) that combine_kernel merges with a log-sum-exp rescale.  Multi-query decode with two or
@@ -337,13 +338,14 @@ struct DecodeLds {
   static size_t bytes(int B) { return cnt(B) + 8 * static_cast<size_t>(B); }
 };
 
-// Work units of one sequence (per kv head), or -1 when its counters are out of range.
-__device__ __forceinline__ int seq_units(const CacheDev& c, int max_tokens, int b) {
+// Weighted work units of one sequence (per kv head): its compressed units plus ww per window
+// unit, or -1 when its counters are out of range.
+__device__ __forceinline__ int seq_units(const CacheDev& c, int max_tokens, int b, int ww) {
   const int nq = c.n_quant[b], nr = c.R > 0 ? c.n_res[b] : 0;
   if (nq < 0 || nr < 0 || nr > c.R || (!c.table && nq > c.cap) ||
       (c.table && (nq + TILE - 1) / TILE > c.max_blocks) || nq > max_tokens - nr)
     return -1;
-  return (nq + 31) / 32 + (nr + 31) / 32;
+  return (nq + 31) / 32 + ww * ((nr + 31) / 32);
 }
 
 // Ranges actually used of nb workgroups over S segments.  When every segment has the same number
@@ -370,6 +372,9 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
   const int nqs = MQ ? p.nqs : 1;
   constexpr bool ASYM = SCH == KVQ_ASYM;
   constexpr bool F8 = SCH == KVQ_FP8;  // E4M3 bytes, one scale per kv head (or tensor) per side
+  // A segment's units are its compressed units, then WW slots per window unit; a window unit
+  // belongs to the workgroup whose range holds its first slot.
+  constexpr int WW = window_weight(KB);
   extern __shared__ __align__(16) unsigned char smem[];
   const CacheDev& c = p.c;
   const int B = c.B, H = c.H;
@@ -393,7 +398,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
     if (wave == 0) {
       int un = 0;
       if (lane < B) {
-        un = seq_units(c, p.max_tokens, lane);
+        un = seq_units(c, p.max_tokens, lane, WW);
         cnt[2 * lane] = c.n_quant[lane];
         cnt[2 * lane + 1] = c.R > 0 ? c.n_res[lane] : 0;
         if (un < 0 && blockIdx.x == 0) atomicOr(c.err, KVQ_ERR_TOKENS);
@@ -425,7 +430,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
     int* scan = reinterpret_cast<int*>(red);
     int s = 0, umin = INT_MAX, umax = 0, useq = 0;
     for (int i = tid * per; i < min(B, (tid + 1) * per); i++) {
-      const int un = seq_units(c, p.max_tokens, i);
+      const int un = seq_units(c, p.max_tokens, i, WW);
       cnt[2 * i] = c.n_quant[i];  // kept for the segment starts (the loads above hit the cache)
       cnt[2 * i + 1] = c.R > 0 ? c.n_res[i] : 0;
       if (un < 0) {
@@ -460,7 +465,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
     int run = scan[tid] - s;
     for (int i = tid * per; i < min(B, (tid + 1) * per); i++) {
       pre[i] = run;
-      run += max(seq_units(c, p.max_tokens, i), 0) * H * nqs;
+      run += max(seq_units(c, p.max_tokens, i, WW), 0) * H * nqs;
     }
     if (tid == 255) pre[B] = scan[255];
     __syncthreads();
@@ -1155,7 +1160,10 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
     }
 
     // ---------------------------- BF16 window units ----------------------------
-    if (x < xend) {
+    // window units whose first slot lies in this range, interleaved over the block's waves
+    const int wend = xend > uq ? (xend - uq + WW - 1) / WW : 0;
+    int jw = (qblk < nqb) ? (max(kk, uq) - uq + WW - 1) / WW + wave % WPQ : wend;
+    if (jw < wend) {
       // bf16 query operand in natural channel order, masked like the f16 one
       bf16x8 qw[4];
       const bool keep = KPC ? (cg == 0) : (((32 * g) / kgroup) == cg);
@@ -1167,8 +1175,8 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
       }
       const uint16_t* kr = c.kres + (static_cast<size_t>(b) * H + h) * c.R * D;
       const uint16_t* vr = c.vres + (static_cast<size_t>(b) * H + h) * c.R * D;
-      for (; x < xend; x += xstep) {
-        const int r0 = 32 * (x - uq);
+      for (; jw < wend; jw += xstep) {
+        const int r0 = 32 * jw;
         const int nvA = min(16, nr - r0), nvB = max(0, min(16, nr - r0 - 16));
         float s2[8];
 #pragma unroll

@@ -83,6 +83,13 @@ struct DecodeParams {
 
 constexpr int PART_STRIDE = D + 4;
 
+// Work weight of a BF16 window unit (32 rows of bf16 keys and values, 16 KB) against a
+// compressed unit of `bits`-bit codes (32 slots of codes plus their scale rows): about the ratio
+// of their HBM bytes, so that unit ranges of equal weight carry about equal bytes.
+__host__ __device__ constexpr int window_weight(int bits) {
+  return bits == 2 ? 5 : bits == 4 ? 4 : bits == 8 ? 2 : 1;
+}
+
 // Slots one append/flush call moves into the compressed cache (F), window tokens before the
 // call plus new tokens (total), and window length afterwards.  Equal, by construction, to
 // n_new single-token appends each flushing a full window before copying the token in.

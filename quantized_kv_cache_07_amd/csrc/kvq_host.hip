@@ -2,6 +2,7 @@
 //
 // Everything a host can check is checked here before any launch; see include/kvq.h for the
 // contract of each call.
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 
@@ -157,9 +158,12 @@ struct WsLayout {
 };
 
 long units_bound(const kvq_cache* c, int max_tokens) {
-  // compressed and window units of a sequence: at most one more than ceil(max_tokens / 32)
-  // when a window exists (the two parts round up separately)
-  const long per_seq = (static_cast<long>(max_tokens) + 31) / 32 + (c->fmt.residual > 0 ? 1 : 0);
+  // weighted units of a sequence: at most one unit more than ceil(max_tokens / 32) when a window
+  // exists (the two parts round up separately), and window_weight - 1 more per window unit
+  const long R = c->fmt.residual;
+  const long wu = R > 0 ? (std::min<long>(R, max_tokens) + 31) / 32 : 0;
+  const long per_seq = (static_cast<long>(max_tokens) + 31) / 32 + (R > 0 ? 1 : 0) +
+                       (window_weight(c->fmt.k.bits) - 1) * wu;
   return static_cast<long>(c->batch) * c->n_kv_heads * per_seq;
 }
 
