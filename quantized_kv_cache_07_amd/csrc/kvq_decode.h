@@ -375,6 +375,10 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
   // A segment's units are its compressed units, then WW slots per window unit; a window unit
   // belongs to the workgroup whose range holds its first slot.
   constexpr int WW = window_weight(KB);
+  // In a batch of mixed lengths every segment also starts with SEG_W slots of no work, the cost
+  // of a segment start (query staging, first loads) in units, so that a range holding many short
+  // segments holds fewer units.  Batches of equal lengths (segment-aligned ranges) have none.
+  constexpr int SEG_W = SEGMENT_START_WEIGHT;
   extern __shared__ __align__(16) unsigned char smem[];
   const CacheDev& c = p.c;
   const int B = c.B, H = c.H;
@@ -403,7 +407,14 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
         cnt[2 * lane + 1] = c.R > 0 ? c.n_res[lane] : 0;
         if (un < 0 && blockIdx.x == 0) atomicOr(c.err, KVQ_ERR_TOKENS);
       }
-      const int own = max(un, 0) * H * nqs;
+      int umin = (un > 0) ? un : INT_MAX, umax = max(un, 0), useq = (un > 0) ? 1 : 0;
+      for (int off = 32; off > 0; off >>= 1) {
+        umin = min(umin, __shfl_xor(umin, off));
+        umax = max(umax, __shfl_xor(umax, off));
+        useq += __shfl_xor(useq, off);
+      }
+      const int segw = umin != umax ? SEG_W : 0;
+      const int own = (un > 0 ? un + segw : 0) * H * nqs;
       int incl = own;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -412,12 +423,6 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
       }
       if (lane < B) pre[lane] = incl - own;
       if (lane == 63) pre[B] = incl;
-      int umin = (un > 0) ? un : INT_MAX, umax = max(un, 0), useq = (un > 0) ? 1 : 0;
-      for (int off = 32; off > 0; off >>= 1) {
-        umin = min(umin, __shfl_xor(umin, off));
-        umax = max(umax, __shfl_xor(umax, off));
-        useq += __shfl_xor(useq, off);
-      }
       if (lane < WAVES) {  // this wave's totals in slot 0, neutral ones for the others
         ustat[3 * lane] = lane == 0 ? umin : INT_MAX;
         ustat[3 * lane + 1] = lane == 0 ? umax : 0;
@@ -428,20 +433,17 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
   } else {
     const int per = (B + 255) / 256;
     int* scan = reinterpret_cast<int*>(red);
-    int s = 0, umin = INT_MAX, umax = 0, useq = 0;
+    int umin = INT_MAX, umax = 0, useq = 0;
     for (int i = tid * per; i < min(B, (tid + 1) * per); i++) {
       const int un = seq_units(c, p.max_tokens, i, WW);
       cnt[2 * i] = c.n_quant[i];  // kept for the segment starts (the loads above hit the cache)
       cnt[2 * i + 1] = c.R > 0 ? c.n_res[i] : 0;
       if (un < 0) {
         if (blockIdx.x == 0) atomicOr(c.err, KVQ_ERR_TOKENS);
-      } else {
-        s += un * H * nqs;
-        if (un > 0) {
-          umin = min(umin, un);
-          umax = max(umax, un);
-          useq++;
-        }
+      } else if (un > 0) {
+        umin = min(umin, un);
+        umax = max(umax, un);
+        useq++;
       }
     }
     for (int off = 32; off > 0; off >>= 1) {
@@ -454,6 +456,19 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
       ustat[3 * wave + 1] = umax;
       ustat[3 * wave + 2] = useq;
     }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < WAVES; w++) {
+      umin = min(umin, ustat[3 * w]);
+      umax = max(umax, ustat[3 * w + 1]);
+    }
+    const int segw = umin != umax ? SEG_W : 0;
+    auto weighted = [&](int i) {
+      const int un = seq_units(c, p.max_tokens, i, WW);
+      return (un > 0 ? un + segw : 0) * H * nqs;
+    };
+    int s = 0;
+    for (int i = tid * per; i < min(B, (tid + 1) * per); i++) s += weighted(i);
     scan[tid] = s;
     __syncthreads();
     for (int off = 1; off < 256; off <<= 1) {
@@ -465,7 +480,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
     int run = scan[tid] - s;
     for (int i = tid * per; i < min(B, (tid + 1) * per); i++) {
       pre[i] = run;
-      run += max(seq_units(c, p.max_tokens, i, WW), 0) * H * nqs;
+      run += weighted(i);
     }
     if (tid == 255) pre[B] = scan[255];
     __syncthreads();
@@ -516,7 +531,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
   int u = u0;
   bool first_seg = true;
   while (u < u1) {
-    // ---- locate the segment: sequence b, kv head h, query block qblk, first unit kk ----
+    // ---- locate the segment: sequence b, kv head h, query block qblk, first slot kk ----
     int lo = 0, hi = B - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -536,7 +551,8 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
     const int nq = uni(cnt[2 * b]);
     const int nr = uni(cnt[2 * b + 1]);
     const int uq = (nq + 31) / 32;
-    const int xend = kk + (uend - u);
+    const int segw = umin != umax ? SEG_W : 0;
+    const int ku = max(kk - segw, 0), xend = max(kk + (uend - u) - segw, 0);  // in units
 
     // ---- issue the segment's first loads before staging its query: the query rows, the
     // block-table entries and the first unit's codes and scales are in flight together ----
@@ -559,7 +575,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
     }
     // the WPQ waves of a block interleave its units; waves past the last block idle
     const int xstep = WPQ;
-    int x = (qblk < nqb) ? kk + wave % WPQ : xend;
+    int x = (qblk < nqb) ? ku + wave % WPQ : xend;
     const int xq_end = min(xend, uq);
 
     // PV row roles: row 16 pp + n is (part, value group, head hh)
@@ -1162,7 +1178,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
     // ---------------------------- BF16 window units ----------------------------
     // window units whose first slot lies in this range, interleaved over the block's waves
     const int wend = xend > uq ? (xend - uq + WW - 1) / WW : 0;
-    int jw = (qblk < nqb) ? (max(kk, uq) - uq + WW - 1) / WW + wave % WPQ : wend;
+    int jw = (qblk < nqb) ? (max(ku, uq) - uq + WW - 1) / WW + wave % WPQ : wend;
     if (jw < wend) {
       // bf16 query operand in natural channel order, masked like the f16 one
       bf16x8 qw[4];

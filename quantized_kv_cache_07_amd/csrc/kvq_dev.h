@@ -90,6 +90,10 @@ __host__ __device__ constexpr int window_weight(int bits) {
   return bits == 2 ? 5 : bits == 4 ? 4 : bits == 8 ? 2 : 1;
 }
 
+// Work weight of starting a segment (query staging, first loads), in units, given to every
+// segment of a batch of mixed lengths.
+constexpr int SEGMENT_START_WEIGHT = 6;
+
 // Slots one append/flush call moves into the compressed cache (F), window tokens before the
 // call plus new tokens (total), and window length afterwards.  Equal, by construction, to
 // n_new single-token appends each flushing a full window before copying the token in.

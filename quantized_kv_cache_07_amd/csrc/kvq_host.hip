@@ -159,11 +159,12 @@ struct WsLayout {
 
 long units_bound(const kvq_cache* c, int max_tokens) {
   // weighted units of a sequence: at most one unit more than ceil(max_tokens / 32) when a window
-  // exists (the two parts round up separately), and window_weight - 1 more per window unit
+  // exists (the two parts round up separately), window_weight - 1 more per window unit, and the
+  // segment start weight of a batch of mixed lengths
   const long R = c->fmt.residual;
   const long wu = R > 0 ? (std::min<long>(R, max_tokens) + 31) / 32 : 0;
   const long per_seq = (static_cast<long>(max_tokens) + 31) / 32 + (R > 0 ? 1 : 0) +
-                       (window_weight(c->fmt.k.bits) - 1) * wu;
+                       (window_weight(c->fmt.k.bits) - 1) * wu + SEGMENT_START_WEIGHT;
   return static_cast<long>(c->batch) * c->n_kv_heads * per_seq;
 }
 
