@@ -171,6 +171,29 @@ def test_workspace_needs_no_initialisation():
         kc.compare_attention_mq(c, 9, workspace=ws)
 
 
+# Mixed-length batches with windows: a window unit counts its bytes' weight in units (and every
+# segment opens with slots of no work), so range boundaries fall inside window units and inside
+# those slots; forced grid sizes move them around.
+WINDOW_SPLIT_CASES = [
+    # name, k, v, B, Hq, H, R, lens, workgroups
+    ("int4-window-split-7", SYM4, SYM4, 3, 8, 2, 64, [150, 47, 300], 7),
+    ("int4-window-split-13", SYM4, SYM4, 3, 8, 2, 64, [150, 47, 300], 13),
+    ("int2-window-split-11", SYM2_32, SYM2_32, 3, 4, 2, 96, [130, 75, 200], 11),
+    ("int8-window-split-5", SYM8, SYM8, 2, 4, 4, 128, [600, 100], 5),
+    ("kivi-window-split-9", KPC2, ASYM2_32, 2, 8, 2, 128, [700, 300], 9),
+]
+
+
+@pytest.mark.parametrize("name,k,v,B,Hq,H,R,lens,nb", WINDOW_SPLIT_CASES, ids=[c[0] for c in WINDOW_SPLIT_CASES])
+def test_window_units_split_across_ranges(name, k, v, B, Hq, H, R, lens, nb, monkeypatch):
+    announce(test="window_split", name=name, workgroups=nb)
+    monkeypatch.setenv("KVQ_DECODE_BLOCKS", str(nb))
+    pr = kc.build_pair(k, v, B, Hq, H, R, lens, seed=zlib.crc32(name.encode()) % 1000)
+    kc.compare_attention(pr)
+    kc.step(pr, flush_first=False)
+    kc.compare_attention(pr, q_seed_step=1)
+
+
 def test_empty_sequence_gives_zeros():
     announce(test="empty_sequence")
     pr = kc.build_pair(SYM8, SYM8, 3, 2, 2, 0, [0, 40, 0])
