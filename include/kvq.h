@@ -242,6 +242,26 @@ kvq_status kvq_decode_attention_mq(const kvq_cache *cache, const void *q, int32_
                                    float *out, void *workspace, size_t workspace_bytes,
                                    void *stream);
 
+/* Bytes of the library's own decode workspace (see kvq_decode_attention_noalloc). */
+#define KVQ_NOALLOC_WORKSPACE_BYTES ((size_t)16 << 20)
+
+/* kvq_decode_attention() without a caller-supplied workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The workspace is a device array of KVQ_NOALLOC_WORKSPACE_BYTES bytes inside the
+ * library, one copy per GPU, held until the process ends; this call allocates nothing (no
+ * hipMalloc, no allocating library routine).  Its first call on a device looks the array's
+ * address up on that device.
+ *   Arguments, output, results and device faults: as kvq_decode_attention().
+ *   KVQ_ENOSPACE when kvq_decode_workspace_bytes(cache, n_q_heads, max_tokens) exceeds
+ *   KVQ_NOALLOC_WORKSPACE_BYTES (nothing is launched); KVQ_ELAUNCH when the array's device
+ *   address cannot be found.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on one device (two
+ * streams, or two host threads) race and give undefined results; order them on one stream.
+ * Nothing in the array needs to start at zero, and a call reads nothing an earlier call left. */
+kvq_status kvq_decode_attention_noalloc(const kvq_cache *cache, const void *q, int32_t n_q_heads,
+                                        float sm_scale, int32_t max_tokens, float *out,
+                                        void *stream);
+
 /* Synchronise `stream`, copy the device error word into *host_err and return KVQ_EDEVICE if
  * any bit is set, KVQ_OK otherwise.  The word is not cleared. */
 kvq_status kvq_read_error(const kvq_cache *cache, int32_t *host_err, void *stream);

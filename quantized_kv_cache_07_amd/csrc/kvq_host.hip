@@ -5,9 +5,16 @@
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "kvq_dev.h"
 #include "kvq_measure.h"
+
+// Decode workspace of kvq_decode_attention_noalloc(): a device-resident array of the library,
+// one copy per GPU, held until the process ends.  Host code never passes its name to a kernel
+// (on the host that name is a stand-in, not a device address); it passes the address
+// hipGetSymbolAddress() returned for the current device.
+static __device__ __align__(256) unsigned char scratch[KVQ_NOALLOC_WORKSPACE_BYTES];
 
 namespace kvq {
 
@@ -214,6 +221,22 @@ WsLayout ws_layout(const kvq_cache* c, int n_q_heads, int max_tokens, int n_q = 
   return w;
 }
 
+// Device address of `scratch` on the current device, looked up once per device (with that
+// device current) and kept; nullptr when the lookup fails.
+void* scratch_address() {
+  static std::mutex mu;
+  static void* addr[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> g(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
 int device_cus() {
   static int cus[64] = {0};
   int dev = 0;
@@ -413,6 +436,20 @@ kvq_status kvq_decode_attention_mq(const kvq_cache* cache, const void* q, int32_
     default: return KVQ_ENOTSUP;  // unreachable: check_cache accepted the width
   }
   return e == hipSuccess ? KVQ_OK : KVQ_ELAUNCH;
+}
+
+kvq_status kvq_decode_attention_noalloc(const kvq_cache* cache, const void* q, int32_t n_q_heads,
+                                        float sm_scale, int32_t max_tokens, float* out,
+                                        void* stream) {
+  kvq_status s = check_cache(cache);
+  if (s != KVQ_OK) return s;
+  if (n_q_heads < 1 || max_tokens < 1 || n_q_heads % cache->n_kv_heads) return KVQ_EINVAL;
+  const size_t need = ws_layout(cache, n_q_heads, max_tokens).total;
+  if (need > KVQ_NOALLOC_WORKSPACE_BYTES) return KVQ_ENOSPACE;
+  void* ws = scratch_address();
+  if (!ws) return KVQ_ELAUNCH;
+  return kvq_decode_attention_mq(cache, q, 1, n_q_heads, sm_scale, max_tokens, out, ws,
+                                 KVQ_NOALLOC_WORKSPACE_BYTES, stream);
 }
 
 kvq_status kvq_read_error(const kvq_cache* cache, int32_t* host_err, void* stream) {

@@ -30,7 +30,7 @@ STATUS = {0: "KVQ_OK", 1: "KVQ_EINVAL", 2: "KVQ_ENOTSUP", 3: "KVQ_EALIGN", 4: "K
 # Every function declared in include/kvq.h and include/kvq_measure.h.
 EXPORTS = ["kvq_buffer_bytes", "kvq_check_format", "kvq_quantize_append", "kvq_flush_residual",
            "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_decode_workspace_bytes_mq",
-           "kvq_decode_attention_mq", "kvq_read_error",
+           "kvq_decode_attention_mq", "kvq_decode_attention_noalloc", "kvq_read_error",
            "kvq_status_str", "kvq_measure_read", "kvq_measure_read_sink_floats",
            "kvq_measure_copy"]
 
@@ -83,6 +83,7 @@ def _load() -> ctypes.CDLL:
     L.kvq_decode_workspace_bytes_mq.argtypes = [P, i32, i32, i32]
     L.kvq_decode_workspace_bytes_mq.restype = sz
     L.kvq_decode_attention_mq.argtypes = [P, P, i32, i32, f32, i32, P, P, sz, P]
+    L.kvq_decode_attention_noalloc.argtypes = [P, P, i32, f32, i32, P, P]
     L.kvq_read_error.argtypes = [P, P, P]
     L.kvq_status_str.argtypes = [ctypes.c_int]
     L.kvq_status_str.restype = ctypes.c_char_p
@@ -90,7 +91,8 @@ def _load() -> ctypes.CDLL:
     L.kvq_measure_read_sink_floats.restype = i32
     L.kvq_measure_copy.argtypes = [P, P, sz, P]
     for f in ("kvq_check_format", "kvq_quantize_append", "kvq_flush_residual",
-              "kvq_decode_attention", "kvq_decode_attention_mq", "kvq_read_error",
+              "kvq_decode_attention", "kvq_decode_attention_mq", "kvq_decode_attention_noalloc",
+              "kvq_read_error",
               "kvq_measure_read", "kvq_measure_copy"):
         getattr(L, f).restype = ctypes.c_int
     return L
@@ -275,6 +277,24 @@ def decode_attention_mq(cache: Cache, q: torch.Tensor, max_tokens: int,
                                      float(sm_scale), max_tokens, out.data_ptr(),
                                      workspace.data_ptr(), workspace.numel(), _stream(stream))
     _check(st, "kvq_decode_attention_mq")
+    return out
+
+
+def decode_attention_noalloc(cache: Cache, q: torch.Tensor, max_tokens: int,
+                             out: torch.Tensor | None = None, sm_scale: float | None = None,
+                             stream=None) -> torch.Tensor:
+    """kvq_decode_attention_noalloc: as decode_attention, with the library's own workspace (no
+    device allocation by the library; `out` may be preallocated by the caller)."""
+    assert q.dtype == torch.bfloat16 and q.is_contiguous()
+    hq = q.shape[1]
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    st = lib.kvq_decode_attention_noalloc(ctypes.byref(cache.desc), q.data_ptr(), hq,
+                                          float(sm_scale), max_tokens, out.data_ptr(),
+                                          _stream(stream))
+    _check(st, "kvq_decode_attention_noalloc")
     return out
 
 
