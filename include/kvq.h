@@ -163,7 +163,13 @@ typedef struct {
 
 /* Bytes of buffer `which` (KVQ_BUF_*) for a contiguous cache (num_blocks == 0, `capacity`
  * slots per sequence) or a paged pool of `num_blocks` blocks.  Returns 0 for a buffer the
- * format does not use, or for an invalid format.  Pure host arithmetic. */
+ * format does not use, or for an invalid format.  Pure host arithmetic.
+ * The code buffers follow the memory formula of [P2, "Why the KV cache grows so quickly"]:
+ * keys and values together hold 2 * T * H_kv * d_h * b bytes for T slots of b = bits / 8 bytes
+ * per element; the scale (and zero-point) buffers add the per-group fp16 metadata that
+ * [P2, "Worked example: an 8,192-token context"] counts on top (one two-byte scale per 64
+ * elements gives 0.53125 bytes per element at 4 bits: 8,912,896 bytes per layer at H_kv = 8,
+ * T = 8192). */
 size_t kvq_buffer_bytes(const kvq_format *fmt, int32_t batch, int32_t n_kv_heads,
                         int32_t capacity, int32_t num_blocks, int32_t which);
 
@@ -189,9 +195,15 @@ kvq_status kvq_check_format(const kvq_format *fmt);
 kvq_status kvq_quantize_append(const kvq_cache *cache, const void *k_new, const void *v_new,
                                int32_t n_new, void *stream);
 
-/* Flush every sequence whose window holds exactly R tokens; other sequences are untouched.
- * Optional: kvq_quantize_append() flushes by itself when a token finds the window full, and
- * calling this first never changes any result.  No-op launch-free return when R == 0. */
+/* Flush every sequence whose window holds exactly R tokens; other sequences are untouched
+ * [P2, "Why some systems keep a full-precision window": once the BF16 buffer of recent tokens
+ * fills, its contents are quantized and moved into the compressed cache].  The R window rows
+ * are quantized into compressed slots n_quant .. n_quant + R - 1 with the side formats (per-
+ * channel key groups are formed here, over whole groups of the window), then n_quant += R and
+ * n_res = 0.  Optional: kvq_quantize_append() flushes by itself when a token finds the window
+ * full, and calling this first never changes any result.  No-op launch-free return when R == 0.
+ * Paged caches: the block table must map the R slots.  Device faults as kvq_quantize_append()
+ * (the sequence is left unchanged).  Launches two kernels on `stream`. */
 kvq_status kvq_flush_residual(const kvq_cache *cache, void *stream);
 
 /* Workspace bytes kvq_decode_attention() needs for n_q_heads and a host bound max_tokens on

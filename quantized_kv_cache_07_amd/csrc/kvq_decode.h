@@ -27,7 +27,7 @@
 //         scales apply to the products; per-channel key scales are folded into the query (hi +
 //         lo f16 parts) once per key group.
 //   softmax  online, in log2 units; the running max is only raised when a score exceeds it by
-//         more than 8 (weights stay <= 2^8), so the accumulator is rarely rescaled.
+//         more than 1 (weights stay <= 2), so the accumulator is rescaled a few times per segment.
 //   PV    8 MFMA 16x16x32 f16 per row block: D[row][ch] = sum_t P[row][t] V[t][ch] with rows
 //         (hi/lo part, value group, query head) of w * s_v, 32 tokens (both tiles) deep; value
 //         codes enter as f16 subnormals (one AND per two codes), the symmetric offset as one
@@ -54,9 +54,29 @@ typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int WAVES = 4;
 constexpr int RED_STRIDE = D + 4;  // floats per LDS row of the merge buffer
-constexpr float LAZY_LOG2 = 8.0f;  // raise the running max only past this margin
+// Raise the running max only past this margin (log2 units): weights stay <= 2, so a weight times
+// any finite fp16 value scale (<= 65504) stays within the hi + lo f16 parts of the PV operand
+// (v_cvt_pkrtz_f16_f32 saturates at 65504: hi = 65504, lo = w s - 65504 <= 65504).
+constexpr float LAZY_LOG2 = 1.0f;
+// Query rows enter the matrix cores as f16 after a power-of-two prescale 2^-e per row, so any
+// bf16 query fits: the row maximum lands in [2^QE_RAW, 2^(QE_RAW+1)) for raw-code keys (the
+// largest f16 operand q 2^-e / alpha stays below 65504) and in [2^QE_FOLD, 2^(QE_FOLD+1)) when
+// the query is multiplied by per-channel key scales first (q s 2^-e stays below 65504 for any
+// fp16 scale).  The scores come out multiplied by 2^-e and the softmax scale by 2^e.
+constexpr int QE_RAW = 13, QE_FOLD = -1;
 
 // ---- small helpers ------------------------------------------------------------------------
+
+// 2^x for an integer |x| <= 126, exactly.
+__device__ __forceinline__ float exp2i(int x) { return __uint_as_float(static_cast<uint32_t>(127 + x) << 23); }
+
+// Exponent e of a query row's prescale 2^-e: the row maximum mx times 2^-e lies in
+// [2^target, 2^(target+1)); 0 for an all-zero row; clamped to [-100, 100].
+__device__ __forceinline__ int q_exponent(float mx, int target) {
+  if (!(mx > 0.0f)) return 0;
+  const int E = static_cast<int>((__float_as_uint(mx) >> 23) & 0xFFu) - 127;  // floor(log2 mx)
+  return min(max(E - target, -100), 100);
+}
 
 __device__ __forceinline__ f16x2 as_h2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
 __device__ __forceinline__ uint32_t h2_bits(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
@@ -329,7 +349,9 @@ struct DecodeLds {
   static constexpr int qs = ztw + WAVES * 8 * 4;                  // [QB][8][D] bf16
   static constexpr int ustat = qs + QB * 8 * D * 2;               // [WAVES][3] int: min, max,
                                                                   // count of units (> 0)
-  static constexpr int pre = ustat + WAVES * 3 * 4;               // [B + 1] int
+  static constexpr int qe = ustat + WAVES * 3 * 4;                // [QB][8] int: query row
+                                                                  // prescale exponents
+  static constexpr int pre = qe + QB * 8 * 4;                     // [B + 1] int
   // per-channel key folding buffer [WAVES][2][8][D] f16 overlays `red` (never live together)
   static constexpr int kf = red;
   static_assert(WAVES * 2 * 8 * D * 2 <= WAVES * 16 * RED_STRIDE * 4, "kf overlay");
@@ -394,6 +416,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
   int* pre = reinterpret_cast<int*>(smem + DecodeLds<MQ>::pre);
   int* cnt = reinterpret_cast<int*>(smem + DecodeLds<MQ>::cnt(c.B));
   int* ustat = reinterpret_cast<int*>(smem + DecodeLds<MQ>::ustat);
+  int* qe = reinterpret_cast<int*>(smem + DecodeLds<MQ>::qe);
   uint16_t* kf = reinterpret_cast<uint16_t*>(smem + DecodeLds<MQ>::kf) + wave * 2 * 8 * D;
 
   // ---- units per sequence, prefix sum (every workgroup; workgroup 0 publishes it) ----
@@ -678,17 +701,35 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
       load_v(pA, pB);
     }
 
-    // ---- stage the segment's G query rows (bf16) ----
+    // ---- stage the segment's G query rows (bf16) and each row's prescale exponent ----
+    // A row's 16 pieces sit on the 16 lanes of one DPP row: its |q| maximum is a row reduction.
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < QPC; k++) {
       const int piece = tid + 256 * k;
+      float mx = 0.0f;
+      if constexpr (!BF) {
+        const uint32_t w4[4] = {qval[k].x, qval[k].y, qval[k].z, qval[k].w};
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+          mx = max3f(mx, __uint_as_float((w4[i] << 16) & 0x7FFF0000u), __uint_as_float(w4[i] & 0x7FFF0000u));
+        mx = fmaxf(mx, row_ror<8>(mx));
+        mx = fmaxf(mx, row_ror<4>(mx));
+        mx = fmaxf(mx, row_ror<2>(mx));
+        mx = fmaxf(mx, row_ror<1>(mx));
+      }
       if (piece < qpw * G * (D / 8)) {
         const int row = piece / (D / 8);
         reinterpret_cast<uint4*>(qs + ((row / G) * 8 + row % G) * D)[piece % (D / 8)] = qval[k];
+        if (piece % (D / 8) == 0) qe[(row / G) * 8 + row % G] = q_exponent(mx, KPC ? QE_FOLD : QE_RAW);
       }
     }
     __syncthreads();
+    // this lane's QK column head: its query prescale 2^-e and the softmax scale of its scores
+    // over compressed units, sm_scale log2(e) 2^e (BF16 storage: no prescale)
+    const int qe_h = BF ? 0 : qe[qi * 8 + hh];
+    const float qsc = exp2i(-qe_h);
+    const float sl2 = p.sm_log2 * exp2i(qe_h);
     const uint16_t* qsw = qs + qi * 8 * D;  // this wave's query rows
     // causal limit (multi-query): the block's first query token sees the first lim_min cached
     // tokens (the query tokens are the last nqt), column n's token lim_min + hh / gkv of them;
@@ -712,7 +753,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
       for (int j = 0; j < 4; j++) {
         const u16x8 raw = *reinterpret_cast<const u16x8*>(qsw + hh * D + 32 * g + 8 * j);
 #pragma unroll
-        for (int i = 0; i < 8; i++) qb[j][i] = static_cast<_Float16>(bf16_to_f32(raw[i]));
+        for (int i = 0; i < 8; i++) qb[j][i] = static_cast<_Float16>(bf16_to_f32(raw[i]) * qsc);
       }
       const int32_t* fks = reinterpret_cast<const int32_t*>(c.ks);
       const int32_t* fvs = reinterpret_cast<const int32_t*>(c.vs);
@@ -725,7 +766,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
         const u16x8 raw = gather_kchan<KB>(qsw + hh * D + 32 * g, j);
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-          const float x = in_grp ? bf16_to_f32(raw[i]) : 0.0f;
+          const float x = in_grp ? bf16_to_f32(raw[i]) * qsc : 0.0f;  // exact: a power of two
           qb[j][i] = static_cast<_Float16>(x * (1.0f / static_cast<float>(kelem_alpha<KB>(j, i))));
           if constexpr (ASYM) qsum += x;
         }
@@ -769,7 +810,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
     // at a finite sentinel, so empty waves never form inf - inf.
     // With vfold, element i's weight comes out divided by alpha_i of the value codes it meets
     // (the raw-code PV operand), which only shifts its exponent.
-    auto softmax = [&](float (&s2)[8], int nvA, int nvB, auto vfold, int tok0) {
+    auto softmax = [&](float (&s2)[8], int nvA, int nvB, auto vfold, int tok0, float sl2_) {
       const bool full = nvA == 16 && nvB == 16;
       if (!full) {
 #pragma unroll
@@ -785,7 +826,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
       const float m01 = max3f(s2[0], s2[1], s2[2]);
       const float m02 = max3f(s2[3], s2[4], s2[5]);
       float tmax = max3f(max3f(s2[6], s2[7], m01), m02, m02);
-      tmax *= p.sm_log2;
+      tmax *= sl2_;
       if (__ballot(tmax > m_run + LAZY_LOG2) != 0) {
         float hm = fmaxf(tmax, __shfl_xor(tmax, 16));
         hm = fmaxf(hm, __shfl_xor(hm, 32));
@@ -816,7 +857,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
 #pragma unroll
       for (int i = 0; i < 8; i++) {
         const float a = (AT && (i & 2)) ? VLG : 0.0f;  // log2 of element i's token factor
-        s2[i] = __builtin_amdgcn_exp2f(fmaf(s2[i], p.sm_log2, -m_run - a));  // -inf -> 0
+        s2[i] = __builtin_amdgcn_exp2f(fmaf(s2[i], sl2_, -m_run - a));  // -inf -> 0
       }
       const float l1 = (s2[0] + s2[1]) + (s2[4] + s2[5]);
       const float l16 = (s2[2] + s2[3]) + (s2[6] + s2[7]);
@@ -846,8 +887,9 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
         for (int r0 = 0; r0 < G; r0 += 4) {
           const int hw = min(r0 + (lane >> 4), G - 1);
           const u16x8 q8 = gather_kchan<KB>(qsw + hw * D + 32 * (fold_blk / 4), fold_blk % 4);
+          const float fsc = exp2i(-qe[qi * 8 + hw]);  // the folded head's prescale
 #pragma unroll
-          for (int i = 0; i < 8; i++) qfold[r0 / 4][i] = bf16_to_f32(q8[i]);
+          for (int i = 0; i < 8; i++) qfold[r0 / 4][i] = bf16_to_f32(q8[i]) * fsc;
         }
       }
 
@@ -1024,7 +1066,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
         fold_cols8(s2);
         load_k(more ? xn : x, nA, nB);  // key registers are free again
 
-        softmax(s2, nvA, nvB, std::integral_constant<bool, VBF>{}, 32 * x);  // s2: weights / alpha
+        softmax(s2, nvA, nvB, std::integral_constant<bool, VBF>{}, 32 * x, sl2);  // s2: weights / alpha
 
         // ---- P rows (hi / lo f16 parts of w * s_v) and PV ----
         // Rows 16 pp + n with part >= 2 are never read back, so they are left as computed.
@@ -1209,7 +1251,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
           for (int r = 0; r < 4; r++) s2[4 * t + r] = dq[r];
         }
         fold_cols8(s2);
-        softmax(s2, nvA, nvB, std::false_type{}, nq + r0);
+        softmax(s2, nvA, nvB, std::false_type{}, nq + r0, p.sm_log2);
         // P rows: bf16 hi / lo parts of w (truncation; hi + lo carries 16 significant bits)
         bf16x8 pb[NP];
 #pragma unroll

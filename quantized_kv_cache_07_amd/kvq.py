@@ -213,18 +213,66 @@ class Cache:
         return self._describe(seq)
 
 
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _on_device(cache: Cache, *tensors) -> None:
+    """Every tensor on the cache's GPU (checked last, after shapes and dtypes)."""
+    dev = cache.n_quant.device
+    _need(dev.type == "cuda", f"the cache's buffers are on {dev}, not on a GPU")
+    for t in tensors:
+        if t is not None:
+            _need(t.device == dev, f"a tensor on {t.device} for a cache on {dev}")
+
+
 def quantize_append(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor, stream=None,
                     desc: CacheDesc | None = None) -> None:
-    """k_new, v_new: bf16 [batch][n_new][H_kv][128] on the cache's device."""
-    assert k_new.dtype == torch.bfloat16 and k_new.is_contiguous() and v_new.is_contiguous()
+    """k_new, v_new: bf16 [batch][n_new][H_kv][128] on the cache's device (batch of `desc`,
+    1 for a one-sequence view)."""
+    batch = (desc or cache.desc).batch
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _need(isinstance(t, torch.Tensor) and t.dtype == torch.bfloat16,
+              f"{name} must be a bfloat16 tensor")
+        _need(t.is_contiguous(), f"{name} must be contiguous")
+        _need(t.dim() == 4 and t.shape[0] == batch and t.shape[1] >= 1 and
+              t.shape[2] == cache.n_kv_heads and t.shape[3] == HEAD_DIM,
+              f"{name} must be [batch={batch}][n_new>=1][H_kv={cache.n_kv_heads}][{HEAD_DIM}], "
+              f"got {tuple(t.shape)}")
+    _need(k_new.shape == v_new.shape, "k_new and v_new must have the same shape")
+    _on_device(cache, k_new, v_new)
     st = lib.kvq_quantize_append(ctypes.byref(desc or cache.desc), k_new.data_ptr(),
                                  v_new.data_ptr(), k_new.shape[1], _stream(stream))
     _check(st, "kvq_quantize_append")
 
 
 def flush_residual(cache: Cache, stream=None, desc: CacheDesc | None = None) -> None:
+    _on_device(cache)
     _check(lib.kvq_flush_residual(ctypes.byref(desc or cache.desc), _stream(stream)),
            "kvq_flush_residual")
+
+
+def _check_query(cache: Cache, q: torch.Tensor, dims: int) -> None:
+    """q: bf16, contiguous, [batch][H_q][128] (dims 3) or [batch][n_q][H_q][128] (dims 4)."""
+    _need(isinstance(q, torch.Tensor) and q.dtype == torch.bfloat16, "q must be a bfloat16 tensor")
+    _need(q.is_contiguous(), "q must be contiguous")
+    _need(q.dim() == dims and q.shape[0] == cache.batch and q.shape[-1] == HEAD_DIM and
+          q.shape[-2] >= 1 and q.shape[-2] % cache.n_kv_heads == 0 and
+          (dims == 3 or q.shape[1] >= 1),
+          f"q must be [batch={cache.batch}]{'[n_q]' if dims == 4 else ''}[H_q, a multiple of "
+          f"H_kv={cache.n_kv_heads}][{HEAD_DIM}], got {tuple(q.shape)}")
+
+
+def _check_out(out: torch.Tensor, q: torch.Tensor) -> None:
+    _need(isinstance(out, torch.Tensor) and out.dtype == torch.float32, "out must be float32")
+    _need(out.is_contiguous() and tuple(out.shape) == tuple(q.shape),
+          f"out must be a contiguous {tuple(q.shape)} tensor, got {tuple(out.shape)}")
+
+
+def _check_workspace(ws: torch.Tensor) -> None:
+    _need(isinstance(ws, torch.Tensor) and ws.dtype == torch.uint8 and ws.is_contiguous() and
+          ws.dim() == 1, "workspace must be a contiguous 1-D uint8 tensor")
 
 
 def workspace_bytes(cache: Cache, n_q_heads: int, max_tokens: int) -> int:
@@ -235,17 +283,20 @@ def decode_attention(cache: Cache, q: torch.Tensor, max_tokens: int, out: torch.
                      workspace: torch.Tensor | None = None, sm_scale: float | None = None,
                      stream=None) -> torch.Tensor:
     """q: bf16 [batch][H_q][128] -> fp32 [batch][H_q][128]."""
-    assert q.dtype == torch.bfloat16 and q.is_contiguous()
+    _check_query(cache, q, 3)
     hq = q.shape[1]
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(HEAD_DIM)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    _check_out(out, q)
     need = workspace_bytes(cache, hq, max_tokens)
     if need == 0:
         raise KvqError(1, "kvq_decode_workspace_bytes")
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace)
+    _on_device(cache, q, out, workspace)
     st = lib.kvq_decode_attention(ctypes.byref(cache.desc), q.data_ptr(), hq, float(sm_scale),
                                   max_tokens, out.data_ptr(), workspace.data_ptr(),
                                   workspace.numel(), _stream(stream))
@@ -262,17 +313,20 @@ def decode_attention_mq(cache: Cache, q: torch.Tensor, max_tokens: int,
                         sm_scale: float | None = None, stream=None) -> torch.Tensor:
     """q: bf16 [batch][n_q][H_q][128], the queries of each sequence's last n_q cached tokens
     -> fp32 [batch][n_q][H_q][128] (causal)."""
-    assert q.dtype == torch.bfloat16 and q.is_contiguous() and q.dim() == 4
+    _check_query(cache, q, 4)
     nq, hq = q.shape[1], q.shape[2]
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(HEAD_DIM)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    _check_out(out, q)
     need = workspace_bytes_mq(cache, hq, nq, max_tokens)
     if need == 0:
         raise KvqError(1, "kvq_decode_workspace_bytes_mq")
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace)
+    _on_device(cache, q, out, workspace)
     st = lib.kvq_decode_attention_mq(ctypes.byref(cache.desc), q.data_ptr(), nq, hq,
                                      float(sm_scale), max_tokens, out.data_ptr(),
                                      workspace.data_ptr(), workspace.numel(), _stream(stream))
@@ -285,12 +339,14 @@ def decode_attention_noalloc(cache: Cache, q: torch.Tensor, max_tokens: int,
                              stream=None) -> torch.Tensor:
     """kvq_decode_attention_noalloc: as decode_attention, with the library's own workspace (no
     device allocation by the library; `out` may be preallocated by the caller)."""
-    assert q.dtype == torch.bfloat16 and q.is_contiguous()
+    _check_query(cache, q, 3)
     hq = q.shape[1]
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(HEAD_DIM)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    _check_out(out, q)
+    _on_device(cache, q, out)
     st = lib.kvq_decode_attention_noalloc(ctypes.byref(cache.desc), q.data_ptr(), hq,
                                           float(sm_scale), max_tokens, out.data_ptr(),
                                           _stream(stream))
@@ -307,10 +363,17 @@ def read_error(cache: Cache, stream=None) -> int:
 
 
 def measure_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    _need(buf.is_cuda and sink.is_cuda and buf.is_contiguous() and sink.dtype == torch.float32 and
+          sink.numel() >= lib.kvq_measure_read_sink_floats(),
+          "measure_read: contiguous GPU buffer and a float32 GPU sink of "
+          "kvq_measure_read_sink_floats() values")
     _check(lib.kvq_measure_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
                                 _stream(stream)), "kvq_measure_read")
 
 
 def measure_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
+    _need(dst.is_cuda and src.is_cuda and dst.is_contiguous() and src.is_contiguous() and
+          dst.numel() * dst.element_size() >= src.numel() * src.element_size(),
+          "measure_copy: contiguous GPU tensors, dst at least as large as src")
     _check(lib.kvq_measure_copy(dst.data_ptr(), src.data_ptr(), src.numel() * src.element_size(),
                                 _stream(stream)), "kvq_measure_copy")

@@ -89,6 +89,46 @@ def build_pair(k_side, v_side, B, Hq, H, R, lens, paged=False, seed=1, device="c
     return Pair(w, cache, seqs, list(lens), table, nblk, cap_oracle if not paged else 0)
 
 
+def build_pair_rows(k_side, v_side, Hq, H, R, k_rows, v_rows, paged=False, seed=1,
+                    device="cuda", single_tail: int = 0) -> Pair:
+    """A pair from given bf16 bits k_rows[b], v_rows[b] ([T_b][H][128] uint16 each): every
+    sequence gets its rows by one bulk append, except the last `single_tail` rows, appended one
+    token at a time (the per-token append path, windows flushing where due)."""
+    K = kvq()
+    B = len(k_rows)
+    lens = [int(r.shape[0]) for r in k_rows]
+    w = ki.Workload("rows", seed, B, Hq, H, max(max(lens), 1), ki.Side(*k_side), ki.Side(*v_side),
+                    residual=R, paged=paged)
+    table, nblk = None, 0
+    if paged:
+        table, nblk = ki.block_tables(w, lens, extra_tokens=64)
+        cap_oracle = table.shape[1] * 16
+        cache = K.Cache(k_side, v_side, B, H, residual=R, block_table=torch.from_numpy(table),
+                        num_blocks=nblk, device=device)
+    else:
+        gt = k_side[3] if k_side[2] == ki.PER_CHANNEL else 16
+        cap = int(math.ceil((max(lens) + R + 64) / max(gt, 16)) * max(gt, 16))
+        cap_oracle = cap
+        cache = K.Cache(k_side, v_side, B, H, residual=R, capacity=cap, device=device)
+    seqs = [oracle.Sequence(k_side, v_side, H, R, cap_oracle) for _ in range(B)]
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+
+    for b in range(B):
+        kb, vb = np.ascontiguousarray(k_rows[b]), np.ascontiguousarray(v_rows[b])
+        n_bulk = lens[b] - min(single_tail, lens[b])
+        if n_bulk:
+            K.quantize_append(cache, dev(kb[None, :n_bulk]), dev(vb[None, :n_bulk]),
+                              desc=cache.sequence(b))
+            seqs[b].append(kb[:n_bulk], vb[:n_bulk])
+        for t in range(n_bulk, lens[b]):
+            K.quantize_append(cache, dev(kb[None, t:t + 1]), dev(vb[None, t:t + 1]),
+                              desc=cache.sequence(b))
+            seqs[b].append(kb[t:t + 1], vb[t:t + 1])
+    return Pair(w, cache, seqs, lens, table, nblk, cap_oracle if not paged else 0)
+
+
 def step(pr: Pair, flush_first: bool = False, n_new: int = 1) -> None:
     """Append n_new tokens to every sequence (one batch call), optionally flushing first."""
     K = kvq()
@@ -151,11 +191,23 @@ def compare_state(pr: Pair) -> None:
                 assert np.array_equal(got[b, :, :nr[b]], ref[b, :, :nr[b]]), f"{name} seq {b}"
 
 
+def scaled_queries(w, step: int, device, q_scale: float = 1.0) -> torch.Tensor:
+    """The workload's seeded queries times q_scale, rounded to bf16 (the bits both sides get)."""
+    q = ki.queries(w, step, device)
+    if q_scale != 1.0:
+        q = (q.float() * q_scale).to(torch.bfloat16)
+    return q.contiguous()
+
+
 def compare_attention(pr: Pair, q_seed_step: int = 0, max_tokens: int | None = None,
-                      workspace: torch.Tensor | None = None):
+                      workspace: torch.Tensor | None = None, q_scale: float = 1.0,
+                      tol_scale: float = 1.0):
+    """Decode attention against the oracle.  tol_scale multiplies the absolute tolerance for
+    caches whose values are tol_scale times unit-scale values (the bar is stated for unit-scale
+    values; outputs scale with the values)."""
     K = kvq()
     dev = pr.cache.n_quant.device
-    q = ki.queries(pr.w, q_seed_step, dev)
+    q = scaled_queries(pr.w, q_seed_step, dev, q_scale)
     mt = max_tokens or max(s.n_quant + s.n_res for s in pr.seqs) or 1
     out = K.decode_attention(pr.cache, q, max_tokens=mt, sm_scale=SM_SCALE, workspace=workspace)
     torch.cuda.synchronize()
@@ -163,8 +215,9 @@ def compare_attention(pr: Pair, q_seed_step: int = 0, max_tokens: int | None = N
     got = out.cpu().numpy()
     qb = ki.bf16_bits(q)
     ref = np.stack([s.attend(qb[b], SM_SCALE) for b, s in enumerate(pr.seqs)])
+    assert np.all(np.isfinite(got)), "non-finite attention output"
     err = np.abs(got - ref)
-    ok = err <= ATOL + RTOL * np.abs(ref)
+    ok = err <= ATOL * tol_scale + RTOL * np.abs(ref)
     assert ok.all(), (f"attention: {int((~ok).sum())} of {ok.size} outside tolerance; "
                       f"max abs err {err.max():.3e} at {np.unravel_index(err.argmax(), err.shape)}")
     return float(err.max()), got
