@@ -47,7 +47,8 @@
  *               per-token groups they share one record per tile in k_scale (and k_zero):
  *               [tile][head_dim / k_group + head_dim / v_group][16], the key rows then the value
  *               rows, so a tile's rows are one contiguous run (one 128-byte line for 4-bit groups
- *               of 64); v_scale / v_zero are then unused (NULL, 0 bytes).  Per-channel key groups:
+ *               of 64); v_scale / v_zero are then unused (NULL, 0 bytes), and k_zero exists when
+ *               either side is asymmetric (the rows of a symmetric side are unused).  Per-channel key groups:
  *               contiguous [b][h][capacity / group][head_dim]; paged [block][h][head_dim], the
  *               row of key group tau kept with the block of its first token,
  *               block_table[b][tau * group / 16] (other blocks' rows are unused).  FP8: fp32
@@ -174,9 +175,14 @@ size_t kvq_buffer_bytes(const kvq_format *fmt, int32_t batch, int32_t n_kv_heads
                         int32_t capacity, int32_t num_blocks, int32_t which);
 
 /* Check a format without a cache: KVQ_OK, KVQ_EINVAL or KVQ_ENOTSUP.  Supported: head_dim 128;
- * bits 2/4/8 and one scheme, the same for K and V; per-token groups 32/64/128; per-channel
- * grouping for keys only (contiguous or paged), with residual > 0 divisible by the group;
- * FP8 and bits 16 as described above.  Pure host code. */
+ * each side 2, 4 or 8 bits, symmetric or asymmetric, chosen independently for keys and values
+ * (keys and values may warrant different treatment [P2, "Why scales and groups matter"; P3,
+ * "Why Can't You Quantize the KV Cache Like Ordinary Activations?"]); per-token groups
+ * 32/64/128; per-channel grouping for keys only (contiguous or paged), with residual > 0
+ * divisible by the group; FP8 and bits 16 as described above, on both sides (one side FP8 or
+ * BF16 and the other not: KVQ_ENOTSUP).  Keys and values of different integer formats are
+ * served by single-query decode (kvq_decode_attention_mq with n_q > 1 returns KVQ_ENOTSUP for
+ * them).  Pure host code. */
 kvq_status kvq_check_format(const kvq_format *fmt);
 
 /* Append n_new >= 1 new tokens to every sequence of the batch.

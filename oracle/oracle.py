@@ -322,7 +322,9 @@ def empty_images(k_side, v_side, batch: int, n_kv_heads: int, residual: int, cap
         else:
             n = batch * H * (capacity // group) * d
         out[f"{name}_scale"] = np.zeros(n, np.uint16)
-        out[f"{name}_zero"] = np.zeros(n if scheme == ASYM else (1 if n else 0), np.uint16)
+        # zero-points: the side's own, or, in a shared per-tile record, those of either side
+        has_zero = scheme == ASYM or (name == "k" and axis == PER_TOKEN and v_side[1] == ASYM)
+        out[f"{name}_zero"] = np.zeros(n if has_zero else (1 if n else 0), np.uint16)
         out[f"{name}_res"] = np.zeros(batch * H * max(residual, 1) * d, np.uint16)
     return out
 

@@ -19,7 +19,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvq.so")
 SOURCES = ["kvq_host.hip", "kvq_append.hip"] + [
     f"kvq_decode_b{bits}{scheme}.hip" for bits in (2, 4, 8) for scheme in "sa"] + [
-    "kvq_decode_b16.hip", "kvq_decode_b8f.hip"]
+    "kvq_decode_b16.hip", "kvq_decode_b8f.hip"] + [
+    f"kvq_decode_mix_k{bits}{scheme}.hip" for bits in (2, 4, 8) for scheme in "sa"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",

@@ -324,10 +324,10 @@ __device__ __forceinline__ void load_words(const uint8_t* ptr, uint32_t (&w)[KB]
 template <int NP>
 constexpr int scale_rows() { return NP == 2 ? 1 : NP; }
 
-template <int KB, int NP, bool KPC, bool ASYM>
+template <int KB, int VB, int NP, bool KPC>
 struct UnitData {
   uint32_t kw[2][KB];  // key slices of tiles A and B (token n, channels 32 g .. 32 g + 31)
-  uint32_t vw[2][KB];  // value chunks of tiles A and B (tokens 4 g .. 4 g + 3, channels 8 n ..)
+  uint32_t vw[2][VB];  // value chunks of tiles A and B (tokens 4 g .. 4 g + 3, channels 8 n ..)
   uint2 ks[2];         // per-token keys: scale of tokens 4 g .. 4 g + 3 (column's group)
   uint2 kz[2];         // per-token asymmetric keys: zero-points
   uint2 vs[scale_rows<NP>()][2];  // value scales of tokens 4 g .. 4 g + 3 (row's group), tiles A, B
@@ -383,7 +383,9 @@ __device__ __forceinline__ int aligned_ranges(int nb, int S, bool uniform) {
   return (S / k >= (nb + 1) / 2) ? S / k : nb;
 }
 
-template <int KB, int G, bool KPC, int NP, int SCH, int MQ>
+// KB, SCH: key bits and scheme; VB, VSCH: value bits and scheme (equal to the key's for FP8 and
+// BF16 storage).
+template <int KB, int G, bool KPC, int NP, int SCH, int MQ, int VB, int VSCH>
 __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 3 : 2) void decode_kernel(DecodeParams p) {
   // multi-query geometry; single-query instantiations fold it to constants
   const int nqt = MQ ? p.nqt : 1, qbs = MQ ? p.qbs : 1, nqb = MQ ? p.nqb : 1, gkv = MQ ? p.gkv : G;
@@ -392,11 +394,12 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
   constexpr int qpw = MQ == 2 ? 4 : MQ == 3 ? 2 : 1;
   constexpr int WPQ = WAVES / qpw;  // waves per query block
   const int nqs = MQ ? p.nqs : 1;
-  constexpr bool ASYM = SCH == KVQ_ASYM;
+  constexpr bool KASYM = SCH == KVQ_ASYM, VASYM = VSCH == KVQ_ASYM;
+  static_assert((SCH == KVQ_FP8) == (VSCH == KVQ_FP8) && (KB == 16) == (VB == 16), "formats");
   constexpr bool F8 = SCH == KVQ_FP8;  // E4M3 bytes, one scale per kv head (or tensor) per side
   // A segment's units are its compressed units, then WW slots per window unit; a window unit
   // belongs to the workgroup whose range holds its first slot.
-  constexpr int WW = window_weight(KB);
+  constexpr int WW = window_weight2(KB, VB);
   // In a batch of mixed lengths every segment also starts with SEG_W slots of no work, the cost
   // of a segment start (query staging, first loads) in units, so that a range holding many short
   // segments holds fewer units.  Batches of equal lengths (segment-aligned ranges) have none.
@@ -537,19 +540,20 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
   const int kgroup = (F8 || KB == 16) ? D : c.k.group, vgroup = (F8 || KB == 16) ? D : c.v.group;
   const int ngk = KPC ? 2 : D / kgroup;  // QK columns per head: key groups, or hi/lo parts
   const int ngv = D / vgroup;
-  constexpr float koff = ASYM ? 0.0f : static_cast<float>(1 << (KB - 1));
-  constexpr float voff = koff;
+  constexpr float koff = KASYM ? 0.0f : static_cast<float>(1 << (KB - 1));
+  constexpr float voff = VASYM ? 0.0f : static_cast<float>(1 << (VB - 1));
   // Integer value codes enter PV as f16 subnormals alpha u 2^-24 (one and per pair).  alpha is
   // a token-position factor VT (at i % 4 >= 2; the weights come out of the exponential divided
   // by it) times a channel factor of MFMA j, removed with the 2^24 when the compressed units are
   // done.  The offset of symmetric codes (-off times the sum of w s_v) is accumulated apart (zo).
-  constexpr bool VBF = !F8 && KB != 16;
-  constexpr float VLG = KB == 4 ? 4.0f : KB == 2 ? 2.0f : 0.0f;  // log2 VT
-  constexpr float VT = KB == 4 ? 16.0f : KB == 2 ? 4.0f : 1.0f;
+  constexpr bool VBF = !F8 && VB != 16;
+  constexpr float VLG = VB == 4 ? 4.0f : VB == 2 ? 2.0f : 0.0f;  // log2 VT
+  constexpr float VT = VB == 4 ? 16.0f : VB == 2 ? 4.0f : 1.0f;
   constexpr bool BF = KB == 16;  // unquantized BF16 storage: bf16 matrix products, no scales
   const int hh = n % G;          // query head of QK column n and of PV row 16 pp + n
   const int cg = (n / G) % ngk;  // key group (or hi/lo part) of QK column n
-  constexpr long TILE_BYTES = static_cast<long>(TILE) * D * KB / 8;
+  constexpr long K_TILE_BYTES = static_cast<long>(TILE) * D * KB / 8;
+  constexpr long V_TILE_BYTES = static_cast<long>(TILE) * D * VB / 8;
 
   int u = u0;
   bool first_seg = true;
@@ -643,22 +647,24 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
         return *reinterpret_cast<const uint4*>(base + mi);
       }
     };
-    UnitData<KB, NP, KPC, ASYM> d{};
-    const UnpackRegs ur = unpack_regs<KB>();
+    UnitData<KB, VB, NP, KPC> d{};
+    const UnpackRegs ur = unpack_regs<KB>();   // key code masks
+    const UnpackRegs urv = unpack_regs<VB>();  // value code masks
     bool bad_block = false;
     // Every unit issues the same loads (an unusable or absent tile reads tile 0 of the buffer
     // and is ignored), so the compiler can count outstanding loads exactly.
     // Loads address a wave-uniform tile base (scalar registers) plus a 32-bit lane offset
     // that is fixed for the segment, so no per-lane 64-bit address arithmetic is needed.
-    constexpr unsigned SP = (4 * KB < 16) ? 4 * KB : 16;  // bytes of a slice piece
-    const unsigned k_lane = SP * (4 * n + g);                // slice 4 n + g (token n)
-    const unsigned v_lane = SP * (16 * g + n);               // chunk 16 g + n
+    constexpr unsigned SPK = (4 * KB < 16) ? 4 * KB : 16;  // bytes of a key slice piece
+    constexpr unsigned SPV = (4 * VB < 16) ? 4 * VB : 16;  // bytes of a value slice piece
+    const unsigned k_lane = SPK * (4 * n + g);               // slice 4 n + g (token n)
+    const unsigned v_lane = SPV * (16 * g + n);              // chunk 16 g + n
     const unsigned ks_lane = cg * TILE + 4 * g;
     auto load_k = [&](int xx, int pA, int pB) {
       pA = max(pA, 0);
       pB = max(pB, 0);
-      load_words<KB>(c.kc + static_cast<size_t>(pA) * TILE_BYTES + k_lane, d.kw[0]);
-      load_words<KB>(c.kc + static_cast<size_t>(pB) * TILE_BYTES + k_lane, d.kw[1]);
+      load_words<KB>(c.kc + static_cast<size_t>(pA) * K_TILE_BYTES + k_lane, d.kw[0]);
+      load_words<KB>(c.kc + static_cast<size_t>(pB) * K_TILE_BYTES + k_lane, d.kw[1]);
       if constexpr (BF || F8) {
       } else if constexpr (KPC) {
         // a paged key group of 16 or 32 tokens starts at this unit's tile A, whose block then
@@ -666,21 +672,21 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
         const size_t mi = (trow && kgroup <= 2 * TILE) ? static_cast<size_t>(pA) * D + fold_c0
                                                        : kpc_meta((32 * xx) / kgroup);
         d.fs = load_meta8(c.ks, mi);
-        if constexpr (ASYM) d.fz = load_meta8(c.kz, mi);
+        if constexpr (KASYM) d.fz = load_meta8(c.kz, mi);
       } else {
 #pragma unroll
         for (int t = 0; t < 2; t++) {
           const size_t tb = static_cast<size_t>(t ? pB : pA) * c.ks_tile;
           d.ks[t] = *reinterpret_cast<const uint2*>(c.ks + tb + ks_lane);
-          if constexpr (ASYM) d.kz[t] = *reinterpret_cast<const uint2*>(c.kz + tb + ks_lane);
+          if constexpr (KASYM) d.kz[t] = *reinterpret_cast<const uint2*>(c.kz + tb + ks_lane);
         }
       }
     };
     auto load_v = [&](int pA, int pB) {
       pA = max(pA, 0);
       pB = max(pB, 0);
-      load_words<KB>(c.vc + static_cast<size_t>(pA) * TILE_BYTES + v_lane, d.vw[0]);
-      load_words<KB>(c.vc + static_cast<size_t>(pB) * TILE_BYTES + v_lane, d.vw[1]);
+      load_words<VB>(c.vc + static_cast<size_t>(pA) * V_TILE_BYTES + v_lane, d.vw[0]);
+      load_words<VB>(c.vc + static_cast<size_t>(pB) * V_TILE_BYTES + v_lane, d.vw[1]);
       if constexpr (!BF && !F8)
 #pragma unroll
       for (int t = 0; t < 2; t++) {
@@ -689,7 +695,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
         for (int pp = 0; pp < scale_rows<NP>(); pp++) {
           const unsigned lo = rgv[pp] * TILE + 4 * g;
           d.vs[pp][t] = *reinterpret_cast<const uint2*>(c.vs + tb + lo);
-          if constexpr (ASYM) d.vz[pp][t] = *reinterpret_cast<const uint2*>(c.vz + tb + lo);
+          if constexpr (VASYM) d.vz[pp][t] = *reinterpret_cast<const uint2*>(c.vz + tb + lo);
         }
       }
     };
@@ -768,10 +774,10 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
         for (int i = 0; i < 8; i++) {
           const float x = in_grp ? bf16_to_f32(raw[i]) * qsc : 0.0f;  // exact: a power of two
           qb[j][i] = static_cast<_Float16>(x * (1.0f / static_cast<float>(kelem_alpha<KB>(j, i))));
-          if constexpr (ASYM) qsum += x;
+          if constexpr (KASYM) qsum += x;
         }
       }
-      if constexpr (ASYM) {
+      if constexpr (KASYM) {
         qsum += __shfl_xor(qsum, 16);
         qsum += __shfl_xor(qsum, 32);
       }
@@ -927,7 +933,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
               const int k = nat(i);
               sv[i] = (k & 1) ? f16_hi(sw[k / 2]) : f16_lo(sw[k / 2]);
               pv[i] = fmaf(qfold[r0 / 4][i], sv[i], 0.0f);  // exact: 8-bit x 11-bit significands
-              if constexpr (ASYM) zp += qfold[r0 / 4][i] * ((k & 1) ? f16_hi(zwd[k / 2]) : f16_lo(zwd[k / 2]));
+              if constexpr (KASYM) zp += qfold[r0 / 4][i] * ((k & 1) ? f16_hi(zwd[k / 2]) : f16_lo(zwd[k / 2]));
             }
             uint32_t hw4[4], lw4[4];
 #pragma unroll
@@ -941,7 +947,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
             *reinterpret_cast<uint4*>(kf + hw * D + 8 * fold_blk) = uint4{hw4[0], hw4[1], hw4[2], hw4[3]};
             *reinterpret_cast<uint4*>(kf + (8 + hw) * D + 8 * fold_blk) = uint4{lw4[0], lw4[1], lw4[2], lw4[3]};
           }
-          if constexpr (ASYM) {
+          if constexpr (KASYM) {
             zp += row_ror<8>(zp);
             zp += row_ror<4>(zp);
             zp += row_ror<2>(zp);
@@ -953,12 +959,12 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
 #pragma unroll
         for (int j = 0; j < 4; j++)
           qb[j] = *reinterpret_cast<const f16x8*>(kf + (cg * 8 + hh) * D + 8 * (4 * g + j));
-        if constexpr (ASYM) zt = ztw[wave * 8 + hh];
+        if constexpr (KASYM) zt = ztw[wave * 8 + hh];
         wave_lds_sync();
         // subnormal key codes alpha u 2^-24: symmetric codes start at minus the offset,
         // -off alpha 2^-24 against the same operand; asymmetric ones need no start
         dq0 = f32x4{0.f, 0.f, 0.f, 0.f};
-        if constexpr (!ASYM) {
+        if constexpr (!KASYM) {
 #pragma unroll
           for (int j = 0; j < 4; j++) {
             f16x8 bias;
@@ -968,7 +974,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
             dq0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(bias, qb[j], dq0, 0, 0, 0);
           }
         }
-        if constexpr (ASYM) ztc = (cg == 0) ? zt : 0.0f;
+        if constexpr (KASYM) ztc = (cg == 0) ? zt : 0.0f;
       };
 
       for (; x < xq_end; x += xstep) {
@@ -998,7 +1004,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
             const size_t mi = trow ? static_cast<size_t>(max(pB, 0)) * D + fold_c0 : kpc_meta(2 * x + 1);
             const uint4 fs2 = load_meta8(c.ks, mi);
             uint4 fz2 = uint4{0, 0, 0, 0};
-            if constexpr (ASYM) fz2 = load_meta8(c.kz, mi);
+            if constexpr (KASYM) fz2 = load_meta8(c.kz, mi);
             kpc_fold(fs2, fz2);
             dq[1] = dq0;
 #pragma unroll
@@ -1054,7 +1060,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
             s2[4 * t + 1] = fmaf(dq[t][1], f16_hi(k2.x), 0.0f);
             s2[4 * t + 2] = fmaf(dq[t][2], f16_lo(k2.y), 0.0f);
             s2[4 * t + 3] = fmaf(dq[t][3], f16_hi(k2.y), 0.0f);
-            if constexpr (ASYM) {
+            if constexpr (KASYM) {
               const uint2 z2 = d.kz[t];
               s2[4 * t + 0] += f16_lo(z2.x) * qsum;
               s2[4 * t + 1] += f16_hi(z2.x) * qsum;
@@ -1135,7 +1141,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
             ws[4 * t + 1] = fmaf(s2[4 * t + 1], f16_hi(s2v.x), 0.0f);
             ws[4 * t + 2] = fmaf(s2[4 * t + 2], f16_lo(s2v.y), 0.0f);
             ws[4 * t + 3] = fmaf(s2[4 * t + 3], f16_hi(s2v.y), 0.0f);
-            if constexpr (ASYM) {
+            if constexpr (VASYM) {
               const uint2 z2v = d.vz[pp][t];
               float zv[4] = {f16_lo(z2v.x), f16_hi(z2v.x), f16_lo(z2v.y), f16_hi(z2v.y)};
               if (!full) {  // a token past the end may sit on a stand-in tile with any zero-point
@@ -1145,7 +1151,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
               float zp = 0.0f;
 #pragma unroll
               for (int r = 0; r < 4; r++) {
-                const float wa = VBF ? s2[4 * t + r] * static_cast<float>(velem_alpha<KB>(0, r)) : s2[4 * t + r];
+                const float wa = VBF ? s2[4 * t + r] * static_cast<float>(velem_alpha<VB>(0, r)) : s2[4 * t + r];
                 zp = fmaf(wa, zv[r], zp);
               }
               zacc[pp] += zp;
@@ -1179,11 +1185,11 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
         for (int j = 0; j < 8; j++) {
           if constexpr (VBF) {
             // subnormal codes alpha u 2^-24 against weights / token factor
-            const f16x8 vb = vop_sub<KB>(d.vw[0], d.vw[1], j, ur);
+            const f16x8 vb = vop_sub<VB>(d.vw[0], d.vw[1], j, urv);
 #pragma unroll
             for (int pp = 0; pp < NP; pp++)
               acc[pp][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[pp], vb, acc[pp][j], 0, 0, 0);
-            if constexpr (!ASYM) {
+            if constexpr (!VASYM) {
               if (j == 0) {
 #pragma unroll
                 for (int pp = 0; pp < NP; pp++)
@@ -1213,8 +1219,8 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
         for (int j = 0; j < 8; j++)
 #pragma unroll
           for (int r = 0; r < 4; r++)
-            acc[pp][j][r] = fmaf(acc[pp][j][r], 16777216.0f / static_cast<float>(vchan_alpha<KB>(j)),
-                                 ASYM ? 0.0f : zo[pp][r] * 16777216.0f);
+            acc[pp][j][r] = fmaf(acc[pp][j][r], 16777216.0f / static_cast<float>(vchan_alpha<VB>(j)),
+                                 VASYM ? 0.0f : zo[pp][r] * 16777216.0f);
     }
 
     // ---------------------------- BF16 window units ----------------------------
@@ -1334,7 +1340,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
           const int o = lane + 64 * oi;
           const int oh = o / D, ch = o % D;
           const int gv = ch / vgroup;
-          if (pp == 0) Ow[oi] = ASYM ? zw[wave * 32 + gv * G + oh] : 0.0f;
+          if (pp == 0) Ow[oi] = VASYM ? zw[wave * 32 + gv * G + oh] : 0.0f;
 #pragma unroll
           for (int part = 0; part < 2; part++) {
             const int row = (part * ngv + gv) * G + oh;
@@ -1395,7 +1401,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
             const float mv = mw[(w0 + k) * 8 + oh];
             e[oi][k] = __builtin_amdgcn_exp2f(mv - M);  // waves without tokens hold -FLT_MAX
           }
-          if constexpr (ASYM) {
+          if constexpr (VASYM) {
             const int row0 = gv * G + oh;
 #pragma unroll
             for (int k = 0; k < WPQ; k++) O[oi] += e[oi][k] * zw[(w0 + k) * 32 + row0];
@@ -1529,7 +1535,7 @@ __global__ __launch_bounds__(T) void combine_kernel(DecodeParams p) {
 // Workgroups of decode_kernel that are resident at once on the current device.  Each workgroup
 // owns 1/NB of the units, so the grid must never exceed what runs concurrently.  The answer
 // depends on the device and the LDS size alone and is cached per instantiation.
-template <int KB, int G, bool KPC, int NP, int SCH, int MQ>
+template <int KB, int G, bool KPC, int NP, int SCH, int MQ, int VB, int VSCH>
 int decode_resident_blocks(size_t lds) {
   static std::mutex mu;
   static int cached_dev = -1, cached_blocks = 0;
@@ -1542,7 +1548,7 @@ int decode_resident_blocks(size_t lds) {
   }
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<KB, G, KPC, NP, SCH, MQ>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<KB, G, KPC, NP, SCH, MQ, VB, VSCH>,
                                                    256, lds) != hipSuccess)
     return 0;
   std::lock_guard<std::mutex> g(mu);
@@ -1552,14 +1558,14 @@ int decode_resident_blocks(size_t lds) {
   return cached_blocks;
 }
 
-template <int KB, int G, bool KPC, int NP, int SCH, int MQ>
+template <int KB, int G, bool KPC, int NP, int SCH, int MQ, int VB, int VSCH>
 hipError_t launch_decode_t(const DecodeParams& p0, hipStream_t s) {
   DecodeParams p = p0;
   const size_t lds = DecodeLds<MQ>::bytes(p.c.B);
-  const int resident = decode_resident_blocks<KB, G, KPC, NP, SCH, MQ>(lds);
+  const int resident = decode_resident_blocks<KB, G, KPC, NP, SCH, MQ, VB, VSCH>(lds);
   if (resident <= 0) return hipErrorInvalidConfiguration;
   if (p.nblocks > resident) p.nblocks = resident;
-  decode_kernel<KB, G, KPC, NP, SCH, MQ><<<p.nblocks, 256, lds, s>>>(p);
+  decode_kernel<KB, G, KPC, NP, SCH, MQ, VB, VSCH><<<p.nblocks, 256, lds, s>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // slices: about one per 4 partials a segment has on average, 32 outputs per slice at most
@@ -1578,22 +1584,22 @@ hipError_t launch_decode_t(const DecodeParams& p0, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int KB, int SCH, int MQ>
+template <int KB, int SCH, int MQ, int VB, int VSCH>
 hipError_t launch_decode_mq(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s) {
   if constexpr (KB == 16 || SCH == KVQ_FP8) {  // whole-row formats: at most 16 PV rows
     if (kpc || NP != 1) return hipErrorInvalidValue;
     switch (G) {
-      case 1: return launch_decode_t<KB, 1, false, 1, SCH, MQ>(p, s);
-      case 2: return launch_decode_t<KB, 2, false, 1, SCH, MQ>(p, s);
-      case 4: return launch_decode_t<KB, 4, false, 1, SCH, MQ>(p, s);
-      case 8: return launch_decode_t<KB, 8, false, 1, SCH, MQ>(p, s);
+      case 1: return launch_decode_t<KB, 1, false, 1, SCH, MQ, VB, VSCH>(p, s);
+      case 2: return launch_decode_t<KB, 2, false, 1, SCH, MQ, VB, VSCH>(p, s);
+      case 4: return launch_decode_t<KB, 4, false, 1, SCH, MQ, VB, VSCH>(p, s);
+      case 8: return launch_decode_t<KB, 8, false, 1, SCH, MQ, VB, VSCH>(p, s);
       default: return hipErrorInvalidValue;
     }
   } else {
 #define KVQ_CASE(GG, NN)                                                        \
   if (G == GG && NP == NN)                                                      \
-    return kpc ? launch_decode_t<KB, GG, true, NN, SCH, MQ>(p, s)              \
-               : launch_decode_t<KB, GG, false, NN, SCH, MQ>(p, s);
+    return kpc ? launch_decode_t<KB, GG, true, NN, SCH, MQ, VB, VSCH>(p, s)    \
+               : launch_decode_t<KB, GG, false, NN, SCH, MQ, VB, VSCH>(p, s);
   KVQ_CASE(1, 1)
   KVQ_CASE(2, 1)
   KVQ_CASE(4, 1)
@@ -1611,12 +1617,32 @@ hipError_t launch_decode_mq(const DecodeParams& p, int G, int NP, bool kpc, hipS
 // mode 2 gives each wave its own block.
 template <int KB, int SCH>
 hipError_t launch_decode_bits(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s) {
-  if (p.nqt <= 1) return launch_decode_mq<KB, SCH, 0>(p, G, NP, kpc, s);
+  if (p.nqt <= 1) return launch_decode_mq<KB, SCH, 0, KB, SCH>(p, G, NP, kpc, s);
   switch (p.qpw) {
-    case 4: return launch_decode_mq<KB, SCH, 2>(p, G, NP, kpc, s);
-    case 2: return launch_decode_mq<KB, SCH, 3>(p, G, NP, kpc, s);
-    default: return launch_decode_mq<KB, SCH, 1>(p, G, NP, kpc, s);
+    case 4: return launch_decode_mq<KB, SCH, 2, KB, SCH>(p, G, NP, kpc, s);
+    case 2: return launch_decode_mq<KB, SCH, 3, KB, SCH>(p, G, NP, kpc, s);
+    default: return launch_decode_mq<KB, SCH, 1, KB, SCH>(p, G, NP, kpc, s);
   }
+}
+
+// Keys and values in different integer formats (bits and/or scheme): single-query decode only
+// (multi-query calls on such caches return KVQ_ENOTSUP on the host).  One translation unit per
+// key format instantiates the value formats that differ from it.
+template <int KB, int SCH>
+hipError_t launch_decode_mixed(const DecodeParams& p, int vb, int vsch, int G, int NP, bool kpc,
+                               hipStream_t s) {
+  if (p.nqt > 1) return hipErrorInvalidValue;
+#define KVQ_VFMT(VBB, VS)                                                      \
+  if constexpr (VBB != KB || VS != SCH)                                        \
+    if (vb == VBB && vsch == VS) return launch_decode_mq<KB, SCH, 0, VBB, VS>(p, G, NP, kpc, s);
+  KVQ_VFMT(2, KVQ_SYM)
+  KVQ_VFMT(2, KVQ_ASYM)
+  KVQ_VFMT(4, KVQ_SYM)
+  KVQ_VFMT(4, KVQ_ASYM)
+  KVQ_VFMT(8, KVQ_SYM)
+  KVQ_VFMT(8, KVQ_ASYM)
+#undef KVQ_VFMT
+  return hipErrorInvalidValue;
 }
 
 }  // namespace kvq

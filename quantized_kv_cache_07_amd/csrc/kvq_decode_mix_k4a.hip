@@ -1,0 +1,12 @@
+// kvq_decode_mix_k4a.hip -- decode-attention kernels for caches whose keys are 4-bit asymmetric
+// and whose values use another integer format (instantiations of kvq_decode.h).
+#include "kvq_decode.h"
+
+namespace kvq {
+
+hipError_t launch_decode_mixed_k4a(const DecodeParams& p, int vb, int vsch, int G, int NP, bool kpc,
+                                  hipStream_t s) {
+  return launch_decode_mixed<4, KVQ_ASYM>(p, vb, vsch, G, NP, kpc, s);
+}
+
+}  // namespace kvq

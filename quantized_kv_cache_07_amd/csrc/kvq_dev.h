@@ -89,6 +89,10 @@ constexpr int PART_STRIDE = D + 4;
 __host__ __device__ constexpr int window_weight(int bits) {
   return bits == 2 ? 5 : bits == 4 ? 4 : bits == 8 ? 2 : 1;
 }
+// The same for keys of kb bits and values of vb bits (the mean of the two, rounded up).
+__host__ __device__ constexpr int window_weight2(int kb, int vb) {
+  return (window_weight(kb) + window_weight(vb) + 1) / 2;
+}
 
 // Work weight of starting a segment (query staging, first loads), in units, given to every
 // segment of a batch of mixed lengths.

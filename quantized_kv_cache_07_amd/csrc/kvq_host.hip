@@ -28,6 +28,13 @@ hipError_t launch_decode_b4a(const DecodeParams& p, int G, int NP, bool kpc, hip
 hipError_t launch_decode_b8a(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s);
 hipError_t launch_decode_b16(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s);
 hipError_t launch_decode_b8f(const DecodeParams& p, int G, int NP, bool kpc, hipStream_t s);
+// keys and values in different integer formats, one function per key format (v: value format)
+hipError_t launch_decode_mixed_k2s(const DecodeParams& p, int vb, int vsch, int G, int NP, bool kpc, hipStream_t s);
+hipError_t launch_decode_mixed_k2a(const DecodeParams& p, int vb, int vsch, int G, int NP, bool kpc, hipStream_t s);
+hipError_t launch_decode_mixed_k4s(const DecodeParams& p, int vb, int vsch, int G, int NP, bool kpc, hipStream_t s);
+hipError_t launch_decode_mixed_k4a(const DecodeParams& p, int vb, int vsch, int G, int NP, bool kpc, hipStream_t s);
+hipError_t launch_decode_mixed_k8s(const DecodeParams& p, int vb, int vsch, int G, int NP, bool kpc, hipStream_t s);
+hipError_t launch_decode_mixed_k8a(const DecodeParams& p, int vb, int vsch, int G, int NP, bool kpc, hipStream_t s);
 
 namespace {
 
@@ -72,9 +79,15 @@ kvq_status check_format(const kvq_format* f) {
   if (s != KVQ_OK) return s;
   s = check_side(f->v, false, f->residual);
   if (s != KVQ_OK) return s;
-  if (f->k.bits != f->v.bits) return KVQ_ENOTSUP;
-  if (f->k.scheme != f->v.scheme) return KVQ_ENOTSUP;
+  // FP8 and BF16 storage on one side only is not implemented; integer sides combine freely
+  if ((f->k.scheme == KVQ_FP8) != (f->v.scheme == KVQ_FP8)) return KVQ_ENOTSUP;
+  if ((f->k.bits == 16) != (f->v.bits == 16)) return KVQ_ENOTSUP;
   return KVQ_OK;
+}
+
+// Keys and values in different formats (integer widths or schemes).
+bool mixed_format(const kvq_format& f) {
+  return f.k.bits != f.v.bits || f.k.scheme != f.v.scheme;
 }
 
 kvq_status check_cache(const kvq_cache* c) {
@@ -95,7 +108,7 @@ kvq_status check_cache(const kvq_cache* c) {
       (scaled && !shared && !c->v_scale) || !c->n_quant || !c->n_res || !c->err)
     return KVQ_EINVAL;
   if (c->fmt.k.scheme == KVQ_ASYM && !c->k_zero) return KVQ_EINVAL;
-  if (c->fmt.v.scheme == KVQ_ASYM && !shared && !c->v_zero) return KVQ_EINVAL;
+  if (c->fmt.v.scheme == KVQ_ASYM && !(shared ? c->k_zero : c->v_zero)) return KVQ_EINVAL;
   if (c->fmt.residual > 0 && (!c->k_res || !c->v_res)) return KVQ_EINVAL;
   // kernels index 16-slot tiles with 32-bit integers
   const long tiles = c->block_table ? static_cast<long>(c->num_blocks) * c->n_kv_heads
@@ -171,7 +184,7 @@ long units_bound(const kvq_cache* c, int max_tokens) {
   const long R = c->fmt.residual;
   const long wu = R > 0 ? (std::min<long>(R, max_tokens) + 31) / 32 : 0;
   const long per_seq = (static_cast<long>(max_tokens) + 31) / 32 + (R > 0 ? 1 : 0) +
-                       (window_weight(c->fmt.k.bits) - 1) * wu + SEGMENT_START_WEIGHT;
+                       (window_weight2(c->fmt.k.bits, c->fmt.v.bits) - 1) * wu + SEGMENT_START_WEIGHT;
   return static_cast<long>(c->batch) * c->n_kv_heads * per_seq;
 }
 
@@ -312,11 +325,14 @@ size_t kvq_buffer_bytes(const kvq_format* fmt, int32_t batch, int32_t n_kv_heads
         if (which == KVQ_BUF_K_ZERO || which == KVQ_BUF_V_ZERO) return 0;
         return (s.axis == KVQ_PER_HEAD ? static_cast<size_t>(n_kv_heads) : 1) * sizeof(float);
       }
-      if ((which == KVQ_BUF_K_ZERO || which == KVQ_BUF_V_ZERO) && s.scheme != KVQ_ASYM) return 0;
       if (shared_scale_records(*fmt)) {  // one record per tile in the key buffers
         if (which == KVQ_BUF_V_SCALE || which == KVQ_BUF_V_ZERO) return 0;
+        // zero rows exist when either side is asymmetric (a symmetric side's rows are unused)
+        if (which == KVQ_BUF_K_ZERO && fmt->k.scheme != KVQ_ASYM && fmt->v.scheme != KVQ_ASYM)
+          return 0;
         return tiles * (D / fmt->k.group + D / fmt->v.group) * TILE * 2;
       }
+      if ((which == KVQ_BUF_K_ZERO || which == KVQ_BUF_V_ZERO) && s.scheme != KVQ_ASYM) return 0;
       if (s.axis == KVQ_PER_TOKEN) return tiles * (D / s.group) * TILE * 2;
       if (paged) return static_cast<size_t>(num_blocks) * n_kv_heads * D * 2;  // per block
       if (capacity % s.group) return 0;
@@ -425,6 +441,17 @@ kvq_status kvq_decode_attention_mq(const kvq_cache* cache, const void* q, int32_
   const hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
   const bool asym = cache->fmt.k.scheme == KVQ_ASYM;
+  if (mixed_format(cache->fmt)) {
+    if (n_q > 1) return KVQ_ENOTSUP;  // multi-query decode: keys and values in one format only
+    const int vb = cache->fmt.v.bits, vs = cache->fmt.v.scheme;
+    switch (cache->fmt.k.bits) {
+      case 2: e = asym ? launch_decode_mixed_k2a(p, vb, vs, G, NP, kpc, st) : launch_decode_mixed_k2s(p, vb, vs, G, NP, kpc, st); break;
+      case 4: e = asym ? launch_decode_mixed_k4a(p, vb, vs, G, NP, kpc, st) : launch_decode_mixed_k4s(p, vb, vs, G, NP, kpc, st); break;
+      case 8: e = asym ? launch_decode_mixed_k8a(p, vb, vs, G, NP, kpc, st) : launch_decode_mixed_k8s(p, vb, vs, G, NP, kpc, st); break;
+      default: return KVQ_ENOTSUP;
+    }
+    return e == hipSuccess ? KVQ_OK : KVQ_ELAUNCH;
+  }
   switch (cache->fmt.k.bits) {
     case 2: e = asym ? launch_decode_b2a(p, G, NP, kpc, st) : launch_decode_b2s(p, G, NP, kpc, st); break;
     case 4: e = asym ? launch_decode_b4a(p, G, NP, kpc, st) : launch_decode_b4s(p, G, NP, kpc, st); break;

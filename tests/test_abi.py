@@ -41,7 +41,10 @@ def test_every_declared_symbol_is_exported(K):
                                    ((2, 1, 1, 32), (2, 1, 0, 32), 128),
                                    ((4, 1, 0, 32), (4, 1, 0, 32), 32),
                                    ((16, 0, 0, 128), (16, 0, 0, 128), 16),
-                                   ((8, 2, 3, 0), (8, 2, 2, 0), 16)])
+                                   ((8, 2, 3, 0), (8, 2, 2, 0), 16),
+                                   ((8, 0, 0, 64), (4, 1, 0, 32), 16),
+                                   ((4, 1, 0, 64), (2, 0, 0, 32), 0),
+                                   ((2, 1, 1, 32), (4, 0, 0, 64), 64)])
 def test_buffer_sizes_match_the_storage_layout(K, orc, k, v, R):
     fmt = K.make_format(k, v, R)
     B, H = 3, 2
@@ -55,6 +58,8 @@ def test_buffer_sizes_match_the_storage_layout(K, orc, k, v, R):
                 assert got == 4 * (H if side[2] == 3 else 1)
             elif side[1] == 2 and name.endswith("zero"):
                 assert got == 0
+            elif name == "k_zero" and k[2] == 0 and v[1] == 1:
+                assert got == im[name].nbytes > 0  # shared record: the values' zero rows
             elif name.endswith("zero") and side[1] == 0:
                 assert got == 0
             elif name.endswith("res") and R == 0:
@@ -78,19 +83,21 @@ def test_worked_example_footprint(K):
     ((4, 0, 1, 32), (4, 0, 0, 64), 0, 1),     # per-channel keys need a window
     ((4, 0, 1, 32), (4, 0, 0, 64), 48, 1),    # ... whose length the group divides
     ((4, 0, 0, 64), (4, 0, 1, 32), 64, 2),    # per-channel values are not implemented
-    ((8, 0, 0, 64), (4, 0, 0, 64), 0, 2),     # K and V share one bit width
+    ((8, 0, 0, 64), (4, 0, 0, 64), 0, 0),     # K and V widths chosen independently
+    ((2, 1, 1, 32), (4, 0, 0, 32), 64, 0),    # ... and schemes
+    ((4, 0, 0, 64), (8, 1, 0, 128), 0, 0),
     ((4, 2, 0, 64), (4, 0, 0, 64), 0, 1),
     ((4, 0, 0, 64), (4, 0, 0, 64), 24, 1),    # window not a multiple of 16
     ((16, 0, 0, 128), (16, 0, 0, 128), 0, 0),  # unquantized BF16 cache
     ((16, 0, 0, 128), (16, 0, 0, 128), 32, 0),
     ((16, 1, 0, 128), (16, 1, 0, 128), 0, 1),  # BF16 storage has no scheme ...
     ((16, 0, 0, 64), (16, 0, 0, 64), 0, 1),    # ... and no groups
-    ((16, 0, 0, 128), (8, 0, 0, 128), 0, 2),   # K and V share one width
+    ((16, 0, 0, 128), (8, 0, 0, 128), 0, 2),   # BF16 storage on one side only
     ((8, 2, 3, 0), (8, 2, 2, 0), 16, 0),       # FP8 E4M3: per-head keys, per-tensor values
     ((8, 2, 0, 0), (8, 2, 0, 0), 0, 1),        # FP8 scales are per tensor or per head
     ((8, 2, 3, 64), (8, 2, 3, 0), 0, 1),       # ... with no group
     ((4, 2, 3, 0), (4, 2, 3, 0), 0, 1),        # ... on 8-bit codes
-    ((8, 2, 3, 0), (8, 0, 0, 128), 0, 2),      # K and V share one scheme
+    ((8, 2, 3, 0), (8, 0, 0, 128), 0, 2),      # FP8 on one side only
 ])
 def test_check_format(K, k, v, R, status):
     fmt = K.make_format(k, v, R)
@@ -134,6 +141,11 @@ def test_host_errors_return_before_launch(K):
     d2.fmt = K.make_format((4, 0, 0, 32), (4, 0, 0, 64), 32)
     assert L.kvq_decode_attention(ctypes.byref(d2), 0x1000, 16, 0.1, 1000, 0x2000, 0x3000, 1 << 40,
                                   None) == 2      # 4 key groups x 8 heads > 16 MFMA columns
+    d3 = fake_cache(K)
+    d3.fmt = K.make_format((8, 0, 0, 64), (4, 0, 0, 64), 32)
+    ws3 = L.kvq_decode_workspace_bytes_mq(ctypes.byref(d3), 8, 4, 1000)
+    assert L.kvq_decode_attention_mq(ctypes.byref(d3), 0x1000, 4, 8, 0.1, 1000, 0x2000, 0x3000, ws3,
+                                     None) == 2   # multi-query over mixed K/V formats
     assert L.kvq_status_str(6).startswith(b"KVQ_EDEVICE")
 
 

@@ -43,6 +43,10 @@ CODEC_CASES = [
     ("asym4-g64-paged-window", (4, 1, 0, 64), (4, 1, 0, 128), 16, True, [90, 48], 20),
     ("asym2-g32-paged-window", (2, 1, 0, 32), (2, 1, 0, 32), 16, True, [90, 47], 20),
     ("asym2-g64", (2, 1, 0, 64), (2, 1, 0, 64), 0, False, [77, 20], 5),
+    # keys and values in different integer formats
+    ("mix-k8s-v4a-window", (8, 0, 0, 64), (4, 1, 0, 32), 16, False, [90, 40], 20),
+    ("mix-k2a-v8s-paged", (2, 1, 0, 32), (8, 0, 0, 128), 0, True, [70, 33], 5),
+    ("mix-kpc4a-v2s-paged", (4, 1, 1, 32), (2, 0, 0, 64), 64, True, [192, 96], 70),
     # per-channel keys: groups over tokens, formed when a window flushes
     ("kpc2-asym-g32", (2, 1, 1, 32), (2, 1, 0, 32), 64, False, [192, 128], 70),
     ("kpc2-sym-g64-paged", (2, 0, 1, 64), (2, 0, 0, 32), 128, True, [320, 192], 140),

@@ -74,6 +74,15 @@ CASES = [
     ("int2-g64-gqa8-two-row-blocks", (2, 0, 0, 64), (2, 0, 0, 64), 1, 16, 2, 16, [1200], False),
     ("int8-g32-gqa4-two-row-blocks", (8, 0, 0, 32), (8, 0, 0, 32), 2, 8, 2, 0, [321, 1029], True),
     ("asym8-g128-gqa2", (8, 1, 0, 128), (8, 1, 0, 128), 2, 4, 2, 64, [700, 65], False),
+    # keys and values in different integer formats (bit widths and/or schemes)
+    ("mix-k8-v4-gqa4-window", SYM8, SYM4, 2, 8, 2, 32, [777, 190], False),
+    ("mix-k4-v2asym-paged", SYM4, ASYM2_32, 3, 8, 2, 16, [500, 77, 1000], True),
+    ("mix-kivi2-v4sym", KPC2, SYM4, 2, 8, 2, 128, [700, 1300], False),
+    ("mix-k4asym-v8-gqa8-paged", (4, 1, 0, 64), (8, 0, 0, 128), 1, 16, 2, 16, [600], True),
+    ("mix-k2-v8asym-mha", (2, 0, 0, 32), (8, 1, 0, 64), 2, 4, 4, 0, [300, 1031], False),
+    ("mix-kpc8sym-v2-paged", (8, 0, 1, 16), (2, 0, 0, 32), 2, 4, 2, 32, [200, 90], True),
+    ("mix-k8asym-v8sym", (8, 1, 0, 64), SYM8, 2, 8, 2, 0, [321, 64], False),
+    ("mix-k2asym-v4asym-g32", ASYM2_32, ASYM4_32, 2, 4, 2, 16, [400, 33], True),
     # more sequences than one wave scans (the prologue's workgroup-wide prefix sum)
     ("int4-batch70-ragged", SYM4, SYM4, 70, 4, 2, 16, [20 + (37 * i) % 113 for i in range(70)], True),
 ]
