@@ -222,7 +222,33 @@ def settle(st, q, window: int = 10, max_windows: int = 30, tol: float = 0.02) ->
 # CPU baseline: the oracle, as it stands, on a bounded sample of the same sequences
 # ------------------------------------------------------------------------------------------
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_threads() -> int:
+    """Host threads for the N-core leg: the cores this process may run on, at most 16 (one GPU's
+    share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def cpu_baseline(st, gpu_out0, q0, budget_s: float = 15.0):
+    """The oracle's fp64 attention, as it stands, over the shortest sequences of the workload
+    until about budget_s of single-core work: once on one pinned core, then the same sequences
+    on N threads (one sequence per task; the oracle's C calls release the GIL).  Both legs
+    compute the same outputs, compared with the GPU's."""
+    import concurrent.futures as cf
+
     import numpy as np
 
     import kvq_inputs as ki
@@ -233,44 +259,74 @@ def cpu_baseline(st, gpu_out0, q0, budget_s: float = 15.0):
     sm = float(np.float32(1.0 / math.sqrt(HEAD_DIM)))
     order = sorted(range(w.batch), key=lambda b: st.lens[b])  # shortest first: bounded sample
     qb = ki.bf16_bits(q0)
-    used, t_attn, nbytes, max_err = [], 0.0, 0.0, 0.0
+    used, seqs, t_attn, nbytes, max_err = [], [], 0.0, 0.0, 0.0
     ok = True
-    for b in order:
-        T = st.lens[b]
-        seq = oracle.Sequence(w.k.astuple(), w.v.astuple(), w.n_kv_heads, w.residual,
-                              -(-(T + w.residual + 64) // 64) * 64)
-        k, v = ki.prefill_kv(lw, b, T, device="cpu")
-        seq.append(ki.bf16_bits(k), ki.bf16_bits(v))
-        t0 = time.perf_counter()
-        ref = seq.attend(qb[b], sm)
-        dt = time.perf_counter() - t0
-        t_attn += dt
-        nbytes += attention_bytes(w, [seq.n_quant], [seq.n_res])
-        used.append((b, T))
-        err = np.abs(gpu_out0[b] - ref)
-        max_err = max(max_err, float(err.max()))
-        ok = ok and bool(np.all(err <= 2e-3 + 1e-2 * np.abs(ref)))
-        if t_attn >= budget_s:
-            break
+    try:
+        aff = os.sched_getaffinity(0)
+        os.sched_setaffinity(0, {min(aff)})  # the single-core leg on one pinned core
+    except (AttributeError, OSError):
+        aff = None
+    try:
+        for b in order:
+            T = st.lens[b]
+            seq = oracle.Sequence(w.k.astuple(), w.v.astuple(), w.n_kv_heads, w.residual,
+                                  -(-(T + w.residual + 64) // 64) * 64)
+            k, v = ki.prefill_kv(lw, b, T, device="cpu")
+            seq.append(ki.bf16_bits(k), ki.bf16_bits(v))
+            t0 = time.perf_counter()
+            ref = seq.attend(qb[b], sm)
+            t_attn += time.perf_counter() - t0
+            nbytes += attention_bytes(w, [seq.n_quant], [seq.n_res])
+            used.append((b, T))
+            seqs.append(seq)
+            err = np.abs(gpu_out0[b] - ref)
+            max_err = max(max_err, float(err.max()))
+            ok = ok and bool(np.all(err <= 2e-3 + 1e-2 * np.abs(ref)))
+            if t_attn >= budget_s:
+                break
+    finally:
+        if aff is not None:
+            os.sched_setaffinity(0, aff)
+    n = cpu_threads()
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=n) as ex:
+        outs = list(ex.map(lambda i: seqs[i].attend(qb[used[i][0]], sm), range(len(seqs))))
+    t_n = time.perf_counter() - t0
+    same = all(np.array_equal(o, seqs[i].attend(qb[used[i][0]], sm)) for i, o in
+               enumerate(outs[:2]))
+    model = cpu_model()
     return {
-        "value": nbytes / t_attn / 1e9,
+        "value": nbytes / t_n / 1e9,
         "unit": "GB/s",
-        "cores": 1,
+        "cores": n,
         "kind": "oracle",
+        "value_1core": nbytes / t_attn / 1e9,
+        "seconds_1core": round(t_attn, 3),
+        "seconds_ncore": round(t_n, 3),
+        "cpu_model": model,
         "sample": (f"fp64 oracle attention (all {w.n_q_heads} query heads) over sequences "
-                   f"{[b for b, _ in used]} with {sum(t for _, t in used)} cached tokens, "
-                   f"{t_attn:.1f} s on one host core; same algorithmic-byte count as the GPU"),
-    }, {"sequences": [b for b, _ in used], "max_abs_err": max_err, "within_tolerance": ok}
+                   f"{[b for b, _ in used]} with {sum(t for _, t in used)} cached tokens: "
+                   f"{t_attn:.1f} s on one pinned core, {t_n:.2f} s on {n} threads (one sequence "
+                   f"per task) of a {model}; same algorithmic-byte count as the GPU"),
+    }, {"sequences": [b for b, _ in used], "max_abs_err": max_err, "within_tolerance": ok,
+        "ncore_equals_1core": same}
 
 
 # ------------------------------------------------------------------------------------------
 # Counter-derived traffic committed under profiles/
 # ------------------------------------------------------------------------------------------
 
+DECODE_SOURCES = ("kvq_decode.h", "kvq_dev.h", "kvq_host.hip")
+
+
 def decode_source_hash() -> str:
-    """Hash of the decode-attention kernel source (the counters go stale when it changes)."""
-    p = os.path.join(ROOT, "quantized_kv_cache_07_amd", "csrc", "kvq_decode.h")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    """Hash of the sources that decide the decode-attention call's memory traffic: the kernels,
+    the unit weights and layout constants, and the host's launch configuration (the counters go
+    stale when any of them changes)."""
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        h.update(open(os.path.join(ROOT, "quantized_kv_cache_07_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 CALIBRATION_BYTES = 1 << 30  # plain copy of known size, for scaling the byte counters
@@ -308,7 +364,8 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str, command: s
     copy_w = _per_dispatch(wr, "WRITE_SIZE", "measure_copy_kernel") * 1024
     kf, kw = CALIBRATION_BYTES / copy_f, CALIBRATION_BYTES / copy_w
     out = {"workload": workload, "command": command,
-           "kvq_decode_h_sha256_16": decode_source_hash(),
+           "decode_sources": list(DECODE_SOURCES),
+           "decode_sources_sha256_16": decode_source_hash(),
            "calibration": {"copy_bytes": CALIBRATION_BYTES, "fetch_counter_bytes": copy_f,
                            "write_counter_bytes": copy_w, "fetch_scale": kf, "write_scale": kw}}
     total = 0.0
@@ -335,6 +392,66 @@ def summarize_stats(stats_csv: str, command: str, title: str) -> str:
     return "\n".join(lines) + "\n"
 
 
+def summarize_trace(trace_csv: str, bench_json: str, command: str, workload: str) -> str:
+    """Per-dispatch durations of the kvq kernels from a rocprofv3 --kernel-trace CSV, split into
+    the phases of one bench.py run (its JSON line gives the counts): the untimed calls (the
+    prefilled-state call and the settle phase), the warmup and timed steps, and the
+    back-to-back attention loop whose average is the line's roofline figure."""
+    import csv
+    import statistics
+    line = None
+    for raw in open(bench_json):
+        raw = raw.strip()
+        if raw.startswith("{"):
+            line = json.loads(raw)
+    if line is None:
+        raise SystemExit(f"no JSON line in {bench_json}")
+    rows = list(csv.DictReader(open(trace_csv)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    def durs(sub):
+        return [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows
+                if sub in r["Kernel_Name"]]
+    dec, comb = durs("decode_kernel"), durs("combine_kernel")
+    quant, tail = durs("quantize_kernel"), durs("tail_kernel")
+    layers = line["config"].get("layers", 1)
+    W, K, A = line["warmup"], line["steps"], line["roofline"].get("attn_reps", 50)
+    n_loop, n_steps = (A + 3) * layers, (W + K) * layers
+    nd = len(dec)
+    groups = [("untimed (prefilled-state call + settle phase)", 0, nd - n_loop - n_steps),
+              ("warmup steps", nd - n_loop - n_steps, nd - n_loop - K * layers),
+              ("timed steps", nd - n_loop - K * layers, nd - n_loop),
+              ("attention loop (3 warm + the roofline's calls)", nd - n_loop, nd - n_loop + 3 * layers),
+              ("roofline calls", nd - A * layers, nd)]
+    out = [f"# Kernel trace: decode attention, workload {workload}", "",
+           "Command (from the repository root on the GPU box):", "", f"    {command}", "",
+           f"Bench line of the same run: ms_per_step {line['ms_per_step']}, roofline avg_launch_us "
+           f"{line['roofline']['avg_launch_us']} (HIP events around {A} back-to-back calls), frac "
+           f"{line['roofline']['frac']}, settle_calls {line.get('settle_calls')}.", "",
+           "Durations in µs per dispatch (kernel start to end, from the trace).", "",
+           "| phase | kernel | calls | mean | median | min | max |", "|---|---|---|---|---|---|---|"]
+    for name, lo, hi in groups:
+        for kname, xs in (("decode_kernel", dec), ("combine_kernel", comb)):
+            sel = xs[max(lo, 0):max(hi, 0)]
+            if not sel:
+                continue
+            out.append(f"| {name} | {kname} | {len(sel)} | {statistics.mean(sel):.2f} | "
+                       f"{statistics.median(sel):.2f} | {min(sel):.2f} | {max(sel):.2f} |")
+    rl_dec = dec[-A * layers:]
+    rl_comb = comb[-A * layers:] if len(comb) >= A * layers else []
+    tot = statistics.mean(rl_dec) + (statistics.mean(rl_comb) if rl_comb else 0.0)
+    ab = line["roofline"]["algorithmic_bytes_per_launch"]
+    out += ["", f"Roofline calls: decode_kernel + combine_kernel mean {tot:.2f} µs per call "
+            f"(kernel time only; the bench's {line['roofline']['avg_launch_us']} µs also holds the "
+            f"gaps between launches) -> {ab / (tot * 1e-6) / 1e9:.1f} GB/s = "
+            f"{ab / (tot * 1e-6) / 1e9 / HBM_PEAK_GBS:.4f} of 8 TB/s for {ab} algorithmic bytes."]
+    if len(quant) >= K * layers > 0:
+        qt, tt = quant[-K * layers:], tail[-K * layers:]
+        out += ["", f"Append kernels of the timed steps ({len(qt)} calls): quantize_kernel mean "
+                f"{statistics.mean(qt):.2f} µs (median {statistics.median(qt):.2f}), tail_kernel "
+                f"mean {statistics.mean(tt):.2f} µs (median {statistics.median(tt):.2f})."]
+    return "\n".join(out) + "\n"
+
+
 def counter_traffic(workload: str):
     """Per-launch HBM bytes of the decode kernel from the committed rocprofv3 counter summary,
     or None when there is none for this workload or the kernel source changed since."""
@@ -342,7 +459,7 @@ def counter_traffic(workload: str):
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
-    if d.get("kvq_decode_h_sha256_16") != decode_source_hash():
+    if d.get("decode_sources_sha256_16") != decode_source_hash():
         return None
     return d.get("bytes_per_launch")
 
@@ -548,6 +665,9 @@ def main() -> int:
                     help="write profiles/decode_<workload>_traffic.json from two rocprofv3 --pmc runs")
     ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV",
                     help="print a text summary of a rocprofv3 --stats kernel table")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("KERNEL_TRACE_CSV", "BENCH_JSON"),
+                    help="print per-phase kernel durations of one bench run from its rocprofv3 "
+                         "--kernel-trace CSV and its JSON line")
     ap.add_argument("--command", default="", help="the profiling command, recorded in summaries")
     ap.add_argument("--sweep", choices=["crossover", "multiquery"],
                     help="instead of the step benchmark: BF16 vs quantized decode-attention sweep")
@@ -563,6 +683,9 @@ def main() -> int:
         return 0
     if a.summarize_stats:
         print(summarize_stats(a.summarize_stats, a.command, f"kvq kernels, workload {a.workload}"), end="")
+        return 0
+    if a.summarize_trace:
+        print(summarize_trace(*a.summarize_trace, a.command, a.workload), end="")
         return 0
     if a.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
@@ -719,7 +842,7 @@ def main() -> int:
                      "traffic": traffic,
                      "kernel": "decode attention call: decode_kernel + combine_kernel",
                      "algorithmic_bytes_per_launch": int(attn_b),
-                     "avg_launch_us": round(attn_us, 3)},
+                     "avg_launch_us": round(attn_us, 3), "attn_reps": a.attn_reps},
         "stream_read_ceiling_gbs": round(stream_gbs, 1),
         "cpu_baseline": cpu,
         "parity_sample": parity,

@@ -104,7 +104,9 @@ enum { KVQ_PER_TOKEN = 0, KVQ_PER_CHANNEL = 1, KVQ_PER_TENSOR = 2, KVQ_PER_HEAD 
 enum {
   KVQ_ERR_CAPACITY = 1, /* append: a contiguous sequence has no free compressed slot */
   KVQ_ERR_BLOCK = 2,    /* a block-table entry outside [0, num_blocks) or beyond max_blocks */
-  KVQ_ERR_TOKENS = 4    /* decode: n_quant + n_res exceeded max_tokens (sequence skipped) */
+  KVQ_ERR_TOKENS = 4,   /* decode: n_quant + n_res exceeded max_tokens (sequence skipped) */
+  KVQ_ERR_GROUP = 8     /* append/flush with per-channel keys: n_quant is not a multiple of the
+                           key group, so a flush would start inside a group (sequence skipped) */
 };
 
 /* Buffers of a cache, for kvq_buffer_bytes(). */
@@ -196,7 +198,8 @@ kvq_status kvq_check_format(const kvq_format *fmt);
  * After T appends to an empty sequence with R > 0: n_res = (T-1) mod R + 1.
  * Paged caches: the block table must already map every slot the call may write.
  * Device faults: KVQ_ERR_CAPACITY (contiguous slots exhausted), KVQ_ERR_BLOCK (a needed table
- * entry is outside [0, num_blocks) or beyond max_blocks); the sequence is left unchanged.
+ * entry is outside [0, num_blocks) or beyond max_blocks), KVQ_ERR_GROUP (per-channel keys and
+ * an n_quant that is not a multiple of the key group); the sequence is left unchanged.
  * Launches two kernels on `stream`. */
 kvq_status kvq_quantize_append(const kvq_cache *cache, const void *k_new, const void *v_new,
                                int32_t n_new, void *stream);

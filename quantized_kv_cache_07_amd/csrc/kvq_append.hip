@@ -134,7 +134,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(CacheDev c, const uint16_
   const int lo = max(seg0, nq), hi = min(seg0 + S, nq + F);
   if (lo >= hi) return;
   if (!c.table && nq + F > c.cap) return;  // reported by tail_kernel; nothing written
-  if (c.k.axis == KVQ_PER_CHANNEL && (lo != seg0 || hi != seg0 + S)) return;  // whole groups only
+  // per-channel key groups start at multiples of S: a sequence whose n_quant is not one would
+  // split a group (reported by tail_kernel; nothing of the sequence is written)
+  if (c.k.axis == KVQ_PER_CHANNEL && (nq % S != 0 || lo != seg0 || hi != seg0 + S)) return;
   if (tid == 0) {
     int ok = 1;
     if (c.table)
@@ -396,7 +398,10 @@ __global__ __launch_bounds__(256) void tail_kernel(CacheDev c, const uint16_t* k
   const int nr = c.R > 0 ? c.n_res[b] : 0;
   int F, total, nra;
   step_counts(mode, c.R, nr, n_new, F, total, nra);
-  if (tid == 0) s_bad = (nq < 0 || nr < 0 || nr > c.R) ? KVQ_ERR_CAPACITY : 0;
+  if (tid == 0) {
+    s_bad = (nq < 0 || nr < 0 || nr > c.R) ? KVQ_ERR_CAPACITY : 0;
+    if (!s_bad && F > 0 && c.k.axis == KVQ_PER_CHANNEL && nq % c.k.group != 0) s_bad = KVQ_ERR_GROUP;
+  }
   __syncthreads();
   if (F > 0 && !s_bad) {
     if (!c.table) {

@@ -22,7 +22,7 @@ HEAD_DIM = 128
 BLOCK = 16
 (BUF_K_CODES, BUF_V_CODES, BUF_K_SCALE, BUF_V_SCALE, BUF_K_ZERO, BUF_V_ZERO, BUF_K_RES,
  BUF_V_RES) = range(8)
-ERR_CAPACITY, ERR_BLOCK, ERR_TOKENS = 1, 2, 4
+ERR_CAPACITY, ERR_BLOCK, ERR_TOKENS, ERR_GROUP = 1, 2, 4, 8
 
 STATUS = {0: "KVQ_OK", 1: "KVQ_EINVAL", 2: "KVQ_ENOTSUP", 3: "KVQ_EALIGN", 4: "KVQ_ENOSPACE",
           5: "KVQ_ELAUNCH", 6: "KVQ_EDEVICE"}

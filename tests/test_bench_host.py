@@ -17,7 +17,7 @@ def test_traffic_summaries_are_read_back(monkeypatch):
     for path in files:
         d = json.load(open(path))
         wl = os.path.basename(path)[len("decode_"):-len("_traffic.json")]
-        key = "kvq_decode_h_sha256_16"
+        key = "decode_sources_sha256_16"
         assert key in d and d["bytes_per_launch"] > 0
         monkeypatch.setattr(bench, "decode_source_hash", lambda: d[key])
         assert bench.counter_traffic(wl) == d["bytes_per_launch"]

@@ -247,6 +247,27 @@ def test_device_faults_leave_other_sequences_intact():
     assert pr2.cache.n_quant.cpu().tolist() == [16, 6]
 
 
+def test_per_channel_flush_inside_a_group_is_refused():
+    """Per-channel keys: a sequence whose n_quant is not a multiple of the key group (a corrupt
+    or misaligned prefix) would flush into the middle of a group.  The append sets
+    KVQ_ERR_GROUP, writes nothing of that sequence and leaves its counters; the other sequence
+    flushes and appends as usual."""
+    announce(test="per_channel_group_fault")
+    K = kc.kvq()
+    pr = kc.build_pair(KPC2, ASYM2_32, 2, 8, 2, 64, [64, 64], seed=44)
+    kc.compare_state(pr)
+    pr.cache.n_quant[1] = 16  # not a multiple of the 32-token key group; window full (64)
+    codes0 = pr.cache.k_codes.clone()
+    k, v = kc.ki.step_kv(pr.w, 0)
+    K.quantize_append(pr.cache, k.cuda().contiguous(), v.cuda().contiguous())
+    torch.cuda.synchronize()
+    assert K.read_error(pr.cache) & K.ERR_GROUP
+    assert pr.cache.n_quant.tolist() == [64, 16] and pr.cache.n_res.tolist() == [1, 64]
+    # sequence 1's slots (the second half of the contiguous buffer) are untouched
+    half = codes0.numel() // 2
+    assert torch.equal(pr.cache.k_codes[half:], codes0[half:])
+
+
 def test_prefix_shared_blocks_are_read_not_written():
     """Prefix sharing through the block table [P2, "How this connects to paging and prefix
     caching"]: sequence 1 maps sequence 0's first P/16 physical blocks (its compressed prefix,
