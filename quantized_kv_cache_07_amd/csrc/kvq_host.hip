@@ -488,7 +488,11 @@ kvq_status kvq_read_error(const kvq_cache* cache, int32_t* host_err, void* strea
 }
 
 const char* kvq_status_str(kvq_status status) {
-  switch (status) {
+  // a C caller may pass any int: read the value as one (an out-of-range enum load is undefined
+  // in C++)
+  int v;
+  std::memcpy(&v, &status, sizeof v);
+  switch (v) {
     case KVQ_OK: return "KVQ_OK";
     case KVQ_EINVAL: return "KVQ_EINVAL: invalid argument or descriptor";
     case KVQ_ENOTSUP: return "KVQ_ENOTSUP: combination not implemented";

@@ -25,6 +25,49 @@ def kvq():
     return mod
 
 
+CANARY = 4096          # bytes of guard before and after every device buffer of a test cache
+CANARY_BYTE = 0xA5
+
+
+def guarded(t: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
+    """A copy of t inside a larger byte buffer whose first and last CANARY bytes hold a fixed
+    pattern; returns (the copy, the whole buffer)."""
+    nbytes = t.numel() * t.element_size()
+    big = torch.full((2 * CANARY + nbytes,), CANARY_BYTE, dtype=torch.uint8, device=t.device)
+    inner = big[CANARY:CANARY + nbytes].view(t.dtype).view(t.shape)
+    inner.copy_(t)
+    return inner, big
+
+
+def intact(big: torch.Tensor) -> bool:
+    return bool(torch.all(big[:CANARY] == CANARY_BYTE)) and bool(torch.all(big[-CANARY:] == CANARY_BYTE))
+
+
+GUARDED_BUFFERS = ("k_codes", "v_codes", "k_scale", "v_scale", "k_zero", "v_zero", "k_res", "v_res",
+                   "n_quant", "n_res", "err", "block_table")
+
+
+def guard_cache(cache) -> list:
+    """Move every buffer of a cache into a guarded copy (same contents) and re-describe it;
+    returns the guard buffers for check_guards()."""
+    guards = []
+    for name in GUARDED_BUFFERS:
+        t = getattr(cache, name, None)
+        if t is None:
+            continue
+        inner, big = guarded(t)
+        setattr(cache, name, inner)
+        guards.append((name, big))
+    cache.desc = cache._describe()
+    return guards
+
+
+def check_guards(guards) -> None:
+    torch.cuda.synchronize()
+    bad = [name for name, big in guards if not intact(big)]
+    assert not bad, f"writes outside the buffers: guard bytes changed around {bad}"
+
+
 @dataclasses.dataclass
 class Pair:
     w: ki.Workload
@@ -35,6 +78,7 @@ class Pair:
     num_blocks: int
     capacity: int
     steps: int = 0
+    guards: list = dataclasses.field(default_factory=list)
 
 
 def fp8_scales(side, H, is_key):
@@ -70,6 +114,7 @@ def build_pair(k_side, v_side, B, Hq, H, R, lens, paged=False, seed=1, device="c
         cap = capacity or int(math.ceil(need / max(gt, 16)) * max(gt, 16))
         cap_oracle = cap
         cache = K.Cache(k_side, v_side, B, H, residual=R, capacity=cap, device=device, **cache_kw)
+    guards = guard_cache(cache)
     seqs = [oracle.Sequence(k_side, v_side, H, R, cap_oracle, **seq_kw) for _ in range(B)]
     if bulk:
         assert len(set(lens)) == 1
@@ -86,7 +131,8 @@ def build_pair(k_side, v_side, B, Hq, H, R, lens, paged=False, seed=1, device="c
             K.quantize_append(cache, k[None].to(device).contiguous(), v[None].to(device).contiguous(),
                               desc=cache.sequence(b))
             seqs[b].append(ki.bf16_bits(k), ki.bf16_bits(v))
-    return Pair(w, cache, seqs, list(lens), table, nblk, cap_oracle if not paged else 0)
+    return Pair(w, cache, seqs, list(lens), table, nblk, cap_oracle if not paged else 0,
+                guards=guards)
 
 
 def build_pair_rows(k_side, v_side, Hq, H, R, k_rows, v_rows, paged=False, seed=1,
@@ -110,6 +156,7 @@ def build_pair_rows(k_side, v_side, Hq, H, R, k_rows, v_rows, paged=False, seed=
         cap = int(math.ceil((max(lens) + R + 64) / max(gt, 16)) * max(gt, 16))
         cap_oracle = cap
         cache = K.Cache(k_side, v_side, B, H, residual=R, capacity=cap, device=device)
+    guards = guard_cache(cache)
     seqs = [oracle.Sequence(k_side, v_side, H, R, cap_oracle) for _ in range(B)]
 
     def dev(a):
@@ -126,7 +173,7 @@ def build_pair_rows(k_side, v_side, Hq, H, R, k_rows, v_rows, paged=False, seed=
             K.quantize_append(cache, dev(kb[None, t:t + 1]), dev(vb[None, t:t + 1]),
                               desc=cache.sequence(b))
             seqs[b].append(kb[t:t + 1], vb[t:t + 1])
-    return Pair(w, cache, seqs, lens, table, nblk, cap_oracle if not paged else 0)
+    return Pair(w, cache, seqs, lens, table, nblk, cap_oracle if not paged else 0, guards=guards)
 
 
 def step(pr: Pair, flush_first: bool = False, n_new: int = 1) -> None:
@@ -165,6 +212,7 @@ def _u16(t):
 
 def compare_state(pr: Pair) -> None:
     torch.cuda.synchronize()
+    check_guards(pr.guards)
     c = pr.cache
     assert kvq().read_error(c) == 0
     nq = c.n_quant.cpu().numpy()
@@ -209,8 +257,15 @@ def compare_attention(pr: Pair, q_seed_step: int = 0, max_tokens: int | None = N
     dev = pr.cache.n_quant.device
     q = scaled_queries(pr.w, q_seed_step, dev, q_scale)
     mt = max_tokens or max(s.n_quant + s.n_res for s in pr.seqs) or 1
-    out = K.decode_attention(pr.cache, q, max_tokens=mt, sm_scale=SM_SCALE, workspace=workspace)
+    out, out_big = guarded(torch.full(q.shape, float("nan"), dtype=torch.float32, device=dev))
+    extra = []
+    if workspace is None:
+        need = K.workspace_bytes(pr.cache, q.shape[1], mt)
+        workspace, ws_big = guarded(torch.full((need,), 0x5A, dtype=torch.uint8, device=dev))
+        extra.append(("workspace", ws_big))
+    K.decode_attention(pr.cache, q, max_tokens=mt, sm_scale=SM_SCALE, out=out, workspace=workspace)
     torch.cuda.synchronize()
+    check_guards(pr.guards + [("out", out_big)] + extra)
     assert K.read_error(pr.cache) == 0
     got = out.cpu().numpy()
     qb = ki.bf16_bits(q)
@@ -235,8 +290,16 @@ def compare_attention_mq(pr: Pair, n_q: int, q_seed_step: int = 7, max_tokens: i
     K = kvq()
     q = mq_queries(pr, n_q, q_seed_step)
     mt = max_tokens or max(s.n_quant + s.n_res for s in pr.seqs)
-    out = K.decode_attention_mq(pr.cache, q, max_tokens=mt, sm_scale=SM_SCALE, workspace=workspace)
+    out, out_big = guarded(torch.full(q.shape, float("nan"), dtype=torch.float32, device=q.device))
+    extra = []
+    if workspace is None:
+        need = K.workspace_bytes_mq(pr.cache, q.shape[2], n_q, mt)
+        workspace, ws_big = guarded(torch.full((need,), 0x5A, dtype=torch.uint8, device=q.device))
+        extra.append(("workspace", ws_big))
+    K.decode_attention_mq(pr.cache, q, max_tokens=mt, sm_scale=SM_SCALE, out=out,
+                          workspace=workspace)
     torch.cuda.synchronize()
+    check_guards(pr.guards + [("out", out_big)] + extra)
     assert K.read_error(pr.cache) == 0
     got = out.cpu().numpy()
     qb = ki.bf16_bits(q)
