@@ -661,6 +661,9 @@ def main() -> int:
     ap.add_argument("--attn-reps", type=int, default=50)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the timed steps and the attention loop in HIP graphs (removes "
+                         "the host's launch rate from launch-bound workloads such as c2x32)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/decode_<workload>_traffic.json from two rocprofv3 --pmc runs")
     ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV",
@@ -751,11 +754,24 @@ def main() -> int:
     for s in range(a.warmup):
         run_step(st, s)
     torch.cuda.synchronize()
+    step_graph = None
+    if a.graph:
+        # the timed steps captured into one HIP graph (no allocation or memset inside: outputs
+        # and workspace are preallocated); replayed once below, so the host's launch rate is
+        # out of the timed region
+        step_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(step_graph):
+            for s in range(a.warmup, n_total):
+                run_step(st, s)
+        torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     e0.record()
-    for s in range(a.warmup, n_total):
-        run_step(st, s)
+    if step_graph is not None:
+        step_graph.replay()
+    else:
+        for s in range(a.warmup, n_total):
+            run_step(st, s)
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -771,13 +787,34 @@ def main() -> int:
 
     # Decode-attention call alone, on the final state, back to back on the current stream.
     q = st.step_in[-1][0][2]
+    if step_graph is not None:
+        # the graph's last call (the last layer of the last step) left its output in st.out: an
+        # eager call on the same final state must reproduce it bit for bit
+        from_graph = st.out.clone()
+        lw_last, cache_last = st.caches[-1]
+        kvq.decode_attention(cache_last, st.step_in[-1][-1][2], st.max_tokens, out=st.out,
+                             workspace=st.ws)
+        torch.cuda.synchronize()
+        if not torch.equal(from_graph, st.out):
+            raise RuntimeError("graph replay differs from the eager call")
     for _ in range(3):
         attention_only(st, q)
     torch.cuda.synchronize()
+    attn_graph = None
+    if a.graph:
+        attn_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(attn_graph):
+            for _ in range(a.attn_reps):
+                attention_only(st, q)
+        attn_graph.replay()  # untimed first replay
+        torch.cuda.synchronize()
     a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a0.record()
-    for _ in range(a.attn_reps):
-        attention_only(st, q)
+    if attn_graph is not None:
+        attn_graph.replay()
+    else:
+        for _ in range(a.attn_reps):
+            attention_only(st, q)
     a1.record()
     torch.cuda.synchronize()
     attn_us = a0.elapsed_time(a1) * 1e3 / (a.attn_reps * st.layers)
@@ -831,7 +868,8 @@ def main() -> int:
                    "layers": st.layers, "tokens_min": min(st.lens), "tokens_max": max(st.lens),
                    "cached_tokens": int(sum(st.lens)), "residual": w.residual,
                    "paged": w.paged, "step": ("flush where due + append 1 + attention"
-                                              if appends else "attention")},
+                                              if appends else "attention"),
+                   "launch": "hip graph" if a.graph else "eager"},
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
         "kv_tokens_per_s": round(tok_s, 1),
         "flushes_in_timed_steps": flushes,

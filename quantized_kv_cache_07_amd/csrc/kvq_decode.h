@@ -994,6 +994,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
         // masked below, so the MFMAs run unconditionally.
         if constexpr (KPC) kpc_fold(d.fs, d.fz);
         f32x4 dq[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        float ztc_a = ztc;  // tile A's zero-point term (tile B may fold its own group)
         if constexpr (KPC) {
           if (kgroup == 16 && nvB > 0) {
             // tile B opens its own key group: finish tile A with the current fold first
@@ -1002,6 +1003,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
             for (int j = 0; j < 4; j++)
               dq[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop_sub<KB>(d.kw[0], j, ur), qb[j], dq[0], 0, 0, 0);
             const size_t mi = trow ? static_cast<size_t>(max(pB, 0)) * D + fold_c0 : kpc_meta(2 * x + 1);
+            ztc_a = ztc;
             const uint4 fs2 = load_meta8(c.ks, mi);
             uint4 fz2 = uint4{0, 0, 0, 0};
             if constexpr (KASYM) fz2 = load_meta8(c.kz, mi);
@@ -1053,7 +1055,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
             for (int r = 0; r < 4; r++) s2[4 * t + r] = dq[t][r] * f8k;
           } else if constexpr (KPC) {  // hi + lo columns are summed below; zt once, in the hi one
 #pragma unroll
-            for (int r = 0; r < 4; r++) s2[4 * t + r] = fmaf(dq[t][r], 0x1p24f, ztc);
+            for (int r = 0; r < 4; r++) s2[4 * t + r] = fmaf(dq[t][r], 0x1p24f, t ? ztc : ztc_a);
           } else {
             const uint2 k2 = d.ks[t];
             s2[4 * t + 0] = fmaf(dq[t][0], f16_lo(k2.x), 0.0f);

@@ -63,6 +63,10 @@ CASES = [
     ("kivi-int2-paged", KPC2, ASYM2_32, 2, 8, 2, 128, [700, 1300], True),
     ("kpc4-sym-g16-paged", KPC4S, SYM4, 2, 4, 1, 32, [100, 50], True),
     ("kpc4-asym-g64-paged", (4, 1, 1, 64), (4, 1, 0, 32), 1, 8, 2, 64, [500], True),
+    # asymmetric per-channel keys in 16-token groups: tiles A and B of a unit belong to two
+    # groups with their own zero-point terms
+    ("kpc4-asym-g16-gqa8-paged", (4, 1, 1, 16), (4, 0, 0, 128), 1, 16, 2, 16, [260], True),
+    ("kpc2-asym-g16", (2, 1, 1, 16), (2, 1, 0, 32), 2, 8, 2, 32, [300, 77], False),
     # two PV row blocks (hi and lo parts of one set of value-group rows), symmetric and GQA-8
     ("int4-g32-gqa4-two-row-blocks", (4, 0, 0, 32), (4, 0, 0, 32), 2, 8, 2, 0, [345, 1200], False),
     ("kpc8-asym-gqa8-two-row-blocks", (8, 1, 1, 32), (8, 1, 0, 64), 1, 16, 2, 64, [900], False),
