@@ -386,7 +386,7 @@ __device__ __forceinline__ int aligned_ranges(int nb, int S, bool uniform) {
 // KB, SCH: key bits and scheme; VB, VSCH: value bits and scheme (equal to the key's for FP8 and
 // BF16 storage).
 template <int KB, int G, bool KPC, int NP, int SCH, int MQ, int VB, int VSCH>
-__global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 3 : 2) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256, (KB != 16 && MQ != 2 && MQ != 3 && (NP == 1 || G <= 4)) ? 3 : 2) void decode_kernel(DecodeParams p) {
   // multi-query geometry; single-query instantiations fold it to constants
   const int nqt = MQ ? p.nqt : 1, qbs = MQ ? p.qbs : 1, nqb = MQ ? p.nqb : 1, gkv = MQ ? p.gkv : G;
   // query blocks per segment, one per wave (1: the waves interleave the units of one block),
@@ -748,7 +748,6 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
     f32x4 dq0 = f32x4{0.f, 0.f, 0.f, 0.f};  // QK accumulator start of every tile
     float qsum = 0.0f;  // asymmetric per-token keys: sum of q over the column's group
     float zt = 0.0f;    // asymmetric per-channel keys: sum of q * zero over the key group
-    float ztc = 0.0f;   // zt in the hi column of each head, 0 in the lo column
     float f8k = 1.0f, f8v = 1.0f;  // FP8: the key and value scales of kv head h
     if constexpr (BF) {
 #pragma unroll
@@ -793,23 +792,21 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
     }
 
     float m_run = -FLT_MAX, l_run = 0.0f;
-    f32x4 acc[NP][8];
+    // PV accumulator: 16 rows.  With one P operand the rows are (hi/lo part, value group,
+    // query head); with two (NP == 2: 16 (value group, head) rows) the hi and lo operands are
+    // two products into the same rows, so the parts are summed by the matrix cores.
+    constexpr bool PARTS_IN_ROWS = NP == 1;
+    f32x4 acc[8];
 #pragma unroll
-    for (int pp = 0; pp < NP; pp++)
-#pragma unroll
-      for (int j = 0; j < 8; j++) acc[pp][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 8; j++) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     // symmetric subnormal value codes: -off times the sum of each row's products, one product
     // per unit against a constant operand, the same for every channel
-    f32x4 zo[NP];
-#pragma unroll
-    for (int pp = 0; pp < NP; pp++) zo[pp] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 zo = f32x4{0.f, 0.f, 0.f, 0.f};
     f16x8 voffop;
 #pragma unroll
     for (int i = 0; i < 8; i++)
       voffop[i] = static_cast<_Float16>(-voff * ((i & 2) ? VT : 1.0f) * 0x1p-24f);
-    float zacc[NP];
-#pragma unroll
-    for (int pp = 0; pp < NP; pp++) zacc[pp] = 0.0f;
+    float zacc = 0.0f;  // asymmetric values: sum of w z of the lane's row
 
     // ---- online softmax over the 8 raw scores of a pair; returns the weights in s2 ----
     // m_run is in log2 units; weights are exp2(score * sm_log2 - m_run).  The running max starts
@@ -839,8 +836,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
         const float mn = fmaxf(m_run, hm);
         const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
         l_run *= alpha;
-#pragma unroll
-        for (int pp = 0; pp < NP; pp++) zacc[pp] *= alpha;
+        zacc *= alpha;
         float al[G];
 #pragma unroll
         for (int q = 0; q < G; q++)
@@ -851,11 +847,8 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
           if constexpr (G <= 4) a = al[r % G];
           else a = (g & 1) ? al[4 + r] : al[r];
 #pragma unroll
-          for (int pp = 0; pp < NP; pp++)
-#pragma unroll
-            for (int j = 0; j < 8; j++) acc[pp][j][r] *= a;
-#pragma unroll
-          for (int pp = 0; pp < NP; pp++) zo[pp][r] *= a;
+          for (int j = 0; j < 8; j++) acc[j][r] *= a;
+          zo[r] *= a;
         }
         m_run = mn;
       }
@@ -887,15 +880,28 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
     // ---------------------------- compressed units ----------------------------
     if (x < xq_end) {
       // the query of the folding lane's channels, in MFMA element order, as f32 (per segment)
-      float qfold[(G + 3) / 4][8];
+      // the query of the folding lane's 8 channels (natural order, as their scales arrive),
+      // prescaled and as f16 pairs, once per segment: exact for every element within 2^31 of the
+      // row's maximum (a bf16 significand fits an f16 one)
+      f16x2 qn[(G + 3) / 4][4];
       if constexpr (KPC) {
 #pragma unroll
         for (int r0 = 0; r0 < G; r0 += 4) {
           const int hw = min(r0 + (lane >> 4), G - 1);
-          const u16x8 q8 = gather_kchan<KB>(qsw + hw * D + 32 * (fold_blk / 4), fold_blk % 4);
+          const uint16_t* qrow = qsw + hw * D + fold_c0;
+          u16x8 q8;
+          if constexpr (KB == 2) {  // channels c0 .. c0 + 3 and c0 + 8 .. c0 + 11
+            const u16x4 a = *reinterpret_cast<const u16x4*>(qrow);
+            const u16x4 b4 = *reinterpret_cast<const u16x4*>(qrow + 8);
+            q8 = __builtin_shufflevector(a, b4, 0, 1, 2, 3, 4, 5, 6, 7);
+          } else {
+            q8 = *reinterpret_cast<const u16x8*>(qrow);
+          }
           const float fsc = exp2i(-qe[qi * 8 + hw]);  // the folded head's prescale
 #pragma unroll
-          for (int i = 0; i < 8; i++) qfold[r0 / 4][i] = bf16_to_f32(q8[i]) * fsc;
+          for (int w = 0; w < 4; w++)
+            qn[r0 / 4][w] = f16x2{static_cast<_Float16>(bf16_to_f32(q8[2 * w]) * fsc),
+                                  static_cast<_Float16>(bf16_to_f32(q8[2 * w + 1]) * fsc)};
         }
       }
 
@@ -914,38 +920,42 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
       // asymmetric keys, the zero-point term sum_i q_i z_i in the hi column)
       auto kpc_fold = [&](uint4 fs, uint4 fz) {
         // metadata words hold the lane's 8 channels in natural order; element i of the MFMA
-        // block is natural index nat(i)
+        // block is natural index (0,4,1,5,2,6,3,7)[i] (2- and 4-bit) or (0,2,1,3,4,6,5,7)[i]
         uint32_t sw[4] = {fs.x, fs.y, fs.z, fs.w};
         const uint32_t zwd[4] = {fz.x, fz.y, fz.z, fz.w};
         if constexpr (KB != 8) {
 #pragma unroll
           for (int w = 0; w < 4; w++) sw[w] = h2_bits(as_h2(sw[w]) * ia2[w]);
         }
-        auto nat = [](int i) { return (KB == 8) ? ((i & 4) | ((i & 1) << 1) | ((i >> 1) & 1)) : ((i >> 1) | ((i & 1) << 2)); };
 #pragma unroll
         for (int r0 = 0; r0 < G; r0 += 4) {
           const int hw = r0 + (lane >> 4);
           float zp = 0.0f;
           if (hw < G) {
-            float pv[8], sv[8];
+            // q s as f16 hi + lo on packed f16 math: hi = q s rounded, lo = q s - hi by one
+            // fused op, exact (q s has at most 8 + 11 significant bits; q < 1, s <= 65504)
+            f16x8 hn, ln;
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
-              const int k = nat(i);
-              sv[i] = (k & 1) ? f16_hi(sw[k / 2]) : f16_lo(sw[k / 2]);
-              pv[i] = fmaf(qfold[r0 / 4][i], sv[i], 0.0f);  // exact: 8-bit x 11-bit significands
-              if constexpr (KASYM) zp += qfold[r0 / 4][i] * ((k & 1) ? f16_hi(zwd[k / 2]) : f16_lo(zwd[k / 2]));
+            for (int w = 0; w < 4; w++) {
+              const f16x2 sc = as_h2(sw[w]);
+              const f16x2 h2 = qn[r0 / 4][w] * sc;
+              const f16x2 l2 = __builtin_elementwise_fma(qn[r0 / 4][w], sc, -h2);
+              hn[2 * w] = h2[0];
+              hn[2 * w + 1] = h2[1];
+              ln[2 * w] = l2[0];
+              ln[2 * w + 1] = l2[1];
+              if constexpr (KASYM) zp = __builtin_amdgcn_fdot2(qn[r0 / 4][w], as_h2(zwd[w]), zp, false);
             }
-            uint32_t hw4[4], lw4[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-              const f16x2 hi2 = pkrtz(pv[2 * i], pv[2 * i + 1]);
-              hw4[i] = h2_bits(hi2);
-              // q s - hi, exact, in one fused op on the f16 operands
-              lw4[i] = h2_bits(pkrtz(fmaf(qfold[r0 / 4][2 * i], sv[2 * i], -static_cast<float>(hi2[0])),
-                                     fmaf(qfold[r0 / 4][2 * i + 1], sv[2 * i + 1], -static_cast<float>(hi2[1]))));
+            f16x8 he, le;
+            if constexpr (KB == 8) {
+              he = __builtin_shufflevector(hn, hn, 0, 2, 1, 3, 4, 6, 5, 7);
+              le = __builtin_shufflevector(ln, ln, 0, 2, 1, 3, 4, 6, 5, 7);
+            } else {
+              he = __builtin_shufflevector(hn, hn, 0, 4, 1, 5, 2, 6, 3, 7);
+              le = __builtin_shufflevector(ln, ln, 0, 4, 1, 5, 2, 6, 3, 7);
             }
-            *reinterpret_cast<uint4*>(kf + hw * D + 8 * fold_blk) = uint4{hw4[0], hw4[1], hw4[2], hw4[3]};
-            *reinterpret_cast<uint4*>(kf + (8 + hw) * D + 8 * fold_blk) = uint4{lw4[0], lw4[1], lw4[2], lw4[3]};
+            *reinterpret_cast<f16x8*>(kf + hw * D + 8 * fold_blk) = he;
+            *reinterpret_cast<f16x8*>(kf + (8 + hw) * D + 8 * fold_blk) = le;
           }
           if constexpr (KASYM) {
             zp += row_ror<8>(zp);
@@ -962,7 +972,8 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
         if constexpr (KASYM) zt = ztw[wave * 8 + hh];
         wave_lds_sync();
         // subnormal key codes alpha u 2^-24: symmetric codes start at minus the offset,
-        // -off alpha 2^-24 against the same operand; asymmetric ones need no start
+        // -off alpha 2^-24 against the same operand; asymmetric ones start at the zero-point
+        // term sum_i q_i z_i, in the same 2^-24 units, in the hi column of each head
         dq0 = f32x4{0.f, 0.f, 0.f, 0.f};
         if constexpr (!KASYM) {
 #pragma unroll
@@ -974,7 +985,10 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
             dq0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(bias, qb[j], dq0, 0, 0, 0);
           }
         }
-        if constexpr (KASYM) ztc = (cg == 0) ? zt : 0.0f;
+        if constexpr (KASYM) {
+          const float z0 = (cg == 0) ? zt * 0x1p-24f : 0.0f;
+          dq0 = f32x4{z0, z0, z0, z0};
+        }
       };
 
       for (; x < xq_end; x += xstep) {
@@ -994,7 +1008,6 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
         // masked below, so the MFMAs run unconditionally.
         if constexpr (KPC) kpc_fold(d.fs, d.fz);
         f32x4 dq[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-        float ztc_a = ztc;  // tile A's zero-point term (tile B may fold its own group)
         if constexpr (KPC) {
           if (kgroup == 16 && nvB > 0) {
             // tile B opens its own key group: finish tile A with the current fold first
@@ -1003,7 +1016,6 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
             for (int j = 0; j < 4; j++)
               dq[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop_sub<KB>(d.kw[0], j, ur), qb[j], dq[0], 0, 0, 0);
             const size_t mi = trow ? static_cast<size_t>(max(pB, 0)) * D + fold_c0 : kpc_meta(2 * x + 1);
-            ztc_a = ztc;
             const uint4 fs2 = load_meta8(c.ks, mi);
             uint4 fz2 = uint4{0, 0, 0, 0};
             if constexpr (KASYM) fz2 = load_meta8(c.kz, mi);
@@ -1053,9 +1065,9 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
           } else if constexpr (F8) {
 #pragma unroll
             for (int r = 0; r < 4; r++) s2[4 * t + r] = dq[t][r] * f8k;
-          } else if constexpr (KPC) {  // hi + lo columns are summed below; zt once, in the hi one
+          } else if constexpr (KPC) {  // hi + lo columns are summed below, in 2^-24 units
 #pragma unroll
-            for (int r = 0; r < 4; r++) s2[4 * t + r] = fmaf(dq[t][r], 0x1p24f, t ? ztc : ztc_a);
+            for (int r = 0; r < 4; r++) s2[4 * t + r] = dq[t][r];
           } else {
             const uint2 k2 = d.ks[t];
             s2[4 * t + 0] = fmaf(dq[t][0], f16_lo(k2.x), 0.0f);
@@ -1074,7 +1086,8 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
         fold_cols8(s2);
         load_k(more ? xn : x, nA, nB);  // key registers are free again
 
-        softmax(s2, nvA, nvB, std::integral_constant<bool, VBF>{}, 32 * x, sl2);  // s2: weights / alpha
+        softmax(s2, nvA, nvB, std::integral_constant<bool, VBF>{}, 32 * x,
+                KPC ? sl2 * 0x1p24f : sl2);  // s2: weights / alpha
 
         // ---- P rows (hi / lo f16 parts of w * s_v) and PV ----
         // Rows 16 pp + n with part >= 2 are never read back, so they are left as computed.
@@ -1115,7 +1128,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
 #pragma unroll
           for (int j = 0; j < 8; j++) {
             const bf16x8 vb = __builtin_bit_cast(bf16x8, uint4{d.vw[0][2 * j], d.vw[0][2 * j + 1], d.vw[1][2 * j], d.vw[1][2 * j + 1]});
-            acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb, vb, acc[0][j], 0, 0, 0);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb, vb, acc[j], 0, 0, 0);
           }
           load_v(nA, nB);  // value registers are free again
           pA = nA;
@@ -1156,7 +1169,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
                 const float wa = VBF ? s2[4 * t + r] * static_cast<float>(velem_alpha<VB>(0, r)) : s2[4 * t + r];
                 zp = fmaf(wa, zv[r], zp);
               }
-              zacc[pp] += zp;
+              zacc += zp;
             }
           }
           if (!full) {
@@ -1190,12 +1203,12 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
             const f16x8 vb = vop_sub<VB>(d.vw[0], d.vw[1], j, urv);
 #pragma unroll
             for (int pp = 0; pp < NP; pp++)
-              acc[pp][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[pp], vb, acc[pp][j], 0, 0, 0);
+              acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[pp], vb, acc[j], 0, 0, 0);
             if constexpr (!VASYM) {
               if (j == 0) {
 #pragma unroll
                 for (int pp = 0; pp < NP; pp++)
-                  zo[pp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[pp], voffop, zo[pp], 0, 0, 0);
+                  zo = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[pp], voffop, zo, 0, 0, 0);
               }
             }
           } else if constexpr (F8) {
@@ -1203,7 +1216,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
             const f16x8 vb = f8_to_f16x8(d.vw[0][j], d.vw[1][j]);
 #pragma unroll
             for (int pp = 0; pp < NP; pp++)
-              acc[pp][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[pp], vb, acc[pp][j], 0, 0, 0);
+              acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[pp], vb, acc[j], 0, 0, 0);
           }
         }
         load_v(nA, nB);  // value registers are free again
@@ -1216,13 +1229,11 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
     // window rows below add true values
     if constexpr (VBF) {
 #pragma unroll
-      for (int pp = 0; pp < NP; pp++)
+      for (int j = 0; j < 8; j++)
 #pragma unroll
-        for (int j = 0; j < 8; j++)
-#pragma unroll
-          for (int r = 0; r < 4; r++)
-            acc[pp][j][r] = fmaf(acc[pp][j][r], 16777216.0f / static_cast<float>(vchan_alpha<VB>(j)),
-                                 VASYM ? 0.0f : zo[pp][r] * 16777216.0f);
+        for (int r = 0; r < 4; r++)
+          acc[j][r] = fmaf(acc[j][r], 16777216.0f / static_cast<float>(vchan_alpha<VB>(j)),
+                           VASYM ? 0.0f : zo[r] * 16777216.0f);
     }
 
     // ---------------------------- BF16 window units ----------------------------
@@ -1299,8 +1310,8 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
             const int j = 4 * hf + jj;
 #pragma unroll
             for (int pp = 0; pp < NP; pp++)
-              acc[pp][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb[pp], __builtin_bit_cast(bf16x8, col),
-                                                                   acc[pp][j], 0, 0, 0);
+              acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb[pp], __builtin_bit_cast(bf16x8, col),
+                                                               acc[j], 0, 0, 0);
           }
         }
       }
@@ -1309,12 +1320,8 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
     // ---------------------------- merge the four waves ----------------------------
     float lsum = l_run + __shfl_xor(l_run, 16);
     lsum += __shfl_xor(lsum, 32);
-    float zs[NP];
-#pragma unroll
-    for (int pp = 0; pp < NP; pp++) {
-      zs[pp] = zacc[pp] + __shfl_xor(zacc[pp], 16);
-      zs[pp] += __shfl_xor(zs[pp], 32);
-    }
+    float zs = zacc + __shfl_xor(zacc, 16);
+    zs += __shfl_xor(zs, 32);
     __syncthreads();  // every wave is done with kf (overlays red)
     if (lane < G) {
       mw[wave * 8 + lane] = m_run;
@@ -1322,31 +1329,30 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
     }
     if (lane < 16) {
 #pragma unroll
-      for (int pp = 0; pp < NP; pp++) zw[wave * 32 + 16 * pp + lane] = zs[pp];
+      for (int pp = 0; pp < 2; pp++) zw[wave * 32 + 16 * pp + lane] = pp ? 0.0f : zs;
     }
     if constexpr (MQ == 2) {
       // one query block per wave: each wave normalises (or writes the partial of) its own
       // block from its own rows of the merge buffer, no merge across waves
       constexpr int NOW = (G * D) / 64;  // outputs per lane
       float Ow[NOW];
-#pragma unroll
-      for (int pp = 0; pp < NP; pp++) {
-        wave_lds_sync();  // the previous pass's reads (or the m / l / z stores) are done
+      {
+        wave_lds_sync();  // the m / l / z stores are done
 #pragma unroll
         for (int j = 0; j < 8; j++)
 #pragma unroll
-          for (int r = 0; r < 4; r++) red[(wave * 16 + 4 * g + r) * RED_STRIDE + 8 * n + j] = acc[pp][j][r];
+          for (int r = 0; r < 4; r++) red[(wave * 16 + 4 * g + r) * RED_STRIDE + 8 * n + j] = acc[j][r];
         wave_lds_sync();
 #pragma unroll
         for (int oi = 0; oi < NOW; oi++) {
           const int o = lane + 64 * oi;
           const int oh = o / D, ch = o % D;
           const int gv = ch / vgroup;
-          if (pp == 0) Ow[oi] = VASYM ? zw[wave * 32 + gv * G + oh] : 0.0f;
+          Ow[oi] = VASYM ? zw[wave * 32 + gv * G + oh] : 0.0f;
 #pragma unroll
-          for (int part = 0; part < 2; part++) {
+          for (int part = 0; part < (PARTS_IN_ROWS ? 2 : 1); part++) {
             const int row = (part * ngv + gv) * G + oh;
-            if (row / 16 == pp) Ow[oi] += red[(wave * 16 + row % 16) * RED_STRIDE + ch];
+            Ow[oi] += red[(wave * 16 + row) * RED_STRIDE + ch];
           }
         }
       }
@@ -1377,13 +1383,11 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
     // merge the WPQ waves of each of the qpw blocks (one block of all four waves unless mode 3)
     constexpr int NO = (qpw * G * D + 255) / 256;
     float O[NO], Mx[NO], e[NO][WPQ];
-#pragma unroll
-    for (int pp = 0; pp < NP; pp++) {
-      if (pp > 0) __syncthreads();
+    {
 #pragma unroll
       for (int j = 0; j < 8; j++)
 #pragma unroll
-        for (int r = 0; r < 4; r++) red[(wave * 16 + 4 * g + r) * RED_STRIDE + 8 * n + j] = acc[pp][j][r];
+        for (int r = 0; r < 4; r++) red[(wave * 16 + 4 * g + r) * RED_STRIDE + 8 * n + j] = acc[j][r];
       __syncthreads();
 #pragma unroll
       for (int oi = 0; oi < NO; oi++) {
@@ -1392,7 +1396,7 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
         const int qo = o / (G * D), oh = (o % (G * D)) / D, ch = o % D;  // block, row, channel
         const int w0 = qo * WPQ;                                           // its first wave
         const int gv = ch / vgroup;
-        if (pp == 0) {
+        {
           float M = -FLT_MAX;
 #pragma unroll
           for (int k = 0; k < WPQ; k++) M = fmaxf(M, mw[(w0 + k) * 8 + oh]);
@@ -1410,12 +1414,11 @@ __global__ __launch_bounds__(256, (NP == 1 && KB != 16 && MQ != 2 && MQ != 3) ? 
           }
         }
 #pragma unroll
-        for (int part = 0; part < 2; part++) {
+        for (int part = 0; part < (PARTS_IN_ROWS ? 2 : 1); part++) {
           const int row = (part * ngv + gv) * G + oh;
-          if (row / 16 != pp) continue;
 #pragma unroll
           for (int k = 0; k < WPQ; k++)
-            O[oi] += e[oi][k] * red[((w0 + k) * 16 + row % 16) * RED_STRIDE + ch];
+            O[oi] += e[oi][k] * red[((w0 + k) * 16 + row) * RED_STRIDE + ch];
         }
       }
     }
