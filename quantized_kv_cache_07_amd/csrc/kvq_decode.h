@@ -527,6 +527,15 @@ __global__ __launch_bounds__(256, (KB != 16 && MQ != 2 && MQ != 3 && (NP == 1 ||
     if (tid == 0) p.ws_pre[B + 1] = nbe;
   }
   if (static_cast<int>(blockIdx.x) >= nbe) return;
+  if (gridDim.x == 1) {
+    // a single workgroup: no combine runs after this launch, so empty sequences get their
+    // zeros here
+    for (int bb = 0; bb < B; bb++) {
+      if (pre[bb + 1] != pre[bb]) continue;
+      float* o = p.out + static_cast<size_t>(bb) * nqt * p.Hq * D;
+      for (int i = tid; i < nqt * p.Hq * D; i += 256) o[i] = 0.0f;
+    }
+  }
   const long long NBl = nbe;
   const int u0 = static_cast<int>((static_cast<long long>(blockIdx.x) * U) / NBl);
   const int u1 = static_cast<int>((static_cast<long long>(blockIdx.x + 1) * U) / NBl);
@@ -867,11 +876,11 @@ __global__ __launch_bounds__(256, (KB != 16 && MQ != 2 && MQ != 3 && (NP == 1 ||
     auto fold_cols8 = [&](float (&v)[8]) {
       if (ngk >= 2) {
 #pragma unroll
-        for (int i = 0; i < 8; i++) v[i] += row_ror<G>(v[i]);
+        for (int i = 0; i < 8; i++) v[i] = row_ror<G>(v[i]) + v[i];
         if constexpr (2 * G < 16) {
           if (ngk >= 4) {
 #pragma unroll
-            for (int i = 0; i < 8; i++) v[i] += row_ror<2 * G>(v[i]);
+            for (int i = 0; i < 8; i++) v[i] = row_ror<2 * G>(v[i]) + v[i];
           }
         }
       }
@@ -1083,8 +1092,8 @@ __global__ __launch_bounds__(256, (KB != 16 && MQ != 2 && MQ != 3 && (NP == 1 ||
             }
           }
         }
-        fold_cols8(s2);
         load_k(more ? xn : x, nA, nB);  // key registers are free again
+        fold_cols8(s2);
 
         softmax(s2, nvA, nvB, std::integral_constant<bool, VBF>{}, 32 * x,
                 KPC ? sl2 * 0x1p24f : sl2);  // s2: weights / alpha
@@ -1135,9 +1144,11 @@ __global__ __launch_bounds__(256, (KB != 16 && MQ != 2 && MQ != 3 && (NP == 1 ||
           pB = nB;
           continue;
         }
-        // With two row blocks, block 0 takes the hi parts and block 1 the lo parts of the same
-        // products w * s_v, formed once; with one block each lane's row picks its own part.
+        // With two P operands, operand 0 takes the hi parts and operand 1 the lo parts of the
+        // same products w * s_v, formed once; with one, each lane's row picks its own part.
         f16x8 pa[NP];
+        float neg1 = -1.0f;
+        asm volatile("" : "+s"(neg1));
 #pragma unroll
         for (int pp = 0; pp < scale_rows<NP>(); pp++) {
           const float sel = (rpart[pp] == 1) ? 1.0f : 0.0f;
@@ -1157,17 +1168,18 @@ __global__ __launch_bounds__(256, (KB != 16 && MQ != 2 && MQ != 3 && (NP == 1 ||
             ws[4 * t + 2] = fmaf(s2[4 * t + 2], f16_lo(s2v.y), 0.0f);
             ws[4 * t + 3] = fmaf(s2[4 * t + 3], f16_hi(s2v.y), 0.0f);
             if constexpr (VASYM) {
-              const uint2 z2v = d.vz[pp][t];
-              float zv[4] = {f16_lo(z2v.x), f16_hi(z2v.x), f16_lo(z2v.y), f16_hi(z2v.y)};
-              if (!full) {  // a token past the end may sit on a stand-in tile with any zero-point
-#pragma unroll
-                for (int r = 0; r < 4; r++) zv[r] = (s2[4 * t + r] != 0.0f) ? zv[r] : 0.0f;
+              uint2 z2v = d.vz[pp][t];
+              if (!full) {  // a token past the end may sit on a stand-in tile with any zero-point:
+                            // clear the fp16 bits of tokens with no weight
+                z2v.x &= (s2[4 * t] != 0.0f ? 0x0000FFFFu : 0u) | (s2[4 * t + 1] != 0.0f ? 0xFFFF0000u : 0u);
+                z2v.y &= (s2[4 * t + 2] != 0.0f ? 0x0000FFFFu : 0u) | (s2[4 * t + 3] != 0.0f ? 0xFFFF0000u : 0u);
               }
+              const float zv[4] = {f16_lo(z2v.x), f16_hi(z2v.x), f16_lo(z2v.y), f16_hi(z2v.y)};
               float zp = 0.0f;
 #pragma unroll
               for (int r = 0; r < 4; r++) {
                 const float wa = VBF ? s2[4 * t + r] * static_cast<float>(velem_alpha<VB>(0, r)) : s2[4 * t + r];
-                zp = fmaf(wa, zv[r], zp);
+                zp = fmaf(zv[r], wa, zp);  // one mixed-precision fma on the fp16 zero-point
               }
               zacc += zp;
             }
@@ -1185,8 +1197,10 @@ __global__ __launch_bounds__(256, (KB != 16 && MQ != 2 && MQ != 3 && (NP == 1 ||
             const f16x2 hi2 = pkrtz(ws[2 * i], ws[2 * i + 1]);
             if constexpr (NP == 2) {
               pk[i] = h2_bits(hi2);
-              pl[i] = h2_bits(pkrtz(ws[2 * i] - static_cast<float>(hi2[0]),
-                                    ws[2 * i + 1] - static_cast<float>(hi2[1])));
+              // ws - hi, exact, as one mixed-precision fma on the fp16 hi part (the -1 is kept in
+              // a register: as a literal the fma folds to a subtraction of a converted hi)
+              pl[i] = h2_bits(pkrtz(fmaf(static_cast<float>(hi2[0]), neg1, ws[2 * i]),
+                                    fmaf(static_cast<float>(hi2[1]), neg1, ws[2 * i + 1])));
             } else {
               const float r0 = fmaf(-sel, static_cast<float>(hi2[0]), ws[2 * i]);
               const float r1 = fmaf(-sel, static_cast<float>(hi2[1]), ws[2 * i + 1]);
@@ -1573,6 +1587,9 @@ hipError_t launch_decode_t(const DecodeParams& p0, hipStream_t s) {
   decode_kernel<KB, G, KPC, NP, SCH, MQ, VB, VSCH><<<p.nblocks, 256, lds, s>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // one workgroup saw every segment whole and wrote every output (empty sequences included):
+  // nothing to combine
+  if (p.nblocks == 1) return hipSuccess;
   // slices: about one per 4 partials a segment has on average, 32 outputs per slice at most
   const int avg = p.nblocks / (p.c.B * p.c.H * p.nqs);
   int slices = 1;

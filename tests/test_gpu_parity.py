@@ -142,6 +142,9 @@ ALIGN_CASES = [
     ("prime-segment-count-falls-back", SYM4, SYM4, 7, 2, 1, 0, [300] * 7, 5),
     ("uniform-with-empty-sequence", SYM4, SYM4, 3, 8, 2, 0, [0, 500, 500], 5),
     ("ragged-keeps-plain-ranges", SYM4, SYM4, 3, 8, 2, 0, [100, 500, 500], 5),
+    # one workgroup: no combine launch; it writes the empty sequence's zeros itself
+    ("single-workgroup-with-empty-sequence", SYM4, SYM4, 3, 8, 2, 32, [300, 0, 77], 1),
+    ("single-workgroup-kivi", KPC2, ASYM2_32, 2, 8, 2, 64, [200, 90], 1),
 ]
 
 
@@ -212,6 +215,10 @@ def test_empty_sequence_gives_zeros():
     pr = kc.build_pair(SYM8, SYM8, 3, 2, 2, 0, [0, 40, 0])
     err, got = kc.compare_attention(pr, max_tokens=64)
     assert np.all(got[0] == 0) and np.all(got[2] == 0)
+    # small enough for one workgroup (two units per wave at most): the decode launch alone
+    pr = kc.build_pair(SYM8, SYM8, 2, 1, 1, 0, [0, 40])
+    err, got = kc.compare_attention(pr, max_tokens=40)
+    assert np.all(got[0] == 0)
 
 
 def test_deterministic_and_paged_equals_contiguous():
