@@ -378,6 +378,20 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str, command: s
     return out
 
 
+def summarize_pmc(dirs, kernel_substr: str = "decode_kernel") -> str:
+    """Mean per dispatch of every counter in rocprofv3 --pmc output directories (one line per
+    directory, one pass each), over the dispatches of kernels whose name holds kernel_substr."""
+    out = []
+    for d in dirs:
+        rows = _counter_rows(d)
+        names = sorted({r["Counter_Name"] for r in rows})
+        n = len({r.get("Dispatch_Id") or r.get("Correlation_Id") for r in rows
+                 if kernel_substr in r["Kernel_Name"]})
+        vals = " ".join(f"{c}={_per_dispatch(rows, c, kernel_substr):.4g}" for c in names)
+        out.append(f"{os.path.basename(os.path.normpath(d))}: {vals} (dispatches {n})")
+    return "\n".join(out) + "\n"
+
+
 def summarize_stats(stats_csv: str, command: str, title: str) -> str:
     import csv
     rows = list(csv.DictReader(open(stats_csv)))
@@ -671,6 +685,9 @@ def main() -> int:
     ap.add_argument("--summarize-trace", nargs=2, metavar=("KERNEL_TRACE_CSV", "BENCH_JSON"),
                     help="print per-phase kernel durations of one bench run from its rocprofv3 "
                          "--kernel-trace CSV and its JSON line")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="PMC_DIR",
+                    help="print per-dispatch means of the counters of decode_kernel in rocprofv3 "
+                         "--pmc output directories")
     ap.add_argument("--command", default="", help="the profiling command, recorded in summaries")
     ap.add_argument("--sweep", choices=["crossover", "multiquery"],
                     help="instead of the step benchmark: BF16 vs quantized decode-attention sweep")
@@ -683,6 +700,9 @@ def main() -> int:
         out = os.path.join(ROOT, "profiles", f"decode_{a.workload}_traffic.json")
         json.dump(d, open(out, "w"), indent=1)
         print(json.dumps(d, indent=1))
+        return 0
+    if a.summarize_pmc:
+        print(summarize_pmc(a.summarize_pmc), end="")
         return 0
     if a.summarize_stats:
         print(summarize_stats(a.summarize_stats, a.command, f"kvq kernels, workload {a.workload}"), end="")

@@ -4,6 +4,10 @@ Flags: -O3, no fast-math (HIP's default correctly rounded fp32 division is kept)
 fp32 arithmetic disabled (-Xclang -target-feature -Xclang -packed-fp32-ops).  f16 denormals must
 stay enabled (the default): the decode kernels feed code fields to the matrix cores as exact f16
 subnormals, so no denormal-flushing option may be added here.
+
+`--qk-valu` builds the same sources with -DKVQ_QK_VALU=1 into libkvq_qkvalu.so: single-query MHA
+8-bit symmetric caches then take QK on the vector ALU (v_dot2_f32_f16) instead of the matrix
+cores.  That library exists to compare the two; the binding loads it when KVQ_LIBRARY names it.
 """
 from __future__ import annotations
 
@@ -17,6 +21,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvq.so")
+LIB_QK_VALU = os.path.join(HERE, "libkvq_qkvalu.so")
 SOURCES = ["kvq_host.hip", "kvq_append.hip"] + [
     f"kvq_decode_b{bits}{scheme}.hip" for bits in (2, 4, 8) for scheme in "sa"] + [
     "kvq_decode_b16.hip", "kvq_decode_b8f.hip"] + [
@@ -28,9 +33,9 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, build_dir: str = BUILD, defines: tuple = ()) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *(f"-D{d}" for d in defines), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                     if "packed-fp32-ops" not in l)
@@ -41,20 +46,22 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = True, qk_valu: bool = False) -> str:
+    build_dir, lib = (BUILD + "_qkvalu", LIB_QK_VALU) if qk_valu else (BUILD, LIB)
+    defines = ("KVQ_QK_VALU=1",) if qk_valu else ()
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, build_dir, defines), SOURCES))
+    tmp = lib + ".tmp"
     r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":
-    build()
+    build(qk_valu="--qk-valu" in sys.argv[1:])

@@ -42,6 +42,14 @@
 
 #include "kvq_dev.h"
 
+// QK of single-query MHA (G = 1) 8-bit symmetric per-token caches on the vector ALU instead of
+// the matrix cores: v_dot2_f32_f16 over the raw code pairs, then DPP row sums.  Off by default
+// (the two run at the same HBM-bound speed); a build with -DKVQ_QK_VALU=1 selects it, for the
+// comparison of the two.
+#ifndef KVQ_QK_VALU
+#define KVQ_QK_VALU 0
+#endif
+
 namespace kvq {
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -559,6 +567,11 @@ __global__ __launch_bounds__(256, (KB != 16 && MQ != 2 && MQ != 3 && (NP == 1 ||
   constexpr float VLG = VB == 4 ? 4.0f : VB == 2 ? 2.0f : 0.0f;  // log2 VT
   constexpr float VT = VB == 4 ? 16.0f : VB == 2 ? 4.0f : 1.0f;
   constexpr bool BF = KB == 16;  // unquantized BF16 storage: bf16 matrix products, no scales
+  // QK on the vector ALU (KVQ_QK_VALU builds): lane (g, n) dots token 4 g + n % 4 with the
+  // query over channel block n / 4, scales by its (token, key group) scale and sums the four
+  // blocks along its row; every column of the row then holds the token's whole score
+  constexpr bool VQK = KVQ_QK_VALU && G == 1 && KB == 8 && VB == 8 && SCH == KVQ_SYM &&
+                       VSCH == KVQ_SYM && !KPC && MQ == 0;
   const int hh = n % G;          // query head of QK column n and of PV row 16 pp + n
   const int cg = (n / G) % ngk;  // key group (or hi/lo part) of QK column n
   constexpr long K_TILE_BYTES = static_cast<long>(TILE) * D * KB / 8;
@@ -666,9 +679,11 @@ __global__ __launch_bounds__(256, (KB != 16 && MQ != 2 && MQ != 3 && (NP == 1 ||
     // that is fixed for the segment, so no per-lane 64-bit address arithmetic is needed.
     constexpr unsigned SPK = (4 * KB < 16) ? 4 * KB : 16;  // bytes of a key slice piece
     constexpr unsigned SPV = (4 * VB < 16) ? 4 * VB : 16;  // bytes of a value slice piece
-    const unsigned k_lane = SPK * (4 * n + g);               // slice 4 n + g (token n)
+    const unsigned k_lane = VQK ? SPK * (4 * (4 * g + (n & 3)) + (n >> 2))  // token 4 g + n % 4
+                                : SPK * (4 * n + g);                    // slice 4 n + g (token n)
     const unsigned v_lane = SPV * (16 * g + n);              // chunk 16 g + n
-    const unsigned ks_lane = cg * TILE + 4 * g;
+    // scales of tokens 4 g .. 4 g + 3 in the lane's key group (VQK: the group of block n / 4)
+    const unsigned ks_lane = (VQK ? (32 * (n >> 2)) / kgroup : cg) * TILE + 4 * g;
     auto load_k = [&](int xx, int pA, int pB) {
       pA = max(pA, 0);
       pB = max(pB, 0);
@@ -753,6 +768,8 @@ __global__ __launch_bounds__(256, (KB != 16 && MQ != 2 && MQ != 3 && (NP == 1 ||
 
     // ---- QK operand: f16 query, masked to the column's key group ----
     f16x8 qb[4];
+    f16x2 qv[16];       // VQK: query pairs of the lane's channel block, in code-pair order
+    float qbias = 0.0f;  // VQK: -(1024 + off) times the sum of those query values
     bf16x8 qbf[4];                            // BF16 storage: the bf16 query as it is
     f32x4 dq0 = f32x4{0.f, 0.f, 0.f, 0.f};  // QK accumulator start of every tile
     float qsum = 0.0f;  // asymmetric per-token keys: sum of q over the column's group
@@ -773,6 +790,18 @@ __global__ __launch_bounds__(256, (KB != 16 && MQ != 2 && MQ != 3 && (NP == 1 ||
       const int32_t* fvs = reinterpret_cast<const int32_t*>(c.vs);
       f8k = __int_as_float(ld_uniform(fks + (c.k.axis == KVQ_PER_HEAD ? h : 0)));
       f8v = __int_as_float(ld_uniform(fvs + (c.v.axis == KVQ_PER_HEAD ? h : 0)));
+    } else if constexpr (VQK) {
+      // pair r of a code word holds channels 4 (r / 2) + r % 2 and that + 2 (bytes 0, 2 or 1, 3)
+      const uint16_t* qrow = qsw + 32 * (n >> 2);
+      float qs_ = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int c0 = 4 * (r / 2) + r % 2;
+        qv[r] = f16x2{static_cast<_Float16>(bf16_to_f32(qrow[c0]) * qsc),
+                      static_cast<_Float16>(bf16_to_f32(qrow[c0 + 2]) * qsc)};
+        qs_ += static_cast<float>(qv[r][0]) + static_cast<float>(qv[r][1]);
+      }
+      qbias = -(1024.0f + koff) * qs_;
     } else if constexpr (!KPC) {
       const bool in_grp = ((32 * g) / kgroup) == cg;
 #pragma unroll
@@ -1056,6 +1085,25 @@ __global__ __launch_bounds__(256, (KB != 16 && MQ != 2 && MQ != 3 && (NP == 1 ||
             dq[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qbf[j], dq[0], 0, 0, 0);
             dq[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qbf[j], dq[1], 0, 0, 0);
           }
+        } else if constexpr (VQK) {
+#pragma unroll
+          for (int t = 0; t < 2; t++) {
+            float part = qbias;  // this lane's block: sum of (1024 + u) q, less (1024 + off) sum q
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+              part = __builtin_amdgcn_fdot2(as_h2(rawpair<KB>(d.kw[t], r, ur)), qv[r], part, false);
+            const uint2 k2 = d.ks[t];
+            const uint32_t kw2 = (n & 2) ? k2.y : k2.x;
+            part *= (n & 1) ? f16_hi(kw2) : f16_lo(kw2);
+            part = row_ror<4>(part) + part;
+            part = row_ror<8>(part) + part;
+            // token 4 g + r's score is in lanes 4 i + r of the row: broadcast it (quad_perm r)
+            const int pi = __float_as_int(part);
+            dq[t][0] = __int_as_float(__builtin_amdgcn_mov_dpp(pi, 0x00, 0xF, 0xF, true));
+            dq[t][1] = __int_as_float(__builtin_amdgcn_mov_dpp(pi, 0x55, 0xF, 0xF, true));
+            dq[t][2] = __int_as_float(__builtin_amdgcn_mov_dpp(pi, 0xAA, 0xF, 0xF, true));
+            dq[t][3] = __int_as_float(__builtin_amdgcn_mov_dpp(pi, 0xFF, 0xF, 0xF, true));
+          }
         } else {
           dq[0] = dq0;
           dq[1] = dq0;
@@ -1074,7 +1122,7 @@ __global__ __launch_bounds__(256, (KB != 16 && MQ != 2 && MQ != 3 && (NP == 1 ||
           } else if constexpr (F8) {
 #pragma unroll
             for (int r = 0; r < 4; r++) s2[4 * t + r] = dq[t][r] * f8k;
-          } else if constexpr (KPC) {  // hi + lo columns are summed below, in 2^-24 units
+          } else if constexpr (KPC || VQK) {  // KPC: hi + lo columns are summed below, in 2^-24 units
 #pragma unroll
             for (int r = 0; r < 4; r++) s2[4 * t + r] = dq[t][r];
           } else {
@@ -1093,7 +1141,7 @@ __global__ __launch_bounds__(256, (KB != 16 && MQ != 2 && MQ != 3 && (NP == 1 ||
           }
         }
         load_k(more ? xn : x, nA, nB);  // key registers are free again
-        fold_cols8(s2);
+        if constexpr (!VQK) fold_cols8(s2);
 
         softmax(s2, nvA, nvB, std::integral_constant<bool, VBF>{}, 32 * x,
                 KPC ? sl2 * 0x1p24f : sl2);  // s2: weights / alpha

@@ -14,7 +14,8 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libkvq.so")
+# KVQ_LIBRARY may name another build of the same sources (build.py --qk-valu)
+LIB_PATH = os.environ.get("KVQ_LIBRARY") or os.path.join(HERE, "libkvq.so")
 
 SYM, ASYM = 0, 1
 PER_TOKEN, PER_CHANNEL = 0, 1

@@ -50,3 +50,14 @@ def test_settle_stops_on_agreeing_windows(monkeypatch):
     monkeypatch.setattr(torch, "cuda", FakeCuda)
     monkeypatch.setattr(bench, "attention_only", lambda st, q: None)
     assert bench.settle(None, None, window=10) == 40
+
+
+def test_summarize_pmc_means_per_dispatch(tmp_path):
+    # two dispatches of decode_kernel (counter summed over its two dimensions), one of another kernel
+    d = tmp_path / "pmc_x"
+    d.mkdir()
+    rows = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value",
+            "1,kvq::decode_kernel<8>,SQ_WAVES,100", "1,kvq::decode_kernel<8>,SQ_WAVES,20",
+            "2,kvq::decode_kernel<8>,SQ_WAVES,60", "3,kvq::combine_kernel,SQ_WAVES,7"]
+    (d / "run_counter_collection.csv").write_text("\n".join(rows) + "\n")
+    assert bench.summarize_pmc([str(d)]) == "pmc_x: SQ_WAVES=90 (dispatches 2)\n"

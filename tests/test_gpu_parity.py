@@ -44,6 +44,9 @@ CASES = [
     # k, v, B, Hq, H, R, lens, paged
     ("int8-mha-tiny", SYM8, SYM8, 1, 1, 1, 0, [256], False),
     ("int8-mha-ragged", SYM8, SYM8, 3, 4, 4, 0, [5, 300, 1031], False),
+    # MHA 8-bit with several key groups per head (the vector-ALU QK build scales per group)
+    ("int8-g32-mha-window-paged", (8, 0, 0, 32), (8, 0, 0, 32), 2, 4, 4, 64, [700, 33], True),
+    ("int8-g64-mha", (8, 0, 0, 64), (8, 0, 0, 64), 2, 2, 2, 0, [1031, 300], False),
     ("int4-gqa4", SYM4, SYM4, 2, 8, 2, 0, [777, 1500], False),
     ("int4-gqa4-window", SYM4, SYM4, 2, 8, 2, 32, [777, 190], False),
     ("int4-paged-window", SYM4, SYM4, 3, 8, 2, 128, [1000, 129, 40], True),
