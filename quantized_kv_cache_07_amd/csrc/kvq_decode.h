@@ -383,6 +383,14 @@ __device__ __forceinline__ int seq_units(const CacheDev& c, int max_tokens, int 
 // workgroup: nb rounded down to a multiple of S (each segment split m ways), or S / k with k | S
 // (k whole segments per range), whichever aligned count is largest, if it keeps at least half of
 // the workgroups.  Otherwise all nb ranges (Stream-K over the unit sequence).
+// floor(a / b) for 0 <= a < 2^53 and b > 0 through one f64 division (a few instructions, where
+// a 64-bit integer division is a long sequence).  The quotient is rounded to nearest; one that
+// falls short of an integer n falls short by at least 1 / b, more than the rounding error
+// q 2^-53 while a < 2^53, so it cannot round up to n.
+__device__ __forceinline__ long long floor_div(long long a, long long b) {
+  return static_cast<long long>(static_cast<double>(a) / static_cast<double>(b));
+}
+
 __device__ __forceinline__ int aligned_ranges(int nb, int S, bool uniform) {
   if (!uniform || S <= 0) return nb;
   if (S <= nb) return (nb / S) * S;
@@ -545,8 +553,28 @@ __global__ __launch_bounds__(256, (KB != 16 && MQ != 2 && MQ != 3 && (NP == 1 ||
     }
   }
   const long long NBl = nbe;
-  const int u0 = static_cast<int>((static_cast<long long>(blockIdx.x) * U) / NBl);
-  const int u1 = static_cast<int>((static_cast<long long>(blockIdx.x + 1) * U) / NBl);
+  const int u0 = static_cast<int>(floor_div(static_cast<long long>(blockIdx.x) * U, NBl));
+  const int u1 = static_cast<int>(floor_div(static_cast<long long>(blockIdx.x + 1) * U, NBl));
+  // Even progress of the workgroups that share a compute unit.  The issue arbiter favours the
+  // oldest waves, so the first workgroup dispatched to a CU would finish its range well before
+  // the last one, which then runs alone at a fraction of the CU's throughput (on the KIVI layer
+  // the three workgroups of a CU ended at 68, 82 and 96 us on average).  Each wave starts at the
+  // top priority and drops a level when its workgroup has done 50%, 75% and 90% of its range:
+  // a workgroup ahead of the others on its CU yields issue slots until they catch up, and the
+  // last band, where the order is again by age, is short.
+  const int span = u1 - u0;
+  int band = 0;
+  __builtin_amdgcn_s_setprio(3);
+  auto pace = [&](int done) {
+    const int nb = (20 * done >= 18 * span) ? 3 : (20 * done >= 15 * span) ? 2 : (20 * done >= 10 * span) ? 1 : 0;
+    if (nb == band) return;
+    band = nb;
+    switch (nb) {
+      case 1: __builtin_amdgcn_s_setprio(2); break;
+      case 2: __builtin_amdgcn_s_setprio(1); break;
+      default: __builtin_amdgcn_s_setprio(0); break;
+    }
+  };
   if (u0 == u1) {
     // An empty range still owns slot 0, which the combine may read: make it neutral.
     float* part = p.ws_part + static_cast<size_t>(blockIdx.x) * 2 * qpw * G * PART_STRIDE;
@@ -1030,6 +1058,7 @@ __global__ __launch_bounds__(256, (KB != 16 && MQ != 2 && MQ != 3 && (NP == 1 ||
       };
 
       for (; x < xq_end; x += xstep) {
+        pace((u - u0) + (x - ku));
         const int xn = x + xstep;
         const bool more = xn < xq_end;
         // after the last unit, reload the current tiles (cache hits) so the load count per
@@ -1515,7 +1544,7 @@ __global__ __launch_bounds__(256, (KB != 16 && MQ != 2 && MQ != 3 && (NP == 1 ||
 
 // First workgroup whose unit range [k U / NB, (k+1) U / NB) contains unit u.
 __device__ __forceinline__ int block_of(long long u, long long U, long long NB) {
-  return static_cast<int>(((u + 1) * NB - 1) / U);
+  return static_cast<int>(floor_div((u + 1) * NB - 1, U));
 }
 
 // Merge the partials of each (sequence, kv head) that more than one workgroup worked on; write
@@ -1562,7 +1591,7 @@ __global__ __launch_bounds__(T) void combine_kernel(DecodeParams p) {
   const long long us = pre[b] + static_cast<long long>(sidx) * ub, ue = us + ub;
   const int kf = block_of(us, U, NB), kl = block_of(ue - 1, U, NB);
   if (kf == kl) return;  // one workgroup saw the whole sequence and wrote the output
-  const int s0 = ((static_cast<long long>(kf) * U) / NB == us) ? 0 : 1;
+  const int s0 = (floor_div(static_cast<long long>(kf) * U, NB) == us) ? 0 : 1;
   for (int o0 = 0; o0 < opb; o0 += opp) {
     const int o = static_cast<int>(blockIdx.y) * opb + o0 + oi;
     const int oh = o / D, ch = o % D;
