@@ -223,12 +223,14 @@ WsLayout ws_layout(const kvq_cache* c, int n_q_heads, int max_tokens, int n_q = 
   // small batches get fewer, fuller workgroups: about two units per wave (on the 8 K-token
   // worked example 12.7 us per call against 16.0 us at one unit per wave and 14.1 us at four)
   // (the 4 / qpw waves of a block share its units)
-  // (the segment-start weight is not work: a batch that one workgroup covers in two units per
-  // wave runs on one workgroup, with no partials to combine)
+  // (the segment-start weight is not work: a batch that one workgroup covers in three units
+  // per wave runs on one workgroup, with no partials and no combine launch, which costs more
+  // than the third unit: the one-sequence 256-token layer took 8.6 us per call on two
+  // workgroups with the combine)
   const long wpq = 4 / w.qpw;
   const long work = units_bound(c, max_tokens) -
                     static_cast<long>(c->batch) * c->n_kv_heads * SEGMENT_START_WEIGHT;
-  const long ub = (work * w.nqs + 2 * wpq - 1) / (2 * wpq);
+  const long ub = (work * w.nqs <= 3 * wpq) ? 1 : (work * w.nqs + 2 * wpq - 1) / (2 * wpq);
   if (nb > ub) nb = ub;
   if (nb < 1) nb = 1;
   w.nblocks = static_cast<int>(nb);
