@@ -124,6 +124,14 @@ __global__ __launch_bounds__(256) void quantize_kernel(CacheDev c, const uint16_
 
   const int tid = threadIdx.x;
   const int b = blockIdx.y / c.H, h = blockIdx.y % c.H;
+  constexpr int PIECES = D * 2 / 16;  // 16-byte pieces of a bf16 row
+  // One new token and no window (a decode step): the token is this workgroup's only slot
+  // wherever the counters put it, so its two rows load in parallel with the counters.
+  const bool one_row = mode == MODE_APPEND && c.R == 0 && n_new == 1;
+  uint4 row_piece = uint4{0u, 0u, 0u, 0u};
+  if (one_row && tid < 2 * PIECES)
+    row_piece = reinterpret_cast<const uint4*>((tid < PIECES ? knew : vnew) +
+                                               (static_cast<size_t>(b) * c.H + h) * D)[tid % PIECES];
   const int nq = c.n_quant[b];
   int nr = c.R > 0 ? c.n_res[b] : 0;
   if (nq < 0 || nr < 0 || nr > c.R) return;  // corrupt counters: reported by tail_kernel
@@ -156,8 +164,10 @@ __global__ __launch_bounds__(256) void quantize_kernel(CacheDev c, const uint16_
   const int ngv = fp8 ? 0 : D / V.group;
 
   // Phase 0: the pending bf16 rows of this segment into LDS (16-byte pieces).
-  {
-    const int pieces = D * 2 / 16;
+  if (one_row) {
+    if (tid < 2 * PIECES) reinterpret_cast<uint4*>(&xs[lo - seg0][tid / PIECES][0])[tid % PIECES] = row_piece;
+  } else {
+    const int pieces = PIECES;
     const int n_items = (hi - lo) * 2 * pieces;
     for (int it = tid; it < n_items; it += blockDim.x) {
       const int piece = it % pieces;
@@ -176,7 +186,6 @@ __global__ __launch_bounds__(256) void quantize_kernel(CacheDev c, const uint16_
   // row t is halfword 4 (ch % 8) + t % 4 of chunk (t / 4) (D / 8) + ch / 8), and there is no
   // metadata.
   if (K.bits == 16) {
-    constexpr int PIECES = D * 2 / 16;
     for (int it = tid; it < (hi - lo) * PIECES; it += blockDim.x) {
       const int slot = lo + it / PIECES, pc = it % PIECES;
       bool ok = true;
@@ -352,8 +361,15 @@ __global__ __launch_bounds__(256) void quantize_kernel(CacheDev c, const uint16_
       // word q of the chunk sequence: word q % bits of chunk q / bits
       uint32_t* dst = reinterpret_cast<uint32_t*>(c.vc + tile * tile_bytes +
                                                   slab_byte(V.bits, q / V.bits, 32 * (q % V.bits)));
-      if (mask != 0xFFFFFFFFu) val = (*dst & ~mask) | val;
-      *dst = val;
+      if (mask == 0xFFFFFFFFu) {
+        *dst = val;
+      } else if (mask != 0u) {
+        // fields of slots outside [lo, hi) keep their bits: clear this range's fields, then set
+        // them (two atomics from one thread to one word apply in order; nothing waits on them,
+        // where a read-modify-write would put a memory round trip on the append's path)
+        atomicAnd(dst, ~mask);
+        atomicOr(dst, val);
+      }
     }
   }
   // Phase 2c: metadata (none for FP8: its scales are the caller's).
