@@ -300,8 +300,48 @@ __device__ __forceinline__ uint2 ld_stream2(const void* p) {
   return uint2{v[0], v[1]};
 }
 
-// A lane's slice of a tile (4 KB bytes) at `ptr`; 8- and 16-bit slices are stored as 16-byte
-// pieces one 1 KiB slab apart, so each load instruction of a wave reads 1 KiB contiguously.
+// Buffer loads from a wave-uniform base: the base sits in the scalar resource and each lane
+// adds a 32-bit byte offset, so a load costs no 64-bit address arithmetic per lane.  The
+// resource's last word is the raw-buffer setting of this GPU family; the record count is the
+// 2 GiB maximum (every offset here is within a tile or a scale row).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t buf(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
+}
+constexpr int BUF_NT = 2;  // nontemporal cache policy (as the streaming loads above)
+__device__ __forceinline__ uint4 bld4(rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, BUF_NT));
+}
+template <int AUX = BUF_NT>
+__device__ __forceinline__ uint2 bld2(rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX));
+}
+
+// A lane's slice of a tile (4 KB bytes) at byte `off` of the tile's resource; 8- and 16-bit
+// slices are stored as 16-byte pieces one 1 KiB slab apart, so each load instruction of a wave
+// reads 1 KiB contiguously.
+template <int KB>
+__device__ __forceinline__ void load_words(rsrc_t r, unsigned off, uint32_t (&w)[KB]) {
+  if constexpr (KB == 16) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const uint4 a = bld4(r, off + 1024 * i);
+      w[4 * i] = a.x; w[4 * i + 1] = a.y; w[4 * i + 2] = a.z; w[4 * i + 3] = a.w;
+    }
+  } else if constexpr (KB == 8) {
+    const uint4 a = bld4(r, off);
+    const uint4 b = bld4(r, off + 1024);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+  } else if constexpr (KB == 4) {
+    const uint4 a = bld4(r, off);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+  } else {
+    const uint2 a = bld2(r, off);
+    w[0] = a.x; w[1] = a.y;
+  }
+}
+
 template <int KB>
 __device__ __forceinline__ void load_words(const uint8_t* ptr, uint32_t (&w)[KB]) {
   if constexpr (KB == 16) {
@@ -682,19 +722,21 @@ __global__ __launch_bounds__(256, (KB != 16 && MQ != 2 && MQ != 3 && (NP == 1 ||
     // per-channel key group tau's metadata row: contiguous [b][h][cap / Gt], paged with the
     // block of the group's first token (an unusable entry reads row 0; the block error is
     // reported where the codes are read)
+    // (the row's first element; a lane reads its 8 channels from fold_c0 on)
     auto kpc_meta = [&](int tau) -> size_t {
-      if (!trow) return ((static_cast<size_t>(b) * H + h) * (c.cap / kgroup) + tau) * D + fold_c0;
+      if (!trow) return ((static_cast<size_t>(b) * H + h) * (c.cap / kgroup) + tau) * D;
       const int blk = ld_uniform(trow + (tau * kgroup) / TILE);
       const int pb_ = (blk < 0 || blk >= c.num_blocks) ? 0 : blk;
-      return (static_cast<size_t>(pb_) * H + h) * D + fold_c0;
+      return (static_cast<size_t>(pb_) * H + h) * D;
     };
-    auto load_meta8 = [&](const uint16_t* base, size_t mi) -> uint4 {
+    auto load_meta8 = [&](const uint16_t* row) -> uint4 {
+      const rsrc_t r = buf(row);
       if constexpr (KB == 2) {
-        const uint2 a = *reinterpret_cast<const uint2*>(base + mi);
-        const uint2 bb = *reinterpret_cast<const uint2*>(base + mi + 8);
+        const uint2 a = bld2<0>(r, 2 * fold_c0);
+        const uint2 bb = bld2<0>(r, 2 * fold_c0 + 16);
         return uint4{a.x, a.y, bb.x, bb.y};
       } else {
-        return *reinterpret_cast<const uint4*>(base + mi);
+        return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, 2 * fold_c0, 0, 0));
       }
     };
     UnitData<KB, VB, NP, KPC> d{};
@@ -715,30 +757,40 @@ __global__ __launch_bounds__(256, (KB != 16 && MQ != 2 && MQ != 3 && (NP == 1 ||
     auto load_k = [&](int xx, int pA, int pB) {
       pA = max(pA, 0);
       pB = max(pB, 0);
-      load_words<KB>(c.kc + static_cast<size_t>(pA) * K_TILE_BYTES + k_lane, d.kw[0]);
-      load_words<KB>(c.kc + static_cast<size_t>(pB) * K_TILE_BYTES + k_lane, d.kw[1]);
+      if constexpr (BF) {  // (buffer loads raise the BF16 kernel's registers past 3 waves)
+        load_words<KB>(c.kc + static_cast<size_t>(pA) * K_TILE_BYTES + k_lane, d.kw[0]);
+        load_words<KB>(c.kc + static_cast<size_t>(pB) * K_TILE_BYTES + k_lane, d.kw[1]);
+      } else {
+        load_words<KB>(buf(c.kc + static_cast<size_t>(pA) * K_TILE_BYTES), k_lane, d.kw[0]);
+        load_words<KB>(buf(c.kc + static_cast<size_t>(pB) * K_TILE_BYTES), k_lane, d.kw[1]);
+      }
       if constexpr (BF || F8) {
       } else if constexpr (KPC) {
         // a paged key group of 16 or 32 tokens starts at this unit's tile A, whose block then
         // holds the group's metadata row: no second block-table read
-        const size_t mi = (trow && kgroup <= 2 * TILE) ? static_cast<size_t>(pA) * D + fold_c0
-                                                       : kpc_meta((32 * xx) / kgroup);
-        d.fs = load_meta8(c.ks, mi);
-        if constexpr (KASYM) d.fz = load_meta8(c.kz, mi);
+        const size_t mrow = (trow && kgroup <= 2 * TILE) ? static_cast<size_t>(pA) * D
+                                                         : kpc_meta((32 * xx) / kgroup);
+        d.fs = load_meta8(c.ks + mrow);
+        if constexpr (KASYM) d.fz = load_meta8(c.kz + mrow);
       } else {
 #pragma unroll
         for (int t = 0; t < 2; t++) {
           const size_t tb = static_cast<size_t>(t ? pB : pA) * c.ks_tile;
-          d.ks[t] = *reinterpret_cast<const uint2*>(c.ks + tb + ks_lane);
-          if constexpr (KASYM) d.kz[t] = *reinterpret_cast<const uint2*>(c.kz + tb + ks_lane);
+          d.ks[t] = bld2<0>(buf(c.ks + tb), 2 * ks_lane);
+          if constexpr (KASYM) d.kz[t] = bld2<0>(buf(c.kz + tb), 2 * ks_lane);
         }
       }
     };
     auto load_v = [&](int pA, int pB) {
       pA = max(pA, 0);
       pB = max(pB, 0);
-      load_words<VB>(c.vc + static_cast<size_t>(pA) * V_TILE_BYTES + v_lane, d.vw[0]);
-      load_words<VB>(c.vc + static_cast<size_t>(pB) * V_TILE_BYTES + v_lane, d.vw[1]);
+      if constexpr (BF) {
+        load_words<VB>(c.vc + static_cast<size_t>(pA) * V_TILE_BYTES + v_lane, d.vw[0]);
+        load_words<VB>(c.vc + static_cast<size_t>(pB) * V_TILE_BYTES + v_lane, d.vw[1]);
+      } else {
+        load_words<VB>(buf(c.vc + static_cast<size_t>(pA) * V_TILE_BYTES), v_lane, d.vw[0]);
+        load_words<VB>(buf(c.vc + static_cast<size_t>(pB) * V_TILE_BYTES), v_lane, d.vw[1]);
+      }
       if constexpr (!BF && !F8)
 #pragma unroll
       for (int t = 0; t < 2; t++) {
@@ -746,8 +798,8 @@ __global__ __launch_bounds__(256, (KB != 16 && MQ != 2 && MQ != 3 && (NP == 1 ||
 #pragma unroll
         for (int pp = 0; pp < scale_rows<NP>(); pp++) {
           const unsigned lo = rgv[pp] * TILE + 4 * g;
-          d.vs[pp][t] = *reinterpret_cast<const uint2*>(c.vs + tb + lo);
-          if constexpr (VASYM) d.vz[pp][t] = *reinterpret_cast<const uint2*>(c.vz + tb + lo);
+          d.vs[pp][t] = bld2<0>(buf(c.vs + tb), 2 * lo);
+          if constexpr (VASYM) d.vz[pp][t] = bld2<0>(buf(c.vz + tb), 2 * lo);
         }
       }
     };
@@ -1082,10 +1134,10 @@ __global__ __launch_bounds__(256, (KB != 16 && MQ != 2 && MQ != 3 && (NP == 1 ||
 #pragma unroll
             for (int j = 0; j < 4; j++)
               dq[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop_sub<KB>(d.kw[0], j, ur), qb[j], dq[0], 0, 0, 0);
-            const size_t mi = trow ? static_cast<size_t>(max(pB, 0)) * D + fold_c0 : kpc_meta(2 * x + 1);
-            const uint4 fs2 = load_meta8(c.ks, mi);
+            const size_t mrow = trow ? static_cast<size_t>(max(pB, 0)) * D : kpc_meta(2 * x + 1);
+            const uint4 fs2 = load_meta8(c.ks + mrow);
             uint4 fz2 = uint4{0, 0, 0, 0};
-            if constexpr (KASYM) fz2 = load_meta8(c.kz, mi);
+            if constexpr (KASYM) fz2 = load_meta8(c.kz + mrow);
             kpc_fold(fs2, fz2);
             dq[1] = dq0;
 #pragma unroll
