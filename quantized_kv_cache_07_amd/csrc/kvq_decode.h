@@ -757,7 +757,8 @@ __global__ __launch_bounds__(256, (KB != 16 && MQ != 2 && MQ != 3 && (NP == 1 ||
     auto load_k = [&](int xx, int pA, int pB) {
       pA = max(pA, 0);
       pB = max(pB, 0);
-      if constexpr (BF) {  // (buffer loads raise the BF16 kernel's registers past 3 waves)
+      if constexpr (BF || F8) {  // (measured: buffer loads made the BF16 kernel need more
+                                 // registers, and the FP8 multi-query kernels 15% slower)
         load_words<KB>(c.kc + static_cast<size_t>(pA) * K_TILE_BYTES + k_lane, d.kw[0]);
         load_words<KB>(c.kc + static_cast<size_t>(pB) * K_TILE_BYTES + k_lane, d.kw[1]);
       } else {
@@ -784,7 +785,7 @@ __global__ __launch_bounds__(256, (KB != 16 && MQ != 2 && MQ != 3 && (NP == 1 ||
     auto load_v = [&](int pA, int pB) {
       pA = max(pA, 0);
       pB = max(pB, 0);
-      if constexpr (BF) {
+      if constexpr (BF || F8) {
         load_words<VB>(c.vc + static_cast<size_t>(pA) * V_TILE_BYTES + v_lane, d.vw[0]);
         load_words<VB>(c.vc + static_cast<size_t>(pB) * V_TILE_BYTES + v_lane, d.vw[1]);
       } else {
