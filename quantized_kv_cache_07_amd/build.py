@@ -24,7 +24,7 @@ LIB = os.path.join(HERE, "libkvq.so")
 LIB_QK_VALU = os.path.join(HERE, "libkvq_qkvalu.so")
 SOURCES = ["kvq_host.hip", "kvq_append.hip"] + [
     f"kvq_decode_b{bits}{scheme}.hip" for bits in (2, 4, 8) for scheme in "sa"] + [
-    "kvq_decode_b16.hip", "kvq_decode_b8f.hip"] + [
+    "kvq_decode_b16.hip", "kvq_decode_b8f.hip", "kvq_decode_dense.hip"] + [
     f"kvq_decode_mix_k{bits}{scheme}.hip" for bits in (2, 4, 8) for scheme in "sa"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

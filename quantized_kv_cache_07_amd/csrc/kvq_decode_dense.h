@@ -1,0 +1,716 @@
+// kvq_decode_dense.h -- causal multi-query decode with sixteen query rows per wave (gfx950).
+//
+//   out[b][i][hq] = softmax(sm_scale q_i K^T + causal mask) V    [P2 = llmdaily.org "KV-cache
+//   quantization -- making long-context inference fit in memory", "Why the KV cache grows so
+//   quickly", attention equation; the query tokens are the last n_q cached tokens], over the
+//   compressed tokens dequantized in registers as they stream in (P3 = oh-bug.com "KV Cache
+//   Quantization in Practice", "Misconception 1"), then the BF16 window.
+//
+// For integer caches with per-token key groups of 64 or 128 channels and n_q x (query heads per
+// kv head) >= 16.  A query block is 16 rows (query tokens x GQA heads); a workgroup's four waves
+// take four blocks of one (sequence, kv head) and walk the same units, so the codes stream once
+// for up to 64 rows.  Per wave and unit (32 tokens):
+//   QK^T  the key codes enter as raw f16 (1024 + alpha u, one and-or per pair) against the 16
+//         query rows, one accumulator per key group (the query operand masked to the group's
+//         channels), the bias removed by the accumulator start; the scores are the group sums
+//         times each token's group scale: exact products, as in the single-query kernel.
+//   PV    P = the 16 rows' weights as f16; the value codes are dequantized to f16 in registers,
+//         s (u - off) 2^-8 (or s u + z), one subtraction and one multiply (or fma) per two codes
+//         after the raw-form unpack.  Rounding w and v to f16 (11 bits) keeps the output within
+//         the pages' tolerance; the 2^-8 keeps every finite fp16 scale times a code below the
+//         f16 limit and is removed before the window rows add true values.
+// Split segments leave partials for combine_kernel, as in the single-query kernel.
+#pragma once
+
+#include "kvq_decode.h"
+
+namespace kvq {
+
+constexpr int DROWS = 16;  // query rows of a dense block
+
+struct DenseLds {
+  static constexpr int red = 0;                                  // [WAVES][16][RED_STRIDE] f32
+  static constexpr int mw = red + WAVES * 16 * RED_STRIDE * 4;   // [WAVES][16] f32
+  static constexpr int lw = mw + WAVES * DROWS * 4;              // [WAVES][16] f32
+  static constexpr int qs = lw + WAVES * DROWS * 4;              // [4][16][D] bf16
+  static constexpr int ustat = qs + 4 * DROWS * D * 2;           // [WAVES][3] int
+  static constexpr int qe = ustat + WAVES * 3 * 4;               // [4][16] int
+  static constexpr int pre = qe + 4 * DROWS * 4;                 // [B + 1] int
+  // a unit's value operands, dequantized once per workgroup: [2 units][8 products][64 lanes]
+  // x 16 bytes, in the merge rows (which hold nothing while units stream)
+  static constexpr int vbuf = red;
+  __host__ __device__ static size_t cnt(int B) { return static_cast<size_t>(pre) + 4 * static_cast<size_t>(B + 1); }
+  static size_t bytes(int B) { return cnt(B) + 8 * static_cast<size_t>(B); }
+};
+static_assert(WAVES * 16 * RED_STRIDE * 4 >= 2 * 8 * 64 * 16, "value operands fit the merge rows");
+
+// Code words of a value chunk that wave w dequantizes: products 2 w and 2 w + 1 use pairs
+// 4 w .. 4 w + 3 of each tile, i.e. words 2 w, 2 w + 1 of 8-bit chunks, word w of 4-bit chunks
+// and half of word w / 2 of 2-bit chunks (the wave shifts odd halves down by 8 bits).
+template <int KB>
+constexpr int vwords() { return KB == 8 ? 2 : 1; }
+template <int KB>
+__device__ __forceinline__ unsigned vword_off(int w) {
+  if constexpr (KB == 8) return 1024u * (w / 2) + 8u * (w % 2);
+  else if constexpr (KB == 4) return 4u * w;
+  else return 4u * (w / 2);
+}
+template <int KB>
+__device__ __forceinline__ void load_vwords(rsrc_t r, unsigned off, int w, uint32_t (&x)[vwords<KB>()]) {
+  if constexpr (KB == 8) {
+    const uint2 a = bld2(r, off);
+    x[0] = a.x;
+    x[1] = a.y;
+  } else {
+    x[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, BUF_NT);
+    if constexpr (KB == 2) x[0] >>= 8 * (w & 1);
+  }
+}
+
+// KB: code bits of keys and values (the same format on both sides); SCH: KVQ_SYM or KVQ_ASYM;
+// NGK: key groups per row (1: groups of 128 channels, 2: groups of 64).
+template <int KB, int SCH, int NGK>
+__global__ __launch_bounds__(256, 2) void dense_kernel(DecodeParams p) {
+  constexpr int G = DROWS;
+  constexpr int qpw = 4;  // query blocks per segment, one per wave
+  constexpr bool ASYM = SCH == KVQ_ASYM;
+  constexpr int WW = window_weight2(KB, KB);
+  constexpr int SEG_W = SEGMENT_START_WEIGHT;
+  const int nqt = p.nqt, qbs = p.qbs, nqb = p.nqb, gkv = p.gkv, nqs = p.nqs;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const CacheDev& c = p.c;
+  const int B = c.B, H = c.H;
+  const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63;
+  const int g = lane >> 4, n = lane & 15;
+
+  float* red = reinterpret_cast<float*>(smem + DenseLds::red);
+  float* mw = reinterpret_cast<float*>(smem + DenseLds::mw);
+  float* lw = reinterpret_cast<float*>(smem + DenseLds::lw);
+  uint16_t* qs = reinterpret_cast<uint16_t*>(smem + DenseLds::qs);
+  int* pre = reinterpret_cast<int*>(smem + DenseLds::pre);
+  int* cnt = reinterpret_cast<int*>(smem + DenseLds::cnt(c.B));
+  int* ustat = reinterpret_cast<int*>(smem + DenseLds::ustat);
+  int* qe = reinterpret_cast<int*>(smem + DenseLds::qe);
+
+  // ---- units per sequence and their prefix sum (every workgroup; workgroup 0 publishes it) ----
+  {
+    const int per = (B + 255) / 256;
+    int* scan = reinterpret_cast<int*>(red);
+    int umin = INT_MAX, umax = 0, useq = 0;
+    for (int i = tid * per; i < min(B, (tid + 1) * per); i++) {
+      const int un = seq_units(c, p.max_tokens, i, WW);
+      cnt[2 * i] = c.n_quant[i];
+      cnt[2 * i + 1] = c.R > 0 ? c.n_res[i] : 0;
+      if (un < 0) {
+        if (blockIdx.x == 0) atomicOr(c.err, KVQ_ERR_TOKENS);
+      } else if (un > 0) {
+        umin = min(umin, un);
+        umax = max(umax, un);
+        useq++;
+      }
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+      umin = min(umin, __shfl_xor(umin, off));
+      umax = max(umax, __shfl_xor(umax, off));
+      useq += __shfl_xor(useq, off);
+    }
+    if (lane == 0) {
+      ustat[3 * wave] = umin;
+      ustat[3 * wave + 1] = umax;
+      ustat[3 * wave + 2] = useq;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < WAVES; w++) {
+      umin = min(umin, ustat[3 * w]);
+      umax = max(umax, ustat[3 * w + 1]);
+    }
+    const int segw = umin != umax ? SEG_W : 0;
+    auto weighted = [&](int i) {
+      const int un = seq_units(c, p.max_tokens, i, WW);
+      return (un > 0 ? un + segw : 0) * H * nqs;
+    };
+    int s = 0;
+    for (int i = tid * per; i < min(B, (tid + 1) * per); i++) s += weighted(i);
+    scan[tid] = s;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int v = (tid >= off) ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    int run = scan[tid] - s;
+    for (int i = tid * per; i < min(B, (tid + 1) * per); i++) {
+      pre[i] = run;
+      run += weighted(i);
+    }
+    if (tid == 255) pre[B] = scan[255];
+    __syncthreads();
+  }
+
+  const int U = uni(pre[B]);
+  int umin = ustat[0], umax = ustat[1], useq = ustat[2];
+#pragma unroll
+  for (int w = 1; w < WAVES; w++) {
+    umin = min(umin, ustat[3 * w]);
+    umax = max(umax, ustat[3 * w + 1]);
+    useq += ustat[3 * w + 2];
+  }
+  const int nbe = uni(aligned_ranges(gridDim.x, useq * H * nqs, umin == umax));
+  if (blockIdx.x == 0) {
+    for (int i = tid; i <= B; i += 256) p.ws_pre[i] = pre[i];
+    if (tid == 0) p.ws_pre[B + 1] = nbe;
+  }
+  if (static_cast<int>(blockIdx.x) >= nbe) return;
+  if (gridDim.x == 1) {  // no combine runs after a one-workgroup launch: empty sequences here
+    for (int bb = 0; bb < B; bb++) {
+      if (pre[bb + 1] != pre[bb]) continue;
+      float* o = p.out + static_cast<size_t>(bb) * nqt * p.Hq * D;
+      for (int i = tid; i < nqt * p.Hq * D; i += 256) o[i] = 0.0f;
+    }
+  }
+  const long long NBl = nbe;
+  const int u0 = static_cast<int>(floor_div(static_cast<long long>(blockIdx.x) * U, NBl));
+  const int u1 = static_cast<int>(floor_div(static_cast<long long>(blockIdx.x + 1) * U, NBl));
+  if (u0 == u1) {
+    float* part = p.ws_part + static_cast<size_t>(blockIdx.x) * 2 * qpw * G * PART_STRIDE;
+    for (int i = tid; i < qpw * G * PART_STRIDE; i += 256) part[i] = (i % PART_STRIDE == 0) ? -FLT_MAX : 0.0f;
+    return;
+  }
+
+  constexpr int kgroup = D / NGK, ngk = NGK;
+  const int vgroup = c.v.group;
+  constexpr float off = ASYM ? 0.0f : static_cast<float>(1 << (KB - 1));
+  constexpr long TILE_BYTES = static_cast<long>(TILE) * D * KB / 8;
+  constexpr unsigned SP = (4 * KB < 16) ? 4 * KB : 16;  // bytes of a slice piece
+  const unsigned k_lane = SP * (4 * n + g);             // key slice 4 n + g: token n, channels 32 g ..
+  // value chunk 16 g + n (tokens 4 g .., channels 8 n ..): the words this wave dequantizes
+  const unsigned vw_lane = SP * (16 * g + n) + vword_off<KB>(wave);
+  const int kgl = (32 * g) / kgroup;                    // key group of this lane's channels
+  const unsigned vs_lane = ((8 * n) / vgroup) * TILE + 4 * g;  // value scale row of this lane
+  const int qi = wave;
+  const UnpackRegs ur = unpack_regs<KB>();
+
+  int u = u0;
+  bool first_seg = true;
+  while (u < u1) {
+    // ---- the segment: sequence b, kv head h, query-block group qgrp, first unit kk ----
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= u) lo = mid; else hi = mid - 1;
+    }
+    const int b = uni(lo);
+    const int pb0 = uni(pre[b]);
+    const int ub = uni((pre[b + 1] - pb0) / (H * nqs));
+    const int sidx = (u - pb0) / ub, kk = (u - pb0) % ub;
+    const int h = sidx / nqs, qgrp = sidx % nqs;
+    const int qblk = qgrp * qpw + qi;
+    const int seg_abs_end = pb0 + (sidx + 1) * ub;
+    const int uend = min(u1, seg_abs_end);
+    const bool complete = (kk == 0) && (uend == seg_abs_end);
+    const int slot = first_seg ? 0 : 1;
+    const int nq = uni(cnt[2 * b]);
+    const int nr = uni(cnt[2 * b + 1]);
+    const int uq = (nq + 31) / 32;
+    const int segw = umin != umax ? SEG_W : 0;
+    const int ku = max(kk - segw, 0), xend = max(kk + (uend - u) - segw, 0);
+    // causal limit: block qblk's first query token sees the first lim_min cached tokens, row v's
+    // token lim_min + v / gkv of them
+    const int lim_min = uni(nq + nr - nqt + qblk * qbs + 1);
+
+    // query rows of the four blocks: row v of block bi = query token (qgrp 4 + bi) qbs + v / gkv,
+    // head h gkv + v % gkv (zero past the last); four 16-byte pieces per thread
+    uint4 qval[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      qval[k] = uint4{0u, 0u, 0u, 0u};
+      const int piece = tid + 256 * k;
+      const int row = piece / (D / 8), bi = row / G, v = row % G;
+      const int qg = (qgrp * qpw + bi) * qbs + v / gkv;
+      if (qg < nqt)
+        qval[k] = reinterpret_cast<const uint4*>(
+            p.q + ((static_cast<size_t>(b) * nqt + qg) * p.Hq + static_cast<size_t>(h) * gkv + v % gkv) *
+                      D)[piece % (D / 8)];
+    }
+    // every wave walks all units: an active wave for its block, and every wave dequantizes its
+    // quarter of each unit's values for the others
+    const bool active = qblk < nqb;
+    int x = ku;
+    const int xq_end = min(xend, uq);
+
+    const int seq_tile0 = (b * H + h) * (c.cap / TILE);
+    const int* trow = c.table ? c.table + static_cast<size_t>(b) * c.max_blocks : nullptr;
+    auto phys_of = [&](int t) -> int {
+      if (!trow) return seq_tile0 + t;
+      const int blk = ld_uniform(trow + t);
+      if (blk < 0 || blk >= c.num_blocks) return -1;
+      return blk * H + h;
+    };
+    constexpr int VW = vwords<KB>();
+    uint32_t kw[2][KB], vw[2][VW];
+    uint2 ks[NGK][2], kz[NGK][2], vsc[2], vz[2];
+    auto load_k = [&](int pA, int pB) {
+      pA = max(pA, 0);
+      pB = max(pB, 0);
+      load_words<KB>(buf(c.kc + static_cast<size_t>(pA) * TILE_BYTES), k_lane, kw[0]);
+      load_words<KB>(buf(c.kc + static_cast<size_t>(pB) * TILE_BYTES), k_lane, kw[1]);
+#pragma unroll
+      for (int t = 0; t < 2; t++) {
+        const size_t tb = static_cast<size_t>(t ? pB : pA) * c.ks_tile;
+#pragma unroll
+        for (int gi = 0; gi < NGK; gi++) {
+          if (gi < ngk) {
+            ks[gi][t] = bld2<0>(buf(c.ks + tb), 2 * (gi * TILE + 4 * g));
+            if constexpr (ASYM) kz[gi][t] = bld2<0>(buf(c.kz + tb), 2 * (gi * TILE + 4 * g));
+          }
+        }
+      }
+    };
+    auto load_v = [&](int pA, int pB) {
+      pA = max(pA, 0);
+      pB = max(pB, 0);
+      load_vwords<KB>(buf(c.vc + static_cast<size_t>(pA) * TILE_BYTES), vw_lane, wave, vw[0]);
+      load_vwords<KB>(buf(c.vc + static_cast<size_t>(pB) * TILE_BYTES), vw_lane, wave, vw[1]);
+#pragma unroll
+      for (int t = 0; t < 2; t++) {
+        const size_t tb = static_cast<size_t>(t ? pB : pA) * c.vs_tile;
+        vsc[t] = bld2<0>(buf(c.vs + tb), 2 * vs_lane);
+        if constexpr (ASYM) vz[t] = bld2<0>(buf(c.vz + tb), 2 * vs_lane);
+      }
+    };
+    // tiles of unit y, and how many of their tokens are valid (0 for a bad block entry)
+    auto tiles_of = [&](int y, int& a, int& b) {
+      a = phys_of(2 * y);
+      b = (32 * y + 16 < nq) ? phys_of(2 * y + 1) : -1;
+    };
+    auto valid_of = [&](int y, int a, int b, int& va, int& vb) {
+      va = a >= 0 ? min(16, nq - 32 * y) : 0;
+      vb = b >= 0 ? min(16, nq - 32 * y - 16) : 0;
+    };
+    int pA = -1, pB = -1, nA = -1, nB = -1;  // tiles of units x and x + 1
+    if (x < xq_end) {
+      tiles_of(x, pA, pB);
+      if (active) load_k(pA, pB);
+      load_v(pA, pB);
+      if (x + 1 < xq_end) tiles_of(x + 1, nA, nB);
+    }
+
+    // ---- stage the 64 query rows and each row's prescale exponent ----
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const int piece = tid + 256 * k;
+      float mx = 0.0f;
+      const uint32_t w4[4] = {qval[k].x, qval[k].y, qval[k].z, qval[k].w};
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        mx = max3f(mx, __uint_as_float((w4[i] << 16) & 0x7FFF0000u), __uint_as_float(w4[i] & 0x7FFF0000u));
+      mx = fmaxf(mx, row_ror<8>(mx));
+      mx = fmaxf(mx, row_ror<4>(mx));
+      mx = fmaxf(mx, row_ror<2>(mx));
+      mx = fmaxf(mx, row_ror<1>(mx));
+      const int row = piece / (D / 8);
+      reinterpret_cast<uint4*>(qs + row * D)[piece % (D / 8)] = qval[k];
+      if (piece % (D / 8) == 0) qe[row] = q_exponent(mx, QE_RAW);
+    }
+    __syncthreads();
+    // this lane's QK column = row n of the wave's block: its prescale 2^-e and the softmax
+    // scale of its scores, sm_scale log2(e) 2^e
+    const int qe_n = qe[qi * G + n];
+    const float qsc = exp2i(-qe_n);
+    const float sl2 = p.sm_log2 * exp2i(qe_n);
+    const uint16_t* qrow = qs + (qi * G + n) * D;
+
+    // ---- QK operands: the row's query, prescaled, divided by each field's alpha, masked to
+    // key group gi; every tile's accumulator starts at minus the group's raw-code bias ----
+    f16x8 qb[NGK][4];
+    f32x4 dq0[NGK];
+    float qsum[NGK];  // asymmetric keys: sum of the prescaled query over the group's channels
+#pragma unroll
+    for (int gi = 0; gi < NGK; gi++) {
+      qsum[gi] = 0.0f;
+      dq0[gi] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const bool in_grp = kgl == gi;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const u16x8 raw = gather_kchan<KB>(qrow + 32 * g, j);
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+          const float xq = in_grp ? bf16_to_f32(raw[i]) * qsc : 0.0f;
+          qb[gi][j][i] = static_cast<_Float16>(xq * (1.0f / static_cast<float>(kelem_alpha<KB>(j, i))));
+          if constexpr (ASYM) qsum[gi] += xq;
+        }
+      }
+      if constexpr (ASYM) {
+        qsum[gi] += __shfl_xor(qsum[gi], 16);
+        qsum[gi] += __shfl_xor(qsum[gi], 32);
+      }
+      if (gi < ngk) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          f16x8 bias;
+#pragma unroll
+          for (int i = 0; i < 8; i++)
+            bias[i] = static_cast<_Float16>(-(1024.0f + static_cast<float>(kelem_alpha<KB>(j, i)) * off));
+          dq0[gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bias, qb[gi][j], dq0[gi], 0, 0, 0);
+        }
+      }
+    }
+
+    float m_run = -FLT_MAX, l_run = 0.0f;
+    f32x4 acc[8];  // rows 4 g + r (query rows), columns = channels 8 n + j of product j
+#pragma unroll
+    for (int j = 0; j < 8; j++) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // ---- online softmax of the 8 scores of a unit (column n, tokens 4 g + r of tiles A, B) ----
+    auto softmax = [&](float (&s2)[8], int nvA, int nvB, int tok0, float sl2_) {
+      if (!(nvA == 16 && nvB == 16)) {
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+          if (4 * g + (i & 3) >= (i < 4 ? nvA : nvB)) s2[i] = -INFINITY;
+      }
+      if (tok0 + 32 > lim_min) {
+        const int lim = lim_min + n / gkv;
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+          if (tok0 + 16 * (i >> 2) + 4 * g + (i & 3) >= lim) s2[i] = -INFINITY;
+      }
+      const float m01 = max3f(s2[0], s2[1], s2[2]);
+      const float m02 = max3f(s2[3], s2[4], s2[5]);
+      float tmax = max3f(max3f(s2[6], s2[7], m01), m02, m02);
+      tmax *= sl2_;
+      if (__ballot(tmax > m_run + LAZY_LOG2) != 0) {
+        float hm = fmaxf(tmax, __shfl_xor(tmax, 16));
+        hm = fmaxf(hm, __shfl_xor(hm, 32));
+        const float mn = fmaxf(m_run, hm);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+        l_run *= alpha;
+        // accumulator row 4 g + r belongs to column (row) 4 g + r, whose alpha lane 4 g + r holds
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          const float a0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), r));
+          const float a1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 4 + r));
+          const float a2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 8 + r));
+          const float a3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 12 + r));
+          const float a = (g == 0) ? a0 : (g == 1) ? a1 : (g == 2) ? a2 : a3;
+#pragma unroll
+          for (int j = 0; j < 8; j++) acc[j][r] *= a;
+        }
+        m_run = mn;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; i++) s2[i] = __builtin_amdgcn_exp2f(fmaf(s2[i], sl2_, -m_run));
+      l_run += (s2[0] + s2[1]) + (s2[2] + s2[3]) + ((s2[4] + s2[5]) + (s2[6] + s2[7]));
+    };
+
+    // ---------------------------- compressed units ----------------------------
+    // Unit y's value operands go to LDS buffer y & 1, one quarter per wave: products 2 wave and
+    // 2 wave + 1.  Element i of product j is raw pair (2 j + (i / 2) % 2) of tile i / 4, field
+    // i % 2; its scale is token 4 g + i % 4's of the lane's value group, times 2^-8 / alpha.
+    uint4* vbuf = reinterpret_cast<uint4*>(smem + DenseLds::vbuf);
+    auto put_values = [&](int y, int nvA, int nvB) {
+      uint32_t svb[4] = {vsc[0].x, vsc[0].y, vsc[1].x, vsc[1].y};
+      uint32_t zvb[4] = {vz[0].x, vz[0].y, vz[1].x, vz[1].y};
+      // a tile past the sequence end may hold any bytes (0 * NaN is NaN): clear the fp16 bits
+      // of the scales and zero-points of tokens past the end.  (By validity, not by weight: a
+      // value operand serves every query row, and a token one row's causal limit hides is seen
+      // by the next.)
+      if (!(nvA == 16 && nvB == 16)) {
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const int nv = (q < 2) ? nvA : nvB, t0 = 4 * g + 2 * (q % 2);
+          const uint32_t keep = (t0 < nv ? 0x0000FFFFu : 0u) | (t0 + 1 < nv ? 0xFFFF0000u : 0u);
+          svb[q] &= keep;
+          if constexpr (ASYM) zvb[q] &= keep;
+        }
+      }
+      f16x2 sv[4], zv2[4];
+      const f16x2 k8 = h2s(0x1p-8f);
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        sv[q] = as_h2(svb[q]) * k8;
+        if constexpr (ASYM) zv2[q] = as_h2(zvb[q]) * k8;
+      }
+#pragma unroll
+      for (int jj = 0; jj < 2; jj++) {
+        uint32_t vbw[4];
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          // q = 2 t + (pair parity): tile t, the wave's pair 2 jj + q % 2
+          const int t = q / 2, pr = 2 * jj + (q % 2);
+          const f16x2 raw = as_h2(rawpair<KB>(vw[t], pr, ur));
+          const float a0 = static_cast<float>(pair_alpha<KB>(pr));
+          const f16x2 inva = h2s(1.0f / a0);
+          f16x2 v2;
+          if constexpr (ASYM) {
+            const f16x2 tt = raw - h2s(1024.0f);                    // alpha u, exact
+            v2 = __builtin_elementwise_fma(tt, sv[q] * inva, zv2[q]);  // (s u + z) 2^-8
+          } else {
+            const f16x2 tt = raw - h2s(1024.0f + a0 * off);         // alpha (u - off), exact
+            v2 = tt * (sv[q] * inva);                                // s (u - off) 2^-8
+          }
+          vbw[q] = __builtin_bit_cast(uint32_t, v2);
+        }
+        vbuf[((y & 1) * 8 + 2 * wave + jj) * 64 + lane] = uint4{vbw[0], vbw[1], vbw[2], vbw[3]};
+      }
+    };
+    if (x < xq_end) {
+      bool bad_block = false;
+      for (; x < xq_end; x++) {
+        const bool more = x + 1 < xq_end;
+        int nvA, nvB;
+        valid_of(x, pA, pB, nvA, nvB);
+        bad_block |= pA < 0 || (32 * x + 16 < nq && pB < 0);
+        put_values(x, nvA, nvB);
+        int nnA = -1, nnB = -1;  // tiles of unit x + 2
+        if (x + 2 < xq_end) tiles_of(x + 2, nnA, nnB);
+        if (more) load_v(nA, nB);  // value registers are free again
+
+        f16x8 pa;
+        if (active) {
+          // QK^T: one accumulator per (tile, key group), the four chains interleaved; stand-in
+          // tiles are masked by the softmax
+          f32x4 dq[2][NGK];
+#pragma unroll
+          for (int t = 0; t < 2; t++)
+#pragma unroll
+            for (int gi = 0; gi < NGK; gi++) dq[t][gi] = dq0[gi];
+#pragma unroll
+          for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int t = 0; t < 2; t++) {
+              const f16x8 kop = kop_raw<KB>(kw[t], j, ur);
+#pragma unroll
+              for (int gi = 0; gi < NGK; gi++)
+                if (gi < ngk) dq[t][gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qb[gi][j], dq[t][gi], 0, 0, 0);
+            }
+          float s2[8];
+#pragma unroll
+          for (int t = 0; t < 2; t++) {
+#pragma unroll
+            for (int r = 0; r < 4; r++) s2[4 * t + r] = 0.0f;
+#pragma unroll
+            for (int gi = 0; gi < NGK; gi++) {
+              if (gi >= ngk) continue;
+              const uint2 k2 = ks[gi][t];
+              const float sc[4] = {f16_lo(k2.x), f16_hi(k2.x), f16_lo(k2.y), f16_hi(k2.y)};
+#pragma unroll
+              for (int r = 0; r < 4; r++) s2[4 * t + r] = fmaf(dq[t][gi][r], sc[r], s2[4 * t + r]);
+              if constexpr (ASYM) {
+                const uint2 z2 = kz[gi][t];
+                const float zk[4] = {f16_lo(z2.x), f16_hi(z2.x), f16_lo(z2.y), f16_hi(z2.y)};
+#pragma unroll
+                for (int r = 0; r < 4; r++) s2[4 * t + r] = fmaf(zk[r], qsum[gi], s2[4 * t + r]);
+              }
+            }
+          }
+          if (more) load_k(nA, nB);  // key registers are free again
+          softmax(s2, nvA, nvB, 32 * x, sl2);
+
+          // P: the weights as f16 (element i: token 4 g + i % 4 of tile i / 4)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const f16x2 w2 = pkrtz(s2[2 * i], s2[2 * i + 1]);
+            pa[2 * i] = w2[0];
+            pa[2 * i + 1] = w2[1];
+          }
+        }
+        // every wave's quarter of unit x is in LDS (and every wave is done reading unit x - 1's)
+        __syncthreads();
+        if (active) {
+          uint4 vop[8];
+#pragma unroll
+          for (int j = 0; j < 8; j++) vop[j] = vbuf[((x & 1) * 8 + j) * 64 + lane];
+#pragma unroll
+          for (int j = 0; j < 8; j++)
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, __builtin_bit_cast(f16x8, vop[j]), acc[j], 0, 0, 0);
+        }
+        pA = nA;
+        pB = nB;
+        nA = nnA;
+        nB = nnB;
+      }
+      if (bad_block && lane == 0) atomicOr(c.err, KVQ_ERR_BLOCK);
+    }
+    // the compressed units' values were taken times 2^-8
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) acc[j][r] *= 256.0f;
+
+    // ---------------------------- BF16 window units ----------------------------
+    const int wend = xend > uq ? (xend - uq + WW - 1) / WW : 0;
+    int jw = (qblk < nqb) ? (max(ku, uq) - uq + WW - 1) / WW : wend;
+    if (jw < wend) {
+      bf16x8 qw[4];
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        qw[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(qrow + 32 * g + 8 * j));
+      const uint16_t* kr = c.kres + (static_cast<size_t>(b) * H + h) * c.R * D;
+      const uint16_t* vr = c.vres + (static_cast<size_t>(b) * H + h) * c.R * D;
+      for (; jw < wend; jw++) {
+        const int r0 = 32 * jw;
+        const int nvA = min(16, nr - r0), nvB = max(0, min(16, nr - r0 - 16));
+        float s2[8];
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+          f32x4 dq = f32x4{0.f, 0.f, 0.f, 0.f};
+          if ((t ? nvB : nvA) > 0) {
+            const uint4* rowp = reinterpret_cast<const uint4*>(kr + (r0 + 16 * t + n) * D + 32 * g);
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+              dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rowp[j]), qw[j], dq, 0, 0, 0);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; r++) s2[4 * t + r] = dq[r];
+        }
+        softmax(s2, nvA, nvB, nq + r0, p.sm_log2);
+        // P: bf16 hi and lo parts of the weights (hi + lo carries 16 significant bits)
+        bf16x8 ph, pl;
+        {
+          uint32_t hk[4], lk[4];
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            uint32_t eh[2], el[2];
+#pragma unroll
+            for (int k2 = 0; k2 < 2; k2++) {
+              const float wv = s2[2 * i + k2];
+              const float hv = __uint_as_float(__float_as_uint(wv) & 0xFFFF0000u);
+              eh[k2] = __float_as_uint(hv) >> 16;
+              el[k2] = __float_as_uint(wv - hv) >> 16;
+            }
+            hk[i] = eh[0] | (eh[1] << 16);
+            lk[i] = el[0] | (el[1] << 16);
+          }
+          ph = __builtin_bit_cast(bf16x8, uint4{hk[0], hk[1], hk[2], hk[3]});
+          pl = __builtin_bit_cast(bf16x8, uint4{lk[0], lk[1], lk[2], lk[3]});
+        }
+#pragma unroll
+        for (int hf = 0; hf < 2; hf++) {
+          uint2 vrow[8];
+#pragma unroll
+          for (int i = 0; i < 8; i++) {
+            const int t = i / 4, row = r0 + 16 * t + 4 * g + (i % 4);
+            const bool ok = 4 * g + (i % 4) < (t ? nvB : nvA);
+            vrow[i] = ok ? *reinterpret_cast<const uint2*>(vr + row * D + 8 * n + 4 * hf) : uint2{0, 0};
+          }
+#pragma unroll
+          for (int jj = 0; jj < 4; jj++) {
+            u16x8 col;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+              const uint32_t wv = (jj < 2) ? vrow[i].x : vrow[i].y;
+              col[i] = static_cast<unsigned short>((jj & 1) ? (wv >> 16) : (wv & 0xFFFFu));
+            }
+            const int j = 4 * hf + jj;
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, __builtin_bit_cast(bf16x8, col), acc[j], 0, 0, 0);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, __builtin_bit_cast(bf16x8, col), acc[j], 0, 0, 0);
+          }
+        }
+      }
+    }
+
+    // ---------------------------- the wave's block: output or partial ----------------------------
+    float lsum = l_run + __shfl_xor(l_run, 16);
+    lsum += __shfl_xor(lsum, 32);
+    __syncthreads();  // every wave is done with the previous segment's rows of red
+    if (lane < G) {
+      mw[wave * G + lane] = m_run;
+      lw[wave * G + lane] = lsum;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) red[(wave * 16 + 4 * g + r) * RED_STRIDE + 8 * n + j] = acc[j][r];
+    wave_lds_sync();
+    if (qblk < nqb) {
+#pragma unroll 4
+      for (int oi = 0; oi < (G * D) / 64; oi++) {
+        const int o = lane + 64 * oi;
+        const int oh = o / D, ch = o % D;
+        const float O = red[(wave * 16 + oh) * RED_STRIDE + ch];
+        const float L = lw[wave * G + oh];
+        if (complete) {
+          const int qg = qblk * qbs + oh / gkv;
+          if (qg < nqt)
+            p.out[((static_cast<size_t>(b) * nqt + qg) * p.Hq + static_cast<size_t>(h) * gkv + oh % gkv) * D + ch] =
+                (L > 0.0f) ? O / L : 0.0f;
+        } else {
+          float* part = p.ws_part + (((static_cast<size_t>(blockIdx.x) * 2 + slot) * qpw + qi) * G + oh) * PART_STRIDE;
+          if (ch == 0) {
+            part[0] = mw[wave * G + oh];
+            part[1] = L;
+          }
+          part[4 + ch] = O;
+        }
+      }
+    } else if (!complete) {
+      // a block past the last one still owns its partial rows: neutral
+#pragma unroll 4
+      for (int oi = 0; oi < (G * D) / 64; oi++) {
+        const int o = lane + 64 * oi;
+        const int oh = o / D, ch = o % D;
+        float* part = p.ws_part + (((static_cast<size_t>(blockIdx.x) * 2 + slot) * qpw + qi) * G + oh) * PART_STRIDE;
+        if (ch == 0) {
+          part[0] = -FLT_MAX;
+          part[1] = 0.0f;
+        }
+        part[4 + ch] = 0.0f;
+      }
+    }
+    u = uend;
+    first_seg = false;
+  }
+}
+
+// Launch of the dense multi-query kernel and of the combine that merges its partials.
+template <int KB, int SCH, int NGK>
+hipError_t launch_dense_t(const DecodeParams& p0, hipStream_t s) {
+  DecodeParams p = p0;
+  const size_t lds = DenseLds::bytes(p.c.B);
+  static std::mutex mu;
+  static int cached_dev = -1, cached_blocks = 0;
+  static size_t cached_lds = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+  int resident = 0;
+  {
+    std::lock_guard<std::mutex> gd(mu);
+    if (dev == cached_dev && lds == cached_lds) resident = cached_blocks;
+  }
+  if (resident == 0) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipErrorInvalidDevice;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, dense_kernel<KB, SCH, NGK>, 256, lds) != hipSuccess)
+      return hipErrorInvalidConfiguration;
+    resident = cus * per_cu;
+    std::lock_guard<std::mutex> gd(mu);
+    cached_dev = dev;
+    cached_lds = lds;
+    cached_blocks = resident;
+  }
+  if (resident <= 0) return hipErrorInvalidConfiguration;
+  if (p.nblocks > resident) p.nblocks = resident;
+  dense_kernel<KB, SCH, NGK><<<p.nblocks, 256, lds, s>>>(p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.nblocks == 1) return hipSuccess;
+  const int avg = p.nblocks / (p.c.B * p.c.H * p.nqs);
+  int slices = 1;
+  while (slices < 16 && slices * 2 <= avg / 4 && (DROWS * D) / (slices * 2) >= 32) slices *= 2;
+  const dim3 grid(p.c.B * p.c.H * p.nqb, slices);
+  switch (avg < 8 ? 0 : slices) {
+    case 0: combine_kernel<DROWS, 1, 256><<<grid, 256, 0, s>>>(p); break;
+    case 1: combine_kernel<DROWS, 1, 1024><<<grid, 1024, 0, s>>>(p); break;
+    case 2: combine_kernel<DROWS, 2, 1024><<<grid, 1024, 0, s>>>(p); break;
+    case 4: combine_kernel<DROWS, 4, 1024><<<grid, 1024, 0, s>>>(p); break;
+    case 8: combine_kernel<DROWS, 8, 1024><<<grid, 1024, 0, s>>>(p); break;
+    default: combine_kernel<DROWS, 16, 1024><<<grid, 1024, 0, s>>>(p); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -35,6 +35,8 @@ hipError_t launch_decode_mixed_k4s(const DecodeParams& p, int vb, int vsch, int 
 hipError_t launch_decode_mixed_k4a(const DecodeParams& p, int vb, int vsch, int G, int NP, bool kpc, hipStream_t s);
 hipError_t launch_decode_mixed_k8s(const DecodeParams& p, int vb, int vsch, int G, int NP, bool kpc, hipStream_t s);
 hipError_t launch_decode_mixed_k8a(const DecodeParams& p, int vb, int vsch, int G, int NP, bool kpc, hipStream_t s);
+// multi-query decode with 16 query rows per wave (kvq_decode_dense.h)
+hipError_t launch_decode_dense(const DecodeParams& p, int bits, bool asym, hipStream_t s);
 
 namespace {
 
@@ -193,8 +195,32 @@ int device_cus();
 // Query tokens per segment for multi-query decode: the largest power of two (at most the
 // next power of two >= n_q) that keeps the segment within 8 rows, 16 QK columns (one per key
 // group and row) and 32 PV rows (hi / lo part, value group, row).
+// Multi-query decode takes the dense kernel (16 query rows per wave, the four waves of a
+// workgroup on four blocks of one (sequence, kv head), values dequantized once per workgroup)
+// for integer caches with the same format on both sides and per-token key groups of 64 or 128
+// channels, once the query rows of a kv head fill its four blocks (n_q x GQA heads >= 64): with
+// fewer rows its idle waves cost as much as busy ones and the blocked kernel is faster.
+// KVQ_MQ_DENSE=0 turns it off, KVQ_MQ_DENSE=1 takes it from 16 rows on.
+bool dense_mq(const kvq_cache* c, int gkv, int n_q) {
+  const kvq_side& k = c->fmt.k;
+  const kvq_side& v = c->fmt.v;
+  if (n_q < 2 || n_q * gkv < 16 || 16 % gkv != 0) return false;
+  if (k.scheme != KVQ_SYM && k.scheme != KVQ_ASYM) return false;
+  if (k.bits != 2 && k.bits != 4 && k.bits != 8) return false;
+  if (k.bits != v.bits || k.scheme != v.scheme) return false;
+  if (k.axis != KVQ_PER_TOKEN || v.axis != KVQ_PER_TOKEN) return false;
+  if (k.group != 64 && k.group != 128) return false;
+  int rows_min = 64;
+  if (const char* e = std::getenv("KVQ_MQ_DENSE")) {
+    if (e[0] == '0') return false;
+    if (e[0] == '1') rows_min = 16;
+  }
+  return n_q * gkv >= rows_min;
+}
+
 int query_block(const kvq_cache* c, int gkv, int n_q) {
   if (n_q <= 1) return 1;
+  if (dense_mq(c, gkv, n_q)) return 16 / gkv;
   const bool whole_row = c->fmt.k.scheme == KVQ_FP8 || c->fmt.k.bits == 16;
   const bool kpc = c->fmt.k.axis == KVQ_PER_CHANNEL;
   const int ngk = kpc ? 2 : whole_row ? 1 : D / c->fmt.k.group;
@@ -212,8 +238,9 @@ WsLayout ws_layout(const kvq_cache* c, int n_q_heads, int max_tokens, int n_q = 
   w.nqb = (n_q + w.qbs - 1) / w.qbs;
   w.G = gkv * w.qbs;
   // several blocks share a segment, so the waves of a workgroup read the same codes: four blocks
-  // one per wave, or two blocks of two waves each (with more blocks than waves would idle)
-  w.qpw = w.nqb >= 4 ? 4 : w.nqb >= 2 ? 2 : 1;
+  // one per wave, or two blocks of two waves each (with more blocks than waves would idle); the
+  // dense kernel always has one block per wave
+  w.qpw = dense_mq(c, gkv, n_q) ? 4 : w.nqb >= 4 ? 4 : w.nqb >= 2 ? 2 : 1;
   w.nqs = (w.nqb + w.qpw - 1) / w.qpw;
   long nb = static_cast<long>(device_cus()) * 4;
   if (const char* e = std::getenv("KVQ_DECODE_BLOCKS")) {
@@ -417,8 +444,9 @@ kvq_status kvq_decode_attention_mq(const kvq_cache* cache, const void* q, int32_
   if (workspace_bytes < w.total) return KVQ_ENOSPACE;
   const int G = w.G;
   const int ngv = D / vgroup;
+  const bool dense = dense_mq(cache, gkv, n_q);
   const int rows = 2 * G * ngv;  // PV rows: (hi/lo part, value group, row)
-  if (rows > 32) return KVQ_ENOTSUP;
+  if (rows > 32 && !dense) return KVQ_ENOTSUP;
   const int NP = rows > 16 ? 2 : 1;
   if (units_bound(cache, max_tokens) * w.nqb * 64 >= (1L << 31)) return KVQ_ENOTSUP;
 
@@ -447,6 +475,10 @@ kvq_status kvq_decode_attention_mq(const kvq_cache* cache, const void* q, int32_
   const hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
   const bool asym = cache->fmt.k.scheme == KVQ_ASYM;
+  if (dense) {
+    e = launch_decode_dense(p, cache->fmt.k.bits, asym, st);
+    return e == hipSuccess ? KVQ_OK : KVQ_ELAUNCH;
+  }
   if (mixed_format(cache->fmt)) {
     if (n_q > 1) return KVQ_ENOTSUP;  // multi-query decode: keys and values in one format only
     const int vb = cache->fmt.v.bits, vs = cache->fmt.v.scheme;

@@ -26,7 +26,7 @@ static void fail(const char* what) {
 
 static hipError_t check_decode(const DecodeParams& p, int G, int NP) {
   g_launches++;
-  if (G < 1 || G > 8 || (NP != 1 && NP != 2)) fail("decode G / NP");
+  if (G < 1 || G > 16 || (G > 8 && G != 16) || (NP != 1 && NP != 2)) fail("decode G / NP");
   if (p.nblocks < 1) fail("decode nblocks");
   const char* pre_end = reinterpret_cast<const char*>(p.ws_pre + p.c.B + 2);
   const char* part = reinterpret_cast<const char*>(p.ws_part);
@@ -61,6 +61,12 @@ KVQ_MIX(launch_decode_mixed_k4a)
 KVQ_MIX(launch_decode_mixed_k8s)
 KVQ_MIX(launch_decode_mixed_k8a)
 #undef KVQ_MIX
+hipError_t launch_decode_dense(const DecodeParams& p, int bits, bool, hipStream_t) {
+  if (bits != 2 && bits != 4 && bits != 8) fail("dense bits");
+  if (p.qpw != 4 || p.qbs * p.gkv != 16) fail("dense query blocks");
+  if (p.c.k.group != 64 && p.c.k.group != 128) fail("dense key group");
+  return check_decode(p, 16, 1);
+}
 
 hipError_t launch_append(const CacheDev& c, const uint16_t*, const uint16_t*, int n_new, int mode,
                          hipStream_t) {

@@ -159,17 +159,32 @@ def test_binding_refuses_to_run_without_library(tmp_path, monkeypatch):
     importlib.reload(mod)
 
 
-def test_multi_query_workspace_grows_with_the_blocks_a_segment_holds(K):
+def test_multi_query_workspace_grows_with_the_blocks_a_segment_holds(K, monkeypatch):
     """Multi-query decode sizes its partial slots by the query blocks one segment holds: one
     block (the waves interleave its units), two blocks of two waves, or four of one wave each.
-    Per workgroup a slot pair holds qpw x G rows of 132 floats."""
+    Per workgroup a slot pair holds qpw x G rows of 132 floats.  With 64 or more query rows per
+    kv head the dense kernel takes the call: four blocks of 16 rows (from 16 rows on when
+    KVQ_MQ_DENSE=1 forces it)."""
     L = K.lib
     d = fake_cache(K)  # INT4 group 64, H_kv = 2, GQA-4 with 8 query heads: G = 8 rows per block
     one = L.kvq_decode_workspace_bytes(ctypes.byref(d), 8, 1000)
     assert L.kvq_decode_workspace_bytes_mq(ctypes.byref(d), 8, 1, 1000) == one
-    sizes = {nq: L.kvq_decode_workspace_bytes_mq(ctypes.byref(d), 8, nq, 1000)
-             for nq in (2, 4, 6, 8, 16)}
-    assert all(v > 0 for v in sizes.values())
-    # n_q = 2 is one block of two tokens; 4 and 6 are two or three blocks (two per segment),
-    # 8 and 16 four or more (four per segment): the per-workgroup slots grow 1 : 2 : 4
-    assert sizes[4] > sizes[2] and sizes[8] > sizes[4]
+
+    def sizes():
+        s = {nq: L.kvq_decode_workspace_bytes_mq(ctypes.byref(d), 8, nq, 1000) for nq in (2, 4, 6, 8, 16)}
+        assert all(v > 0 for v in s.values())
+        return s
+    # blocked kernel: 2 is one block of two tokens, 4 and 6 two or three blocks (two per
+    # segment), 8 four blocks (four per segment): the per-workgroup slots grow 1 : 2 : 4
+    monkeypatch.setenv("KVQ_MQ_DENSE", "0")
+    off = sizes()
+    assert off[4] > off[2] and off[8] > off[4]
+    # by default n_q = 16 (64 rows) is dense: four 16-row blocks per workgroup, twice the rows of
+    # the blocked kernel's four 8-row blocks
+    monkeypatch.delenv("KVQ_MQ_DENSE")
+    auto = sizes()
+    assert all(auto[nq] == off[nq] for nq in (2, 4, 6, 8)) and off[8] < auto[16] < 2 * off[8]
+    # forced from 16 rows (n_q = 4) on
+    monkeypatch.setenv("KVQ_MQ_DENSE", "1")
+    forced = sizes()
+    assert forced[2] == off[2] and forced[4] == forced[6] == forced[8] == forced[16] == auto[16]

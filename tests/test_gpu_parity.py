@@ -349,14 +349,25 @@ MQ_CASES = [
     ("mq-int4-gqa4-two-blocks", SYM4, SYM4, 2, 8, 2, 32, [777, 190], False, 4),
     ("mq-kivi-int2-three-blocks", KPC2, ASYM2_32, 2, 8, 2, 128, [700, 1300], False, 3),
     ("mq-asym4-paged-two-blocks", ASYM4_32, ASYM4_32, 2, 4, 2, 16, [250, 999], True, 3),
+    # the dense kernel: 16 query rows per wave, four blocks per workgroup (key groups of 64 or
+    # 128); it takes 64 or more rows per kv head by itself, and these cases force it from 16 rows
+    # on (KVQ_MQ_DENSE=1) for idle waves, partial blocks and segments split over workgroups
+    ("mq-dense-asym4-g64-gqa4", (4, 1, 0, 64), (4, 1, 0, 64), 2, 8, 2, 32, [600, 130], False, 8),
+    ("mq-dense-int8-mha-paged", SYM8, SYM8, 2, 2, 2, 16, [500, 77], True, 16),
+    ("mq-dense-int2-g64-gqa8", (2, 0, 0, 64), (2, 0, 0, 64), 1, 16, 2, 0, [900], False, 4),
+    ("mq-dense-asym8-gqa2-long", (8, 1, 0, 128), (8, 1, 0, 128), 1, 4, 2, 128, [3000], False, 32),
+    ("mq-dense-int4-gqa4-two-segments", SYM4, SYM4, 2, 8, 2, 0, [700, 1500], False, 24),
+    ("mq-dense-asym2-g64-paged-window", (2, 1, 0, 64), (2, 1, 0, 64), 2, 8, 2, 64, [333, 1100], True, 5),
 ]
 
 
 @pytest.mark.parametrize("name,k,v,B,Hq,H,R,lens,paged,nq", MQ_CASES, ids=[c[0] for c in MQ_CASES])
-def test_multi_query_decode(name, k, v, B, Hq, H, R, lens, paged, nq):
+def test_multi_query_decode(name, k, v, B, Hq, H, R, lens, paged, nq, monkeypatch):
     """Multi-query decode: append the n_q query tokens (single-token steps, so windows flush
     where due), then attend with each query seeing the tokens up to its own."""
     announce(test="multi_query", name=name)
+    if name.startswith("mq-dense"):
+        monkeypatch.setenv("KVQ_MQ_DENSE", "1")
     pr = kc.build_pair(k, v, B, Hq, H, R, lens, paged=paged, seed=zlib.crc32(name.encode()) % 1000,
                        extra_tokens=64 + nq)
     for _ in range(nq):
