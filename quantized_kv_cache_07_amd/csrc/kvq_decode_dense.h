@@ -36,17 +36,20 @@ struct DenseLds {
   static constexpr int ustat = qs + 4 * DROWS * D * 2;           // [WAVES][3] int
   static constexpr int qe = ustat + WAVES * 3 * 4;               // [4][16] int
   static constexpr int pre = qe + 4 * DROWS * 4;                 // [B + 1] int
-  // a unit's value operands, dequantized once per workgroup: [2 units][8 products][64 lanes]
-  // x 16 bytes, in the merge rows (which hold nothing while units stream)
+  // a unit's operands, unpacked once per workgroup, in the merge rows (which hold nothing while
+  // units stream): values dequantized [2 units][8 products][64 lanes] x 16 bytes, then raw key
+  // codes [2 units][2 tiles][4 key slices][64 lanes] x 16 bytes
   static constexpr int vbuf = red;
+  static constexpr int kbuf = red + 2 * 8 * 64 * 16;
   __host__ __device__ static size_t cnt(int B) { return static_cast<size_t>(pre) + 4 * static_cast<size_t>(B + 1); }
   static size_t bytes(int B) { return cnt(B) + 8 * static_cast<size_t>(B); }
 };
-static_assert(WAVES * 16 * RED_STRIDE * 4 >= 2 * 8 * 64 * 16, "value operands fit the merge rows");
+static_assert(WAVES * 16 * RED_STRIDE * 4 >= 2 * (8 + 8) * 64 * 16, "unit operands fit the merge rows");
 
-// Code words of a value chunk that wave w dequantizes: products 2 w and 2 w + 1 use pairs
-// 4 w .. 4 w + 3 of each tile, i.e. words 2 w, 2 w + 1 of 8-bit chunks, word w of 4-bit chunks
-// and half of word w / 2 of 2-bit chunks (the wave shifts odd halves down by 8 bits).
+// Code words of a value chunk (or key slice) that wave w unpacks: pairs 4 w .. 4 w + 3, i.e.
+// words 2 w, 2 w + 1 of 8-bit codes, word w of 4-bit codes and half of word w / 2 of 2-bit codes
+// (the wave shifts odd halves down by 8 bits); value products 2 w and 2 w + 1 use these pairs,
+// and so does the part of a key slice that lane group w of a QK product takes.
 template <int KB>
 constexpr int vwords() { return KB == 8 ? 2 : 1; }
 template <int KB>
@@ -68,9 +71,11 @@ __device__ __forceinline__ void load_vwords(rsrc_t r, unsigned off, int w, uint3
 }
 
 // KB: code bits of keys and values (the same format on both sides); SCH: KVQ_SYM or KVQ_ASYM;
-// NGK: key groups per row (1: groups of 128 channels, 2: groups of 64).
+// NGK: key groups per row (1: groups of 128 channels, 2: groups of 64).  Three workgroups per
+// CU for 4- and 8-bit codes (168 VGPRs; the few spills the compiler makes fall outside the unit
+// loop, and 16 queries ran 7-19% faster than at two), two for 2-bit codes (three ran 6% slower).
 template <int KB, int SCH, int NGK>
-__global__ __launch_bounds__(256, 2) void dense_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256, KB == 2 ? 2 : 3) void dense_kernel(DecodeParams p) {
   constexpr int G = DROWS;
   constexpr int qpw = 4;  // query blocks per segment, one per wave
   constexpr bool ASYM = SCH == KVQ_ASYM;
@@ -184,10 +189,11 @@ __global__ __launch_bounds__(256, 2) void dense_kernel(DecodeParams p) {
   constexpr float off = ASYM ? 0.0f : static_cast<float>(1 << (KB - 1));
   constexpr long TILE_BYTES = static_cast<long>(TILE) * D * KB / 8;
   constexpr unsigned SP = (4 * KB < 16) ? 4 * KB : 16;  // bytes of a slice piece
-  const unsigned k_lane = SP * (4 * n + g);             // key slice 4 n + g: token n, channels 32 g ..
+  // key slice 4 n + g (token n, channels 32 g ..): the words this wave unpacks for lane group
+  // `wave` of QK product g
+  const unsigned kw_lane = SP * (4 * n + g) + vword_off<KB>(wave);
   // value chunk 16 g + n (tokens 4 g .., channels 8 n ..): the words this wave dequantizes
   const unsigned vw_lane = SP * (16 * g + n) + vword_off<KB>(wave);
-  const int kgl = (32 * g) / kgroup;                    // key group of this lane's channels
   const unsigned vs_lane = ((8 * n) / vgroup) * TILE + 4 * g;  // value scale row of this lane
   const int qi = wave;
   const UnpackRegs ur = unpack_regs<KB>();
@@ -249,13 +255,15 @@ __global__ __launch_bounds__(256, 2) void dense_kernel(DecodeParams p) {
       return blk * H + h;
     };
     constexpr int VW = vwords<KB>();
-    uint32_t kw[2][KB], vw[2][VW];
+    uint32_t kw[2][VW], vw[2][VW];
     uint2 ks[NGK][2], kz[NGK][2], vsc[2], vz[2];
     auto load_k = [&](int pA, int pB) {
+      load_vwords<KB>(buf(c.kc + static_cast<size_t>(max(pA, 0)) * TILE_BYTES), kw_lane, wave, kw[0]);
+      load_vwords<KB>(buf(c.kc + static_cast<size_t>(max(pB, 0)) * TILE_BYTES), kw_lane, wave, kw[1]);
+    };
+    auto load_ks = [&](int pA, int pB) {  // key scales (and zero-points): the scores only
       pA = max(pA, 0);
       pB = max(pB, 0);
-      load_words<KB>(buf(c.kc + static_cast<size_t>(pA) * TILE_BYTES), k_lane, kw[0]);
-      load_words<KB>(buf(c.kc + static_cast<size_t>(pB) * TILE_BYTES), k_lane, kw[1]);
 #pragma unroll
       for (int t = 0; t < 2; t++) {
         const size_t tb = static_cast<size_t>(t ? pB : pA) * c.ks_tile;
@@ -292,7 +300,8 @@ __global__ __launch_bounds__(256, 2) void dense_kernel(DecodeParams p) {
     int pA = -1, pB = -1, nA = -1, nB = -1;  // tiles of units x and x + 1
     if (x < xq_end) {
       tiles_of(x, pA, pB);
-      if (active) load_k(pA, pB);
+      load_k(pA, pB);
+      if (active) load_ks(pA, pB);
       load_v(pA, pB);
       if (x + 1 < xq_end) tiles_of(x + 1, nA, nB);
     }
@@ -323,39 +332,39 @@ __global__ __launch_bounds__(256, 2) void dense_kernel(DecodeParams p) {
     const float sl2 = p.sm_log2 * exp2i(qe_n);
     const uint16_t* qrow = qs + (qi * G + n) * D;
 
-    // ---- QK operands: the row's query, prescaled, divided by each field's alpha, masked to
-    // key group gi; every tile's accumulator starts at minus the group's raw-code bias ----
-    f16x8 qb[NGK][4];
+    // ---- QK operands: product j takes key slice j (channels 32 j .. 32 j + 31, one key group),
+    // lane group g its pairs 4 g .. 4 g + 3; the row's query over the same channels, prescaled and
+    // divided by each field's alpha.  Every tile's accumulator for group gi starts at minus the
+    // group's raw-code bias. ----
+    f16x8 qn[4];
     f32x4 dq0[NGK];
     float qsum[NGK];  // asymmetric keys: sum of the prescaled query over the group's channels
 #pragma unroll
     for (int gi = 0; gi < NGK; gi++) {
       qsum[gi] = 0.0f;
       dq0[gi] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const bool in_grp = kgl == gi;
+    }
+    f16x8 bias;
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const u16x8 raw = gather_kchan<KB>(qrow + 32 * g, j);
+    for (int i = 0; i < 8; i++)
+      bias[i] = static_cast<_Float16>(-(1024.0f + static_cast<float>(pair_alpha<KB>(i / 2)) * off));
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-          const float xq = in_grp ? bf16_to_f32(raw[i]) * qsc : 0.0f;
-          qb[gi][j][i] = static_cast<_Float16>(xq * (1.0f / static_cast<float>(kelem_alpha<KB>(j, i))));
-          if constexpr (ASYM) qsum[gi] += xq;
-        }
+    for (int j = 0; j < 4; j++) {
+      const int gi = j / (4 / NGK);
+      const u16x8 raw = gather_kchan<KB>(qrow + 32 * j, g);
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const float xq = bf16_to_f32(raw[i]) * qsc;
+        qn[j][i] = static_cast<_Float16>(xq * (1.0f / static_cast<float>(pair_alpha<KB>(i / 2))));
+        if constexpr (ASYM) qsum[gi] += xq;
       }
-      if constexpr (ASYM) {
+      dq0[gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bias, qn[j], dq0[gi], 0, 0, 0);
+    }
+    if constexpr (ASYM) {
+#pragma unroll
+      for (int gi = 0; gi < NGK; gi++) {
         qsum[gi] += __shfl_xor(qsum[gi], 16);
         qsum[gi] += __shfl_xor(qsum[gi], 32);
-      }
-      if (gi < ngk) {
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          f16x8 bias;
-#pragma unroll
-          for (int i = 0; i < 8; i++)
-            bias[i] = static_cast<_Float16>(-(1024.0f + static_cast<float>(kelem_alpha<KB>(j, i)) * off));
-          dq0[gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bias, qb[gi][j], dq0[gi], 0, 0, 0);
-        }
       }
     }
 
@@ -456,6 +465,14 @@ __global__ __launch_bounds__(256, 2) void dense_kernel(DecodeParams p) {
         vbuf[((y & 1) * 8 + 2 * wave + jj) * 64 + lane] = uint4{vbw[0], vbw[1], vbw[2], vbw[3]};
       }
     };
+    // unit y's raw key codes to LDS buffer y & 1: this wave's part (lane group `wave`) of key slice
+    // 4 n + g of each tile, as QK product g's operand for token n
+    uint4* kbuf = reinterpret_cast<uint4*>(smem + DenseLds::kbuf);
+    auto put_keys = [&](int y) {
+#pragma unroll
+      for (int t = 0; t < 2; t++)
+        kbuf[(((y & 1) * 2 + t) * 4 + g) * 64 + 16 * wave + n] = __builtin_bit_cast(uint4, kop_raw<KB>(kw[t], 0, ur));
+    };
     if (x < xq_end) {
       bool bad_block = false;
       for (; x < xq_end; x++) {
@@ -463,15 +480,25 @@ __global__ __launch_bounds__(256, 2) void dense_kernel(DecodeParams p) {
         int nvA, nvB;
         valid_of(x, pA, pB, nvA, nvB);
         bad_block |= pA < 0 || (32 * x + 16 < nq && pB < 0);
+        put_keys(x);
         put_values(x, nvA, nvB);
         int nnA = -1, nnB = -1;  // tiles of unit x + 2
         if (x + 2 < xq_end) tiles_of(x + 2, nnA, nnB);
-        if (more) load_v(nA, nB);  // value registers are free again
+        if (more) {  // code registers are free again
+          load_k(nA, nB);
+          load_v(nA, nB);
+        }
+        // every wave's quarter of unit x is in LDS (and every wave is done reading unit x - 1's)
+        __syncthreads();
 
         f16x8 pa;
         if (active) {
-          // QK^T: one accumulator per (tile, key group), the four chains interleaved; stand-in
-          // tiles are masked by the softmax
+          // QK^T: one accumulator per (tile, key group); stand-in tiles are masked by the softmax
+          uint4 kop[2][4];
+#pragma unroll
+          for (int t = 0; t < 2; t++)
+#pragma unroll
+            for (int j = 0; j < 4; j++) kop[t][j] = kbuf[(((x & 1) * 2 + t) * 4 + j) * 64 + lane];
           f32x4 dq[2][NGK];
 #pragma unroll
           for (int t = 0; t < 2; t++)
@@ -481,10 +508,8 @@ __global__ __launch_bounds__(256, 2) void dense_kernel(DecodeParams p) {
           for (int j = 0; j < 4; j++)
 #pragma unroll
             for (int t = 0; t < 2; t++) {
-              const f16x8 kop = kop_raw<KB>(kw[t], j, ur);
-#pragma unroll
-              for (int gi = 0; gi < NGK; gi++)
-                if (gi < ngk) dq[t][gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qb[gi][j], dq[t][gi], 0, 0, 0);
+              const int gi = j / (4 / NGK);
+              dq[t][gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, kop[t][j]), qn[j], dq[t][gi], 0, 0, 0);
             }
           float s2[8];
 #pragma unroll
@@ -506,7 +531,7 @@ __global__ __launch_bounds__(256, 2) void dense_kernel(DecodeParams p) {
               }
             }
           }
-          if (more) load_k(nA, nB);  // key registers are free again
+          if (more) load_ks(nA, nB);  // scale registers are free again
           softmax(s2, nvA, nvB, 32 * x, sl2);
 
           // P: the weights as f16 (element i: token 4 g + i % 4 of tile i / 4)
@@ -517,8 +542,6 @@ __global__ __launch_bounds__(256, 2) void dense_kernel(DecodeParams p) {
             pa[2 * i + 1] = w2[1];
           }
         }
-        // every wave's quarter of unit x is in LDS (and every wave is done reading unit x - 1's)
-        __syncthreads();
         if (active) {
           uint4 vop[8];
 #pragma unroll
