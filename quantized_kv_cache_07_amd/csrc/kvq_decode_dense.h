@@ -7,18 +7,20 @@
 //   Quantization in Practice", "Misconception 1"), then the BF16 window.
 //
 // For integer caches with per-token key groups of 64 or 128 channels and n_q x (query heads per
-// kv head) >= 16.  A query block is 16 rows (query tokens x GQA heads); a workgroup's four waves
-// take four blocks of one (sequence, kv head) and walk the same units, so the codes stream once
-// for up to 64 rows.  Per wave and unit (32 tokens):
-//   QK^T  the key codes enter as raw f16 (1024 + alpha u, one and-or per pair) against the 16
-//         query rows, one accumulator per key group (the query operand masked to the group's
-//         channels), the bias removed by the accumulator start; the scores are the group sums
-//         times each token's group scale: exact products, as in the single-query kernel.
-//   PV    P = the 16 rows' weights as f16; the value codes are dequantized to f16 in registers,
-//         s (u - off) 2^-8 (or s u + z), one subtraction and one multiply (or fma) per two codes
-//         after the raw-form unpack.  Rounding w and v to f16 (11 bits) keeps the output within
-//         the pages' tolerance; the 2^-8 keeps every finite fp16 scale times a code below the
-//         f16 limit and is removed before the window rows add true values.
+// kv head) >= 16 (the host takes it from 64).  A query block is 16 rows (query tokens x GQA
+// heads); a workgroup's four waves take four blocks of one (sequence, kv head) and walk the same
+// units, so the codes stream once for up to 64 rows.  Per unit (32 tokens) each wave unpacks a
+// quarter of the unit's operands into LDS, one barrier, then every wave reads all of them:
+//   QK^T  raw key codes as f16 (1024 + alpha u, one and-or per pair), re-ordered so that product
+//         j takes key slice j (channels 32 j .. 32 j + 31, inside one key group), against the 16
+//         query rows divided by alpha; the bias is removed by the accumulator start and each
+//         group's sum is multiplied by the token's group scale: exact products, as in the
+//         single-query kernel.
+//   PV    P = the 16 rows' weights as f16; the values dequantized to f16, s (u - off) 2^-8 (or
+//         (s u + z) 2^-8), one subtraction and one multiply (or fma) per two codes after the
+//         raw-form unpack.  Rounding w and v to f16 (11 bits) keeps the output within the
+//         pages' tolerance; the 2^-8 keeps every finite fp16 scale times a code below the f16
+//         limit and is removed before the window rows add true values.
 // Split segments leave partials for combine_kernel, as in the single-query kernel.
 #pragma once
 
@@ -58,16 +60,27 @@ __device__ __forceinline__ unsigned vword_off(int w) {
   else if constexpr (KB == 4) return 4u * w;
   else return 4u * (w / 2);
 }
+// The words at byte voff + soff of resource r (soff: the tile's byte offset, wave-uniform).
 template <int KB>
-__device__ __forceinline__ void load_vwords(rsrc_t r, unsigned off, int w, uint32_t (&x)[vwords<KB>()]) {
+__device__ __forceinline__ void load_vwords(rsrc_t r, unsigned voff, int soff, uint32_t (&x)[vwords<KB>()]) {
   if constexpr (KB == 8) {
-    const uint2 a = bld2(r, off);
+    const uint2 a = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, BUF_NT));
     x[0] = a.x;
     x[1] = a.y;
   } else {
-    x[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, BUF_NT);
-    if constexpr (KB == 2) x[0] >>= 8 * (w & 1);
+    x[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, BUF_NT);
   }
+}
+// The loaded words of wave w as the array rawpair() indexes: 2-bit codes of an odd wave are the
+// upper halves' fields, shifted down here (at use, not at the load, which would wait for it).
+template <int KB>
+__device__ __forceinline__ void vwords_at_use(const uint32_t (&x)[vwords<KB>()], int w, uint32_t (&y)[vwords<KB>()]) {
+#pragma unroll
+  for (int i = 0; i < vwords<KB>(); i++) y[i] = (KB == 2) ? x[i] >> (8 * (w & 1)) : x[i];
+}
+// 8 bytes of scale (or zero-point) rows at byte voff + soff of resource r
+__device__ __forceinline__ uint2 ld_rows(rsrc_t r, unsigned voff, int soff) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
 }
 
 // KB: code bits of keys and values (the same format on both sides); SCH: KVQ_SYM or KVQ_ASYM;
@@ -184,7 +197,6 @@ __global__ __launch_bounds__(256, KB == 2 ? 2 : 3) void dense_kernel(DecodeParam
     return;
   }
 
-  constexpr int kgroup = D / NGK, ngk = NGK;
   const int vgroup = c.v.group;
   constexpr float off = ASYM ? 0.0f : static_cast<float>(1 << (KB - 1));
   constexpr long TILE_BYTES = static_cast<long>(TILE) * D * KB / 8;
@@ -246,10 +258,20 @@ __global__ __launch_bounds__(256, KB == 2 ? 2 : 3) void dense_kernel(DecodeParam
     int x = ku;
     const int xq_end = min(xend, uq);
 
-    const int seq_tile0 = (b * H + h) * (c.cap / TILE);
+    // Tiles are addressed from a base per segment: the sequence's first tile (contiguous) or the
+    // pool's (paged), one buffer resource per array, and a tile's byte offset from that base as the
+    // load's scalar offset (the host admits only caches whose offsets stay below 2^31).
     const int* trow = c.table ? c.table + static_cast<size_t>(b) * c.max_blocks : nullptr;
+    const size_t tile_base = trow ? 0 : static_cast<size_t>(b * H + h) * (c.cap / TILE);
+    const rsrc_t rK = buf(c.kc + tile_base * TILE_BYTES);
+    const rsrc_t rV = buf(c.vc + tile_base * TILE_BYTES);
+    const rsrc_t rS = buf(c.ks + tile_base * c.ks_tile);  // key rows, then value rows, per tile
+    const rsrc_t rZ = buf(ASYM ? c.kz + tile_base * c.ks_tile : c.ks);
+    const int rec_bytes = 2 * c.ks_tile;
+    const unsigned vrow_off = static_cast<unsigned>(c.vs - c.ks) * 2;  // value rows in the record
+    // tile index from the base (-1: an unusable table entry)
     auto phys_of = [&](int t) -> int {
-      if (!trow) return seq_tile0 + t;
+      if (!trow) return t;
       const int blk = ld_uniform(trow + t);
       if (blk < 0 || blk >= c.num_blocks) return -1;
       return blk * H + h;
@@ -258,34 +280,28 @@ __global__ __launch_bounds__(256, KB == 2 ? 2 : 3) void dense_kernel(DecodeParam
     uint32_t kw[2][VW], vw[2][VW];
     uint2 ks[NGK][2], kz[NGK][2], vsc[2], vz[2];
     auto load_k = [&](int pA, int pB) {
-      load_vwords<KB>(buf(c.kc + static_cast<size_t>(max(pA, 0)) * TILE_BYTES), kw_lane, wave, kw[0]);
-      load_vwords<KB>(buf(c.kc + static_cast<size_t>(max(pB, 0)) * TILE_BYTES), kw_lane, wave, kw[1]);
+      load_vwords<KB>(rK, kw_lane, max(pA, 0) * static_cast<int>(TILE_BYTES), kw[0]);
+      load_vwords<KB>(rK, kw_lane, max(pB, 0) * static_cast<int>(TILE_BYTES), kw[1]);
     };
     auto load_ks = [&](int pA, int pB) {  // key scales (and zero-points): the scores only
-      pA = max(pA, 0);
-      pB = max(pB, 0);
 #pragma unroll
       for (int t = 0; t < 2; t++) {
-        const size_t tb = static_cast<size_t>(t ? pB : pA) * c.ks_tile;
+        const int so = max(t ? pB : pA, 0) * rec_bytes;
 #pragma unroll
         for (int gi = 0; gi < NGK; gi++) {
-          if (gi < ngk) {
-            ks[gi][t] = bld2<0>(buf(c.ks + tb), 2 * (gi * TILE + 4 * g));
-            if constexpr (ASYM) kz[gi][t] = bld2<0>(buf(c.kz + tb), 2 * (gi * TILE + 4 * g));
-          }
+          ks[gi][t] = ld_rows(rS, 2 * (gi * TILE + 4 * g), so);
+          if constexpr (ASYM) kz[gi][t] = ld_rows(rZ, 2 * (gi * TILE + 4 * g), so);
         }
       }
     };
     auto load_v = [&](int pA, int pB) {
-      pA = max(pA, 0);
-      pB = max(pB, 0);
-      load_vwords<KB>(buf(c.vc + static_cast<size_t>(pA) * TILE_BYTES), vw_lane, wave, vw[0]);
-      load_vwords<KB>(buf(c.vc + static_cast<size_t>(pB) * TILE_BYTES), vw_lane, wave, vw[1]);
+      load_vwords<KB>(rV, vw_lane, max(pA, 0) * static_cast<int>(TILE_BYTES), vw[0]);
+      load_vwords<KB>(rV, vw_lane, max(pB, 0) * static_cast<int>(TILE_BYTES), vw[1]);
 #pragma unroll
       for (int t = 0; t < 2; t++) {
-        const size_t tb = static_cast<size_t>(t ? pB : pA) * c.vs_tile;
-        vsc[t] = bld2<0>(buf(c.vs + tb), 2 * vs_lane);
-        if constexpr (ASYM) vz[t] = bld2<0>(buf(c.vz + tb), 2 * vs_lane);
+        const int so = max(t ? pB : pA, 0) * rec_bytes;
+        vsc[t] = ld_rows(rS, vrow_off + 2 * vs_lane, so);
+        if constexpr (ASYM) vz[t] = ld_rows(rZ, vrow_off + 2 * vs_lane, so);
       }
     };
     // tiles of unit y, and how many of their tokens are valid (0 for a bad block entry)
@@ -435,6 +451,9 @@ __global__ __launch_bounds__(256, KB == 2 ? 2 : 3) void dense_kernel(DecodeParam
           if constexpr (ASYM) zvb[q] &= keep;
         }
       }
+      uint32_t vu[2][VW];
+      vwords_at_use<KB>(vw[0], wave, vu[0]);
+      vwords_at_use<KB>(vw[1], wave, vu[1]);
       f16x2 sv[4], zv2[4];
       const f16x2 k8 = h2s(0x1p-8f);
 #pragma unroll
@@ -449,7 +468,7 @@ __global__ __launch_bounds__(256, KB == 2 ? 2 : 3) void dense_kernel(DecodeParam
         for (int q = 0; q < 4; q++) {
           // q = 2 t + (pair parity): tile t, the wave's pair 2 jj + q % 2
           const int t = q / 2, pr = 2 * jj + (q % 2);
-          const f16x2 raw = as_h2(rawpair<KB>(vw[t], pr, ur));
+          const f16x2 raw = as_h2(rawpair<KB>(vu[t], pr, ur));
           const float a0 = static_cast<float>(pair_alpha<KB>(pr));
           const f16x2 inva = h2s(1.0f / a0);
           f16x2 v2;
@@ -470,8 +489,11 @@ __global__ __launch_bounds__(256, KB == 2 ? 2 : 3) void dense_kernel(DecodeParam
     uint4* kbuf = reinterpret_cast<uint4*>(smem + DenseLds::kbuf);
     auto put_keys = [&](int y) {
 #pragma unroll
-      for (int t = 0; t < 2; t++)
-        kbuf[(((y & 1) * 2 + t) * 4 + g) * 64 + 16 * wave + n] = __builtin_bit_cast(uint4, kop_raw<KB>(kw[t], 0, ur));
+      for (int t = 0; t < 2; t++) {
+        uint32_t ku[VW];
+        vwords_at_use<KB>(kw[t], wave, ku);
+        kbuf[(((y & 1) * 2 + t) * 4 + g) * 64 + 16 * wave + n] = __builtin_bit_cast(uint4, kop_raw<KB>(ku, 0, ur));
+      }
     };
     if (x < xq_end) {
       bool bad_block = false;
@@ -518,7 +540,6 @@ __global__ __launch_bounds__(256, KB == 2 ? 2 : 3) void dense_kernel(DecodeParam
             for (int r = 0; r < 4; r++) s2[4 * t + r] = 0.0f;
 #pragma unroll
             for (int gi = 0; gi < NGK; gi++) {
-              if (gi >= ngk) continue;
               const uint2 k2 = ks[gi][t];
               const float sc[4] = {f16_lo(k2.x), f16_hi(k2.x), f16_lo(k2.y), f16_hi(k2.y)};
 #pragma unroll

@@ -198,8 +198,9 @@ int device_cus();
 // Multi-query decode takes the dense kernel (16 query rows per wave, the four waves of a
 // workgroup on four blocks of one (sequence, kv head), values dequantized once per workgroup)
 // for integer caches with the same format on both sides and per-token key groups of 64 or 128
-// channels, once the query rows of a kv head fill its four blocks (n_q x GQA heads >= 64): with
-// fewer rows its idle waves cost as much as busy ones and the blocked kernel is faster.
+// channels whose tiles lie within 2 GiB of their base, once the query rows of a kv head fill its
+// four blocks (n_q x GQA heads >= 64): with fewer rows its idle waves cost as much as busy ones
+// and the blocked kernel is faster.
 // KVQ_MQ_DENSE=0 turns it off, KVQ_MQ_DENSE=1 takes it from 16 rows on.
 bool dense_mq(const kvq_cache* c, int gkv, int n_q) {
   const kvq_side& k = c->fmt.k;
@@ -210,6 +211,13 @@ bool dense_mq(const kvq_cache* c, int gkv, int n_q) {
   if (k.bits != v.bits || k.scheme != v.scheme) return false;
   if (k.axis != KVQ_PER_TOKEN || v.axis != KVQ_PER_TOKEN) return false;
   if (k.group != 64 && k.group != 128) return false;
+  // tiles are addressed by 31-bit byte offsets from the sequence's first tile (contiguous) or
+  // the pool's (paged)
+  const long tiles = c->block_table ? static_cast<long>(c->num_blocks) * c->n_kv_heads
+                                    : c->capacity / TILE;
+  const long rec = 2L * (D / k.group + D / v.group) * TILE;  // bytes of a tile's scale record
+  if (tiles * (static_cast<long>(TILE) * D * k.bits / 8) >= (1L << 31) || tiles * rec >= (1L << 31))
+    return false;
   int rows_min = 64;
   if (const char* e = std::getenv("KVQ_MQ_DENSE")) {
     if (e[0] == '0') return false;
