@@ -6,8 +6,8 @@
 //   compressed tokens dequantized in registers as they stream in (P3 = oh-bug.com "KV Cache
 //   Quantization in Practice", "Misconception 1"), then the BF16 window.
 //
-// For integer caches with per-token key groups of 64 or 128 channels and n_q x (query heads per
-// kv head) >= 16 (the host takes it from 64).  A query block is 16 rows (query tokens x GQA
+// For integer caches with per-token key groups of 32, 64 or 128 channels and n_q x (query heads
+// per kv head) >= 16 (the host takes it from 64).  A query block is 16 rows (query tokens x GQA
 // heads); a workgroup's four waves take four blocks of one (sequence, kv head) and walk the same
 // units, so the codes stream once for up to 64 rows.  Per unit (32 tokens) each wave unpacks a
 // quarter of the unit's operands into LDS, one barrier, then every wave reads all of them:
@@ -84,11 +84,12 @@ __device__ __forceinline__ uint2 ld_rows(rsrc_t r, unsigned voff, int soff) {
 }
 
 // KB: code bits of keys and values (the same format on both sides); SCH: KVQ_SYM or KVQ_ASYM;
-// NGK: key groups per row (1: groups of 128 channels, 2: groups of 64).  Three workgroups per
-// CU for 4- and 8-bit codes (168 VGPRs; the few spills the compiler makes fall outside the unit
-// loop, and 16 queries ran 7-19% faster than at two), two for 2-bit codes (three ran 6% slower).
+// NGK: key groups per row (1: groups of 128 channels, 2: of 64, 4: of 32).  Three workgroups per
+// CU for 4- and 8-bit codes in groups of 64 or 128 (168 VGPRs; the few spills the compiler makes
+// fall outside the unit loop, and 16 queries ran 7-19% faster than at two), two for 2-bit codes
+// (three ran 6% slower) and for groups of 32 (four key groups spill heavily at 168).
 template <int KB, int SCH, int NGK>
-__global__ __launch_bounds__(256, KB == 2 ? 2 : 3) void dense_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256, (KB == 2 || NGK == 4) ? 2 : 3) void dense_kernel(DecodeParams p) {
   constexpr int G = DROWS;
   constexpr int qpw = 4;  // query blocks per segment, one per wave
   constexpr bool ASYM = SCH == KVQ_ASYM;

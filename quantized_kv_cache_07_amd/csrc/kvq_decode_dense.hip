@@ -1,6 +1,6 @@
 // kvq_decode_dense.hip -- instantiations of the dense multi-query decode kernel
 // (kvq_decode_dense.h) for 2-, 4- and 8-bit symmetric and asymmetric caches with key groups of
-// 64 or 128 channels.
+// 32, 64 or 128 channels.
 #include "kvq_decode_dense.h"
 
 namespace kvq {
@@ -17,6 +17,7 @@ hipError_t launch_groups(const DecodeParams& p, int bits, bool asym, hipStream_t
 
 hipError_t launch_decode_dense(const DecodeParams& p, int bits, bool asym, hipStream_t s) {
   switch (p.c.k.group) {
+    case 32: return launch_groups<4>(p, bits, asym, s);
     case 64: return launch_groups<2>(p, bits, asym, s);
     case 128: return launch_groups<1>(p, bits, asym, s);
     default: return hipErrorInvalidValue;

@@ -196,12 +196,12 @@ int device_cus();
 // next power of two >= n_q) that keeps the segment within 8 rows, 16 QK columns (one per key
 // group and row) and 32 PV rows (hi / lo part, value group, row).
 // Multi-query decode takes the dense kernel (16 query rows per wave, the four waves of a
-// workgroup on four blocks of one (sequence, kv head), values dequantized once per workgroup)
-// for integer caches with the same format on both sides and per-token key groups of 64 or 128
-// channels whose tiles lie within 2 GiB of their base, once the query rows of a kv head fill its
-// four blocks (n_q x GQA heads >= 64): with fewer rows its idle waves cost as much as busy ones
-// and the blocked kernel is faster.
-// KVQ_MQ_DENSE=0 turns it off, KVQ_MQ_DENSE=1 takes it from 16 rows on.
+// workgroup on four blocks of one (sequence, kv head), keys and values unpacked once per
+// workgroup) for integer caches with the same format on both sides and per-token key groups of
+// 32, 64 or 128 channels whose tiles lie within 2 GiB of their base, once a kv head has query
+// rows for two of its blocks (n_q x GQA heads >= 32; the waves of empty blocks only unpack their
+// share), for 8-bit codes from one block on.  KVQ_MQ_DENSE=0 turns it off, KVQ_MQ_DENSE=1 takes
+// it from 16 rows on.
 bool dense_mq(const kvq_cache* c, int gkv, int n_q) {
   const kvq_side& k = c->fmt.k;
   const kvq_side& v = c->fmt.v;
@@ -210,7 +210,7 @@ bool dense_mq(const kvq_cache* c, int gkv, int n_q) {
   if (k.bits != 2 && k.bits != 4 && k.bits != 8) return false;
   if (k.bits != v.bits || k.scheme != v.scheme) return false;
   if (k.axis != KVQ_PER_TOKEN || v.axis != KVQ_PER_TOKEN) return false;
-  if (k.group != 64 && k.group != 128) return false;
+  if (k.group != 32 && k.group != 64 && k.group != 128) return false;
   // tiles are addressed by 31-bit byte offsets from the sequence's first tile (contiguous) or
   // the pool's (paged)
   const long tiles = c->block_table ? static_cast<long>(c->num_blocks) * c->n_kv_heads
@@ -218,7 +218,12 @@ bool dense_mq(const kvq_cache* c, int gkv, int n_q) {
   const long rec = 2L * (D / k.group + D / v.group) * TILE;  // bytes of a tile's scale record
   if (tiles * (static_cast<long>(TILE) * D * k.bits / 8) >= (1L << 31) || tiles * rec >= (1L << 31))
     return false;
-  int rows_min = 64;
+  // measured on the GQA-4 sweep: from 32 rows the dense kernel beats the blocked one (4-bit
+  // 287 against 326 us, 2-bit group 32 341 against 489 us), 8-bit codes already at 16 (268
+  // against 312 us); formats the blocked kernel cannot serve for this GQA group (more than 16 QK
+  // columns or 32 PV rows per query token) take it from 16 rows on
+  const bool blocked_fits = (D / k.group) * gkv <= 16 && 2 * gkv * (D / v.group) <= 32;
+  int rows_min = (!blocked_fits || k.bits == 8) ? 16 : 32;
   if (const char* e = std::getenv("KVQ_MQ_DENSE")) {
     if (e[0] == '0') return false;
     if (e[0] == '1') rows_min = 16;
@@ -446,13 +451,13 @@ kvq_status kvq_decode_attention_mq(const kvq_cache* cache, const void* q, int32_
   const bool whole_row = cache->fmt.k.scheme == KVQ_FP8 || cache->fmt.k.bits == 16;
   const int kgroup = whole_row ? D : cache->fmt.k.group;
   const int vgroup = whole_row ? D : cache->fmt.v.group;
-  if (!kpc && (D / kgroup) * gkv > 16) return KVQ_ENOTSUP;
+  const bool dense = dense_mq(cache, gkv, n_q);
+  if (!kpc && (D / kgroup) * gkv > 16 && !dense) return KVQ_ENOTSUP;
   if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVQ_EALIGN;
   const WsLayout w = ws_layout(cache, n_q_heads, max_tokens, n_q);
   if (workspace_bytes < w.total) return KVQ_ENOSPACE;
   const int G = w.G;
   const int ngv = D / vgroup;
-  const bool dense = dense_mq(cache, gkv, n_q);
   const int rows = 2 * G * ngv;  // PV rows: (hi/lo part, value group, row)
   if (rows > 32 && !dense) return KVQ_ENOTSUP;
   const int NP = rows > 16 ? 2 : 1;

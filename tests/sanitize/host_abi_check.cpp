@@ -64,7 +64,7 @@ KVQ_MIX(launch_decode_mixed_k8a)
 hipError_t launch_decode_dense(const DecodeParams& p, int bits, bool, hipStream_t) {
   if (bits != 2 && bits != 4 && bits != 8) fail("dense bits");
   if (p.qpw != 4 || p.qbs * p.gkv != 16) fail("dense query blocks");
-  if (p.c.k.group != 64 && p.c.k.group != 128) fail("dense key group");
+  if (p.c.k.group != 32 && p.c.k.group != 64 && p.c.k.group != 128) fail("dense key group");
   return check_decode(p, 16, 1);
 }
 

@@ -162,9 +162,9 @@ def test_binding_refuses_to_run_without_library(tmp_path, monkeypatch):
 def test_multi_query_workspace_grows_with_the_blocks_a_segment_holds(K, monkeypatch):
     """Multi-query decode sizes its partial slots by the query blocks one segment holds: one
     block (the waves interleave its units), two blocks of two waves, or four of one wave each.
-    Per workgroup a slot pair holds qpw x G rows of 132 floats.  With 64 or more query rows per
-    kv head the dense kernel takes the call: four blocks of 16 rows (from 16 rows on when
-    KVQ_MQ_DENSE=1 forces it)."""
+    Per workgroup a slot pair holds qpw x G rows of 132 floats.  With 32 or more query rows per
+    kv head (4-bit codes) the dense kernel takes the call: four blocks of 16 rows (from 16 rows
+    on when KVQ_MQ_DENSE=1 forces it)."""
     L = K.lib
     d = fake_cache(K)  # INT4 group 64, H_kv = 2, GQA-4 with 8 query heads: G = 8 rows per block
     one = L.kvq_decode_workspace_bytes(ctypes.byref(d), 8, 1000)
@@ -179,11 +179,12 @@ def test_multi_query_workspace_grows_with_the_blocks_a_segment_holds(K, monkeypa
     monkeypatch.setenv("KVQ_MQ_DENSE", "0")
     off = sizes()
     assert off[4] > off[2] and off[8] > off[4]
-    # by default n_q = 16 (64 rows) is dense: four 16-row blocks per workgroup, twice the rows of
-    # the blocked kernel's four 8-row blocks
+    # by default n_q = 8 and 16 (32 and 64 rows) are dense: four 16-row blocks per workgroup,
+    # twice the rows of the blocked kernel's four 8-row blocks
     monkeypatch.delenv("KVQ_MQ_DENSE")
     auto = sizes()
-    assert all(auto[nq] == off[nq] for nq in (2, 4, 6, 8)) and off[8] < auto[16] < 2 * off[8]
+    assert all(auto[nq] == off[nq] for nq in (2, 4, 6))
+    assert auto[8] == auto[16] and off[8] < auto[8] < 2 * off[8]
     # forced from 16 rows (n_q = 4) on
     monkeypatch.setenv("KVQ_MQ_DENSE", "1")
     forced = sizes()

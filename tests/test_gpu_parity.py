@@ -358,6 +358,9 @@ MQ_CASES = [
     ("mq-dense-asym8-gqa2-long", (8, 1, 0, 128), (8, 1, 0, 128), 1, 4, 2, 128, [3000], False, 32),
     ("mq-dense-int4-gqa4-two-segments", SYM4, SYM4, 2, 8, 2, 0, [700, 1500], False, 24),
     ("mq-dense-asym2-g64-paged-window", (2, 1, 0, 64), (2, 1, 0, 64), 2, 8, 2, 64, [333, 1100], True, 5),
+    ("mq-dense-int2-g32-gqa4", (2, 0, 0, 32), (2, 0, 0, 32), 2, 8, 2, 0, [900, 260], False, 16),
+    ("mq-dense-asym4-g32-paged-window", (4, 1, 0, 32), (4, 1, 0, 32), 2, 16, 2, 32, [700, 90], True, 4),
+    ("mq-dense-asym8-g32-mha", (8, 1, 0, 32), (8, 1, 0, 32), 1, 2, 2, 0, [1200], False, 17),
 ]
 
 
