@@ -278,17 +278,21 @@ def compare_attention(pr: Pair, q_seed_step: int = 0, max_tokens: int | None = N
     return float(err.max()), got
 
 
-def mq_queries(pr: Pair, n_q: int, q_seed_step: int = 7):
-    """bf16 [B][n_q][H_q][128] queries for the last n_q cached tokens of every sequence."""
+def mq_queries(pr: Pair, n_q: int, q_seed_step: int = 7, q_scale: float = 1.0):
+    """bf16 [B][n_q][H_q][128] queries for the last n_q cached tokens of every sequence (times
+    q_scale, rounded to bf16)."""
     dev = pr.cache.n_quant.device
-    return torch.stack([ki.queries(pr.w, q_seed_step + i, dev) for i in range(n_q)], dim=1).contiguous()
+    return torch.stack([scaled_queries(pr.w, q_seed_step + i, dev, q_scale) for i in range(n_q)],
+                       dim=1).contiguous()
 
 
 def compare_attention_mq(pr: Pair, n_q: int, q_seed_step: int = 7, max_tokens: int | None = None,
-                         workspace: torch.Tensor | None = None):
-    """Multi-query decode of the last n_q cached tokens against the oracle (causal)."""
+                         workspace: torch.Tensor | None = None, q_scale: float = 1.0,
+                         tol_scale: float = 1.0):
+    """Multi-query decode of the last n_q cached tokens against the oracle (causal); q_scale and
+    tol_scale as in compare_attention."""
     K = kvq()
-    q = mq_queries(pr, n_q, q_seed_step)
+    q = mq_queries(pr, n_q, q_seed_step, q_scale)
     mt = max_tokens or max(s.n_quant + s.n_res for s in pr.seqs)
     out, out_big = guarded(torch.full(q.shape, float("nan"), dtype=torch.float32, device=q.device))
     extra = []
@@ -304,8 +308,9 @@ def compare_attention_mq(pr: Pair, n_q: int, q_seed_step: int = 7, max_tokens: i
     got = out.cpu().numpy()
     qb = ki.bf16_bits(q)
     ref = np.stack([s.attend_mq(qb[b], SM_SCALE) for b, s in enumerate(pr.seqs)])
+    assert np.all(np.isfinite(got)), "non-finite multi-query attention output"
     err = np.abs(got - ref)
-    ok = err <= ATOL + RTOL * np.abs(ref)
+    ok = err <= ATOL * tol_scale + RTOL * np.abs(ref)
     assert ok.all(), (f"multi-query attention: {int((~ok).sum())} of {ok.size} outside tolerance; "
                       f"max abs err {err.max():.3e} at {np.unravel_index(err.argmax(), err.shape)}")
     return float(err.max()), got

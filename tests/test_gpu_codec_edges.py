@@ -153,3 +153,50 @@ def test_value_scales_near_fp16_limit(name, k, v, c, off, R, paged):
     vs = (pr.cache.k_scale if shared else pr.cache.v_scale).view(torch.float16).float()
     assert float(vs.abs().max()) > 32768, float(vs.abs().max())
     kc.compare_attention(pr, tol_scale=vmax)
+
+
+DENSE_FORMATS = [
+    # name, k, v, Hq, H, R, lens, paged: formats the dense multi-query kernel serves
+    ("int4-g64-gqa4-window", SYM4, SYM4, 8, 2, 32, [300, 77], False),
+    ("asym4-g32-gqa2-paged", (4, 1, 0, 32), (4, 1, 0, 32), 4, 2, 16, [250, 99], True),
+    ("int8-g128-mha", (8, 0, 0, 128), (8, 0, 0, 128), 2, 2, 0, [200, 33], False),
+    ("int2-g64-gqa8", (2, 0, 0, 64), (2, 0, 0, 64), 16, 2, 16, [260, 50], True),
+]
+
+
+@pytest.mark.parametrize("q_scale", [1e5, 1e-30, 0.0])
+@pytest.mark.parametrize("name,k,v,Hq,H,R,lens,paged", DENSE_FORMATS, ids=[c[0] for c in DENSE_FORMATS])
+def test_dense_multi_query_magnitudes(name, k, v, Hq, H, R, lens, paged, q_scale, monkeypatch):
+    """The dense multi-query kernel (forced from 16 rows) takes the same exact power-of-two query
+    prescale: queries beyond f16 and below it attend like ordinary ones, q = 0 gives the mean of
+    the values visible to each query."""
+    print("case:", name, "dense multi-query q_scale", q_scale, flush=True)
+    monkeypatch.setenv("KVQ_MQ_DENSE", "1")
+    pr = kc.build_pair(k, v, len(lens), Hq, H, R, lens, paged=paged,
+                       seed=zlib.crc32(name.encode()) % 1000)
+    kc.compare_attention_mq(pr, 8, q_scale=q_scale)
+
+
+@pytest.mark.parametrize("name,k,v,c,off,R,paged",
+                         [cse for cse in VALUE_SCALE_CASES if cse[1][2] == 0],
+                         ids=[cse[0] for cse in VALUE_SCALE_CASES if cse[1][2] == 0])
+def test_dense_multi_query_value_scales_near_fp16_limit(name, k, v, c, off, R, paged, monkeypatch):
+    """Value scales near 65504 through the dense multi-query kernel: the values enter its
+    products as s (u - off) 2^-8 (or (s u + z) 2^-8) in f16, which stays finite for every fp16
+    scale, and the outputs match the oracle within the bar scaled by the value magnitude."""
+    print("case:", name, "dense multi-query value scale", c, flush=True)
+    monkeypatch.setenv("KVQ_MQ_DENSE", "1")
+    H, Hq, lens = 2, 8, [260, 90]
+    w = kc.ki.Workload("vs", zlib.crc32(name.encode()) % 1000, 2, Hq, H, 260,
+                       kc.ki.Side(*k), kc.ki.Side(*v), residual=R)
+    k_rows, v_rows, vmax = [], [], 1.0
+    for b, T in enumerate(lens):
+        kk, vv = kc.ki.prefill_kv(w, b, T)
+        x = vv.float()
+        vv = (x * c if v[1] == 0 else x.abs() * c + off).to(torch.bfloat16)
+        vmax = max(vmax, float(vv.float().abs().max()))
+        k_rows.append(kc.ki.bf16_bits(kk))
+        v_rows.append(kc.ki.bf16_bits(vv))
+    pr = kc.build_pair_rows(k, v, Hq, H, R, k_rows, v_rows, paged=paged, seed=w.seed,
+                            single_tail=20)
+    kc.compare_attention_mq(pr, 6, tol_scale=vmax)
