@@ -694,6 +694,10 @@ def main() -> int:
     ap.add_argument("--sweep-batches", default="1,16")
     ap.add_argument("--sweep-lengths", default="512,2048,8192,32768,131072")
     ap.add_argument("--sweep-out", default="", help="write the sweep's markdown table here")
+    ap.add_argument("--sweep-nq", default="1,2,4,8,16",
+                    help="multi-query sweep: query tokens per sequence (1 is the single-query base)")
+    ap.add_argument("--pmc-kernel", default="decode_kernel",
+                    help="--summarize-pmc: the kernels (name substring) whose dispatches are averaged")
     a = ap.parse_args()
     if a.summarize_counters:
         d = summarize_counters(*a.summarize_counters, a.workload, a.command)
@@ -702,7 +706,7 @@ def main() -> int:
         print(json.dumps(d, indent=1))
         return 0
     if a.summarize_pmc:
-        print(summarize_pmc(a.summarize_pmc), end="")
+        print(summarize_pmc(a.summarize_pmc, a.pmc_kernel), end="")
         return 0
     if a.summarize_stats:
         print(summarize_stats(a.summarize_stats, a.command, f"kvq kernels, workload {a.workload}"), end="")
@@ -726,7 +730,10 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     if a.sweep == "multiquery":
-        rows = sweep_multiquery(16, 32768, [1, 2, 4, 8, 16])
+        nqs = [int(x) for x in a.sweep_nq.split(",")]
+        if nqs[0] != 1:
+            raise SystemExit("--sweep-nq must start with 1 (the single-query base of the table)")
+        rows = sweep_multiquery(16, 32768, nqs)
         if a.sweep_out:
             open(a.sweep_out, "w").write(multiquery_table(rows, a.command or "python bench.py --sweep multiquery"))
         return 0
