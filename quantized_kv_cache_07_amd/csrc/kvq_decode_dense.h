@@ -503,6 +503,10 @@ __global__ __launch_bounds__(256, (KB == 2 || NGK == 4) ? 2 : 3) void dense_kern
         int nvA, nvB;
         valid_of(x, pA, pB, nvA, nvB);
         bad_block |= pA < 0 || (32 * x + 16 < nq && pB < 0);
+        // wave priorities per phase: a wave past the barrier (QK, softmax) issues before one in
+        // its PV products, and both before one unpacking (16 queries: INT4 355-360 -> 338-339 us,
+        // INT8 345-348 -> 332-333 us against no priorities; the opposite order was slower)
+        __builtin_amdgcn_s_setprio(0);
         put_keys(x);
         put_values(x, nvA, nvB);
         int nnA = -1, nnB = -1;  // tiles of unit x + 2
@@ -513,6 +517,7 @@ __global__ __launch_bounds__(256, (KB == 2 || NGK == 4) ? 2 : 3) void dense_kern
         }
         // every wave's quarter of unit x is in LDS (and every wave is done reading unit x - 1's)
         __syncthreads();
+        __builtin_amdgcn_s_setprio(2);
 
         f16x8 pa;
         if (active) {
@@ -564,6 +569,7 @@ __global__ __launch_bounds__(256, (KB == 2 || NGK == 4) ? 2 : 3) void dense_kern
             pa[2 * i + 1] = w2[1];
           }
         }
+        __builtin_amdgcn_s_setprio(1);
         if (active) {
           uint4 vop[8];
 #pragma unroll
