@@ -4,7 +4,12 @@ formats (2/4/8 bits, symmetric or asymmetric, chosen independently; per-token gr
 ratios 1/2/4/8, 1-4 kv heads, windows of 0-128 tokens, lengths 0-300 per sequence, contiguous
 or paged caches.  Each case: codes, scales and windows bit-exact after the prefill, attention
 within the bar, one decode step (window flushes where due), both again.  The draw is fixed by
-the case index, so a failure names a reproducible case."""
+the case index, so a failure names a reproducible case.
+
+A second set of 24 draws goes through the dense multi-query kernel (forced from 16 query rows
+per kv head): one integer format on both sides (2/4/8 bits, symmetric or asymmetric, per-token
+key groups of 32/64/128), GQA 1/2/4/8, 16-96 query rows per kv head, windows, lengths 0-400,
+contiguous or paged."""
 from __future__ import annotations
 
 import sys
@@ -73,3 +78,33 @@ def test_random_case(i):
     kc.step(pr, flush_first=bool(i % 2))
     kc.compare_state(pr)
     kc.compare_attention(pr, q_seed_step=1)
+
+
+def draw_dense(i: int):
+    rng = np.random.default_rng(7100 + i)
+    bits, sch = int(rng.choice([2, 4, 8])), int(rng.integers(2))
+    side = (bits, sch, 0, int(rng.choice([32, 64, 128])))
+    G = int(rng.choice([1, 2, 4, 8]))
+    H = int(rng.choice([1, 2]))
+    R = int(rng.choice([0, 16, 32, 64, 128]))
+    n_q = int(rng.integers(max(2, -(-16 // G)), 96 // G + 1))
+    B = int(rng.integers(1, 4))
+    lens = [int(rng.integers(0, 401)) for _ in range(B)]
+    if max(lens) == 0:
+        lens[0] = 1
+    paged = bool(rng.integers(2))
+    return side, B, G * H, H, R, lens, paged, n_q
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_dense_multi_query(i, monkeypatch):
+    side, B, Hq, H, R, lens, paged, n_q = draw_dense(i)
+    print("case:", i, dict(side=side, B=B, Hq=Hq, H=H, R=R, lens=lens, paged=paged, n_q=n_q),
+          flush=True)
+    monkeypatch.setenv("KVQ_MQ_DENSE", "1")
+    pr = kc.build_pair(side, side, B, Hq, H, R, lens, paged=paged, seed=700 + i,
+                       extra_tokens=64 + n_q)
+    for _ in range(min(n_q, 8)):  # the last query tokens are appended (windows flush where due)
+        kc.step(pr)
+    kc.compare_state(pr)
+    kc.compare_attention_mq(pr, n_q)
