@@ -361,6 +361,8 @@ MQ_CASES = [
     ("mq-dense-int2-g32-gqa4", (2, 0, 0, 32), (2, 0, 0, 32), 2, 8, 2, 0, [900, 260], False, 16),
     ("mq-dense-asym4-g32-paged-window", (4, 1, 0, 32), (4, 1, 0, 32), 2, 16, 2, 32, [700, 90], True, 4),
     ("mq-dense-asym8-g32-mha", (8, 1, 0, 32), (8, 1, 0, 32), 1, 2, 2, 0, [1200], False, 17),
+    ("mq-dense-int4-k64-v32-window", (4, 0, 0, 64), (4, 0, 0, 32), 2, 8, 2, 32, [500, 140], False, 8),
+    ("mq-dense-asym2-k128-v64-paged", (2, 1, 0, 128), (2, 1, 0, 64), 2, 4, 2, 16, [420, 77], True, 12),
 ]
 
 
