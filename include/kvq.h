@@ -253,14 +253,14 @@ size_t kvq_decode_workspace_bytes_mq(const kvq_cache *cache, int32_t n_q_heads, 
  * so quickly", attention equation, one row per query; P3, "Step 3: Deploy a Fallback-Capable FP8
  * First": prefill-heavy workloads gain least].  The K/V tiles streamed from HBM are dequantized
  * once per block of query rows and multiplied against all of them on the matrix cores.  With 32
- * or more query rows per kv head (n_q * n_q_heads / n_kv_heads; 16 for 8-bit codes) on a
- * 2/4/8-bit cache whose two sides share one format with per-token key groups of 32, 64 or 128,
- * one pass over the codes serves up to 64 rows: the values are dequantized once per workgroup
- * to f16 and the weights rounded to f16 (each within 2^-11 relative; the result stays within
- * 2e-3 + 1e-2 |ref| of the exact attention over the dequantized cache).  Formats beyond
- * kvq_decode_attention's column limits
- * (for example key groups of 32 with G = 8) take that path from 16 rows on (n_q * G >= 16)
- * instead of returning KVQ_ENOTSUP.  Environment KVQ_MQ_DENSE=0 turns that path off.
+ * or more query rows per kv head (n_q * n_q_heads / n_kv_heads; 16 for 8-bit codes) on a cache
+ * whose two sides share one format (2/4/8-bit with per-token key groups of 32, 64 or 128, or FP8
+ * E4M3), one pass over the codes serves up to 64 rows: the values are dequantized once per
+ * workgroup to f16 (FP8 exactly) and the weights rounded to f16 (each within 2^-11 relative;
+ * the result stays within 2e-3 + 1e-2 |ref| of the exact attention over the dequantized cache).
+ * Formats beyond kvq_decode_attention's column limits (for example key groups of 32 with G = 8)
+ * take that path from 16 rows on (n_q * G >= 16) instead of returning KVQ_ENOTSUP.  Environment
+ * KVQ_MQ_DENSE=0 turns that path off.
  *   q:   bf16 [batch][n_q][n_q_heads][head_dim], device, 16-byte aligned
  *   out: fp32 [batch][n_q][n_q_heads][head_dim], device
  *   n_q: 1 .. max_tokens; n_q = 1 is kvq_decode_attention.

@@ -83,7 +83,8 @@ __device__ __forceinline__ uint2 ld_rows(rsrc_t r, unsigned voff, int soff) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
 }
 
-// KB: code bits of keys and values (the same format on both sides); SCH: KVQ_SYM or KVQ_ASYM;
+// KB: code bits of keys and values (the same format on both sides); SCH: KVQ_SYM, KVQ_ASYM or
+// KVQ_FP8 (E4M3 bytes with one fp32 scale per kv head or tensor; KB 8, NGK 1);
 // NGK: key groups per row (1: groups of 128 channels, 2: of 64, 4: of 32).  Three workgroups per
 // CU for 4- and 8-bit codes in groups of 64 or 128 (168 VGPRs; the few spills the compiler makes
 // fall outside the unit loop, and 16 queries ran 7-19% faster than at two), two for 2-bit codes
@@ -93,6 +94,8 @@ __global__ __launch_bounds__(256, (KB == 2 || NGK == 4) ? 2 : 3) void dense_kern
   constexpr int G = DROWS;
   constexpr int qpw = 4;  // query blocks per segment, one per wave
   constexpr bool ASYM = SCH == KVQ_ASYM;
+  constexpr bool F8 = SCH == KVQ_FP8;
+  static_assert(!F8 || (KB == 8 && NGK == 1), "FP8 caches: bytes, no groups");
   constexpr int WW = window_weight2(KB, KB);
   constexpr int SEG_W = SEGMENT_START_WEIGHT;
   const int nqt = p.nqt, qbs = p.qbs, nqb = p.nqb, gkv = p.gkv, nqs = p.nqs;
@@ -285,6 +288,7 @@ __global__ __launch_bounds__(256, (KB == 2 || NGK == 4) ? 2 : 3) void dense_kern
       load_vwords<KB>(rK, kw_lane, max(pB, 0) * static_cast<int>(TILE_BYTES), kw[1]);
     };
     auto load_ks = [&](int pA, int pB) {  // key scales (and zero-points): the scores only
+      if constexpr (F8) return;
 #pragma unroll
       for (int t = 0; t < 2; t++) {
         const int so = max(t ? pB : pA, 0) * rec_bytes;
@@ -298,6 +302,7 @@ __global__ __launch_bounds__(256, (KB == 2 || NGK == 4) ? 2 : 3) void dense_kern
     auto load_v = [&](int pA, int pB) {
       load_vwords<KB>(rV, vw_lane, max(pA, 0) * static_cast<int>(TILE_BYTES), vw[0]);
       load_vwords<KB>(rV, vw_lane, max(pB, 0) * static_cast<int>(TILE_BYTES), vw[1]);
+      if constexpr (F8) return;  // one scale per head or tensor
 #pragma unroll
       for (int t = 0; t < 2; t++) {
         const int so = max(t ? pB : pA, 0) * rec_bytes;
@@ -346,7 +351,13 @@ __global__ __launch_bounds__(256, (KB == 2 || NGK == 4) ? 2 : 3) void dense_kern
     // scale of its scores, sm_scale log2(e) 2^e
     const int qe_n = qe[qi * G + n];
     const float qsc = exp2i(-qe_n);
-    const float sl2 = p.sm_log2 * exp2i(qe_n);
+    // FP8: the key scale of kv head h multiplies every score, the value scale the output
+    float f8k = 1.0f, f8v = 1.0f;
+    if constexpr (F8) {
+      f8k = __int_as_float(ld_uniform(reinterpret_cast<const int32_t*>(c.ks) + (c.k.axis == KVQ_PER_HEAD ? h : 0)));
+      f8v = __int_as_float(ld_uniform(reinterpret_cast<const int32_t*>(c.vs) + (c.v.axis == KVQ_PER_HEAD ? h : 0)));
+    }
+    const float sl2 = p.sm_log2 * exp2i(qe_n) * f8k;
     const uint16_t* qrow = qs + (qi * G + n) * D;
 
     // ---- QK operands: product j takes key slice j (channels 32 j .. 32 j + 31, one key group),
@@ -368,14 +379,15 @@ __global__ __launch_bounds__(256, (KB == 2 || NGK == 4) ? 2 : 3) void dense_kern
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const int gi = j / (4 / NGK);
-      const u16x8 raw = gather_kchan<KB>(qrow + 32 * j, g);
+      // FP8 bytes convert in natural channel order (no fields, no bias)
+      const u16x8 raw = F8 ? *reinterpret_cast<const u16x8*>(qrow + 32 * j + 8 * g) : gather_kchan<KB>(qrow + 32 * j, g);
 #pragma unroll
       for (int i = 0; i < 8; i++) {
         const float xq = bf16_to_f32(raw[i]) * qsc;
-        qn[j][i] = static_cast<_Float16>(xq * (1.0f / static_cast<float>(pair_alpha<KB>(i / 2))));
+        qn[j][i] = static_cast<_Float16>(F8 ? xq : xq * (1.0f / static_cast<float>(pair_alpha<KB>(i / 2))));
         if constexpr (ASYM) qsum[gi] += xq;
       }
-      dq0[gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bias, qn[j], dq0[gi], 0, 0, 0);
+      if constexpr (!F8) dq0[gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bias, qn[j], dq0[gi], 0, 0, 0);
     }
     if constexpr (ASYM) {
 #pragma unroll
@@ -437,6 +449,25 @@ __global__ __launch_bounds__(256, (KB == 2 || NGK == 4) ? 2 : 3) void dense_kern
     // i % 2; its scale is token 4 g + i % 4's of the lane's value group, times 2^-8 / alpha.
     uint4* vbuf = reinterpret_cast<uint4*>(smem + DenseLds::vbuf);
     auto put_values = [&](int y, int nvA, int nvB) {
+      if constexpr (F8) {
+        // E4M3 bytes convert exactly to f16 (the head's scale multiplies the output); byte b of
+        // a value word is token 4 g + (0, 2, 1, 3)[b].  Bytes of tokens past the end are
+        // cleared (they may hold NaN codes).
+        uint32_t keep[2] = {~0u, ~0u};
+        if (!(nvA == 16 && nvB == 16)) {
+#pragma unroll
+          for (int t = 0; t < 2; t++) {
+            const int nv = t ? nvB : nvA;
+            keep[t] = (4 * g < nv ? 0x000000FFu : 0u) | (4 * g + 2 < nv ? 0x0000FF00u : 0u) |
+                      (4 * g + 1 < nv ? 0x00FF0000u : 0u) | (4 * g + 3 < nv ? 0xFF000000u : 0u);
+          }
+        }
+#pragma unroll
+        for (int jj = 0; jj < 2; jj++)
+          vbuf[((y & 1) * 8 + 2 * wave + jj) * 64 + lane] =
+              __builtin_bit_cast(uint4, f8_to_f16x8(vw[0][jj] & keep[0], vw[1][jj] & keep[1]));
+        return;
+      }
       uint32_t svb[4] = {vsc[0].x, vsc[0].y, vsc[1].x, vsc[1].y};
       uint32_t zvb[4] = {vz[0].x, vz[0].y, vz[1].x, vz[1].y};
       // a tile past the sequence end may hold any bytes (0 * NaN is NaN): clear the fp16 bits
@@ -493,7 +524,9 @@ __global__ __launch_bounds__(256, (KB == 2 || NGK == 4) ? 2 : 3) void dense_kern
       for (int t = 0; t < 2; t++) {
         uint32_t ku[VW];
         vwords_at_use<KB>(kw[t], wave, ku);
-        kbuf[(((y & 1) * 2 + t) * 4 + g) * 64 + 16 * wave + n] = __builtin_bit_cast(uint4, kop_raw<KB>(ku, 0, ur));
+        kbuf[(((y & 1) * 2 + t) * 4 + g) * 64 + 16 * wave + n] =
+            F8 ? __builtin_bit_cast(uint4, f8_to_f16x8(ku[0], ku[VW - 1]))
+               : __builtin_bit_cast(uint4, kop_raw<KB>(ku, 0, ur));
       }
     };
     if (x < xq_end) {
@@ -544,6 +577,11 @@ __global__ __launch_bounds__(256, (KB == 2 || NGK == 4) ? 2 : 3) void dense_kern
           for (int t = 0; t < 2; t++) {
 #pragma unroll
             for (int r = 0; r < 4; r++) s2[4 * t + r] = 0.0f;
+            if constexpr (F8) {  // the head's key scale is in sl2
+#pragma unroll
+              for (int r = 0; r < 4; r++) s2[4 * t + r] = dq[t][0][r];
+              continue;
+            }
 #pragma unroll
             for (int gi = 0; gi < NGK; gi++) {
               const uint2 k2 = ks[gi][t];
@@ -561,10 +599,12 @@ __global__ __launch_bounds__(256, (KB == 2 || NGK == 4) ? 2 : 3) void dense_kern
           if (more) load_ks(nA, nB);  // scale registers are free again
           softmax(s2, nvA, nvB, 32 * x, sl2);
 
-          // P: the weights as f16 (element i: token 4 g + i % 4 of tile i / 4)
+          // P: the weights as f16, element i: token 4 g + i % 4 of tile i / 4 (FP8: token
+          // 4 g + (0, 2, 1, 3)[i % 4], the order of the converted value bytes)
 #pragma unroll
           for (int i = 0; i < 4; i++) {
-            const f16x2 w2 = pkrtz(s2[2 * i], s2[2 * i + 1]);
+            const int a = F8 ? 4 * (i / 2) + (i % 2) : 2 * i, b = F8 ? a + 2 : a + 1;
+            const f16x2 w2 = pkrtz(s2[a], s2[b]);
             pa[2 * i] = w2[0];
             pa[2 * i + 1] = w2[1];
           }
@@ -585,11 +625,11 @@ __global__ __launch_bounds__(256, (KB == 2 || NGK == 4) ? 2 : 3) void dense_kern
       }
       if (bad_block && lane == 0) atomicOr(c.err, KVQ_ERR_BLOCK);
     }
-    // the compressed units' values were taken times 2^-8
+    // the compressed units' values were taken times 2^-8 (FP8: without the head's value scale)
 #pragma unroll
     for (int j = 0; j < 8; j++)
 #pragma unroll
-      for (int r = 0; r < 4; r++) acc[j][r] *= 256.0f;
+      for (int r = 0; r < 4; r++) acc[j][r] *= F8 ? f8v : 256.0f;
 
     // ---------------------------- BF16 window units ----------------------------
     const int wend = xend > uq ? (xend - uq + WW - 1) / WW : 0;

@@ -363,6 +363,9 @@ MQ_CASES = [
     ("mq-dense-asym8-g32-mha", (8, 1, 0, 32), (8, 1, 0, 32), 1, 2, 2, 0, [1200], False, 17),
     ("mq-dense-int4-k64-v32-window", (4, 0, 0, 64), (4, 0, 0, 32), 2, 8, 2, 32, [500, 140], False, 8),
     ("mq-dense-asym2-k128-v64-paged", (2, 1, 0, 128), (2, 1, 0, 64), 2, 4, 2, 16, [420, 77], True, 12),
+    ("mq-dense-fp8-head-gqa4-window", (8, 2, 3, 0), (8, 2, 3, 0), 2, 8, 2, 32, [600, 45], False, 8),
+    ("mq-dense-fp8-tensor-mha-paged", (8, 2, 2, 0), (8, 2, 2, 0), 2, 4, 4, 16, [333, 700], True, 16),
+    ("mq-dense-fp8-k-head-v-tensor-gqa8", (8, 2, 3, 0), (8, 2, 2, 0), 1, 16, 2, 0, [1000], False, 3),
 ]
 
 
