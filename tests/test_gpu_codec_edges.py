@@ -161,6 +161,7 @@ DENSE_FORMATS = [
     ("asym4-g32-gqa2-paged", (4, 1, 0, 32), (4, 1, 0, 32), 4, 2, 16, [250, 99], True),
     ("int8-g128-mha", (8, 0, 0, 128), (8, 0, 0, 128), 2, 2, 0, [200, 33], False),
     ("int2-g64-gqa8", (2, 0, 0, 64), (2, 0, 0, 64), 16, 2, 16, [260, 50], True),
+    ("fp8-head-gqa4-paged", (8, 2, 3, 0), (8, 2, 3, 0), 8, 2, 16, [300, 77], True),
 ]
 
 

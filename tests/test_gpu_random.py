@@ -7,9 +7,9 @@ within the bar, one decode step (window flushes where due), both again.  The dra
 the case index, so a failure names a reproducible case.
 
 A second set of 24 draws goes through the dense multi-query kernel (forced from 16 query rows
-per kv head): one integer format on both sides (2/4/8 bits, symmetric or asymmetric, per-token
-key groups of 32/64/128), GQA 1/2/4/8, 16-96 query rows per kv head, windows, lengths 0-400,
-contiguous or paged."""
+per kv head): one format on both sides (2/4/8 bits, symmetric or asymmetric, per-token key
+groups of 32/64/128; every sixth draw FP8 E4M3), GQA 1/2/4/8, 16-96 query rows per kv head,
+windows, lengths 0-400, contiguous or paged."""
 from __future__ import annotations
 
 import sys
@@ -84,6 +84,8 @@ def draw_dense(i: int):
     rng = np.random.default_rng(7100 + i)
     bits, sch = int(rng.choice([2, 4, 8])), int(rng.integers(2))
     side = (bits, sch, 0, int(rng.choice([32, 64, 128])))
+    if i % 6 == 5:  # FP8 E4M3, one scale per kv head or per tensor
+        side = (8, 2, int(rng.choice([2, 3])), 0)
     G = int(rng.choice([1, 2, 4, 8]))
     H = int(rng.choice([1, 2]))
     R = int(rng.choice([0, 16, 32, 64, 128]))
