@@ -254,10 +254,11 @@ size_t kvq_decode_workspace_bytes_mq(const kvq_cache *cache, int32_t n_q_heads, 
  * First": prefill-heavy workloads gain least].  The K/V tiles streamed from HBM are dequantized
  * once per block of query rows and multiplied against all of them on the matrix cores.  With 32
  * or more query rows per kv head (n_q * n_q_heads / n_kv_heads; 16 for 8-bit codes) on a cache
- * whose two sides share one format (2/4/8-bit with per-token key groups of 32, 64 or 128, or FP8
- * E4M3), one pass over the codes serves up to 64 rows: the values are dequantized once per
- * workgroup to f16 (FP8 exactly) and the weights rounded to f16 (each within 2^-11 relative;
- * the result stays within 2e-3 + 1e-2 |ref| of the exact attention over the dequantized cache).
+ * whose two sides share one format (2/4/8-bit with per-token key groups of 32, 64 or 128, FP8
+ * E4M3 or BF16), one pass over the codes serves up to 64 rows: the values are dequantized once
+ * per workgroup to f16 (FP8 exactly; BF16 values are used as stored) and the weights rounded to
+ * f16 (each within 2^-11 relative; BF16: bf16 hi + lo parts; the result stays within
+ * 2e-3 + 1e-2 |ref| of the exact attention over the dequantized cache).
  * Formats beyond kvq_decode_attention's column limits (for example key groups of 32 with G = 8)
  * take that path from 16 rows on (n_q * G >= 16) instead of returning KVQ_ENOTSUP.  Environment
  * KVQ_MQ_DENSE=0 turns that path off.

@@ -51,19 +51,28 @@ static_assert(WAVES * 16 * RED_STRIDE * 4 >= 2 * (8 + 8) * 64 * 16, "unit operan
 // Code words of a value chunk (or key slice) that wave w unpacks: pairs 4 w .. 4 w + 3, i.e.
 // words 2 w, 2 w + 1 of 8-bit codes, word w of 4-bit codes and half of word w / 2 of 2-bit codes
 // (the wave shifts odd halves down by 8 bits); value products 2 w and 2 w + 1 use these pairs,
-// and so does the part of a key slice that lane group w of a QK product takes.
+// and so does the part of a key slice that lane group w of a QK product takes.  BF16 storage
+// (16-byte pieces one 1 KiB slab apart): piece w of a key slice (8 channels) or of a value chunk
+// (channels 2 w and 2 w + 1 of its four tokens).
 template <int KB>
-constexpr int vwords() { return KB == 8 ? 2 : 1; }
+constexpr int vwords() { return KB == 16 ? 4 : KB == 8 ? 2 : 1; }
 template <int KB>
 __device__ __forceinline__ unsigned vword_off(int w) {
-  if constexpr (KB == 8) return 1024u * (w / 2) + 8u * (w % 2);
+  if constexpr (KB == 16) return 1024u * w;
+  else if constexpr (KB == 8) return 1024u * (w / 2) + 8u * (w % 2);
   else if constexpr (KB == 4) return 4u * w;
   else return 4u * (w / 2);
 }
-// The words at byte voff + soff of resource r (soff: the tile's byte offset, wave-uniform).
+// The key words at byte voff + soff of resource r (soff: the tile's byte offset, wave-uniform).
 template <int KB>
 __device__ __forceinline__ void load_vwords(rsrc_t r, unsigned voff, int soff, uint32_t (&x)[vwords<KB>()]) {
-  if constexpr (KB == 8) {
+  if constexpr (KB == 16) {
+    const uint4 a = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, BUF_NT));
+    x[0] = a.x;
+    x[1] = a.y;
+    x[2] = a.z;
+    x[3] = a.w;
+  } else if constexpr (KB == 8) {
     const uint2 a = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, BUF_NT));
     x[0] = a.x;
     x[1] = a.y;
@@ -71,6 +80,7 @@ __device__ __forceinline__ void load_vwords(rsrc_t r, unsigned voff, int soff, u
     x[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, BUF_NT);
   }
 }
+
 // The loaded words of wave w as the array rawpair() indexes: 2-bit codes of an odd wave are the
 // upper halves' fields, shifted down here (at use, not at the load, which would wait for it).
 template <int KB>
@@ -83,8 +93,9 @@ __device__ __forceinline__ uint2 ld_rows(rsrc_t r, unsigned voff, int soff) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
 }
 
-// KB: code bits of keys and values (the same format on both sides); SCH: KVQ_SYM, KVQ_ASYM or
-// KVQ_FP8 (E4M3 bytes with one fp32 scale per kv head or tensor; KB 8, NGK 1);
+// KB: code bits of keys and values (the same format on both sides; 16: BF16 storage); SCH:
+// KVQ_SYM, KVQ_ASYM or KVQ_FP8 (E4M3 bytes with one fp32 scale per kv head or tensor; KB 8,
+// NGK 1);
 // NGK: key groups per row (1: groups of 128 channels, 2: of 64, 4: of 32).  Three workgroups per
 // CU for 4- and 8-bit codes in groups of 64 or 128 (168 VGPRs; the few spills the compiler makes
 // fall outside the unit loop, and 16 queries ran 7-19% faster than at two), two for 2-bit codes
@@ -95,7 +106,9 @@ __global__ __launch_bounds__(256, (KB == 2 || NGK == 4) ? 2 : 3) void dense_kern
   constexpr int qpw = 4;  // query blocks per segment, one per wave
   constexpr bool ASYM = SCH == KVQ_ASYM;
   constexpr bool F8 = SCH == KVQ_FP8;
+  constexpr bool BF = KB == 16;
   static_assert(!F8 || (KB == 8 && NGK == 1), "FP8 caches: bytes, no groups");
+  static_assert(!BF || (SCH == KVQ_SYM && NGK == 1), "BF16 caches: no scales, no groups");
   constexpr int WW = window_weight2(KB, KB);
   constexpr int SEG_W = SEGMENT_START_WEIGHT;
   const int nqt = p.nqt, qbs = p.qbs, nqb = p.nqb, gkv = p.gkv, nqs = p.nqs;
@@ -288,7 +301,7 @@ __global__ __launch_bounds__(256, (KB == 2 || NGK == 4) ? 2 : 3) void dense_kern
       load_vwords<KB>(rK, kw_lane, max(pB, 0) * static_cast<int>(TILE_BYTES), kw[1]);
     };
     auto load_ks = [&](int pA, int pB) {  // key scales (and zero-points): the scores only
-      if constexpr (F8) return;
+      if constexpr (F8 || BF) return;
 #pragma unroll
       for (int t = 0; t < 2; t++) {
         const int so = max(t ? pB : pA, 0) * rec_bytes;
@@ -302,7 +315,7 @@ __global__ __launch_bounds__(256, (KB == 2 || NGK == 4) ? 2 : 3) void dense_kern
     auto load_v = [&](int pA, int pB) {
       load_vwords<KB>(rV, vw_lane, max(pA, 0) * static_cast<int>(TILE_BYTES), vw[0]);
       load_vwords<KB>(rV, vw_lane, max(pB, 0) * static_cast<int>(TILE_BYTES), vw[1]);
-      if constexpr (F8) return;  // one scale per head or tensor
+      if constexpr (F8 || BF) return;  // one scale per head or tensor, or none
 #pragma unroll
       for (int t = 0; t < 2; t++) {
         const int so = max(t ? pB : pA, 0) * rec_bytes;
@@ -357,7 +370,8 @@ __global__ __launch_bounds__(256, (KB == 2 || NGK == 4) ? 2 : 3) void dense_kern
       f8k = __int_as_float(ld_uniform(reinterpret_cast<const int32_t*>(c.ks) + (c.k.axis == KVQ_PER_HEAD ? h : 0)));
       f8v = __int_as_float(ld_uniform(reinterpret_cast<const int32_t*>(c.vs) + (c.v.axis == KVQ_PER_HEAD ? h : 0)));
     }
-    const float sl2 = p.sm_log2 * exp2i(qe_n) * f8k;
+    // (BF16 storage: the bf16 query as it is, no prescale)
+    const float sl2 = BF ? p.sm_log2 : p.sm_log2 * exp2i(qe_n) * f8k;
     const uint16_t* qrow = qs + (qi * G + n) * D;
 
     // ---- QK operands: product j takes key slice j (channels 32 j .. 32 j + 31, one key group),
@@ -379,8 +393,13 @@ __global__ __launch_bounds__(256, (KB == 2 || NGK == 4) ? 2 : 3) void dense_kern
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const int gi = j / (4 / NGK);
-      // FP8 bytes convert in natural channel order (no fields, no bias)
-      const u16x8 raw = F8 ? *reinterpret_cast<const u16x8*>(qrow + 32 * j + 8 * g) : gather_kchan<KB>(qrow + 32 * j, g);
+      // FP8 bytes convert in natural channel order (no fields, no bias); BF16 keys take the bf16
+      // query bits as they are
+      const u16x8 raw = (F8 || BF) ? *reinterpret_cast<const u16x8*>(qrow + 32 * j + 8 * g) : gather_kchan<KB>(qrow + 32 * j, g);
+      if constexpr (BF) {
+        qn[j] = __builtin_bit_cast(f16x8, raw);
+        continue;
+      }
 #pragma unroll
       for (int i = 0; i < 8; i++) {
         const float xq = bf16_to_f32(raw[i]) * qsc;
@@ -449,6 +468,26 @@ __global__ __launch_bounds__(256, (KB == 2 || NGK == 4) ? 2 : 3) void dense_kern
     // i % 2; its scale is token 4 g + i % 4's of the lane's value group, times 2^-8 / alpha.
     uint4* vbuf = reinterpret_cast<uint4*>(smem + DenseLds::vbuf);
     auto put_values = [&](int y, int nvA, int nvB) {
+      if constexpr (BF) {
+        // BF16 values as they are: word 2 jj + h of the wave's piece holds tokens 4 g + 2 h and
+        // + 1 of channel 8 n + 2 wave + jj, so product 2 wave + jj is words 2 jj, 2 jj + 1 of
+        // each tile.  Halves of tokens past the end are cleared (they may hold NaN).
+        uint32_t w[2][4];
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+          const int nv = t ? nvB : nvA;
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const int r0 = 4 * g + 2 * (q % 2);
+            const uint32_t keep = (r0 < nv ? 0x0000FFFFu : 0u) | (r0 + 1 < nv ? 0xFFFF0000u : 0u);
+            w[t][q] = (nvA == 16 && nvB == 16) ? vw[t][q] : vw[t][q] & keep;
+          }
+        }
+#pragma unroll
+        for (int jj = 0; jj < 2; jj++)
+          vbuf[((y & 1) * 8 + 2 * wave + jj) * 64 + lane] = uint4{w[0][2 * jj], w[0][2 * jj + 1], w[1][2 * jj], w[1][2 * jj + 1]};
+        return;
+      }
       if constexpr (F8) {
         // E4M3 bytes convert exactly to f16 (the head's scale multiplies the output); byte b of
         // a value word is token 4 g + (0, 2, 1, 3)[b].  Bytes of tokens past the end are
@@ -524,9 +563,11 @@ __global__ __launch_bounds__(256, (KB == 2 || NGK == 4) ? 2 : 3) void dense_kern
       for (int t = 0; t < 2; t++) {
         uint32_t ku[VW];
         vwords_at_use<KB>(kw[t], wave, ku);
-        kbuf[(((y & 1) * 2 + t) * 4 + g) * 64 + 16 * wave + n] =
-            F8 ? __builtin_bit_cast(uint4, f8_to_f16x8(ku[0], ku[VW - 1]))
-               : __builtin_bit_cast(uint4, kop_raw<KB>(ku, 0, ur));
+        uint4 op;
+        if constexpr (BF) op = uint4{ku[0], ku[VW > 1 ? 1 : 0], ku[VW > 2 ? 2 : 0], ku[VW > 3 ? 3 : 0]};
+        else if constexpr (F8) op = __builtin_bit_cast(uint4, f8_to_f16x8(ku[0], ku[VW - 1]));
+        else op = __builtin_bit_cast(uint4, kop_raw<KB>(ku, 0, ur));
+        kbuf[(((y & 1) * 2 + t) * 4 + g) * 64 + 16 * wave + n] = op;
       }
     };
     if (x < xq_end) {
@@ -553,6 +594,7 @@ __global__ __launch_bounds__(256, (KB == 2 || NGK == 4) ? 2 : 3) void dense_kern
         __builtin_amdgcn_s_setprio(2);
 
         f16x8 pa;
+        bf16x8 ph, pl;  // BF16 storage: the weights' bf16 hi and lo parts (16 significant bits)
         if (active) {
           // QK^T: one accumulator per (tile, key group); stand-in tiles are masked by the softmax
           uint4 kop[2][4];
@@ -570,14 +612,18 @@ __global__ __launch_bounds__(256, (KB == 2 || NGK == 4) ? 2 : 3) void dense_kern
 #pragma unroll
             for (int t = 0; t < 2; t++) {
               const int gi = j / (4 / NGK);
-              dq[t][gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, kop[t][j]), qn[j], dq[t][gi], 0, 0, 0);
+              if constexpr (BF)
+                dq[t][gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[t][j]),
+                                                                    __builtin_bit_cast(bf16x8, qn[j]), dq[t][gi], 0, 0, 0);
+              else
+                dq[t][gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, kop[t][j]), qn[j], dq[t][gi], 0, 0, 0);
             }
           float s2[8];
 #pragma unroll
           for (int t = 0; t < 2; t++) {
 #pragma unroll
             for (int r = 0; r < 4; r++) s2[4 * t + r] = 0.0f;
-            if constexpr (F8) {  // the head's key scale is in sl2
+            if constexpr (F8 || BF) {  // FP8: the head's key scale is in sl2
 #pragma unroll
               for (int r = 0; r < 4; r++) s2[4 * t + r] = dq[t][0][r];
               continue;
@@ -601,12 +647,31 @@ __global__ __launch_bounds__(256, (KB == 2 || NGK == 4) ? 2 : 3) void dense_kern
 
           // P: the weights as f16, element i: token 4 g + i % 4 of tile i / 4 (FP8: token
           // 4 g + (0, 2, 1, 3)[i % 4], the order of the converted value bytes)
+          if constexpr (BF) {
+            uint32_t hk[4], lk[4];
 #pragma unroll
-          for (int i = 0; i < 4; i++) {
-            const int a = F8 ? 4 * (i / 2) + (i % 2) : 2 * i, b = F8 ? a + 2 : a + 1;
-            const f16x2 w2 = pkrtz(s2[a], s2[b]);
-            pa[2 * i] = w2[0];
-            pa[2 * i + 1] = w2[1];
+            for (int i = 0; i < 4; i++) {
+              uint32_t eh[2], el[2];
+#pragma unroll
+              for (int k2 = 0; k2 < 2; k2++) {
+                const float wv = s2[2 * i + k2];
+                const float hv = __uint_as_float(__float_as_uint(wv) & 0xFFFF0000u);
+                eh[k2] = __float_as_uint(hv) >> 16;
+                el[k2] = __float_as_uint(wv - hv) >> 16;
+              }
+              hk[i] = eh[0] | (eh[1] << 16);
+              lk[i] = el[0] | (el[1] << 16);
+            }
+            ph = __builtin_bit_cast(bf16x8, uint4{hk[0], hk[1], hk[2], hk[3]});
+            pl = __builtin_bit_cast(bf16x8, uint4{lk[0], lk[1], lk[2], lk[3]});
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              const int a = F8 ? 4 * (i / 2) + (i % 2) : 2 * i, b = F8 ? a + 2 : a + 1;
+              const f16x2 w2 = pkrtz(s2[a], s2[b]);
+              pa[2 * i] = w2[0];
+              pa[2 * i + 1] = w2[1];
+            }
           }
         }
         __builtin_amdgcn_s_setprio(1);
@@ -615,8 +680,14 @@ __global__ __launch_bounds__(256, (KB == 2 || NGK == 4) ? 2 : 3) void dense_kern
 #pragma unroll
           for (int j = 0; j < 8; j++) vop[j] = vbuf[((x & 1) * 8 + j) * 64 + lane];
 #pragma unroll
-          for (int j = 0; j < 8; j++)
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, __builtin_bit_cast(f16x8, vop[j]), acc[j], 0, 0, 0);
+          for (int j = 0; j < 8; j++) {
+            if constexpr (BF) {
+              acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, __builtin_bit_cast(bf16x8, vop[j]), acc[j], 0, 0, 0);
+              acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, __builtin_bit_cast(bf16x8, vop[j]), acc[j], 0, 0, 0);
+            } else {
+              acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, __builtin_bit_cast(f16x8, vop[j]), acc[j], 0, 0, 0);
+            }
+          }
         }
         pA = nA;
         pB = nB;
@@ -629,7 +700,7 @@ __global__ __launch_bounds__(256, (KB == 2 || NGK == 4) ? 2 : 3) void dense_kern
 #pragma unroll
     for (int j = 0; j < 8; j++)
 #pragma unroll
-      for (int r = 0; r < 4; r++) acc[j][r] *= F8 ? f8v : 256.0f;
+      for (int r = 0; r < 4; r++) acc[j][r] *= F8 ? f8v : BF ? 1.0f : 256.0f;
 
     // ---------------------------- BF16 window units ----------------------------
     const int wend = xend > uq ? (xend - uq + WW - 1) / WW : 0;

@@ -197,10 +197,10 @@ int device_cus();
 // group and row) and 32 PV rows (hi / lo part, value group, row).
 // Multi-query decode takes the dense kernel (16 query rows per wave, the four waves of a
 // workgroup on four blocks of one (sequence, kv head), keys and values unpacked once per
-// workgroup) for caches with the same format on both sides, integer with per-token key groups of
-// 32, 64 or 128 channels or FP8 E4M3, whose tiles lie within 2 GiB of their base, once a kv head
-// has query rows for two of its blocks (n_q x GQA heads >= 32; the waves of empty blocks only
-// unpack their share), for 8-bit codes from one block on.  KVQ_MQ_DENSE=0 turns it off, KVQ_MQ_DENSE=1 takes
+// workgroup) for caches with the same format on both sides (integer with per-token key groups of
+// 32, 64 or 128 channels, FP8 E4M3 or BF16) whose tiles lie within 2 GiB of their base, once a kv
+// head has query rows for two of its blocks (n_q x GQA heads >= 32; the waves of empty blocks
+// only unpack their share), for 8- and 16-bit codes from one block on.  KVQ_MQ_DENSE=0 turns it off, KVQ_MQ_DENSE=1 takes
 // it from 16 rows on.
 bool dense_mq(const kvq_cache* c, int gkv, int n_q) {
   const kvq_side& k = c->fmt.k;
@@ -208,7 +208,8 @@ bool dense_mq(const kvq_cache* c, int gkv, int n_q) {
   if (n_q < 2 || n_q * gkv < 16 || 16 % gkv != 0) return false;
   if (k.bits != v.bits || k.scheme != v.scheme) return false;
   const bool f8 = k.scheme == KVQ_FP8;  // E4M3 on both sides (per-head or per-tensor scales)
-  if (!f8) {
+  const bool bf = k.bits == 16;         // BF16 storage on both sides
+  if (!f8 && !bf) {
     if (k.scheme != KVQ_SYM && k.scheme != KVQ_ASYM) return false;
     if (k.bits != 2 && k.bits != 4 && k.bits != 8) return false;
     if (k.axis != KVQ_PER_TOKEN || v.axis != KVQ_PER_TOKEN) return false;
@@ -218,15 +219,15 @@ bool dense_mq(const kvq_cache* c, int gkv, int n_q) {
   // the pool's (paged)
   const long tiles = c->block_table ? static_cast<long>(c->num_blocks) * c->n_kv_heads
                                     : c->capacity / TILE;
-  const long rec = f8 ? 0 : 2L * (D / k.group + D / v.group) * TILE;  // a tile's scale record
+  const long rec = (f8 || bf) ? 0 : 2L * (D / k.group + D / v.group) * TILE;  // a tile's scale record
   if (tiles * (static_cast<long>(TILE) * D * k.bits / 8) >= (1L << 31) || tiles * rec >= (1L << 31))
     return false;
   // measured on the GQA-4 sweep: from 32 rows the dense kernel beats the blocked one (4-bit
   // 287 against 326 us, 2-bit group 32 341 against 489 us), 8-bit codes already at 16 (268
   // against 312 us); formats the blocked kernel cannot serve for this GQA group (more than 16 QK
   // columns or 32 PV rows per query token) take it from 16 rows on
-  const bool blocked_fits = f8 || ((D / k.group) * gkv <= 16 && 2 * gkv * (D / v.group) <= 32);
-  int rows_min = (!blocked_fits || k.bits == 8) ? 16 : 32;
+  const bool blocked_fits = f8 || bf || ((D / k.group) * gkv <= 16 && 2 * gkv * (D / v.group) <= 32);
+  int rows_min = (!blocked_fits || k.bits >= 8) ? 16 : 32;
   if (const char* e = std::getenv("KVQ_MQ_DENSE")) {
     if (e[0] == '0') return false;
     if (e[0] == '1') rows_min = 16;

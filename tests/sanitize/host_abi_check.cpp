@@ -62,9 +62,10 @@ KVQ_MIX(launch_decode_mixed_k8s)
 KVQ_MIX(launch_decode_mixed_k8a)
 #undef KVQ_MIX
 hipError_t launch_decode_dense(const DecodeParams& p, int bits, int scheme, hipStream_t) {
-  if (bits != 2 && bits != 4 && bits != 8) fail("dense bits");
+  if (bits != 2 && bits != 4 && bits != 8 && bits != 16) fail("dense bits");
   if (p.qpw != 4 || p.qbs * p.gkv != 16) fail("dense query blocks");
-  if (scheme == KVQ_FP8 ? bits != 8 : (p.c.k.group != 32 && p.c.k.group != 64 && p.c.k.group != 128))
+  if (scheme == KVQ_FP8 ? bits != 8
+                        : bits != 16 && p.c.k.group != 32 && p.c.k.group != 64 && p.c.k.group != 128)
     fail("dense key format");
   return check_decode(p, 16, 1);
 }

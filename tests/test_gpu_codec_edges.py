@@ -162,6 +162,7 @@ DENSE_FORMATS = [
     ("int8-g128-mha", (8, 0, 0, 128), (8, 0, 0, 128), 2, 2, 0, [200, 33], False),
     ("int2-g64-gqa8", (2, 0, 0, 64), (2, 0, 0, 64), 16, 2, 16, [260, 50], True),
     ("fp8-head-gqa4-paged", (8, 2, 3, 0), (8, 2, 3, 0), 8, 2, 16, [300, 77], True),
+    ("bf16-mha-window", (16, 0, 0, 128), (16, 0, 0, 128), 2, 2, 32, [260, 99], False),
 ]
 
 

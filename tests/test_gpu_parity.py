@@ -366,6 +366,8 @@ MQ_CASES = [
     ("mq-dense-fp8-head-gqa4-window", (8, 2, 3, 0), (8, 2, 3, 0), 2, 8, 2, 32, [600, 45], False, 8),
     ("mq-dense-fp8-tensor-mha-paged", (8, 2, 2, 0), (8, 2, 2, 0), 2, 4, 4, 16, [333, 700], True, 16),
     ("mq-dense-fp8-k-head-v-tensor-gqa8", (8, 2, 3, 0), (8, 2, 2, 0), 1, 16, 2, 0, [1000], False, 3),
+    ("mq-dense-bf16-gqa4-window", BF16, BF16, 2, 8, 2, 32, [500, 61], False, 8),
+    ("mq-dense-bf16-mha-paged", BF16, BF16, 2, 2, 2, 16, [300, 777], True, 19),
 ]
 
 

@@ -8,7 +8,7 @@ the case index, so a failure names a reproducible case.
 
 A second set of 24 draws goes through the dense multi-query kernel (forced from 16 query rows
 per kv head): one format on both sides (2/4/8 bits, symmetric or asymmetric, per-token key
-groups of 32/64/128; every sixth draw FP8 E4M3), GQA 1/2/4/8, 16-96 query rows per kv head,
+groups of 32/64/128; some draws FP8 E4M3 or BF16), GQA 1/2/4/8, 16-96 query rows per kv head,
 windows, lengths 0-400, contiguous or paged."""
 from __future__ import annotations
 
@@ -86,6 +86,8 @@ def draw_dense(i: int):
     side = (bits, sch, 0, int(rng.choice([32, 64, 128])))
     if i % 6 == 5:  # FP8 E4M3, one scale per kv head or per tensor
         side = (8, 2, int(rng.choice([2, 3])), 0)
+    elif i % 8 == 6:  # BF16 storage
+        side = (16, 0, 0, 128)
     G = int(rng.choice([1, 2, 4, 8]))
     H = int(rng.choice([1, 2]))
     R = int(rng.choice([0, 16, 32, 64, 128]))
