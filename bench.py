@@ -561,6 +561,10 @@ def sweep_crossover(batches, lengths, calls_per_graph: int = 20, replays: int = 
     return rows
 
 
+# the multi-query sweep adds 2-bit codes in key groups of 64 (a dense-kernel instance of its own)
+MQ_FORMATS = dict(SWEEP_FORMATS, **{"int2-g64": (2, 0, 0, 64)})
+
+
 def sweep_multiquery(batch: int, tokens: int, nqs, calls_per_graph: int = 10,
                      replays: int = 5) -> list[dict]:
     """Device time of one multi-query decode call (n_q query tokens per sequence, causal, the
@@ -572,7 +576,7 @@ def sweep_multiquery(batch: int, tokens: int, nqs, calls_per_graph: int = 10,
     from quantized_kv_cache_07_amd import kvq
 
     rows = []
-    for name, side in SWEEP_FORMATS.items():
+    for name, side in MQ_FORMATS.items():
         w = ki.Workload(f"mq-{name}", 13, batch, 32, 8, tokens, ki.Side(*side), ki.Side(*side))
         cap = -(-(tokens + 16) // 16) * 16
         f8 = {"fp8_scales": ([5.0 / 448] * 8, [5.0 / 448] * 8)} if side[1] == 2 else {}
@@ -622,7 +626,7 @@ def sweep_multiquery(batch: int, tokens: int, nqs, calls_per_graph: int = 10,
 
 
 def multiquery_table(rows: list[dict], command: str) -> str:
-    fmts = list(SWEEP_FORMATS)
+    fmts = list(MQ_FORMATS)
     B, T = rows[0]["batch"], rows[0]["tokens"]
     out = ["# Multi-query decode over the quantized cache (MI355X, one GPU)", "",
            "Command (from the repository root on the GPU box):", "", f"    {command}", "",

@@ -97,11 +97,12 @@ __device__ __forceinline__ uint2 ld_rows(rsrc_t r, unsigned voff, int soff) {
 // KVQ_SYM, KVQ_ASYM or KVQ_FP8 (E4M3 bytes with one fp32 scale per kv head or tensor; KB 8,
 // NGK 1);
 // NGK: key groups per row (1: groups of 128 channels, 2: of 64, 4: of 32).  Three workgroups per
-// CU for 4- and 8-bit codes in groups of 64 or 128 (168 VGPRs; the few spills the compiler makes
-// fall outside the unit loop, and 16 queries ran 7-19% faster than at two), two for 2-bit codes
-// (three ran 6% slower) and for groups of 32 (four key groups spill heavily at 168).
+// CU for key groups of 64 or 128 (168 VGPRs; the few spills the compiler makes fall outside the
+// unit loop: 16 queries ran 7-19% faster than at two, symmetric 2-bit codes in groups of 64 17%),
+// two for asymmetric 2-bit codes (the same time at three) and for groups of 32 (slower at three:
+// four key groups' accumulators, 3-4% for 4- and 2-bit codes, 40% for asymmetric 2-bit ones).
 template <int KB, int SCH, int NGK>
-__global__ __launch_bounds__(256, (KB == 2 || NGK == 4) ? 2 : 3) void dense_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256, (NGK == 4 || (KB == 2 && SCH == KVQ_ASYM)) ? 2 : 3) void dense_kernel(DecodeParams p) {
   constexpr int G = DROWS;
   constexpr int qpw = 4;  // query blocks per segment, one per wave
   constexpr bool ASYM = SCH == KVQ_ASYM;
