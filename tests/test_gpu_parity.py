@@ -368,6 +368,8 @@ MQ_CASES = [
     ("mq-dense-fp8-k-head-v-tensor-gqa8", (8, 2, 3, 0), (8, 2, 2, 0), 1, 16, 2, 0, [1000], False, 3),
     ("mq-dense-bf16-gqa4-window", BF16, BF16, 2, 8, 2, 32, [500, 61], False, 8),
     ("mq-dense-bf16-mha-paged", BF16, BF16, 2, 2, 2, 16, [300, 777], True, 19),
+    ("mq-dense-int2-g64-paged-window", (2, 0, 0, 64), (2, 0, 0, 64), 2, 8, 2, 64, [777, 1300], True, 9),
+    ("mq-dense-int2-g128-gqa4", (2, 0, 0, 128), (2, 0, 0, 128), 1, 8, 2, 0, [640], False, 16),
 ]
 
 
