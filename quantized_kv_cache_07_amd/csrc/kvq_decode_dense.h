@@ -6,8 +6,9 @@
 //   compressed tokens dequantized in registers as they stream in (P3 = oh-bug.com "KV Cache
 //   Quantization in Practice", "Misconception 1"), then the BF16 window.
 //
-// For integer caches with per-token key groups of 32, 64 or 128 channels and n_q x (query heads
-// per kv head) >= 16 (the host takes it from 64).  A query block is 16 rows (query tokens x GQA
+// For caches with one format on both sides -- integer with per-token key groups of 32, 64 or 128
+// channels, FP8 E4M3 or BF16 -- and n_q x (query heads per kv head) >= 16 (the host takes it from
+// 32 rows, from 16 for 8- and 16-bit codes).  A query block is 16 rows (query tokens x GQA
 // heads); a workgroup's four waves take four blocks of one (sequence, kv head) and walk the same
 // units, so the codes stream once for up to 64 rows.  Per unit (32 tokens) each wave unpacks a
 // quarter of the unit's operands into LDS, one barrier, then every wave reads all of them:
@@ -21,6 +22,10 @@
 //         raw-form unpack.  Rounding w and v to f16 (11 bits) keeps the output within the
 //         pages' tolerance; the 2^-8 keeps every finite fp16 scale times a code below the f16
 //         limit and is removed before the window rows add true values.
+//   FP8   E4M3 bytes convert exactly to f16 on both sides; the head's key scale goes into the
+//         softmax scale and its value scale multiplies the output.
+//   BF16  the stored bf16 words are the operands as they are (bf16 products; weights as bf16
+//         hi and lo parts).
 // Split segments leave partials for combine_kernel, as in the single-query kernel.
 #pragma once
 
