@@ -204,3 +204,55 @@ def test_full_size_workload(name):
     print(f"  {name}: checking {len(samples)} sampled slots", flush=True)
     _check_codes(st, cache, w, samples)
     sys.stdout.flush()
+
+
+# multi-query decode at the multi-query sweep's shape: batch 16, 32,768 tokens per sequence,
+# H_q 32 / H_kv 8, 16 causal query tokens (64 query rows per kv head: the dense kernel, with the
+# workspace and max_tokens the sweep uses)
+# (FP8 is left to the smaller cases: the oracle's E4M3 encoder takes over a minute for 32 K tokens)
+MQ_FULL = [("int4-g64", (4, 0, 0, 64)), ("int2-g64", (2, 0, 0, 64)), ("int8-g128", (8, 0, 0, 128))]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,side", MQ_FULL)
+def test_full_size_multi_query(name, side):
+    """The first and the last of sequence 0's 16 query tokens against the oracle's attention over
+    the tokens each one sees (the first 32,753 and all 32,768): query i of n_q attends the first
+    T - n_q + i + 1 cached tokens, so each is a single-query attention over a prefix."""
+    from quantized_kv_cache_07_amd import kvq
+    B, T, NQ, HQ, HKV = 16, 32768, 16, 32, 8
+    w = ki.Workload(f"mq-{name}", 13, B, HQ, HKV, T, ki.Side(*side), ki.Side(*side))
+    cap = -(-(T + 16) // 16) * 16
+    f8s = [5.0 / 448] * HKV
+    f8 = {"fp8_scales": (f8s, f8s)} if side[1] == 2 else {}
+    print(f"full-size multi-query {name}: prefill", flush=True)
+    cache = kvq.Cache(side, side, B, HKV, residual=0, capacity=cap, **f8)
+    for b in range(B):
+        k, v = ki.prefill_kv(w, b, T, device="cuda")
+        kvq.quantize_append(cache, k[None].contiguous(), v[None].contiguous(), desc=cache.sequence(b))
+    q = torch.stack([ki.queries(w, i, "cuda") for i in range(NQ)], dim=1).contiguous()
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    ws = torch.empty(kvq.workspace_bytes_mq(cache, HQ, NQ, T), dtype=torch.uint8, device="cuda")
+    kvq.decode_attention_mq(cache, q, T, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    assert kvq.read_error(cache) == 0
+    got = out[0].cpu().numpy()
+    qb = ki.bf16_bits(q[0])
+    del cache
+    torch.cuda.empty_cache()
+    # the oracle replays sequence 0 up to each query's own token
+    ocap = -(-(T + 64) // 64) * 64
+    scales = {"k_fp8_scale": np.float32(f8s), "v_fp8_scale": np.float32(f8s)} if side[1] == 2 else {}
+    seq = oracle.Sequence(side, side, HKV, 0, ocap, **scales)
+    done = 0
+    for i, n_seen in ((0, T - NQ + 1), (NQ - 1, T)):
+        print(f"  {name}: oracle replay to {n_seen} tokens (query {i})", flush=True)
+        while done < n_seen:
+            n = min(16384 - done % 16384, n_seen - done)
+            k, v = ki.prefill_kv(w, 0, n, device="cpu", t0=done)
+            seq.append(ki.bf16_bits(k), ki.bf16_bits(v))
+            done += n
+        ref = seq.attend(qb[i], SM_SCALE)
+        err = np.abs(got[i] - ref)
+        ok = err <= ATOL + RTOL * np.abs(ref)
+        assert ok.all(), (name, i, f"{int((~ok).sum())} outside tolerance, max {err.max():.3e}")
