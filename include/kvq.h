@@ -183,8 +183,7 @@ size_t kvq_buffer_bytes(const kvq_format *fmt, int32_t batch, int32_t n_kv_heads
  * 32/64/128; per-channel grouping for keys only (contiguous or paged), with residual > 0
  * divisible by the group; FP8 and bits 16 as described above, on both sides (one side FP8 or
  * BF16 and the other not: KVQ_ENOTSUP).  Keys and values of different integer formats are
- * served by single-query decode (kvq_decode_attention_mq with n_q > 1 returns KVQ_ENOTSUP for
- * them).  Pure host code. */
+ * served by single-query and multi-query decode alike.  Pure host code. */
 kvq_status kvq_check_format(const kvq_format *fmt);
 
 /* Append n_new >= 1 new tokens to every sequence of the batch.
@@ -253,14 +252,16 @@ size_t kvq_decode_workspace_bytes_mq(const kvq_cache *cache, int32_t n_q_heads, 
  * so quickly", attention equation, one row per query; P3, "Step 3: Deploy a Fallback-Capable FP8
  * First": prefill-heavy workloads gain least].  The K/V tiles streamed from HBM are dequantized
  * once per block of query rows and multiplied against all of them on the matrix cores.  With 32
- * or more query rows per kv head (n_q * n_q_heads / n_kv_heads; 16 for 8-bit codes) on a cache
- * whose two sides share one format (2/4/8-bit with per-token key groups of 32, 64 or 128, FP8
- * E4M3 or BF16), one pass over the codes serves up to 64 rows: the values are dequantized once
+ * or more query rows per kv head (n_q * n_q_heads / n_kv_heads; 16 for 8- and 16-bit codes) on a
+ * cache whose two sides share one format (2/4/8-bit with per-token key groups of 32, 64 or 128,
+ * FP8 E4M3 or BF16), one pass over the codes serves up to 64 rows: the values are dequantized once
  * per workgroup to f16 (FP8 exactly; BF16 values are used as stored) and the weights rounded to
  * f16 (each within 2^-11 relative; BF16: bf16 hi + lo parts; the result stays within
  * 2e-3 + 1e-2 |ref| of the exact attention over the dequantized cache).
  * Formats beyond kvq_decode_attention's column limits (for example key groups of 32 with G = 8)
- * take that path from 16 rows on (n_q * G >= 16) instead of returning KVQ_ENOTSUP.  Environment
+ * take that path from 16 rows on (n_q * G >= 16) instead of returning KVQ_ENOTSUP.  Keys and
+ * values of different formats, and per-channel keys, run on the blocks of query rows (at most 8
+ * rows, 16 QK columns and 32 PV rows per block; beyond that KVQ_ENOTSUP).  Environment
  * KVQ_MQ_DENSE=0 turns that path off.
  *   q:   bf16 [batch][n_q][n_q_heads][head_dim], device, 16-byte aligned
  *   out: fp32 [batch][n_q][n_q_heads][head_dim], device

@@ -1777,16 +1777,21 @@ hipError_t launch_decode_bits(const DecodeParams& p, int G, int NP, bool kpc, hi
   }
 }
 
-// Keys and values in different integer formats (bits and/or scheme): single-query decode only
-// (multi-query calls on such caches return KVQ_ENOTSUP on the host).  One translation unit per
-// key format instantiates the value formats that differ from it.
+// Keys and values in different integer formats (bits and/or scheme): single-query decode and the
+// three multi-query modes, as for one format.
 template <int KB, int SCH>
 hipError_t launch_decode_mixed(const DecodeParams& p, int vb, int vsch, int G, int NP, bool kpc,
                                hipStream_t s) {
-  if (p.nqt > 1) return hipErrorInvalidValue;
-#define KVQ_VFMT(VBB, VS)                                                      \
-  if constexpr (VBB != KB || VS != SCH)                                        \
-    if (vb == VBB && vsch == VS) return launch_decode_mq<KB, SCH, 0, VBB, VS>(p, G, NP, kpc, s);
+#define KVQ_VFMT(VBB, VS)                                                        \
+  if constexpr (VBB != KB || VS != SCH)                                          \
+    if (vb == VBB && vsch == VS) {                                               \
+      if (p.nqt <= 1) return launch_decode_mq<KB, SCH, 0, VBB, VS>(p, G, NP, kpc, s); \
+      switch (p.qpw) {                                                           \
+        case 4: return launch_decode_mq<KB, SCH, 2, VBB, VS>(p, G, NP, kpc, s);  \
+        case 2: return launch_decode_mq<KB, SCH, 3, VBB, VS>(p, G, NP, kpc, s);  \
+        default: return launch_decode_mq<KB, SCH, 1, VBB, VS>(p, G, NP, kpc, s); \
+      }                                                                          \
+    }
   KVQ_VFMT(2, KVQ_SYM)
   KVQ_VFMT(2, KVQ_ASYM)
   KVQ_VFMT(4, KVQ_SYM)

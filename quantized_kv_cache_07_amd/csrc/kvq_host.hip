@@ -497,7 +497,6 @@ kvq_status kvq_decode_attention_mq(const kvq_cache* cache, const void* q, int32_
     return e == hipSuccess ? KVQ_OK : KVQ_ELAUNCH;
   }
   if (mixed_format(cache->fmt)) {
-    if (n_q > 1) return KVQ_ENOTSUP;  // multi-query decode: keys and values in one format only
     const int vb = cache->fmt.v.bits, vs = cache->fmt.v.scheme;
     switch (cache->fmt.k.bits) {
       case 2: e = asym ? launch_decode_mixed_k2a(p, vb, vs, G, NP, kpc, st) : launch_decode_mixed_k2s(p, vb, vs, G, NP, kpc, st); break;

@@ -142,10 +142,10 @@ def test_host_errors_return_before_launch(K):
     assert L.kvq_decode_attention(ctypes.byref(d2), 0x1000, 16, 0.1, 1000, 0x2000, 0x3000, 1 << 40,
                                   None) == 2      # 4 key groups x 8 heads > 16 MFMA columns
     d3 = fake_cache(K)
-    d3.fmt = K.make_format((8, 0, 0, 64), (4, 0, 0, 64), 32)
-    ws3 = L.kvq_decode_workspace_bytes_mq(ctypes.byref(d3), 8, 4, 1000)
-    assert L.kvq_decode_attention_mq(ctypes.byref(d3), 0x1000, 4, 8, 0.1, 1000, 0x2000, 0x3000, ws3,
-                                     None) == 2   # multi-query over mixed K/V formats
+    d3.fmt = K.make_format((4, 0, 0, 32), (8, 0, 0, 64), 32)
+    ws3 = L.kvq_decode_workspace_bytes_mq(ctypes.byref(d3), 16, 4, 1000)
+    assert L.kvq_decode_attention_mq(ctypes.byref(d3), 0x1000, 4, 16, 0.1, 1000, 0x2000, 0x3000, ws3,
+                                     None) == 2   # mixed K/V formats: 4 key groups x 8 heads > 16 columns
     assert L.kvq_status_str(6).startswith(b"KVQ_EDEVICE")
 
 

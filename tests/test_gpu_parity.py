@@ -349,6 +349,13 @@ MQ_CASES = [
     ("mq-int4-gqa4-two-blocks", SYM4, SYM4, 2, 8, 2, 32, [777, 190], False, 4),
     ("mq-kivi-int2-three-blocks", KPC2, ASYM2_32, 2, 8, 2, 128, [700, 1300], False, 3),
     ("mq-asym4-paged-two-blocks", ASYM4_32, ASYM4_32, 2, 4, 2, 16, [250, 999], True, 3),
+    # keys and values in different formats (query blocks of the blocked kernel: four blocks of one
+    # wave, two of two waves, one of four)
+    ("mq-mix-k8-v4-gqa4-window", SYM8, SYM4, 2, 8, 2, 32, [777, 190], False, 16),
+    ("mq-mix-k4-v2asym-paged", SYM4, ASYM2_32, 3, 8, 2, 16, [500, 77, 1000], True, 3),
+    ("mq-mix-kivi2-v4sym", KPC2, SYM4, 2, 8, 2, 128, [700, 1300], False, 2),
+    ("mq-mix-k2-v8asym-mha", (2, 0, 0, 32), (8, 1, 0, 64), 2, 4, 4, 0, [300, 1031], False, 5),
+    ("mq-mix-k4asym-v8-gqa8-paged", (4, 1, 0, 64), SYM8, 1, 16, 2, 16, [600], True, 4),
     # the dense kernel: 16 query rows per wave, four blocks per workgroup (key groups of 64 or
     # 128); it takes 64 or more rows per kv head by itself, and these cases force it from 16 rows
     # on (KVQ_MQ_DENSE=1) for idle waves, partial blocks and segments split over workgroups

@@ -9,7 +9,12 @@ the case index, so a failure names a reproducible case.
 A second set of 24 draws goes through the dense multi-query kernel (forced from 16 query rows
 per kv head): one format on both sides (2/4/8 bits, symmetric or asymmetric, per-token key
 groups of 32/64/128; some draws FP8 E4M3 or BF16), GQA 1/2/4/8, 16-96 query rows per kv head,
-windows, lengths 0-400, contiguous or paged."""
+windows, lengths 0-400, contiguous or paged.
+
+A third set of 24 draws takes the first set's formats and shapes (keys and values in independent
+formats, per-channel keys included) through multi-query decode with 2-12 query tokens per
+sequence (the blocked kernel's query blocks; the dense kernel where one format with enough rows
+takes it)."""
 from __future__ import annotations
 
 import sys
@@ -109,6 +114,20 @@ def test_random_dense_multi_query(i, monkeypatch):
     pr = kc.build_pair(side, side, B, Hq, H, R, lens, paged=paged, seed=700 + i,
                        extra_tokens=64 + n_q)
     for _ in range(min(n_q, 8)):  # the last query tokens are appended (windows flush where due)
+        kc.step(pr)
+    kc.compare_state(pr)
+    kc.compare_attention_mq(pr, n_q)
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_multi_query(i):
+    k, v, B, Hq, H, R, lens, paged = draw(3000 + i)
+    n_q = int(np.random.default_rng(8800 + i).integers(2, 13))
+    lens[0] = max(lens[0], n_q)
+    print("case:", i, dict(k=k, v=v, B=B, Hq=Hq, H=H, R=R, lens=lens, paged=paged, n_q=n_q),
+          flush=True)
+    pr = kc.build_pair(k, v, B, Hq, H, R, lens, paged=paged, seed=900 + i, extra_tokens=64 + n_q)
+    for _ in range(min(n_q, 4)):  # the last query tokens are appended (windows flush where due)
         kc.step(pr)
     kc.compare_state(pr)
     kc.compare_attention_mq(pr, n_q)
