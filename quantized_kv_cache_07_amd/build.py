@@ -50,8 +50,12 @@ def build(verbose: bool = True, qk_valu: bool = False) -> str:
     build_dir, lib = (BUILD + "_qkvalu", LIB_QK_VALU) if qk_valu else (BUILD, LIB)
     defines = ("KVQ_QK_VALU=1",) if qk_valu else ()
     os.makedirs(build_dir, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, build_dir, defines), SOURCES))
+    # one hipcc per core, the largest translation units (the mixed-format kernels) first; each
+    # takes a few GB, so one process per source at once could exhaust a small host's memory
+    order = sorted(SOURCES, key=lambda s: not s.startswith("kvq_decode_mix"))
+    with cf.ThreadPoolExecutor(max_workers=max(1, min(len(SOURCES), os.cpu_count() or 8))) as ex:
+        done = dict(zip(order, ex.map(lambda s: _compile(s, build_dir, defines), order)))
+    objs = [done[s] for s in SOURCES]
     tmp = lib + ".tmp"
     r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs],
                        capture_output=True, text=True)
