@@ -256,3 +256,40 @@ def test_full_size_multi_query(name, side):
         err = np.abs(got[i] - ref)
         ok = err <= ATOL + RTOL * np.abs(ref)
         assert ok.all(), (name, i, f"{int((~ok).sum())} outside tolerance, max {err.max():.3e}")
+
+
+@pytest.mark.timeout(900)
+def test_full_size_multi_query_kivi():
+    """Multi-query decode on the KIVI layer's layout (batch 16, 32,768 tokens per sequence,
+    H_q 32 / H_kv 8, 2-bit asymmetric keys per channel over 32 tokens and values per token in
+    groups of 32, a 128-token BF16 window): 4 causal query tokens per sequence (16 rows per kv
+    head, the blocked kernel's four one-wave blocks), all of sequence 0's outputs against the
+    oracle."""
+    from quantized_kv_cache_07_amd import kvq
+    B, T, NQ, HQ, HKV, R = 16, 32768, 4, 32, 8, 128
+    ks, vs = (2, 1, 1, 32), (2, 1, 0, 32)
+    w = ki.Workload("mq-kivi", 14, B, HQ, HKV, T, ki.Side(*ks), ki.Side(*vs), residual=R)
+    cap = -(-(T + R + 16) // 32) * 32  # per-channel keys: a multiple of the 32-token key group
+    print("full-size multi-query kivi: prefill", flush=True)
+    cache = kvq.Cache(ks, vs, B, HKV, residual=R, capacity=cap)
+    for b in range(B):
+        k, v = ki.prefill_kv(w, b, T, device="cuda")
+        kvq.quantize_append(cache, k[None].contiguous(), v[None].contiguous(), desc=cache.sequence(b))
+    q = torch.stack([ki.queries(w, i, "cuda") for i in range(NQ)], dim=1).contiguous()
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    ws = torch.empty(kvq.workspace_bytes_mq(cache, HQ, NQ, T), dtype=torch.uint8, device="cuda")
+    kvq.decode_attention_mq(cache, q, T, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    assert kvq.read_error(cache) == 0
+    nq_dev, nr_dev = cache.n_quant.cpu().tolist(), cache.n_res.cpu().tolist()
+    got = out[0].cpu().numpy()
+    qb = ki.bf16_bits(q[0])
+    del cache
+    torch.cuda.empty_cache()
+    print("  kivi: oracle replay of sequence 0", flush=True)
+    seq = _replay(w, 0, T, [])
+    assert (seq.n_quant, seq.n_res) == (nq_dev[0], nr_dev[0])
+    ref = seq.attend_mq(qb, SM_SCALE)
+    err = np.abs(got - ref)
+    ok = err <= ATOL + RTOL * np.abs(ref)
+    assert ok.all(), ("kivi multi-query", f"{int((~ok).sum())} outside tolerance, max {err.max():.3e}")
